@@ -1,0 +1,183 @@
+"""CPU oracle for packed variable-length QK rotary position embedding.
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
+CPU-baseline leg are the only callers. The product path (the HIP library and
+its Python binding) never imports this package.
+
+The arithmetic lives in ``rope_oracle.c`` (plain C, fp64/long double); this
+module only marshals numpy arrays through ctypes. See that file's header for
+the pages each function follows and the readings taken where they are silent.
+
+``Oracle(path)`` wraps one build of the C file (the mutation tests load
+deliberately broken builds made on the CPU); the module-level functions use
+the default build, ``oracle/librope_oracle.so``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+F32, BF16, F16 = 0, 1, 2
+_DTYPES = {"f32": F32, "bf16": BF16, "f16": F16}
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _i32(a):
+    return None if a is None else np.ascontiguousarray(a, dtype=np.int32)
+
+
+def _storage(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Element storage for the C side: float32 for f32, raw 16-bit words otherwise."""
+    if dtype == "f32":
+        return np.ascontiguousarray(x, dtype=np.float32)
+    if x.dtype not in (np.uint16, np.int16):
+        raise TypeError("bf16/f16 inputs are passed as their raw 16-bit words")
+    return np.ascontiguousarray(x).view(np.uint16)
+
+
+class Oracle:
+    def __init__(self, path: str):
+        lib = ctypes.CDLL(path)
+        i32, i64, dbl = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
+        vp = ctypes.c_void_p
+        lib.oracle_inv_freq.argtypes = [dbl, i32, vp]
+        lib.oracle_inv_freq.restype = None
+        lib.oracle_cos_sin.argtypes = [vp, i64, i32, dbl, vp, vp]
+        lib.oracle_cos_sin.restype = None
+        lib.oracle_positions.argtypes = [vp, i32, vp, i64, vp, vp]
+        lib.oracle_positions.restype = None
+        lib.oracle_rope.argtypes = [i32, vp, vp, i64, i32, i32, vp, i32, vp, dbl, i32, i32]
+        lib.oracle_rope.restype = i32
+        lib.oracle_rope_rows.argtypes = [i32, vp, vp, vp, i64, i32, i32, vp, i32, vp, dbl, i32,
+                                         i32]
+        lib.oracle_rope_rows.restype = i32
+        lib.oracle_round_bf16.argtypes = [vp, vp, i64]
+        lib.oracle_round_bf16.restype = None
+        lib.oracle_fwd_bwd_seconds.argtypes = [i32, vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, i32,
+                                               i32, vp, i32, vp, dbl, i32]
+        lib.oracle_fwd_bwd_seconds.restype = dbl
+        self.lib = lib
+        self.path = path
+
+    def inv_freq(self, theta: float, D: int) -> np.ndarray:
+        out = np.empty(D // 2, dtype=np.float32)
+        self.lib.oracle_inv_freq(float(theta), int(D), _ptr(out))
+        return out
+
+    def cos_sin(self, positions, D: int, theta: float):
+        pos = _i32(np.atleast_1d(positions))
+        c = np.empty((pos.size, D // 2), dtype=np.float32)
+        s = np.empty_like(c)
+        self.lib.oracle_cos_sin(_ptr(pos), pos.size, int(D), float(theta), _ptr(c), _ptr(s))
+        return c, s
+
+    def positions(self, cu_seqlens, T: int, seqused=None):
+        cu = _i32(cu_seqlens)
+        su = _i32(seqused)
+        pos = np.empty(int(T), dtype=np.int32)
+        seq = np.empty(int(T), dtype=np.int32)
+        self.lib.oracle_positions(_ptr(cu), cu.size - 1, _ptr(su), int(T), _ptr(pos), _ptr(seq))
+        return pos, seq
+
+    def rope(self, x: np.ndarray, cu_seqlens, theta: float, direction: int = 1,
+             dtype: str = "f32", seqused=None, nthreads: int = 1) -> np.ndarray:
+        """Rotate a packed tensor x[T, H, D]; returns the fp32 result, same shape."""
+        xs = _storage(x, dtype)
+        T, H, D = xs.shape
+        cu, su = _i32(cu_seqlens), _i32(seqused)
+        y = np.empty((T, H, D), dtype=np.float32)
+        rc = self.lib.oracle_rope(_DTYPES[dtype], _ptr(xs), _ptr(y), T, H, D, _ptr(cu),
+                                  cu.size - 1, _ptr(su), float(theta), int(direction),
+                                  int(nthreads))
+        if rc != 0:
+            raise ValueError("oracle_rope rejected its arguments")
+        return y
+
+    def rope_rows(self, x_rows: np.ndarray, tokens, cu_seqlens, theta: float, direction: int = 1,
+                  dtype: str = "f32", seqused=None, nthreads: int = 1) -> np.ndarray:
+        """Outputs for the listed tokens only; x_rows[n, H, D] are their input rows."""
+        xs = _storage(x_rows, dtype)
+        n, H, D = xs.shape
+        tok = np.ascontiguousarray(tokens, dtype=np.int64)
+        if tok.size != n:
+            raise ValueError("one token index per input row")
+        cu, su = _i32(cu_seqlens), _i32(seqused)
+        y = np.empty((n, H, D), dtype=np.float32)
+        rc = self.lib.oracle_rope_rows(_DTYPES[dtype], _ptr(xs), _ptr(y), _ptr(tok), n, H, D,
+                                       _ptr(cu), cu.size - 1, _ptr(su), float(theta),
+                                       int(direction), int(nthreads))
+        if rc != 0:
+            raise ValueError("oracle_rope_rows rejected its arguments")
+        return y
+
+    def round_bf16(self, y: np.ndarray) -> np.ndarray:
+        """fp32 -> bf16 bits (uint16), round to nearest even."""
+        ys = np.ascontiguousarray(y, dtype=np.float32)
+        out = np.empty(ys.shape, dtype=np.uint16)
+        self.lib.oracle_round_bf16(_ptr(ys), _ptr(out), ys.size)
+        return out
+
+    def fwd_bwd_seconds(self, q, k, dq, dk, cu_seqlens, theta: float, dtype: str, seqused=None,
+                        nthreads: int = 1) -> float:
+        """Wall time of the oracle's forward on (q, k) plus backward on (dq, dk)."""
+        qs, ks, dqs, dks = (_storage(a, dtype) for a in (q, k, dq, dk))
+        T, Hq, D = qs.shape
+        Hkv = ks.shape[1]
+        outs = [np.empty(a.shape, dtype=np.float32) for a in (qs, ks, dqs, dks)]
+        cu, su = _i32(cu_seqlens), _i32(seqused)
+        sec = self.lib.oracle_fwd_bwd_seconds(_DTYPES[dtype], _ptr(qs), _ptr(ks), _ptr(dqs),
+                                              _ptr(dks), *(_ptr(o) for o in outs), T, Hq, Hkv, D,
+                                              _ptr(cu), cu.size - 1, _ptr(su), float(theta),
+                                              int(nthreads))
+        if sec < 0:
+            raise ValueError("oracle rejected its arguments")
+        return sec
+
+
+_default: Oracle | None = None
+
+
+def default() -> Oracle:
+    global _default
+    if _default is None:
+        if not os.path.exists(_build.LIB_PATH):
+            _build.build()
+        _default = Oracle(_build.LIB_PATH)
+    return _default
+
+
+def inv_freq(theta, D):
+    return default().inv_freq(theta, D)
+
+
+def cos_sin(positions, D, theta):
+    return default().cos_sin(positions, D, theta)
+
+
+def positions(cu_seqlens, T, seqused=None):
+    return default().positions(cu_seqlens, T, seqused)
+
+
+def rope(x, cu_seqlens, theta, direction=1, dtype="f32", seqused=None, nthreads=1):
+    return default().rope(x, cu_seqlens, theta, direction, dtype, seqused, nthreads)
+
+
+def rope_rows(x_rows, tokens, cu_seqlens, theta, direction=1, dtype="f32", seqused=None,
+              nthreads=1):
+    return default().rope_rows(x_rows, tokens, cu_seqlens, theta, direction, dtype, seqused,
+                               nthreads)
+
+
+def round_bf16(y):
+    return default().round_bf16(y)
+
+
+def fwd_bwd_seconds(q, k, dq, dk, cu_seqlens, theta, dtype, seqused=None, nthreads=1):
+    return default().fwd_bwd_seconds(q, k, dq, dk, cu_seqlens, theta, dtype, seqused, nthreads)

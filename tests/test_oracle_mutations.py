@@ -1,0 +1,63 @@
+"""Plants plausible mistakes in copies of the oracle's C source (on the CPU),
+builds each copy, and checks that at least one pin fails for every mistake:
+evidence that the pins constrain every part of the oracle."""
+import os
+
+import pytest
+
+import oracle
+from oracle import build as obuild
+from oracle_checks import ALL_CHECKS
+
+SRC = open(obuild.SRC).read()
+
+# (name, text in rope_oracle.c, replacement)
+MUTATIONS = [
+    ("y1_sign", "double y1 = x1 * c - x2 * s;", "double y1 = x1 * c + x2 * s;"),
+    ("y2_sign", "double y2 = x2 * c + x1 * s;", "double y2 = x2 * c - x1 * s;"),
+    ("transposed_rotation", "double s = (double)dir * (double)sn[j];",
+     "double s = -(double)dir * (double)sn[j];"),
+    ("backward_not_negated", "double s = (double)dir * (double)sn[j];",
+     "double s = (double)sn[j];"),
+    ("interleaved_pairing", "double x2 = load_elem(dtype, x, row_off + j + half);",
+     "double x2 = load_elem(dtype, x, row_off + (j ^ 1));"),
+    ("swapped_halves_store", "y_row[j + half] = (float)y2;", "y_row[j + half] = (float)y1;"),
+    ("exponent_missing_2", "long double e = -(2.0L * (long double)j) / (long double)D;",
+     "long double e = -((long double)j) / (long double)D;"),
+    ("exponent_over_D_minus_2", "long double e = -(2.0L * (long double)j) / (long double)D;",
+     "long double e = -(2.0L * (long double)j) / (long double)(D - 2 > 0 ? D - 2 : 1);"),
+    ("inv_freq_fp32_pow", "out[j] = (float)powl((long double)theta, e);",
+     "out[j] = powf((float)theta, (float)e);"),
+    ("angle_in_double", "*c = (float)cosl((long double)angle);",
+     "*c = (float)cosl((long double)pos * (long double)inv_freq_j);"),
+    ("cos_sin_swapped", "*c = (float)cosl((long double)angle);", "*c = (float)sinl((long double)angle);"),
+    ("cos_fp32_libm", "*c = (float)cosl((long double)angle);", "*c = cosf(angle);"),
+    ("rotation_in_fp32", "double y1 = x1 * c - x2 * s;",
+     "double y1 = (double)((float)x1 * (float)c - (float)x2 * (float)s);"),
+    ("positions_not_reset", "cos_sin_one((int32_t)p, inv_freq[j], &cs[j], &sn[j]);",
+     "cos_sin_one((int32_t)t, inv_freq[j], &cs[j], &sn[j]);"),
+    ("positions_from_1", "if (pos_out) pos_out[t] = (int32_t)p;", "if (pos_out) pos_out[t] = (int32_t)p + 1;"),
+    ("seqused_ignored", "if (seqused && (int64_t)seqused[s] < len) len = seqused[s];", ""),
+    ("row_walk_off_by_one", "if (p >= 0 && p < used_len(cu, seqused, s)) return (int32_t)p;",
+     "if (p >= 0 && p <= used_len(cu, seqused, s)) return (int32_t)p;"),
+    ("bf16_ties_not_even", "if (rest > 0x8000u || (rest == 0x8000u && (keep & 1u))) keep += 1u;",
+     "if (rest >= 0x8000u) keep += 1u;"),
+    ("bf16_truncates", "if (rest > 0x8000u || (rest == 0x8000u && (keep & 1u))) keep += 1u;", ""),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_planted_mistake_is_caught(name, old, new, tmp_path):
+    assert SRC.count(old) == 1, f"mutation site for {name} not found exactly once"
+    src = tmp_path / f"mut_{name}.c"
+    src.write_text(SRC.replace(old, new))
+    lib = obuild.build(str(src), str(tmp_path / f"libmut_{name}.so"))
+    o = oracle.Oracle(lib)
+    failed = []
+    for check in ALL_CHECKS:
+        try:
+            check(o)
+        except AssertionError:
+            failed.append(check.__name__)
+            break
+    assert failed, f"planted mistake {name!r} passed every pin"
