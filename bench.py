@@ -1,0 +1,232 @@
+"""Benchmark: fused packed-varlen QK-RoPE, forward + backward, on one MI355X.
+
+One step = forward RoPE on (Q, K) plus backward RoPE on (dQ, dK) of one packed
+batch: two launches of the fused kernel, every row of the hot path. Default
+workload: the Qwen3-4B-shaped packed batch (T = 16384 tokens from an 80% short /
+20% long length mix, Hq = 32, Hkv = 8, D = 128, bf16, theta = 1e6).
+
+Inputs are synthetic, seeded and resident in HBM before timing starts. Several
+buffer sets are rotated so that the working set between two touches of the
+same buffer exceeds the 256 MB Infinity Cache: every launch reads and writes
+HBM, as a training step would.
+
+Prints ONE JSON line (rank 0). `value` is tokens/s of whole steps (wall clock
+around K steps, bracketed by synchronize). `roofline` uses the kernel's average
+launch duration from HIP events recorded on the launch stream around each
+launch in the timed region; `traffic` comes from the committed rocprofv3 PMC
+summary when it was taken on the current kernel source, else null.
+`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+import workloads  # noqa: E402
+
+METRIC = "fused QK-RoPE fwd+bwd tokens/s and achieved HBM GB/s (% of peak), packed bf16"
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+INFINITY_CACHE_BYTES = 256 * 2 ** 20
+KERNEL_SRC = os.path.join(ROOT, "packed_varlen_rotary_rope_amd", "csrc")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "rope_qk_qwen3_4b_packed_traffic.txt")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(KERNEL_SRC)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(KERNEL_SRC, name), "rb") as fh:
+                h.update(name.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes_per_launch(w: workloads.Workload) -> int:
+    """One read and one write of every rotated element of Q and K (or dQ and dK)."""
+    return 2 * w.valid_tokens * (w.Hq + w.Hkv) * w.D * w.elem_bytes
+
+
+def read_traffic(bytes_per_launch: int):
+    """HBM bytes per launch from the committed PMC summary, if it matches this source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        m = re.match(r"^\s*([a-z_]+)\s*[:=]\s*(\S+)", line)
+        if m:
+            kv[m.group(1)] = m.group(2)
+    if kv.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return int(float(kv["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def make_sets(w, nsets, dev):
+    cu = torch.from_numpy(w.cu_seqlens).to(dev)
+    su = None if w.seqused is None else torch.from_numpy(w.seqused).to(dev)
+    sets = []
+    for i in range(nsets):
+        sets.append({what: workloads.make_tensor(w.shape(what), w.seed(what) + 100 * i, w.dtype,
+                                                 device=dev, chunk_rows=65536)
+                     for what in ("q", "k", "dq", "dk")})
+    return cu, su, sets
+
+
+def cpu_baseline(w, budget_s: float, nthreads: int):
+    """The oracle, as it stands, on the same workload: whole fwd+bwd passes over the
+    batch, repeated until about budget_s seconds of work have been timed."""
+    import oracle
+
+    host = {what: workloads.host_bits(workloads.make_tensor(w.shape(what), w.seed(what), w.dtype))
+            for what in ("q", "k", "dq", "dk")}
+    total, reps = 0.0, 0
+    while total < budget_s and reps < 100:
+        total += oracle.fwd_bwd_seconds(host["q"], host["k"], host["dq"], host["dk"],
+                                        w.cu_seqlens, w.theta, w.dtype, w.seqused, nthreads)
+        reps += 1
+    return {
+        "value": w.valid_tokens * reps / total,
+        "unit": "tokens/s",
+        "cores": nthreads,
+        "kind": "oracle",
+        "sample": f"{reps} full fwd+bwd passes over the {w.name} batch "
+                  f"({w.valid_tokens} tokens, Q/K/dQ/dK), {total:.1f} s timed",
+    }
+
+
+def copy_calibration(gib: float, reps: int):
+    """A plain device copy of known size, for scaling PMC byte counters."""
+    n = int(gib * 2 ** 30) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n * 4, "copy_calibration_bytes_written": n * 4,
+                      "reps": reps}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="qwen3_4b_packed", choices=workloads.names())
+    ap.add_argument("--heads-per-group", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="timed oracle work for cpu_baseline (0 disables it)")
+    ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
+                    help="only run a plain copy of this many GiB (PMC scale factor), then exit")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE={world}). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration > 0:
+        copy_calibration(args.copy_calibration, 5)
+        return
+
+    import packed_varlen_rotary_rope_amd as rope
+
+    dev = torch.device("cuda:0")
+    w = workloads.get(args.workload)
+    set_bytes = 2 * w.T * (w.Hq + w.Hkv) * w.D * w.elem_bytes  # Q, K, dQ, dK
+    nsets = max(2, math.ceil(4 * INFINITY_CACHE_BYTES / set_bytes))
+    cu, su, sets = make_sets(w, nsets, dev)
+    hpg = args.heads_per_group
+
+    def step(s, ev=None):
+        if ev is not None:
+            ev[0].record()
+        rope.qk_apply_(s["q"], s["k"], cu, w.theta, 1, seqused=su, heads_per_group=hpg)
+        if ev is not None:
+            ev[1].record()
+            ev[2].record()
+        rope.qk_apply_(s["dq"], s["dk"], cu, w.theta, -1, seqused=su, heads_per_group=hpg)
+        if ev is not None:
+            ev[3].record()
+
+    for i in range(args.warmup):
+        step(sets[i % nsets])
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(sets[i % nsets], events[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    launch_ms = []
+    for ev in events:
+        launch_ms.append(ev[0].elapsed_time(ev[1]))
+        launch_ms.append(ev[2].elapsed_time(ev[3]))
+    avg_launch_s = float(np.mean(launch_ms)) / 1e3
+    bpl = algorithmic_bytes_per_launch(w)
+    achieved = bpl / avg_launch_s / 1e9
+    tokens_per_step = w.valid_tokens
+    value = tokens_per_step * args.steps / elapsed
+    ms_per_step = elapsed / args.steps * 1e3
+    traffic = read_traffic(bpl)
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) Q/K/dQ/dK, seeded length draws)",
+        "config": {
+            "workload": w.name,
+            "T": w.T, "valid_tokens": w.valid_tokens, "num_seqs": w.num_seqs,
+            "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D, "theta": w.theta,
+            "buffer_sets": nsets, "heads_per_group": hpg or (w.Hq + w.Hkv),
+        },
+        "step_hbm_GBps": 2 * bpl * args.steps / elapsed / 1e9,
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS,
+            "traffic": traffic,
+            "kernel": "rope_qk_kernel",
+            "bytes_per_launch": bpl,
+            "avg_launch_us": avg_launch_s * 1e6,
+            "min_launch_us": float(np.min(launch_ms)) * 1e3,
+        },
+    }
+    if args.cpu_seconds > 0:
+        nthreads = max(1, min(16, len(os.sched_getaffinity(0))))
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, nthreads)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,143 @@
+/*
+ * rope_qk.h -- C ABI of the fused, in-place, packed variable-length QK rotary
+ * position embedding (RoPE) library for AMD Instinct MI355X (gfx950).
+ *
+ * What the operation is (web pages cited by title and section):
+ *  - Unsloth, "Entrainement des LLM 3 fois plus rapide avec les noyaux Unsloth +
+ *    le packing", section "Kernel Triton QK RoPE fusionne avec packing": one
+ *    kernel rotates both Q and K, in place, as x*cos + rotate_half(x)*sin, where
+ *    rotate_half(x) = x @ R and R = [[0, I], [-I, 0]]; the backward pass applies
+ *    R transposed, which is the same rotation with sin negated. Variable-length
+ *    (packed) batches are supported.
+ *  - same page, section "Packing non contamine", and Databricks, "Reduire le
+ *    temps d'entrainement de Qwen de 6x sur AI Runtime", section "Mise en lots,
+ *    tokenisation et padding": samples are packed into one token dimension and
+ *    the RoPE positions restart at every sample, so no sample sees another's
+ *    positions.
+ *  - same Unsloth page, section "Indexage int64 pour les kernels Triton": 64-bit
+ *    offsets are compiled in only where the tensors need them.
+ *  - TRL guide "Entrainement au-dela de 1 M de jetons", YaRN section: theta is
+ *    the model's rope_theta (1e6 for Qwen3).
+ *
+ * Semantics. Q is [T, Hq, D] and K is [T, Hkv, D], row-major and contiguous, in
+ * one dtype. Token t belongs to sequence s when cu_seqlens[s] <= t <
+ * cu_seqlens[s+1]; its position is p = t - cu_seqlens[s]. Tokens before
+ * cu_seqlens[0], at or after cu_seqlens[num_seqs], or with p >= seqused[s] (when
+ * seqused is given) are left bit-for-bit untouched. For every other token,
+ * every head and every j < D/2:
+ *     inv_freq[j] = theta^(-2j/D) rounded once to fp32
+ *     a = fp32(p) * inv_freq[j]                      (one fp32 multiply)
+ *     c, s = cos(a), sin(a) correctly rounded to fp32; s is negated backward
+ *     x1 = X[t,h,j], x2 = X[t,h,j+D/2]  (widened to fp32)
+ *     X[t,h,j]       = round(x1*c - x2*s)
+ *     X[t,h,j+D/2]   = round(x2*c + x1*s)
+ * where the products are formed with an FMA-compensated (Kahan) scheme, so the
+ * fp32 value is within 2 fp32 ulps of the exact real result before it is rounded
+ * to the storage dtype (round to nearest even).
+ *
+ * Ownership and threading. The caller owns every buffer. The library allocates
+ * nothing, keeps no state between calls, never synchronizes and never reads
+ * device memory from the host. Calls only enqueue work on `stream` (a
+ * hipStream_t; NULL means the null stream) and return. Calls on different
+ * streams are independent; the library is reentrant.
+ *
+ * Errors. Arguments are validated on the host before any HIP call; a rejected
+ * call enqueues nothing. A launch failure reported by hipGetLastError maps to
+ * ROPE_ELAUNCH. Faults during execution surface at the caller's next
+ * synchronization. Not validated (undefined behaviour): the contents of
+ * cu_seqlens (must be non-decreasing and within [0, T] for meaningful results;
+ * any contents stay memory-safe, because a work item only touches its own
+ * token's rows), and aliasing between Q and K.
+ */
+#ifndef ROPE_QK_H
+#define ROPE_QK_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ROPE_QK_ABI_VERSION 1
+
+/* Storage dtype of Q and K (computation is fp32 in every case). */
+typedef enum rope_dtype { ROPE_F32 = 0, ROPE_BF16 = 1, ROPE_F16 = 2 } rope_dtype;
+
+typedef enum rope_status {
+  ROPE_OK = 0,
+  ROPE_EINVAL = -1,       /* an argument is out of range or a required pointer is NULL */
+  ROPE_EUNSUPPORTED = -2, /* unknown dtype */
+  ROPE_ELAUNCH = -3       /* the HIP runtime rejected the launch */
+} rope_status;
+
+/* Index-width choice for rope_qk_apply. AUTO selects 64-bit offsets exactly when
+ * T * (Hq + Hkv) * D >= 2^31 (the int64 specialization), 32-bit otherwise. */
+typedef enum rope_index_mode { ROPE_INDEX_AUTO = 0, ROPE_INDEX_32 = 1, ROPE_INDEX_64 = 2 } rope_index_mode;
+
+/* Forward RoPE on Q and K in place, in one kernel launch.
+ *  q, k        device pointers to Q[T, Hq, D] and K[T, Hkv, D]; may be NULL only if
+ *              that tensor has no elements (T == 0 or its head count is 0)
+ *  T           rows (tokens) of Q and K, >= 0
+ *  Hq, Hkv     head counts, 0..4096, not both 0 unless T == 0
+ *  D           head size: even, 2..512
+ *  cu_seqlens  device int32[num_seqs + 1], cumulative sequence starts
+ *  num_seqs    >= 0; with 0 nothing is rotated and cu_seqlens may be NULL
+ *  seqused     device int32[num_seqs] or NULL: rotate only the first seqused[s]
+ *              tokens of sequence s (padded layouts)
+ *  theta       rope_theta, finite and >= 1
+ *  dtype       a rope_dtype value
+ *  stream      hipStream_t to enqueue on (NULL: null stream)
+ * Returns ROPE_OK, ROPE_EINVAL, ROPE_EUNSUPPORTED or ROPE_ELAUNCH. */
+int32_t rope_qk_fwd(void* q, void* k, int64_t T, int32_t Hq, int32_t Hkv, int32_t D,
+                    const int32_t* cu_seqlens, int32_t num_seqs, const int32_t* seqused,
+                    double theta, int32_t dtype, void* stream);
+
+/* Backward RoPE on the gradients dQ and dK in place: the transpose of the forward
+ * rotation, i.e. the forward with sin negated (Unsloth page, fused QK RoPE
+ * section). Needs only cu_seqlens and theta, no saved Q or K. Arguments as in
+ * rope_qk_fwd, with q, k replaced by dq, dk. */
+int32_t rope_qk_bwd(void* dq, void* dk, int64_t T, int32_t Hq, int32_t Hkv, int32_t D,
+                    const int32_t* cu_seqlens, int32_t num_seqs, const int32_t* seqused,
+                    double theta, int32_t dtype, void* stream);
+
+/* The general entry point behind rope_qk_fwd / rope_qk_bwd.
+ *  direction        +1 forward, -1 backward (anything else: ROPE_EINVAL)
+ *  index_mode       a rope_index_mode; ROPE_INDEX_32 is rejected (ROPE_EINVAL)
+ *                   when the tensors need 64-bit offsets
+ *  heads_per_group  0 = all Hq + Hkv heads in one group (cos/sin computed once per
+ *                   token and frequency); n > 0 splits the Q-then-K head list into
+ *                   groups of n heads handled by separate workgroups (more, shorter
+ *                   workgroups; cos/sin recomputed per group)
+ * Other arguments as in rope_qk_fwd. */
+int32_t rope_qk_apply(void* q, void* k, int64_t T, int32_t Hq, int32_t Hkv, int32_t D,
+                      const int32_t* cu_seqlens, int32_t num_seqs, const int32_t* seqused,
+                      double theta, int32_t dtype, int32_t direction, int32_t index_mode,
+                      int32_t heads_per_group, void* stream);
+
+/* Export of the token -> (position, sequence) map the kernels use (test hook,
+ * same device code). pos_out, seq_out: device int32[T] (either may be NULL);
+ * -1 for tokens that are left untouched. Validation as in rope_qk_fwd. */
+int32_t rope_positions(const int32_t* cu_seqlens, int32_t num_seqs, const int32_t* seqused,
+                       int64_t T, int32_t* pos_out, int32_t* seq_out, void* stream);
+
+/* Export of the fp32 cos/sin the kernels use (test hook, same device code):
+ * for each of the n positions in the device array positions (each >= 0) and each
+ * j < D/2, cos_out[i*(D/2) + j] and sin_out[i*(D/2) + j] (device float arrays). */
+int32_t rope_cos_sin(const int32_t* positions, int64_t n, int32_t D, double theta,
+                     float* cos_out, float* sin_out, void* stream);
+
+/* Host-only: the fp32 inverse frequencies theta^(-2j/D), j < D/2, written to the
+ * host array out[D/2]. Same validation of D and theta as rope_qk_fwd. */
+int32_t rope_inv_freq(double theta, int32_t D, float* out);
+
+/* Static description of a status code. */
+const char* rope_status_str(int32_t status);
+
+/* ROPE_QK_ABI_VERSION of the library. */
+int32_t rope_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ROPE_QK_H */

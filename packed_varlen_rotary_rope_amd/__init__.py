@@ -1,0 +1,167 @@
+"""Fused, in-place, packed variable-length QK rotary position embedding (RoPE)
+for AMD Instinct MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``include/rope_qk.h`` (librope_qk.so,
+built from ``csrc/rope_qk.hip``). This module only checks tensor metadata and
+marshals pointers, sizes and the current HIP stream; every step of the
+computation runs in the library's HIP kernels. There is no CPU fallback: if
+the library is missing, importing this package raises.
+
+The operation follows the Unsloth page "Entrainement des LLM 3 fois plus rapide
+avec les noyaux Unsloth + le packing" (section "Kernel Triton QK RoPE fusionne
+avec packing": one in-place kernel for Q and K, rotate_half form, backward =
+sin negated; section "Packing non contamine": positions restart per sample).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "RopeError", "qk_fwd_", "qk_bwd_", "qk_apply_", "positions", "cos_sin", "inv_freq",
+    "abi_version", "LIB_PATH", "INDEX_AUTO", "INDEX_32", "INDEX_64",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librope_qk.so")
+
+F32, BF16, F16 = 0, 1, 2
+INDEX_AUTO, INDEX_32, INDEX_64 = 0, 1, 2
+_DTYPE_CODE = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
+
+
+class RopeError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {_lib.rope_status_str(status).decode()} ({status})")
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python -m packed_varlen_rotary_rope_amd.build` "
+            "(hipcc, gfx950). There is no fallback implementation.")
+    lib = ctypes.CDLL(LIB_PATH)
+    i32, i64, dbl, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_double, ctypes.c_void_p
+    qk = [vp, vp, i64, i32, i32, i32, vp, i32, vp, dbl, i32]
+    lib.rope_qk_fwd.argtypes = qk + [vp]
+    lib.rope_qk_bwd.argtypes = qk + [vp]
+    lib.rope_qk_apply.argtypes = qk + [i32, i32, i32, vp]
+    lib.rope_positions.argtypes = [vp, i32, vp, i64, vp, vp, vp]
+    lib.rope_cos_sin.argtypes = [vp, i64, i32, dbl, vp, vp, vp]
+    lib.rope_inv_freq.argtypes = [dbl, i32, vp]
+    for name in ("rope_qk_fwd", "rope_qk_bwd", "rope_qk_apply", "rope_positions", "rope_cos_sin",
+                 "rope_inv_freq", "rope_abi_version"):
+        getattr(lib, name).restype = i32
+    lib.rope_status_str.argtypes = [i32]
+    lib.rope_status_str.restype = ctypes.c_char_p
+    lib.rope_abi_version.argtypes = []
+    return lib
+
+
+_lib = _load()
+
+
+def abi_version() -> int:
+    return int(_lib.rope_abi_version())
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        raise RopeError(status, what)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _index_tensor(t, name: str, device: torch.device):
+    if t is None:
+        return None
+    if t.dtype != torch.int32 or t.device != device or not t.is_contiguous():
+        raise TypeError(f"{name} must be a contiguous int32 tensor on {device}")
+    return t
+
+
+def _qk_args(q, k, cu_seqlens, seqused):
+    if q.device.type != "cuda" or k.device != q.device:
+        raise TypeError("q and k must be on the same GPU")
+    if q.dtype != k.dtype or q.dtype not in _DTYPE_CODE:
+        raise TypeError("q and k must share one dtype: float32, bfloat16 or float16")
+    if q.dim() != 3 or k.dim() != 3 or q.shape[0] != k.shape[0] or q.shape[2] != k.shape[2]:
+        raise ValueError("expected q[T, Hq, D] and k[T, Hkv, D]")
+    if not (q.is_contiguous() and k.is_contiguous()):
+        raise ValueError("q and k must be contiguous (rotation is in place)")
+    cu = _index_tensor(cu_seqlens, "cu_seqlens", q.device)
+    su = _index_tensor(seqused, "seqused", q.device)
+    num_seqs = cu.numel() - 1
+    if su is not None and su.numel() != num_seqs:
+        raise ValueError("seqused must have one entry per sequence")
+    T, Hq, D = q.shape
+    return T, Hq, k.shape[1], D, cu, num_seqs, su
+
+
+def qk_apply_(q, k, cu_seqlens, theta: float, direction: int = 1, seqused=None,
+              index_mode: int = INDEX_AUTO, heads_per_group: int = 0):
+    """Rotate q[T, Hq, D] and k[T, Hkv, D] in place (direction +1: forward, -1:
+    backward), one kernel launch on the current stream. Returns (q, k)."""
+    T, Hq, Hkv, D, cu, num_seqs, su = _qk_args(q, k, cu_seqlens, seqused)
+    st = _lib.rope_qk_apply(_ptr(q), _ptr(k), T, Hq, Hkv, D, _ptr(cu), num_seqs, _ptr(su),
+                            float(theta), _DTYPE_CODE[q.dtype], int(direction), int(index_mode),
+                            int(heads_per_group), _stream(q.device))
+    _check(st, "rope_qk_apply")
+    return q, k
+
+
+def qk_fwd_(q, k, cu_seqlens, theta: float, seqused=None):
+    """Forward RoPE on q and k in place (one launch). Returns (q, k)."""
+    T, Hq, Hkv, D, cu, num_seqs, su = _qk_args(q, k, cu_seqlens, seqused)
+    st = _lib.rope_qk_fwd(_ptr(q), _ptr(k), T, Hq, Hkv, D, _ptr(cu), num_seqs, _ptr(su),
+                          float(theta), _DTYPE_CODE[q.dtype], _stream(q.device))
+    _check(st, "rope_qk_fwd")
+    return q, k
+
+
+def qk_bwd_(dq, dk, cu_seqlens, theta: float, seqused=None):
+    """Backward RoPE (sin negated) on the gradients dq and dk in place. Returns (dq, dk)."""
+    T, Hq, Hkv, D, cu, num_seqs, su = _qk_args(dq, dk, cu_seqlens, seqused)
+    st = _lib.rope_qk_bwd(_ptr(dq), _ptr(dk), T, Hq, Hkv, D, _ptr(cu), num_seqs, _ptr(su),
+                          float(theta), _DTYPE_CODE[dq.dtype], _stream(dq.device))
+    _check(st, "rope_qk_bwd")
+    return dq, dk
+
+
+def positions(cu_seqlens, T: int, seqused=None):
+    """(pos, seq) int32[T] on the GPU as the kernels compute them; -1 = untouched."""
+    device = cu_seqlens.device
+    cu = _index_tensor(cu_seqlens, "cu_seqlens", device)
+    su = _index_tensor(seqused, "seqused", device)
+    pos = torch.empty(int(T), dtype=torch.int32, device=device)
+    seq = torch.empty(int(T), dtype=torch.int32, device=device)
+    st = _lib.rope_positions(_ptr(cu), cu.numel() - 1, _ptr(su), int(T), _ptr(pos), _ptr(seq),
+                             _stream(device))
+    _check(st, "rope_positions")
+    return pos, seq
+
+
+def cos_sin(pos, D: int, theta: float):
+    """fp32 (cos, sin) [n, D/2] for the int32 positions `pos` (on the GPU)."""
+    p = _index_tensor(pos, "pos", pos.device)
+    c = torch.empty((p.numel(), D // 2), dtype=torch.float32, device=p.device)
+    s = torch.empty_like(c)
+    st = _lib.rope_cos_sin(_ptr(p), p.numel(), int(D), float(theta), _ptr(c), _ptr(s),
+                           _stream(p.device))
+    _check(st, "rope_cos_sin")
+    return c, s
+
+
+def inv_freq(theta: float, D: int) -> torch.Tensor:
+    """Host-computed fp32 inverse frequencies theta^(-2j/D) (a CPU tensor)."""
+    out = torch.empty(D // 2, dtype=torch.float32)
+    _check(_lib.rope_inv_freq(float(theta), int(D), out.data_ptr()), "rope_inv_freq")
+    return out

@@ -1,0 +1,133 @@
+"""C-ABI checks that need no GPU: the library loads and exports every function
+include/rope_qk.h declares; host-side validation rejects bad arguments before
+any HIP call (no kernel is launched by any call here); the host-computed
+inverse frequencies; the generated trig constants."""
+import ctypes
+import os
+import re
+import subprocess
+import sys
+
+import mpmath
+import numpy as np
+import pytest
+
+import oracle
+import packed_varlen_rotary_rope_amd as rope
+from oracle_checks import ref_inv_freq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rope_qk.h")
+CSRC = os.path.join(ROOT, "packed_varlen_rotary_rope_amd", "csrc")
+
+OK, EINVAL, EUNSUPPORTED = 0, -1, -2
+FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: every call below fails validation or is empty
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"^\s*(?:int32_t|const char\*)\s+(rope_\w+)\s*\(", text, re.M)
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) >= {"rope_qk_fwd", "rope_qk_bwd", "rope_qk_apply", "rope_positions",
+                          "rope_cos_sin", "rope_inv_freq", "rope_status_str", "rope_abi_version"}
+    out = subprocess.run(["nm", "-D", "--defined-only", rope.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    lib = rope._lib
+    for n in names:
+        assert hasattr(lib, n)
+
+
+def test_version_and_status_strings():
+    assert rope.abi_version() == 1
+    lib = rope._lib
+    for st in (0, -1, -2, -3):
+        assert lib.rope_status_str(st).decode().startswith("ROPE_")
+    assert b"unknown" in lib.rope_status_str(7)
+
+
+def apply(**kw):
+    a = dict(q=FAKE, k=FAKE, T=16, Hq=4, Hkv=2, D=128, cu=FAKE, num_seqs=2, seqused=None,
+             theta=1e4, dtype=1, direction=1, index_mode=0, hpg=0, stream=None)
+    a.update(kw)
+    return rope._lib.rope_qk_apply(a["q"], a["k"], a["T"], a["Hq"], a["Hkv"], a["D"], a["cu"],
+                                   a["num_seqs"], a["seqused"], a["theta"], a["dtype"],
+                                   a["direction"], a["index_mode"], a["hpg"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(dtype=3), EUNSUPPORTED),
+    (dict(dtype=-1), EUNSUPPORTED),
+    (dict(T=-1), EINVAL),
+    (dict(Hq=-1), EINVAL),
+    (dict(Hkv=-2), EINVAL),
+    (dict(Hq=5000), EINVAL),
+    (dict(Hq=0, Hkv=0), EINVAL),
+    (dict(D=127), EINVAL),
+    (dict(D=0), EINVAL),
+    (dict(D=514), EINVAL),
+    (dict(theta=0.5), EINVAL),
+    (dict(theta=float("nan")), EINVAL),
+    (dict(theta=float("inf")), EINVAL),
+    (dict(theta=-1e4), EINVAL),
+    (dict(num_seqs=-1), EINVAL),
+    (dict(direction=0), EINVAL),
+    (dict(direction=2), EINVAL),
+    (dict(index_mode=3), EINVAL),
+    (dict(hpg=-1), EINVAL),
+    (dict(cu=None), EINVAL),
+    (dict(q=None), EINVAL),
+    (dict(k=None), EINVAL),
+    # Q alone needs 2^31 elements of index space: 32-bit indexing cannot be forced.
+    (dict(T=524288, Hq=32, Hkv=8, D=128, index_mode=1), EINVAL),
+    # Empty work: valid, and returns before touching the GPU.
+    (dict(T=0, q=None, k=None, cu=None), OK),
+    (dict(num_seqs=0, cu=None), OK),
+])
+def test_validation(kw, expect):
+    assert apply(**kw) == expect
+
+
+def test_fwd_bwd_positions_cos_sin_validation():
+    lib = rope._lib
+    args = (FAKE, FAKE, 16, 4, 2, 127, FAKE, 2, None, 1e4, 1, None)
+    assert lib.rope_qk_fwd(*args) == EINVAL
+    assert lib.rope_qk_bwd(*args) == EINVAL
+    assert lib.rope_positions(FAKE, -1, None, 16, FAKE, FAKE, None) == EINVAL
+    assert lib.rope_positions(None, 2, None, 16, FAKE, FAKE, None) == EINVAL
+    assert lib.rope_positions(FAKE, 2, None, -5, FAKE, FAKE, None) == EINVAL
+    assert lib.rope_positions(FAKE, 2, None, 0, FAKE, FAKE, None) == OK
+    assert lib.rope_cos_sin(FAKE, 4, 7, 1e4, FAKE, FAKE, None) == EINVAL
+    assert lib.rope_cos_sin(FAKE, -1, 8, 1e4, FAKE, FAKE, None) == EINVAL
+    assert lib.rope_cos_sin(None, 4, 8, 1e4, FAKE, FAKE, None) == EINVAL
+    assert lib.rope_cos_sin(FAKE, 0, 8, 1e4, FAKE, FAKE, None) == OK
+    assert lib.rope_inv_freq(1e4, 8, None) == EINVAL
+
+
+@pytest.mark.parametrize("theta,D", [(1e4, 16), (1e6, 128), (1e4, 128), (5e5, 64), (1e6, 80),
+                                     (1.0, 4), (1e6, 512)])
+def test_host_inv_freq(theta, D):
+    got = rope.inv_freq(theta, D).numpy()
+    ref = ref_inv_freq(theta, D)  # theta^(-2j/D) to 200 bits, rounded once to fp32
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+    assert np.array_equal(got.view(np.uint32), oracle.inv_freq(theta, D).view(np.uint32))
+
+
+def test_trig_constants_regenerate():
+    sys.path.insert(0, CSRC)
+    try:
+        import gen_trig_constants as gen
+    finally:
+        sys.path.remove(CSRC)
+    assert open(os.path.join(CSRC, "trig_constants.h")).read() == gen.render()
+    # Independent check of the pi/2 split against mpmath's pi.
+    src = open(os.path.join(CSRC, "trig_constants.h")).read()
+    parts = [float(re.search(r"PIO2_%d = ([^;]+);" % i, src).group(1)) for i in (1, 2, 3)]
+    mpmath.mp.prec = 300
+    err = sum(mpmath.mpf(p) for p in parts) - mpmath.pi / 2
+    assert abs(err) < mpmath.mpf(2) ** -150

@@ -1,0 +1,351 @@
+"""GPU parity: the HIP library, called through its C ABI (via the Python
+binding), against the CPU oracle on the same seeded inputs.
+
+Bars (written here, per dtype):
+  * fp32 storage: max |gpu - oracle| <= 1e-5 * max|x| over each tensor;
+  * bf16 / fp16 storage: every element within 1 ulp of the oracle's fp32 result
+    rounded to the storage dtype (ordered-bit distance, +0 == -0);
+  * positions, sequence ids and untouched rows: bit-exact;
+  * cos/sin exports: bit-exact against the oracle's correctly rounded values.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+NTHREADS = max(1, min(16, len(os.sched_getaffinity(0))))
+DEV = torch.device("cuda:0")
+CANARY = {"f32": 0x7FA5A5A5, "bf16": 0x7FA5, "f16": 0x7D25}  # signalling NaNs
+
+
+@pytest.fixture(scope="module")
+def rope():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import packed_varlen_rotary_rope_amd as m
+    return m
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    return workloads.host_bits(t)
+
+
+def ordered(b: np.ndarray, width: int) -> np.ndarray:
+    """Map float bit patterns to integers ordered like the values (+0 and -0 -> 0)."""
+    b = b.astype(np.int64)
+    sign = 1 << (width - 1)
+    return np.where(b & sign, -(b & (sign - 1)), b)
+
+
+def round_ref(ref32: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "bf16":
+        return oracle.round_bf16(ref32)
+    return ref32.astype(np.float16).view(np.uint16)  # numpy: round to nearest even
+
+
+def assert_parity(dtype, got, ref32, x, touched, what):
+    """got, x: storage bits (float32 array for f32, uint16 words otherwise); ref32: oracle."""
+    got, x, ref32 = got.reshape(got.shape[0], -1), x.reshape(x.shape[0], -1), \
+        ref32.reshape(ref32.shape[0], -1)
+    # untouched rows: bit-for-bit
+    if (~touched).any():
+        gu = got[~touched].view(np.uint32 if dtype == "f32" else np.uint16)
+        xu = x[~touched].view(np.uint32 if dtype == "f32" else np.uint16)
+        assert np.array_equal(gu, xu), f"{what}: an untouched row changed"
+    g, r = got[touched], ref32[touched]
+    if dtype == "f32":
+        xmax = float(np.max(np.abs(x[touched]))) if g.size else 0.0
+        err = float(np.max(np.abs(g.astype(np.float64) - r.astype(np.float64)))) if g.size else 0.0
+        assert err <= 1e-5 * xmax, f"{what}: max abs err {err} > 1e-5 * {xmax}"
+    else:
+        d = np.abs(ordered(g, 16) - ordered(round_ref(r, dtype), 16))
+        worst = int(d.max()) if d.size else 0
+        assert worst <= 1, f"{what}: {int((d > 1).sum())} elements beyond 1 ulp (worst {worst})"
+
+
+def _word(dtype: torch.dtype):
+    return torch.int32 if dtype == torch.float32 else torch.int16
+
+
+def _canary(dtype: torch.dtype) -> int:
+    return {torch.float32: CANARY["f32"], torch.bfloat16: CANARY["bf16"],
+            torch.float16: CANARY["f16"]}[dtype]
+
+
+def guarded(t_host: torch.Tensor, guard: int = 4096):
+    """Copy t_host to the GPU inside a larger buffer whose guard regions hold canaries.
+    Returns (view on the GPU, flat buffer, guard)."""
+    n = t_host.numel()
+    flat = torch.empty(n + 2 * guard, dtype=t_host.dtype, device=DEV)
+    flat.view(_word(t_host.dtype)).fill_(_canary(t_host.dtype))  # canaries fit the signed word
+    view = flat[guard:guard + n].view(t_host.shape)
+    view.copy_(t_host)
+    return view, flat, guard
+
+
+def guards_intact(flat: torch.Tensor, guard: int) -> bool:
+    g = torch.cat([flat[:guard], flat[-guard:]]).view(_word(flat.dtype))
+    return bool(torch.all(g == _canary(flat.dtype)))
+
+
+def run_and_check(rope, w, host, cu_np, su_np, theta, dtype, apply_kw=None, guard=True):
+    """host: dict of CPU tensors q, k, dq, dk. Runs fwd on (q, k) and bwd on (dq, dk)."""
+    print(f"[parity] {w} T={host['q'].shape[0]} Hq={host['q'].shape[1]} "
+          f"Hkv={host['k'].shape[1]} D={host['q'].shape[2]} {dtype} {apply_kw or ''}", flush=True)
+    cu = torch.from_numpy(np.asarray(cu_np, dtype=np.int32)).to(DEV)
+    su = None if su_np is None else torch.from_numpy(np.asarray(su_np, dtype=np.int32)).to(DEV)
+    dev, flats = {}, {}
+    for what, t in host.items():
+        if guard:
+            dev[what], flats[what], g = guarded(t)
+        else:
+            dev[what] = t.to(DEV)
+    if apply_kw is None:
+        rope.qk_fwd_(dev["q"], dev["k"], cu, theta, seqused=su)
+        rope.qk_bwd_(dev["dq"], dev["dk"], cu, theta, seqused=su)
+    else:
+        rope.qk_apply_(dev["q"], dev["k"], cu, theta, 1, seqused=su, **apply_kw)
+        rope.qk_apply_(dev["dq"], dev["dk"], cu, theta, -1, seqused=su, **apply_kw)
+    torch.cuda.synchronize()
+    T = host["q"].shape[0]
+    pos, _ = oracle.positions(cu_np, T, su_np)
+    touched = pos >= 0
+    out = {}
+    for what, direction in (("q", 1), ("k", 1), ("dq", -1), ("dk", -1)):
+        x = bits(host[what])
+        got = bits(dev[what])
+        ref = oracle.rope(x, cu_np, theta, direction, dtype, su_np, NTHREADS)
+        assert_parity(dtype, got, ref, x, touched, f"{w}:{what}")
+        if guard:
+            assert guards_intact(flats[what], g), f"{w}:{what}: guard region written"
+        out[what] = got
+    return out
+
+
+def make_host(w: workloads.Workload, canary_untouched: bool = True):
+    host = {what: workloads.make_tensor(w.shape(what), w.seed(what), w.dtype)
+            for what in ("q", "k", "dq", "dk")}
+    if canary_untouched:
+        pos, _ = oracle.positions(w.cu_seqlens, w.T, w.seqused)
+        un = torch.from_numpy(pos < 0)
+        if un.any():
+            for t in host.values():
+                t.view(_word(t.dtype))[un] = CANARY[w.dtype]
+    return host
+
+
+# ---------------------------------------------------------------- full workloads
+
+@pytest.mark.parametrize("name", ["tiny_packed", "qwen3_4b_packed", "qwen3_8b_packed",
+                                  "qwen3_8b_padded", "qwen3_32b_packed"])
+def test_workload_parity(rope, name):
+    w = workloads.get(name)
+    host = make_host(w)
+    run_and_check(rope, name, host, w.cu_seqlens, w.seqused, w.theta, w.dtype)
+
+
+def test_padded_equals_packed(rope):
+    """The padded layout with seqused gives, row for row, the packed layout's result."""
+    a, b = workloads.get("qwen3_8b_packed"), workloads.get("qwen3_8b_padded")
+    print("[parity] packed vs padded qwen3_8b", flush=True)
+    qa = workloads.make_tensor(a.shape("q"), 77, "bf16").to(DEV)
+    ka = workloads.make_tensor(a.shape("k"), 78, "bf16").to(DEV)
+    qb = torch.zeros(b.shape("q"), dtype=torch.bfloat16, device=DEV)
+    kb = torch.zeros(b.shape("k"), dtype=torch.bfloat16, device=DEV)
+    L = a.lengths
+    for s in range(8):
+        qb[2048 * s: 2048 * s + L[s]] = qa[a.cu_seqlens[s]: a.cu_seqlens[s + 1]]
+        kb[2048 * s: 2048 * s + L[s]] = ka[a.cu_seqlens[s]: a.cu_seqlens[s + 1]]
+    rope.qk_fwd_(qa, ka, torch.from_numpy(a.cu_seqlens).to(DEV), a.theta)
+    rope.qk_fwd_(qb, kb, torch.from_numpy(b.cu_seqlens).to(DEV), b.theta,
+                 seqused=torch.from_numpy(b.seqused).to(DEV))
+    for s in range(8):
+        assert torch.equal(qb[2048 * s: 2048 * s + L[s]], qa[a.cu_seqlens[s]: a.cu_seqlens[s + 1]])
+        assert torch.equal(kb[2048 * s: 2048 * s + L[s]], ka[a.cu_seqlens[s]: a.cu_seqlens[s + 1]])
+        assert torch.count_nonzero(qb[2048 * s + L[s]: 2048 * (s + 1)]) == 0
+
+
+def test_long_context_sampled(rope):
+    """524288 tokens, Q = 2^31 elements: the int64 path, at full size, on the launch
+    configuration of a plain fwd/bwd call. Sampled rows against the oracle."""
+    w = workloads.get("long_ctx_512k")
+    print("[parity] long_ctx_512k sampled (int64 path)", flush=True)
+    dev = {what: workloads.make_tensor(w.shape(what), w.seed(what), "bf16", device=DEV,
+                                       chunk_rows=32768)
+           for what in ("q", "k", "dq", "dk")}
+    rng = np.random.default_rng(4242)
+    tokens = np.unique(np.concatenate([np.arange(64), np.arange(w.T - 64, w.T),
+                                       rng.integers(0, w.T, 2048)]))
+    tok_dev = torch.from_numpy(tokens).to(DEV)
+    before = {what: bits(t.index_select(0, tok_dev)) for what, t in dev.items()}
+    cu = torch.from_numpy(w.cu_seqlens).to(DEV)
+    rope.qk_fwd_(dev["q"], dev["k"], cu, w.theta)
+    rope.qk_bwd_(dev["dq"], dev["dk"], cu, w.theta)
+    torch.cuda.synchronize()
+    touched = np.ones(tokens.size, dtype=bool)
+    for what, direction in (("q", 1), ("k", 1), ("dq", -1), ("dk", -1)):
+        got = bits(dev[what].index_select(0, tok_dev))
+        ref = oracle.rope_rows(before[what], tokens, w.cu_seqlens, w.theta, direction, "bf16",
+                               None, NTHREADS)
+        assert_parity("bf16", got, ref, before[what], touched, f"long_ctx:{what}")
+    pos, seq = rope.positions(cu, w.T)
+    assert torch.equal(pos, torch.arange(w.T, dtype=torch.int32, device=DEV))
+    assert int(seq.min()) == 0 and int(seq.max()) == 0
+    del dev
+    torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------- exports
+
+@pytest.mark.parametrize("name", workloads.names())
+def test_positions_export(rope, name):
+    w = workloads.get(name)
+    cu = torch.from_numpy(w.cu_seqlens).to(DEV)
+    su = None if w.seqused is None else torch.from_numpy(w.seqused).to(DEV)
+    pos, seq = rope.positions(cu, w.T, su)
+    rpos, rseq = oracle.positions(w.cu_seqlens, w.T, w.seqused)
+    assert np.array_equal(pos.cpu().numpy(), rpos) and np.array_equal(seq.cpu().numpy(), rseq)
+
+
+def test_positions_edges(rope):
+    cases = [([2, 2, 5, 9], [0, 2, 9], 11), ([0, 0, 0], None, 3), ([0, 7], None, 12),
+             ([3, 3, 3, 10, 10, 11], [1, 0, 4, 0, 1], 16), ([0] + list(range(1, 300)), None, 300)]
+    for cu_l, su_l, T in cases:
+        cu = torch.tensor(cu_l, dtype=torch.int32, device=DEV)
+        su = None if su_l is None else torch.tensor(su_l, dtype=torch.int32, device=DEV)
+        pos, seq = rope.positions(cu, T, su)
+        rpos, rseq = oracle.positions(cu_l, T, su_l)
+        assert np.array_equal(pos.cpu().numpy(), rpos), (cu_l, su_l)
+        assert np.array_equal(seq.cpu().numpy(), rseq), (cu_l, su_l)
+
+
+@pytest.mark.parametrize("theta,D,maxpos", [(1e4, 16, 64), (1e6, 128, 524288), (1e4, 128, 40000),
+                                            (5e5, 64, 70000), (1e6, 80, 20000)])
+def test_cos_sin_export_bit_exact(rope, theta, D, maxpos):
+    pos = np.arange(maxpos, dtype=np.int32)
+    c, s = rope.cos_sin(torch.from_numpy(pos).to(DEV), D, theta)
+    rc, rs = oracle.cos_sin(pos, D, theta)
+    cb, sb = c.cpu().numpy().view(np.uint32), s.cpu().numpy().view(np.uint32)
+    mism = int((cb != rc.view(np.uint32)).sum() + (sb != rs.view(np.uint32)).sum())
+    assert mism == 0, f"{mism} of {2 * rc.size} cos/sin values differ from the oracle"
+
+
+# ---------------------------------------------------------------- launch variants
+
+@pytest.mark.parametrize("name", ["tiny_packed", "qwen3_4b_packed"])
+def test_variants_bit_identical(rope, name):
+    """int64 indexing forced, and head groups of several sizes: same bits as default."""
+    w = workloads.get(name)
+    cu = torch.from_numpy(w.cu_seqlens).to(DEV)
+    q0 = workloads.make_tensor(w.shape("q"), w.seed("q"), w.dtype).to(DEV)
+    k0 = workloads.make_tensor(w.shape("k"), w.seed("k"), w.dtype).to(DEV)
+    q_ref, k_ref = q0.clone(), k0.clone()
+    rope.qk_fwd_(q_ref, k_ref, cu, w.theta)
+    H = w.Hq + w.Hkv
+    for kw in (dict(index_mode=rope.INDEX_64), dict(index_mode=rope.INDEX_32),
+               dict(heads_per_group=1), dict(heads_per_group=3), dict(heads_per_group=8),
+               dict(heads_per_group=H - 1), dict(heads_per_group=4 * H),
+               dict(index_mode=rope.INDEX_64, heads_per_group=5)):
+        print(f"[parity] {name} variant {kw}", flush=True)
+        q, k = q0.clone(), k0.clone()
+        rope.qk_apply_(q, k, cu, w.theta, 1, **kw)
+        assert torch.equal(q.view(torch.int16 if w.dtype != "f32" else torch.int32),
+                           q_ref.view(torch.int16 if w.dtype != "f32" else torch.int32)), kw
+        assert torch.equal(k, k_ref), kw
+
+
+# ---------------------------------------------------------------- edge cases
+
+EDGE = [
+    # (label, lengths (cu from 0 unless cu given), T, Hq, Hkv, D, dtype, theta, seqused, cu)
+    ("ragged_bf16_D128", [37, 0, 300, 1, 5], 343, 3, 1, 128, "bf16", 1e6, None, None),
+    ("bf16_D2_vec1", [9, 20], 29, 4, 2, 2, "bf16", 1e4, None, None),
+    ("bf16_D6_vec1", [9, 20], 29, 4, 2, 6, "bf16", 1e4, None, None),
+    ("bf16_D12_vec2", [30, 3], 33, 2, 2, 12, "bf16", 1e4, None, None),
+    ("bf16_D40_vec4", [30, 3], 33, 2, 2, 40, "bf16", 1e4, None, None),
+    ("bf16_D80_nc5", [50, 70], 120, 3, 2, 80, "bf16", 1e6, None, None),
+    ("bf16_D256", [50, 70], 120, 3, 2, 256, "bf16", 1e6, None, None),
+    ("bf16_D512_max", [50, 70], 120, 2, 1, 512, "bf16", 1e6, None, None),
+    ("f32_D64", [10, 100, 17], 127, 4, 4, 64, "f32", 1e4, None, None),
+    ("f32_D2", [10, 100, 17], 127, 1, 1, 2, "f32", 1e4, None, None),
+    ("f16_D128", [10, 100, 17], 127, 8, 2, 128, "f16", 5e5, None, None),
+    ("k_only", [40, 24], 64, 0, 4, 64, "bf16", 1e4, None, None),
+    ("q_only", [40, 24], 64, 4, 0, 64, "bf16", 1e4, None, None),
+    ("cu_offset_tail_seqused", None, 40, 3, 1, 32, "bf16", 1e4, [0, 5, 100, 2], [3, 3, 12, 30, 35]),
+    ("many_tiny_seqs", [1] * 200 + [2] * 50, 320, 2, 2, 64, "bf16", 1e4, None, None),
+    ("theta_one", [33, 31], 64, 2, 2, 64, "bf16", 1.0, None, None),
+    ("heads_many", [20, 13], 33, 96, 16, 64, "bf16", 1e4, None, None),
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=[c[0] for c in EDGE])
+def test_edge_cases(rope, case):
+    label, lengths, T, Hq, Hkv, D, dtype, theta, su, cu = case
+    if cu is None:
+        cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    cu = np.asarray(cu, dtype=np.int32)
+    su = None if su is None else np.asarray(su, dtype=np.int32)
+    g = 9000 + len(label)
+    host = {"q": workloads.make_tensor((T, Hq, D), g, dtype),
+            "k": workloads.make_tensor((T, Hkv, D), g + 1, dtype),
+            "dq": workloads.make_tensor((T, Hq, D), g + 2, dtype),
+            "dk": workloads.make_tensor((T, Hkv, D), g + 3, dtype)}
+    run_and_check(rope, label, host, cu, su, theta, dtype)
+
+
+def test_misaligned_views(rope):
+    """Views that start 1 element off a 16-byte boundary take the narrow-access path."""
+    T, Hq, Hkv, D = 50, 3, 2, 128
+    cu = np.array([0, 20, 50], dtype=np.int32)
+    print("[parity] misaligned views", flush=True)
+    buf_q = torch.empty(T * Hq * D + 1, dtype=torch.bfloat16, device=DEV)
+    buf_k = torch.empty(T * Hkv * D + 1, dtype=torch.bfloat16, device=DEV)
+    q = buf_q[1:].view(T, Hq, D)
+    k = buf_k[1:].view(T, Hkv, D)
+    hq = workloads.make_tensor((T, Hq, D), 31, "bf16")
+    hk = workloads.make_tensor((T, Hkv, D), 32, "bf16")
+    q.copy_(hq)
+    k.copy_(hk)
+    assert q.data_ptr() % 16 != 0
+    rope.qk_fwd_(q, k, torch.from_numpy(cu).to(DEV), 1e6)
+    torch.cuda.synchronize()
+    touched = np.ones(T, dtype=bool)
+    for name, dv, hv, H in (("q", q, hq, Hq), ("k", k, hk, Hkv)):
+        ref = oracle.rope(bits(hv), cu, 1e6, 1, "bf16")
+        assert_parity("bf16", bits(dv), ref, bits(hv), touched, f"misaligned:{name}")
+
+
+def test_bwd_after_fwd_is_identity_fp32(rope):
+    w = workloads.get("tiny_packed")
+    cu = torch.from_numpy(w.cu_seqlens).to(DEV)
+    x = workloads.make_tensor((w.T, w.Hq, w.D), 5, "f32").to(DEV)
+    y = workloads.make_tensor((w.T, w.Hkv, w.D), 6, "f32").to(DEV)
+    q, k = x.clone(), y.clone()
+    rope.qk_fwd_(q, k, cu, w.theta)
+    assert not torch.equal(q, x)
+    rope.qk_bwd_(q, k, cu, w.theta)
+    assert torch.max(torch.abs(q - x)) <= 8 * 2.0 ** -24 * torch.max(torch.abs(x))
+    assert torch.max(torch.abs(k - y)) <= 8 * 2.0 ** -24 * torch.max(torch.abs(y))
+
+
+def test_binding_rejects_bad_tensors(rope):
+    cu = torch.tensor([0, 4], dtype=torch.int32, device=DEV)
+    q = torch.zeros(4, 2, 8, dtype=torch.bfloat16, device=DEV)
+    k = torch.zeros(4, 1, 8, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(TypeError):
+        rope.qk_fwd_(q, k.float(), cu, 1e4)
+    with pytest.raises(ValueError):
+        rope.qk_fwd_(q.transpose(0, 1), k, cu, 1e4)
+    with pytest.raises(TypeError):
+        rope.qk_fwd_(q, k, cu.long(), 1e4)
+    with pytest.raises(rope.RopeError):
+        rope.qk_fwd_(q, k, cu, 0.5)
+    with pytest.raises(rope.RopeError):
+        rope.qk_fwd_(torch.zeros(4, 2, 7, dtype=torch.bfloat16, device=DEV),
+                     torch.zeros(4, 1, 7, dtype=torch.bfloat16, device=DEV), cu, 1e4)
