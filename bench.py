@@ -125,7 +125,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="qwen3_4b_packed", choices=workloads.names())
-    ap.add_argument("--heads-per-group", type=int, default=0)
+    ap.add_argument("--tokens-per-wave", type=int, default=0, help="0: library default")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="timed oracle work for cpu_baseline (0 disables it)")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
@@ -152,16 +152,16 @@ def main():
     set_bytes = 2 * w.T * (w.Hq + w.Hkv) * w.D * w.elem_bytes  # Q, K, dQ, dK
     nsets = max(2, math.ceil(4 * INFINITY_CACHE_BYTES / set_bytes))
     cu, su, sets = make_sets(w, nsets, dev)
-    hpg = args.heads_per_group
+    tpw = args.tokens_per_wave
 
     def step(s, ev=None):
         if ev is not None:
             ev[0].record()
-        rope.qk_apply_(s["q"], s["k"], cu, w.theta, 1, seqused=su, heads_per_group=hpg)
+        rope.qk_apply_(s["q"], s["k"], cu, w.theta, 1, seqused=su, tokens_per_wave=tpw)
         if ev is not None:
             ev[1].record()
             ev[2].record()
-        rope.qk_apply_(s["dq"], s["dk"], cu, w.theta, -1, seqused=su, heads_per_group=hpg)
+        rope.qk_apply_(s["dq"], s["dk"], cu, w.theta, -1, seqused=su, tokens_per_wave=tpw)
         if ev is not None:
             ev[3].record()
 
@@ -206,7 +206,7 @@ def main():
             "workload": w.name,
             "T": w.T, "valid_tokens": w.valid_tokens, "num_seqs": w.num_seqs,
             "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D, "theta": w.theta,
-            "buffer_sets": nsets, "heads_per_group": hpg or (w.Hq + w.Hkv),
+            "buffer_sets": nsets, "tokens_per_wave": tpw or "auto",
         },
         "step_hbm_GBps": 2 * bpl * args.steps / elapsed / 1e9,
         "roofline": {

@@ -104,15 +104,15 @@ int32_t rope_qk_bwd(void* dq, void* dk, int64_t T, int32_t Hq, int32_t Hkv, int3
  *  direction        +1 forward, -1 backward (anything else: ROPE_EINVAL)
  *  index_mode       a rope_index_mode; ROPE_INDEX_32 is rejected (ROPE_EINVAL)
  *                   when the tensors need 64-bit offsets
- *  heads_per_group  0 = all Hq + Hkv heads in one group (cos/sin computed once per
- *                   token and frequency); n > 0 splits the Q-then-K head list into
- *                   groups of n heads handled by separate workgroups (more, shorter
- *                   workgroups; cos/sin recomputed per group)
+ *  tokens_per_wave  launch geometry: each 64-lane wave rotates this many consecutive
+ *                   tokens, one at a time, all Q and K heads of each (0 = chosen by
+ *                   the library from T; 1..1024 otherwise). Results do not depend
+ *                   on it.
  * Other arguments as in rope_qk_fwd. */
 int32_t rope_qk_apply(void* q, void* k, int64_t T, int32_t Hq, int32_t Hkv, int32_t D,
                       const int32_t* cu_seqlens, int32_t num_seqs, const int32_t* seqused,
                       double theta, int32_t dtype, int32_t direction, int32_t index_mode,
-                      int32_t heads_per_group, void* stream);
+                      int32_t tokens_per_wave, void* stream);
 
 /* Export of the token -> (position, sequence) map the kernels use (test hook,
  * same device code). pos_out, seq_out: device int32[T] (either may be NULL);

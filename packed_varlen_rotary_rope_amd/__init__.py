@@ -107,13 +107,13 @@ def _qk_args(q, k, cu_seqlens, seqused):
 
 
 def qk_apply_(q, k, cu_seqlens, theta: float, direction: int = 1, seqused=None,
-              index_mode: int = INDEX_AUTO, heads_per_group: int = 0):
+              index_mode: int = INDEX_AUTO, tokens_per_wave: int = 0):
     """Rotate q[T, Hq, D] and k[T, Hkv, D] in place (direction +1: forward, -1:
     backward), one kernel launch on the current stream. Returns (q, k)."""
     T, Hq, Hkv, D, cu, num_seqs, su = _qk_args(q, k, cu_seqlens, seqused)
     st = _lib.rope_qk_apply(_ptr(q), _ptr(k), T, Hq, Hkv, D, _ptr(cu), num_seqs, _ptr(su),
                             float(theta), _DTYPE_CODE[q.dtype], int(direction), int(index_mode),
-                            int(heads_per_group), _stream(q.device))
+                            int(tokens_per_wave), _stream(q.device))
     _check(st, "rope_qk_apply")
     return q, k
 

@@ -14,18 +14,23 @@
 //            group of heads.
 //
 // Work decomposition (memory-bound: one read and one write of every Q/K element,
-// no MFMA). A lane owns one (token, chunk) pair, where a chunk is VEC
-// consecutive elements of the first half of a head row (16 bytes for bf16/f16
-// with VEC = 8, fp32 with VEC = 4) together with the matching VEC elements of the
-// second half, D/2 further on. The lane
-//   1. maps its token to (sequence, position) by binary search over cu_seqlens,
-//   2. computes the VEC fp32 cos/sin values of its frequencies once,
-//   3. walks the heads of its head group -- Q heads, then K heads -- and for each
-//      head loads the two 16-byte chunks, rotates in fp32, rounds to the storage
-//      dtype and stores them back in place.
+// no MFMA). A wave owns one token at a time (a contiguous run of tpw tokens);
+// its 64 lanes cover (head row, chunk) pairs of that token, where a chunk is
+// VEC consecutive elements of the first half of a head row (16 bytes: VEC = 8
+// for bf16/f16, 4 for fp32) together with the matching VEC elements of the
+// second half, D/2 further on. For D = 128 in bf16 that is 8 rows x 8 chunks per
+// wave step, so each load instruction covers 2 KB of one token's rows. Per token:
+//   1. the wave maps the token to (sequence, position) with a wave-uniform
+//      binary search over cu_seqlens [U-Pack];
+//   2. each lane computes the correctly rounded fp32 cos/sin of one frequency
+//      (D/2 <= 64) or a few, into a per-wave LDS table: every (token, frequency)
+//      pair is evaluated exactly once in the whole launch;
+//   3. the wave walks the token's Q rows, then its K rows, 64/nc rows per step
+//      [U-Group]; each lane loads its two chunks, reads its cos/sin from the
+//      table, rotates in fp32, rounds to the storage dtype, stores in place.
 // The lane that reads a pair (j, j + D/2) is the one that writes it, so the
-// in-place update needs no synchronization. Per wave, each load instruction
-// touches whole 128-byte half-rows (8 lanes x 16 B for D = 128 bf16).
+// in-place update needs no synchronization between lanes. Loads and stores are
+// non-temporal: the data is streamed once and never reused.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -35,25 +40,22 @@
 
 namespace {
 
-constexpr int kBlock = 256;     // threads per workgroup (4 waves of 64)
+constexpr int kBlock = 256;     // threads per workgroup
+constexpr int kWaves = kBlock / 64;  // waves per workgroup, one token at a time each
 constexpr int kMaxHalf = 256;   // D <= 512
 constexpr int kMaxHeads = 4096;
-constexpr int kUnroll = 8;      // head rows in flight per lane
+constexpr int kUnroll = 4;      // wave steps (row groups) whose loads are in flight together
+constexpr int kMaxTokensPerWave = 1024;
 // A dispatch's grid size in work-items is a 32-bit field: blocks * kBlock < 2^32.
 constexpr int64_t kMaxBlocksX = (int64_t)0xffffffffu / kBlock;
 
 struct RopeParams {
-  alignas(16) float inv_freq[kMaxHalf];  // first: 16-byte aligned for vector loads
-  void* q;
-  void* k;
+  alignas(16) float inv_freq[kMaxHalf];
   int64_t T;
-  const int32_t* cu;
-  const int32_t* seqused;
   int32_t num_seqs;
   int32_t Hq, Hkv, D;
   int32_t nc;   // chunks per half row: (D/2) / VEC
-  int32_t tpb;  // tokens per workgroup: kBlock / nc
-  int32_t hpg;  // heads per group (blockIdx.y selects the group)
+  int32_t tpw;  // tokens per wave
   float sin_sign;
 };
 
@@ -160,88 +162,189 @@ __device__ inline void rotate_chunk(Chunk<T, VEC>& lo, Chunk<T, VEC>& hi, const 
   narrow(y2, hi);
 }
 
-// Rotate `nrows` consecutive head rows starting at row pointer `row` (already
-// offset to this lane's chunk): loads for kUnroll rows are issued before any of
-// them is used, so each lane keeps 2*kUnroll 16-byte loads in flight.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+template <int BYTES> struct WordOf;
+template <> struct WordOf<16> { typedef u32x4 type; };
+template <> struct WordOf<8> { typedef u32x2 type; };
+template <> struct WordOf<4> { typedef uint32_t type; };
+template <> struct WordOf<2> { typedef uint16_t type; };
+
+// Streaming (non-temporal) access to one chunk.
 template <typename T, int VEC>
-__device__ inline void rotate_rows(T* __restrict__ base, uint32_t off, int nrows, uint32_t D,
-                                   uint32_t half, const float (&cs)[VEC], const float (&sn)[VEC]) {
+__device__ inline Chunk<T, VEC> load_chunk(const T* p) {
+  typedef typename WordOf<VEC * sizeof(T)>::type W;
+  return __builtin_bit_cast(Chunk<T, VEC>, __builtin_nontemporal_load(reinterpret_cast<const W*>(p)));
+}
+template <typename T, int VEC>
+__device__ inline void store_chunk(T* p, const Chunk<T, VEC>& c) {
+  typedef typename WordOf<VEC * sizeof(T)>::type W;
+  __builtin_nontemporal_store(__builtin_bit_cast(W, c), reinterpret_cast<W*>(p));
+}
+
+// Orders LDS traffic between the lanes of one wave (wave-local table, no s_barrier).
+__device__ inline void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Rotate the H rows of one token. `row0` points at the token's first row. Lane
+// items are (row r, chunk c) = (r0 + k*step_r, c0) for k = 0, 1, ...: this is the
+// layout when nc divides 64 (step_c == 0), so each lane keeps one chunk and its
+// cos/sin in registers for the whole token.
+template <typename T, int VEC>
+__device__ inline void rotate_rows_fixed_chunk(T* __restrict__ row0, int H, uint32_t D, uint32_t half,
+                                               int r0, int c, int step_r, const float (&cs)[VEC],
+                                               const float (&sn)[VEC]) {
   using C = Chunk<T, VEC>;
-  int r = 0;
-  for (; r + kUnroll <= nrows; r += kUnroll) {
+  for (int r = r0; r < H; r += kUnroll * step_r) {
     C lo[kUnroll], hi[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const uint32_t o = off + (uint32_t)(r + u) * D;
-      lo[u] = *reinterpret_cast<const C*>(base + o);
-      hi[u] = *reinterpret_cast<const C*>(base + o + half);
+      const int ru = r + u * step_r;
+      if (ru < H) {
+        const uint32_t o = (uint32_t)ru * D + (uint32_t)(c * VEC);
+        lo[u] = load_chunk<T, VEC>(row0 + o);
+        hi[u] = load_chunk<T, VEC>(row0 + o + half);
+      }
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const uint32_t o = off + (uint32_t)(r + u) * D;
-      rotate_chunk(lo[u], hi[u], cs, sn);
-      *reinterpret_cast<C*>(base + o) = lo[u];
-      *reinterpret_cast<C*>(base + o + half) = hi[u];
+      const int ru = r + u * step_r;
+      if (ru < H) {
+        const uint32_t o = (uint32_t)ru * D + (uint32_t)(c * VEC);
+        rotate_chunk(lo[u], hi[u], cs, sn);
+        store_chunk<T, VEC>(row0 + o, lo[u]);
+        store_chunk<T, VEC>(row0 + o + half, hi[u]);
+      }
     }
-  }
-  for (; r < nrows; ++r) {
-    const uint32_t o = off + (uint32_t)r * D;
-    C lo = *reinterpret_cast<const C*>(base + o);
-    C hi = *reinterpret_cast<const C*>(base + o + half);
-    rotate_chunk(lo, hi, cs, sn);
-    *reinterpret_cast<C*>(base + o) = lo;
-    *reinterpret_cast<C*>(base + o + half) = hi;
   }
 }
 
-// Pointer to the first row of this workgroup's first token in a [T, H, D] tensor.
-// [U-int64]: with LONG_INDEX the workgroup base offset is formed in 64 bits (it is
-// uniform, so this is scalar arithmetic); without it, in 32 bits, which the host
-// only selects when every offset of the launch fits. Per-lane offsets relative to
-// this base are 32-bit in both cases (tpb * H * D < 2^29).
+// General layout (nc does not divide 64): lane items advance by 64 (row, chunk)
+// pairs in row-major order, so the chunk changes from step to step and cos/sin
+// are read from the wave's LDS table per item.
+template <typename T, int VEC>
+__device__ inline void rotate_rows_general(T* __restrict__ row0, int H, uint32_t D, uint32_t half,
+                                           int nc, int r0, int c0, int step_r, int step_c,
+                                           const float* cs_tab, const float* sn_tab) {
+  using C = Chunk<T, VEC>;
+  int r = r0, c = c0;
+  while (r < H) {
+    C lo[kUnroll], hi[kUnroll];
+    int cc[kUnroll], rr[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      rr[u] = r;
+      cc[u] = c;
+      if (r < H) {
+        const uint32_t o = (uint32_t)r * D + (uint32_t)(c * VEC);
+        lo[u] = load_chunk<T, VEC>(row0 + o);
+        hi[u] = load_chunk<T, VEC>(row0 + o + half);
+      }
+      r += step_r;
+      c += step_c;
+      if (c >= nc) {
+        c -= nc;
+        r += 1;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      if (rr[u] < H) {
+        float cs[VEC], sn[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          cs[e] = cs_tab[cc[u] * VEC + e];
+          sn[e] = sn_tab[cc[u] * VEC + e];
+        }
+        const uint32_t o = (uint32_t)rr[u] * D + (uint32_t)(cc[u] * VEC);
+        rotate_chunk(lo[u], hi[u], cs, sn);
+        store_chunk<T, VEC>(row0 + o, lo[u]);
+        store_chunk<T, VEC>(row0 + o + half, hi[u]);
+      }
+    }
+  }
+}
+
+// First row of token t in a [T, H, D] tensor. [U-int64]: with LONG_INDEX the
+// offset is formed in 64 bits; without it, in 32 bits, which the host selects only
+// when every offset of the launch fits. t is wave-uniform, so either way this is
+// scalar arithmetic; per-lane offsets below it are 32-bit (H * D < 2^22).
 template <typename T, bool LONG_INDEX>
-__device__ inline T* block_base(void* p, int64_t t0, int32_t H, int32_t D) {
-  if (LONG_INDEX) return static_cast<T*>(p) + t0 * (int64_t)H * (int64_t)D;
-  return static_cast<T*>(p) + (uint32_t)((uint32_t)t0 * (uint32_t)H * (uint32_t)D);
+__device__ inline T* token_row0(T* p, int64_t t, int32_t H, int32_t D) {
+  if (LONG_INDEX) return p + t * (int64_t)H * (int64_t)D;
+  return p + (uint32_t)((uint32_t)t * (uint32_t)H * (uint32_t)D);
 }
 
 // ---- the fused QK kernel (a1..a7) ---------------------------------------------------
 template <typename T, int VEC, bool LONG_INDEX>
-__global__ __launch_bounds__(kBlock) void rope_qk_kernel(const RopeParams p) {
-  const int tid = threadIdx.x;
-  const int tl = tid / p.nc;  // token within the workgroup
-  const int c = tid - tl * p.nc;
-  if (tl >= p.tpb) return;
-  const int64_t t0 = (int64_t)blockIdx.x * p.tpb;
-  const int64_t t = t0 + tl;
-  if (t >= p.T) return;
-  int32_t seq;
-  const int32_t pos = token_position(p.cu, p.num_seqs, p.seqused, t, &seq);
-  if (pos < 0) return;
-
-  // This lane's VEC inverse frequencies, fetched together before any sin/cos.
-  const Chunk<float, VEC> f = *reinterpret_cast<const Chunk<float, VEC>*>(&p.inv_freq[c * VEC]);
-  float cs[VEC], sn[VEC];
-#pragma unroll
-  for (int e = 0; e < VEC; ++e) {
-    rope_trig::sincos_f32_cr(rope_angle(pos, f.v[e]), sn[e], cs[e]);
-    sn[e] *= p.sin_sign;  // backward: R transposed = sin negated
-  }
-
+__global__ __launch_bounds__(kBlock) void rope_qk_kernel(T* __restrict__ q, T* __restrict__ k,
+                                                         const int32_t* __restrict__ cu,
+                                                         const int32_t* __restrict__ seqused,
+                                                         const RopeParams p) {
+  __shared__ float lds_cs[kWaves][kMaxHalf];
+  __shared__ float lds_sn[kWaves][kMaxHalf];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t t_begin = ((int64_t)blockIdx.x * kWaves + wave) * p.tpw;
   const uint32_t D = (uint32_t)p.D;
   const uint32_t half = D >> 1;
-  const int hb = (int)blockIdx.y * p.hpg;  // this group's heads, Q first then K
-  const int he = min(p.Hq + p.Hkv, hb + p.hpg);
-  if (hb < p.Hq) {
-    T* base = block_base<T, LONG_INDEX>(p.q, t0, p.Hq, p.D);
-    const uint32_t off = ((uint32_t)tl * (uint32_t)p.Hq + (uint32_t)hb) * D + (uint32_t)(c * VEC);
-    rotate_rows<T, VEC>(base, off, min(he, p.Hq) - hb, D, half, cs, sn);
+  const int nc = p.nc;
+  // This lane's first (row, chunk) item and the per-step advance over 64 items.
+  const int step_r = 64 / nc, step_c = 64 % nc;
+  const int r0 = lane < nc ? 0 : lane / nc;
+  const int c0 = lane - r0 * nc;
+  // This lane's frequencies j = lane + 64*i (same for every token).
+  float f[kMaxHalf / 64];
+#pragma unroll
+  for (int i = 0; i < kMaxHalf / 64; ++i) {
+    const uint32_t j = (uint32_t)lane + 64u * i;
+    f[i] = j < half ? p.inv_freq[j] : 0.0f;
   }
-  if (he > p.Hq) {
-    const int kb = max(hb, p.Hq) - p.Hq;
-    T* base = block_base<T, LONG_INDEX>(p.k, t0, p.Hkv, p.D);
-    const uint32_t off = ((uint32_t)tl * (uint32_t)p.Hkv + (uint32_t)kb) * D + (uint32_t)(c * VEC);
-    rotate_rows<T, VEC>(base, off, he - p.Hq - kb, D, half, cs, sn);
+
+  for (int it = 0; it < p.tpw; ++it) {
+    const int64_t t = t_begin + it;
+    if (t >= p.T) break;
+    int32_t seq;
+    const int32_t pos = token_position(cu, p.num_seqs, seqused, t, &seq);  // wave-uniform
+    if (pos < 0) continue;
+
+    // a3: this token's fp32 cos/sin table, each (token, frequency) computed once.
+#pragma unroll
+    for (int i = 0; i < kMaxHalf / 64; ++i) {
+      const uint32_t j = (uint32_t)lane + 64u * i;
+      if (j < half) {
+        float sn, cs;
+        rope_trig::sincos_f32_cr(rope_angle(pos, f[i]), sn, cs);
+        lds_cs[wave][j] = cs;
+        lds_sn[wave][j] = sn * p.sin_sign;  // backward: R transposed = sin negated
+      }
+    }
+    wave_lds_sync();
+
+    // a4/a5: Q rows then K rows of this token, in place.
+    T* qrow = token_row0<T, LONG_INDEX>(q, t, p.Hq, p.D);
+    T* krow = token_row0<T, LONG_INDEX>(k, t, p.Hkv, p.D);
+    if (step_c == 0) {
+      if (lane < step_r * nc) {
+        float cs[VEC], sn[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          cs[e] = lds_cs[wave][c0 * VEC + e];
+          sn[e] = lds_sn[wave][c0 * VEC + e];
+        }
+        rotate_rows_fixed_chunk<T, VEC>(qrow, p.Hq, D, half, r0, c0, step_r, cs, sn);
+        rotate_rows_fixed_chunk<T, VEC>(krow, p.Hkv, D, half, r0, c0, step_r, cs, sn);
+      }
+    } else {
+      rotate_rows_general<T, VEC>(qrow, p.Hq, D, half, nc, r0, c0, step_r, step_c,
+                                  lds_cs[wave], lds_sn[wave]);
+      rotate_rows_general<T, VEC>(krow, p.Hkv, D, half, nc, r0, c0, step_r, step_c,
+                                  lds_cs[wave], lds_sn[wave]);
+    }
+    wave_lds_sync();  // the table is rewritten for the next token
   }
 }
 
@@ -299,31 +402,42 @@ int32_t chunk_bytes(int32_t D, int32_t esize, const void* q, const void* k) {
 }
 
 template <typename T, int VEC>
-int32_t launch_vec(const RopeParams& p, bool long_index, dim3 grid, hipStream_t stream) {
+int32_t launch_vec(void* q, void* k, const int32_t* cu, const int32_t* seqused,
+                   const RopeParams& p, bool long_index, unsigned blocks, hipStream_t stream) {
+  T* qt = static_cast<T*>(q);
+  T* kt = static_cast<T*>(k);
   if (long_index)
-    hipLaunchKernelGGL((rope_qk_kernel<T, VEC, true>), grid, dim3(kBlock), 0, stream, p);
+    hipLaunchKernelGGL((rope_qk_kernel<T, VEC, true>), dim3(blocks), dim3(kBlock), 0, stream, qt,
+                       kt, cu, seqused, p);
   else
-    hipLaunchKernelGGL((rope_qk_kernel<T, VEC, false>), grid, dim3(kBlock), 0, stream, p);
+    hipLaunchKernelGGL((rope_qk_kernel<T, VEC, false>), dim3(blocks), dim3(kBlock), 0, stream, qt,
+                       kt, cu, seqused, p);
   return hipGetLastError() == hipSuccess ? ROPE_OK : ROPE_ELAUNCH;
 }
 
+// Tokens per wave when the caller does not choose: about 16K waves in flight over
+// the launch (a few rounds of 8 waves per SIMD on 1024 SIMDs), one token per wave
+// for batches up to 16K tokens.
+int32_t auto_tokens_per_wave(int64_t T) {
+  int64_t tpw = (T + 16383) / 16384;
+  return (int32_t)(tpw < 1 ? 1 : (tpw > 64 ? 64 : tpw));
+}
+
 template <typename T>
-int32_t launch_typed(RopeParams& p, int32_t bytes, bool long_index, hipStream_t stream) {
+int32_t launch_typed(void* q, void* k, const int32_t* cu, const int32_t* seqused, RopeParams& p,
+                     int32_t bytes, bool long_index, hipStream_t stream) {
   const int32_t vec = bytes / (int32_t)sizeof(T);
   p.nc = (p.D / 2) / vec;
-  if (p.nc > kBlock) return ROPE_EINVAL;  // cannot happen for D <= 512 and vec >= 1
-  p.tpb = kBlock / p.nc;
-  const int64_t gx = (p.T + p.tpb - 1) / p.tpb;
-  const int32_t H = p.Hq + p.Hkv;
-  const int64_t gy = (H + p.hpg - 1) / p.hpg;
-  if (gx > kMaxBlocksX || gy > 65535) return ROPE_EINVAL;
-  const dim3 grid((unsigned)gx, (unsigned)gy);
+  const int64_t waves = (p.T + p.tpw - 1) / p.tpw;
+  const int64_t blocks = (waves + kWaves - 1) / kWaves;
+  if (blocks > kMaxBlocksX) return ROPE_EINVAL;
   switch (vec) {
-    case 1: return launch_vec<T, 1>(p, long_index, grid, stream);
-    case 2: return launch_vec<T, 2>(p, long_index, grid, stream);
-    case 4: return launch_vec<T, 4>(p, long_index, grid, stream);
+    case 1: return launch_vec<T, 1>(q, k, cu, seqused, p, long_index, (unsigned)blocks, stream);
+    case 2: return launch_vec<T, 2>(q, k, cu, seqused, p, long_index, (unsigned)blocks, stream);
+    case 4: return launch_vec<T, 4>(q, k, cu, seqused, p, long_index, (unsigned)blocks, stream);
     default:
-      if constexpr (sizeof(T) == 2) return launch_vec<T, 8>(p, long_index, grid, stream);
+      if constexpr (sizeof(T) == 2)
+        return launch_vec<T, 8>(q, k, cu, seqused, p, long_index, (unsigned)blocks, stream);
       return ROPE_EINVAL;
   }
 }
@@ -335,7 +449,7 @@ extern "C" {
 int32_t rope_qk_apply(void* q, void* k, int64_t T, int32_t Hq, int32_t Hkv, int32_t D,
                       const int32_t* cu_seqlens, int32_t num_seqs, const int32_t* seqused,
                       double theta, int32_t dtype, int32_t direction, int32_t index_mode,
-                      int32_t heads_per_group, void* stream) {
+                      int32_t tokens_per_wave, void* stream) {
   if (dtype != ROPE_F32 && dtype != ROPE_BF16 && dtype != ROPE_F16) return ROPE_EUNSUPPORTED;
   if (T < 0 || T > ((int64_t)1 << 40)) return ROPE_EINVAL;
   if (Hq < 0 || Hkv < 0 || Hq > kMaxHeads || Hkv > kMaxHeads) return ROPE_EINVAL;
@@ -343,7 +457,7 @@ int32_t rope_qk_apply(void* q, void* k, int64_t T, int32_t Hq, int32_t Hkv, int3
   if (num_seqs < 0 || num_seqs == INT32_MAX) return ROPE_EINVAL;
   if (direction != 1 && direction != -1) return ROPE_EINVAL;
   if (index_mode < ROPE_INDEX_AUTO || index_mode > ROPE_INDEX_64) return ROPE_EINVAL;
-  if (heads_per_group < 0) return ROPE_EINVAL;
+  if (tokens_per_wave < 0 || tokens_per_wave > kMaxTokensPerWave) return ROPE_EINVAL;
   const int32_t H = Hq + Hkv;
   if (T > 0 && H == 0) return ROPE_EINVAL;
   if (T == 0 || num_seqs == 0) return ROPE_OK;  // nothing is rotated
@@ -355,26 +469,23 @@ int32_t rope_qk_apply(void* q, void* k, int64_t T, int32_t Hq, int32_t Hkv, int3
   const bool long_index = needs_long || index_mode == ROPE_INDEX_64;
 
   RopeParams p;
-  p.q = Hq > 0 ? q : nullptr;
-  p.k = Hkv > 0 ? k : nullptr;
   p.T = T;
-  p.cu = cu_seqlens;
-  p.seqused = seqused;
   p.num_seqs = num_seqs;
   p.Hq = Hq;
   p.Hkv = Hkv;
   p.D = D;
-  p.hpg = heads_per_group == 0 ? H : (heads_per_group < H ? heads_per_group : H);
+  p.tpw = tokens_per_wave == 0 ? auto_tokens_per_wave(T) : tokens_per_wave;
   p.sin_sign = direction > 0 ? 1.0f : -1.0f;
   host_inv_freq(theta, D, p.inv_freq);
 
-  const int32_t esize = elem_size(dtype);
-  const int32_t bytes = chunk_bytes(D, esize, p.q, p.k);
+  void* qp = Hq > 0 ? q : nullptr;
+  void* kp = Hkv > 0 ? k : nullptr;
+  const int32_t bytes = chunk_bytes(D, elem_size(dtype), qp, kp);
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (dtype) {
-    case ROPE_F32: return launch_typed<float>(p, bytes, long_index, s);
-    case ROPE_BF16: return launch_typed<__bf16>(p, bytes, long_index, s);
-    default: return launch_typed<_Float16>(p, bytes, long_index, s);
+    case ROPE_F32: return launch_typed<float>(qp, kp, cu_seqlens, seqused, p, bytes, long_index, s);
+    case ROPE_BF16: return launch_typed<__bf16>(qp, kp, cu_seqlens, seqused, p, bytes, long_index, s);
+    default: return launch_typed<_Float16>(qp, kp, cu_seqlens, seqused, p, bytes, long_index, s);
   }
 }
 

@@ -53,11 +53,11 @@ def test_version_and_status_strings():
 
 def apply(**kw):
     a = dict(q=FAKE, k=FAKE, T=16, Hq=4, Hkv=2, D=128, cu=FAKE, num_seqs=2, seqused=None,
-             theta=1e4, dtype=1, direction=1, index_mode=0, hpg=0, stream=None)
+             theta=1e4, dtype=1, direction=1, index_mode=0, tpw=0, stream=None)
     a.update(kw)
     return rope._lib.rope_qk_apply(a["q"], a["k"], a["T"], a["Hq"], a["Hkv"], a["D"], a["cu"],
                                    a["num_seqs"], a["seqused"], a["theta"], a["dtype"],
-                                   a["direction"], a["index_mode"], a["hpg"], a["stream"])
+                                   a["direction"], a["index_mode"], a["tpw"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,expect", [
@@ -79,7 +79,8 @@ def apply(**kw):
     (dict(direction=0), EINVAL),
     (dict(direction=2), EINVAL),
     (dict(index_mode=3), EINVAL),
-    (dict(hpg=-1), EINVAL),
+    (dict(tpw=-1), EINVAL),
+    (dict(tpw=1025), EINVAL),
     (dict(cu=None), EINVAL),
     (dict(q=None), EINVAL),
     (dict(k=None), EINVAL),

@@ -240,18 +240,17 @@ def test_cos_sin_export_bit_exact(rope, theta, D, maxpos):
 
 @pytest.mark.parametrize("name", ["tiny_packed", "qwen3_4b_packed"])
 def test_variants_bit_identical(rope, name):
-    """int64 indexing forced, and head groups of several sizes: same bits as default."""
+    """int64 indexing forced, and several launch geometries: same bits as default."""
     w = workloads.get(name)
     cu = torch.from_numpy(w.cu_seqlens).to(DEV)
     q0 = workloads.make_tensor(w.shape("q"), w.seed("q"), w.dtype).to(DEV)
     k0 = workloads.make_tensor(w.shape("k"), w.seed("k"), w.dtype).to(DEV)
     q_ref, k_ref = q0.clone(), k0.clone()
     rope.qk_fwd_(q_ref, k_ref, cu, w.theta)
-    H = w.Hq + w.Hkv
     for kw in (dict(index_mode=rope.INDEX_64), dict(index_mode=rope.INDEX_32),
-               dict(heads_per_group=1), dict(heads_per_group=3), dict(heads_per_group=8),
-               dict(heads_per_group=H - 1), dict(heads_per_group=4 * H),
-               dict(index_mode=rope.INDEX_64, heads_per_group=5)):
+               dict(tokens_per_wave=1), dict(tokens_per_wave=3), dict(tokens_per_wave=8),
+               dict(tokens_per_wave=min(w.T, 1024)), dict(tokens_per_wave=1024),
+               dict(index_mode=rope.INDEX_64, tokens_per_wave=5)):
         print(f"[parity] {name} variant {kw}", flush=True)
         q, k = q0.clone(), k0.clone()
         rope.qk_apply_(q, k, cu, w.theta, 1, **kw)
