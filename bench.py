@@ -12,8 +12,8 @@ HBM, as a training step would.
 
 Prints ONE JSON line (rank 0). `value` is tokens/s of whole steps (wall clock
 around K steps, bracketed by synchronize). `roofline` uses the kernel's average
-launch duration from HIP events recorded on the launch stream around each
-launch in the timed region; `traffic` comes from the committed rocprofv3 PMC
+launch duration from HIP events (timing-only, no system fence) recorded on the
+launch stream around both launches of every 4th step of the timed region; `traffic` comes from the committed rocprofv3 PMC
 summary when it was taken on the current kernel source, else null.
 `cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
 """
@@ -39,6 +39,7 @@ import workloads  # noqa: E402
 METRIC = "fused QK-RoPE fwd+bwd tokens/s and achieved HBM GB/s (% of peak), packed bf16"
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
 INFINITY_CACHE_BYTES = 256 * 2 ** 20
+EVENT_EVERY = 4
 KERNEL_SRC = os.path.join(ROOT, "packed_varlen_rotary_rope_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "rope_qk_qwen3_4b_packed_traffic.txt")
 
@@ -72,6 +73,117 @@ def read_traffic(bytes_per_launch: int):
         return int(float(kv["hbm_bytes_per_launch"]))
     except (KeyError, ValueError):
         return None
+
+
+class HipEvent:
+    """A HIP timing event created with hipEventDisableSystemFence: recording it
+    takes a timestamp on the stream without the system-scope cache writeback and
+    invalidate of a default event, so the interval around one launch is close to
+    the launch itself. Bound to the HIP runtime already mapped in this process
+    (the one torch and the library use)."""
+
+    _lib = None
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    @classmethod
+    def lib(cls):
+        if cls._lib is None:
+            import ctypes
+            paths = sorted({ln.split()[-1] for ln in open("/proc/self/maps")
+                            if "libamdhip64" in ln and ln.split()[-1].startswith("/")})
+            if not paths:
+                raise RuntimeError("no HIP runtime mapped in this process")
+            lib = ctypes.CDLL(paths[0])
+            lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                ctypes.c_void_p]
+            lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            cls._lib = lib
+        return cls._lib
+
+    def __init__(self):
+        import ctypes
+        self._ev = ctypes.c_void_p()
+        if self.lib().hipEventCreateWithFlags(ctypes.byref(self._ev), self.DISABLE_SYSTEM_FENCE):
+            raise RuntimeError("hipEventCreateWithFlags failed")
+
+    def record(self, stream: int):
+        if self.lib().hipEventRecord(self._ev, stream):
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_ms(self, end: "HipEvent") -> float:
+        import ctypes
+        ms = ctypes.c_float()
+        if self.lib().hipEventElapsedTime(ctypes.byref(ms), self._ev, end._ev):
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def __del__(self):
+        if self._lib is not None and self._ev:
+            self._lib.hipEventDestroy(self._ev)
+
+
+def _dispatch_means(csv_path: str) -> dict:
+    """Mean Counter_Value (KiB) per kernel name over the dispatches of a rocprofv3
+    --pmc CSV."""
+    import csv
+    acc = {}
+    with open(csv_path) as fh:
+        for row in csv.DictReader(fh):
+            acc.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+    return {k: (sum(v) / len(v), len(v)) for k, v in acc.items()}
+
+
+def write_traffic_summary(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, command: str):
+    """HBM bytes per launch of the rope kernel from two PMC passes (FETCH_SIZE, then
+    WRITE_SIZE), each scaled by what the same counter reads for a plain 1 GiB device
+    copy (written and read once), as a small text summary that main() reads back."""
+    w = workloads.get("qwen3_4b_packed")
+    bpl = algorithmic_bytes_per_launch(w)
+    copy_bytes = 2 ** 30
+
+    def kernel(means, key):
+        hits = [(k, v) for k, v in means.items() if key in k]
+        if not hits:
+            raise SystemExit(f"no dispatch of {key} in the counter file")
+        return max(hits, key=lambda kv: kv[1][1])[1]
+
+    def copy_kernel(means):
+        return max(means.items(), key=lambda kv: kv[1][0])[1]  # the 1 GiB copy dominates
+
+    f_k, nf = kernel(_dispatch_means(fetch_csv), "rope_qk_kernel")
+    w_k, nw = kernel(_dispatch_means(write_csv), "rope_qk_kernel")
+    f_c, _ = copy_kernel(_dispatch_means(copy_fetch_csv))
+    w_c, _ = copy_kernel(_dispatch_means(copy_write_csv))
+    f_scale = copy_bytes / (f_c * 1024.0)
+    w_scale = copy_bytes / (w_c * 1024.0)
+    read_b = f_k * 1024.0 * f_scale
+    write_b = w_k * 1024.0 * w_scale
+    lines = [
+        "# HBM traffic of rope_qk_kernel (bf16, D=128, Hq=32, Hkv=8) on the qwen3_4b_packed",
+        "# workload (T=16384), one launch = forward or backward over Q and K.",
+        "# Two rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE) over the same bench",
+        "# command, each counter scaled by its reading for a plain 1 GiB device copy.",
+        f"# commands: {command}",
+        f"fetch_kib_per_dispatch: {f_k:.1f}",
+        f"write_kib_per_dispatch: {w_k:.1f}",
+        f"dispatches_counted: {nf} {nw}",
+        f"copy_fetch_kib_for_1GiB: {f_c:.1f}",
+        f"copy_write_kib_for_1GiB: {w_c:.1f}",
+        f"fetch_scale: {f_scale:.5f}",
+        f"write_scale: {w_scale:.5f}",
+        f"hbm_read_bytes_per_launch: {read_b:.0f}",
+        f"hbm_write_bytes_per_launch: {write_b:.0f}",
+        f"hbm_bytes_per_launch: {read_b + write_b:.0f}",
+        f"algorithmic_bytes_per_launch: {bpl}",
+        f"traffic_over_algorithmic: {(read_b + write_b) / bpl:.4f}",
+        f"kernel_source_sha256_16: {kernel_source_hash()}",
+    ]
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def make_sets(w, nsets, dev):
@@ -130,7 +242,15 @@ def main():
                     help="timed oracle work for cpu_baseline (0 disables it)")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
                     help="only run a plain copy of this many GiB (PMC scale factor), then exit")
+    ap.add_argument("--traffic-summary", nargs=4, default=None,
+                    metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="write the PMC traffic summary from rocprofv3 counter CSVs, then exit")
+    ap.add_argument("--traffic-command", default="", help="commands recorded in that summary")
     args = ap.parse_args()
+
+    if args.traffic_summary:
+        write_traffic_summary(*args.traffic_summary, command=args.traffic_command)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -150,37 +270,43 @@ def main():
     dev = torch.device("cuda:0")
     w = workloads.get(args.workload)
     set_bytes = 2 * w.T * (w.Hq + w.Hkv) * w.D * w.elem_bytes  # Q, K, dQ, dK
-    nsets = max(2, math.ceil(4 * INFINITY_CACHE_BYTES / set_bytes))
+    # Enough sets that a buffer is touched again only after >= 8x the Infinity
+    # Cache's capacity of other traffic: no launch can be served from it.
+    nsets = max(2, math.ceil(8 * INFINITY_CACHE_BYTES / set_bytes))
     cu, su, sets = make_sets(w, nsets, dev)
     tpw = args.tokens_per_wave
 
+    stream = torch.cuda.current_stream(dev).cuda_stream  # the stream the library launches on
+
     def step(s, ev=None):
         if ev is not None:
-            ev[0].record()
+            ev[0].record(stream)
         rope.qk_apply_(s["q"], s["k"], cu, w.theta, 1, seqused=su, tokens_per_wave=tpw)
         if ev is not None:
-            ev[1].record()
-            ev[2].record()
+            ev[1].record(stream)
+            ev[2].record(stream)
         rope.qk_apply_(s["dq"], s["dk"], cu, w.theta, -1, seqused=su, tokens_per_wave=tpw)
         if ev is not None:
-            ev[3].record()
+            ev[3].record(stream)
 
     for i in range(args.warmup):
         step(sets[i % nsets])
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # Per-launch HIP events, on the launch stream, around both launches of every
+    # EVENT_EVERY-th step of the timed region (fewer event packets between kernels).
+    events = {i: [HipEvent() for _ in range(4)] for i in range(0, args.steps, EVENT_EVERY)}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(sets[i % nsets], events[i])
+        step(sets[i % nsets], events.get(i))
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
     launch_ms = []
-    for ev in events:
-        launch_ms.append(ev[0].elapsed_time(ev[1]))
-        launch_ms.append(ev[2].elapsed_time(ev[3]))
+    for ev in events.values():
+        launch_ms.append(ev[0].elapsed_ms(ev[1]))
+        launch_ms.append(ev[2].elapsed_ms(ev[3]))
     avg_launch_s = float(np.mean(launch_ms)) / 1e3
     bpl = algorithmic_bytes_per_launch(w)
     achieved = bpl / avg_launch_s / 1e9
