@@ -64,7 +64,7 @@ def read_traffic(bytes_per_launch: int):
         return None
     kv = {}
     for line in open(TRAFFIC_FILE):
-        m = re.match(r"^\s*([a-z_]+)\s*[:=]\s*(\S+)", line)
+        m = re.match(r"^\s*([a-z_0-9]+)\s*[:=]\s*(\S+)", line)
         if m:
             kv[m.group(1)] = m.group(2)
     if kv.get("kernel_source_sha256_16") != kernel_source_hash():
