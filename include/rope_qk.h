@@ -114,17 +114,60 @@ int32_t rope_qk_apply(void* q, void* k, int64_t T, int32_t Hq, int32_t Hkv, int3
                       double theta, int32_t dtype, int32_t direction, int32_t index_mode,
                       int32_t tokens_per_wave, void* stream);
 
+/* The most general entry point: positions from explicit ids or from cu_seqlens
+ * with per-sequence offsets, and linear position interpolation.
+ *  seq_offsets   device int32[num_seqs] or NULL: added to every position of
+ *                sequence s (a context-parallel shard of a longer sequence passes
+ *                the global position of its first token). A token whose shifted
+ *                position falls outside [0, 2^31) is left untouched.
+ *  position_ids  device int32[T] or NULL: when given, token t has position
+ *                position_ids[t] and cu_seqlens, num_seqs, seqused and seq_offsets
+ *                are ignored (may be NULL / 0); a negative id leaves the token
+ *                untouched. This is the per-example position_ids representation of
+ *                a 1-D packed batch (Databricks, "Reduire le temps d'entrainement de
+ *                Qwen de 6x sur AI Runtime", section "Mise en lots, tokenisation et
+ *                padding").
+ *  pos_scale     linear position interpolation factor s, rounded to fp32, finite
+ *                and >= 1: the angle becomes fp32(fp32(pos) / s) * inv_freq[j], so
+ *                position s*p rotates exactly like position p (TRL guide
+ *                "Entrainement au-dela de 1 M de jetons", YaRN section: with factor 4,
+ *                position 100000 is treated as position 25000). 1 = no scaling.
+ * Other arguments as in rope_qk_apply. */
+int32_t rope_qk_apply_ex(void* q, void* k, int64_t T, int32_t Hq, int32_t Hkv, int32_t D,
+                         const int32_t* cu_seqlens, int32_t num_seqs, const int32_t* seqused,
+                         const int32_t* seq_offsets, const int32_t* position_ids, double theta,
+                         double pos_scale, int32_t dtype, int32_t direction, int32_t index_mode,
+                         int32_t tokens_per_wave, void* stream);
+
+/* Forward / backward RoPE with explicit positions: position_ids is a device
+ * int32[T] (required when T > 0); negative ids leave their token untouched.
+ * Other arguments as in rope_qk_fwd. */
+int32_t rope_qk_fwd_pos(void* q, void* k, int64_t T, int32_t Hq, int32_t Hkv, int32_t D,
+                        const int32_t* position_ids, double theta, int32_t dtype, void* stream);
+int32_t rope_qk_bwd_pos(void* dq, void* dk, int64_t T, int32_t Hq, int32_t Hkv, int32_t D,
+                        const int32_t* position_ids, double theta, int32_t dtype, void* stream);
+
 /* Export of the token -> (position, sequence) map the kernels use (test hook,
  * same device code). pos_out, seq_out: device int32[T] (either may be NULL);
  * -1 for tokens that are left untouched. Validation as in rope_qk_fwd. */
 int32_t rope_positions(const int32_t* cu_seqlens, int32_t num_seqs, const int32_t* seqused,
                        int64_t T, int32_t* pos_out, int32_t* seq_out, void* stream);
 
+/* rope_positions with the position sources of rope_qk_apply_ex (seq_offsets,
+ * position_ids). seq_out is -1 for every token when position_ids is given. */
+int32_t rope_positions_ex(const int32_t* cu_seqlens, int32_t num_seqs, const int32_t* seqused,
+                          const int32_t* seq_offsets, const int32_t* position_ids, int64_t T,
+                          int32_t* pos_out, int32_t* seq_out, void* stream);
+
 /* Export of the fp32 cos/sin the kernels use (test hook, same device code):
  * for each of the n positions in the device array positions (each >= 0) and each
  * j < D/2, cos_out[i*(D/2) + j] and sin_out[i*(D/2) + j] (device float arrays). */
 int32_t rope_cos_sin(const int32_t* positions, int64_t n, int32_t D, double theta,
                      float* cos_out, float* sin_out, void* stream);
+
+/* rope_cos_sin with linear position interpolation (pos_scale as in rope_qk_apply_ex). */
+int32_t rope_cos_sin_ex(const int32_t* positions, int64_t n, int32_t D, double theta,
+                        double pos_scale, float* cos_out, float* sin_out, void* stream);
 
 /* Host-only: the fp32 inverse frequencies theta^(-2j/D), j < D/2, written to the
  * host array out[D/2]. Same validation of D and theta as rope_qk_fwd. */

@@ -63,6 +63,16 @@ class Oracle:
         lib.oracle_fwd_bwd_seconds.argtypes = [i32, vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, i32,
                                                i32, vp, i32, vp, dbl, i32]
         lib.oracle_fwd_bwd_seconds.restype = dbl
+        lib.oracle_cos_sin_ex.argtypes = [vp, i64, i32, dbl, dbl, vp, vp]
+        lib.oracle_cos_sin_ex.restype = None
+        lib.oracle_positions_ex.argtypes = [vp, i32, vp, vp, vp, i64, vp, vp]
+        lib.oracle_positions_ex.restype = None
+        lib.oracle_rope_ex.argtypes = [i32, vp, vp, i64, i32, i32, vp, i32, vp, vp, vp, dbl, dbl,
+                                       i32, i32]
+        lib.oracle_rope_ex.restype = i32
+        lib.oracle_rope_rows_ex.argtypes = [i32, vp, vp, vp, i64, i32, i32, vp, i32, vp, vp, vp,
+                                            dbl, dbl, i32, i32]
+        lib.oracle_rope_rows_ex.restype = i32
         self.lib = lib
         self.path = path
 
@@ -71,50 +81,57 @@ class Oracle:
         self.lib.oracle_inv_freq(float(theta), int(D), _ptr(out))
         return out
 
-    def cos_sin(self, positions, D: int, theta: float):
+    def cos_sin(self, positions, D: int, theta: float, pos_scale: float = 1.0):
         pos = _i32(np.atleast_1d(positions))
         c = np.empty((pos.size, D // 2), dtype=np.float32)
         s = np.empty_like(c)
-        self.lib.oracle_cos_sin(_ptr(pos), pos.size, int(D), float(theta), _ptr(c), _ptr(s))
+        self.lib.oracle_cos_sin_ex(_ptr(pos), pos.size, int(D), float(theta), float(pos_scale),
+                                   _ptr(c), _ptr(s))
         return c, s
 
-    def positions(self, cu_seqlens, T: int, seqused=None):
-        cu = _i32(cu_seqlens)
-        su = _i32(seqused)
+    def positions(self, cu_seqlens, T: int, seqused=None, seq_offsets=None, position_ids=None):
+        cu, su, so, pid = (_i32(a) for a in (cu_seqlens, seqused, seq_offsets, position_ids))
         pos = np.empty(int(T), dtype=np.int32)
         seq = np.empty(int(T), dtype=np.int32)
-        self.lib.oracle_positions(_ptr(cu), cu.size - 1, _ptr(su), int(T), _ptr(pos), _ptr(seq))
+        num_seqs = 0 if cu is None else cu.size - 1
+        self.lib.oracle_positions_ex(_ptr(cu), num_seqs, _ptr(su), _ptr(so), _ptr(pid), int(T),
+                                     _ptr(pos), _ptr(seq))
         return pos, seq
 
     def rope(self, x: np.ndarray, cu_seqlens, theta: float, direction: int = 1,
-             dtype: str = "f32", seqused=None, nthreads: int = 1) -> np.ndarray:
+             dtype: str = "f32", seqused=None, nthreads: int = 1, seq_offsets=None,
+             position_ids=None, pos_scale: float = 1.0) -> np.ndarray:
         """Rotate a packed tensor x[T, H, D]; returns the fp32 result, same shape."""
         xs = _storage(x, dtype)
         T, H, D = xs.shape
-        cu, su = _i32(cu_seqlens), _i32(seqused)
+        cu, su, so, pid = (_i32(a) for a in (cu_seqlens, seqused, seq_offsets, position_ids))
+        num_seqs = 0 if cu is None else cu.size - 1
         y = np.empty((T, H, D), dtype=np.float32)
-        rc = self.lib.oracle_rope(_DTYPES[dtype], _ptr(xs), _ptr(y), T, H, D, _ptr(cu),
-                                  cu.size - 1, _ptr(su), float(theta), int(direction),
-                                  int(nthreads))
+        rc = self.lib.oracle_rope_ex(_DTYPES[dtype], _ptr(xs), _ptr(y), T, H, D, _ptr(cu),
+                                     num_seqs, _ptr(su), _ptr(so), _ptr(pid), float(theta),
+                                     float(pos_scale), int(direction), int(nthreads))
         if rc != 0:
-            raise ValueError("oracle_rope rejected its arguments")
+            raise ValueError("oracle_rope_ex rejected its arguments")
         return y
 
     def rope_rows(self, x_rows: np.ndarray, tokens, cu_seqlens, theta: float, direction: int = 1,
-                  dtype: str = "f32", seqused=None, nthreads: int = 1) -> np.ndarray:
+                  dtype: str = "f32", seqused=None, nthreads: int = 1, seq_offsets=None,
+                  position_ids=None, pos_scale: float = 1.0) -> np.ndarray:
         """Outputs for the listed tokens only; x_rows[n, H, D] are their input rows."""
         xs = _storage(x_rows, dtype)
         n, H, D = xs.shape
         tok = np.ascontiguousarray(tokens, dtype=np.int64)
         if tok.size != n:
             raise ValueError("one token index per input row")
-        cu, su = _i32(cu_seqlens), _i32(seqused)
+        cu, su, so, pid = (_i32(a) for a in (cu_seqlens, seqused, seq_offsets, position_ids))
+        num_seqs = 0 if cu is None else cu.size - 1
         y = np.empty((n, H, D), dtype=np.float32)
-        rc = self.lib.oracle_rope_rows(_DTYPES[dtype], _ptr(xs), _ptr(y), _ptr(tok), n, H, D,
-                                       _ptr(cu), cu.size - 1, _ptr(su), float(theta),
-                                       int(direction), int(nthreads))
+        rc = self.lib.oracle_rope_rows_ex(_DTYPES[dtype], _ptr(xs), _ptr(y), _ptr(tok), n, H, D,
+                                          _ptr(cu), num_seqs, _ptr(su), _ptr(so), _ptr(pid),
+                                          float(theta), float(pos_scale), int(direction),
+                                          int(nthreads))
         if rc != 0:
-            raise ValueError("oracle_rope_rows rejected its arguments")
+            raise ValueError("oracle_rope_rows_ex rejected its arguments")
         return y
 
     def round_bf16(self, y: np.ndarray) -> np.ndarray:
@@ -157,22 +174,24 @@ def inv_freq(theta, D):
     return default().inv_freq(theta, D)
 
 
-def cos_sin(positions, D, theta):
-    return default().cos_sin(positions, D, theta)
+def cos_sin(positions, D, theta, pos_scale=1.0):
+    return default().cos_sin(positions, D, theta, pos_scale)
 
 
-def positions(cu_seqlens, T, seqused=None):
-    return default().positions(cu_seqlens, T, seqused)
+def positions(cu_seqlens, T, seqused=None, seq_offsets=None, position_ids=None):
+    return default().positions(cu_seqlens, T, seqused, seq_offsets, position_ids)
 
 
-def rope(x, cu_seqlens, theta, direction=1, dtype="f32", seqused=None, nthreads=1):
-    return default().rope(x, cu_seqlens, theta, direction, dtype, seqused, nthreads)
+def rope(x, cu_seqlens, theta, direction=1, dtype="f32", seqused=None, nthreads=1,
+         seq_offsets=None, position_ids=None, pos_scale=1.0):
+    return default().rope(x, cu_seqlens, theta, direction, dtype, seqused, nthreads, seq_offsets,
+                          position_ids, pos_scale)
 
 
 def rope_rows(x_rows, tokens, cu_seqlens, theta, direction=1, dtype="f32", seqused=None,
-              nthreads=1):
+              nthreads=1, seq_offsets=None, position_ids=None, pos_scale=1.0):
     return default().rope_rows(x_rows, tokens, cu_seqlens, theta, direction, dtype, seqused,
-                               nthreads)
+                               nthreads, seq_offsets, position_ids, pos_scale)
 
 
 def round_bf16(y):

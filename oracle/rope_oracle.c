@@ -39,6 +39,13 @@
  *  R6 the rotation is evaluated exactly (both products are exact in double) and
  *     rounded once to fp32; bf16 outputs are that fp32 value rounded to nearest
  *     even.
+ *  R7 explicit positions: token t uses position_ids[t]; a negative id leaves it
+ *     untouched (Databricks page above: per-example position ids of a 1-D packed
+ *     batch). Per-sequence offsets: position p of sequence s becomes
+ *     p + seq_offsets[s]; a result outside [0, 2^31) leaves the token untouched.
+ *  R8 linear position interpolation by a factor f >= 1 (TRL guide, YaRN section:
+ *     with factor 4, position 100000 is treated as 25000): the fp32 position is
+ *     divided by the fp32 factor (one rounding) before the angle multiply.
  *
  * Parity pins: every function here is checked against something other than
  * itself in tests/test_oracle_pins.py (closed forms, mpmath, the block matrix R
@@ -103,20 +110,28 @@ void oracle_inv_freq(double theta, int32_t D, float* out) {
 
 /* ---- R4 + R5: angle and fp32 cos/sin for one (position, frequency) ------------ */
 
-static void cos_sin_one(int32_t pos, float inv_freq_j, float* c, float* s) {
-  float angle = (float)pos * inv_freq_j; /* one fp32 multiply */
+static void cos_sin_one(int32_t pos, float scale, float inv_freq_j, float* c, float* s) {
+  float p = (float)pos;
+  if (scale != 1.0f) p = p / scale;  /* R8: one fp32 division */
+  float angle = p * inv_freq_j;      /* one fp32 multiply */
   *c = (float)cosl((long double)angle);
   *s = (float)sinl((long double)angle);
 }
 
 /* Table of cos/sin for a list of positions: out[i*(D/2) + j]. */
-void oracle_cos_sin(const int32_t* pos, int64_t npos, int32_t D, double theta,
-                    float* cos_out, float* sin_out) {
+void oracle_cos_sin_ex(const int32_t* pos, int64_t npos, int32_t D, double theta,
+                       double pos_scale, float* cos_out, float* sin_out) {
   float inv_freq[1024];
   oracle_inv_freq(theta, D, inv_freq);
   for (int64_t i = 0; i < npos; ++i)
     for (int32_t j = 0; j < D / 2; ++j)
-      cos_sin_one(pos[i], inv_freq[j], &cos_out[i * (D / 2) + j], &sin_out[i * (D / 2) + j]);
+      cos_sin_one(pos[i], (float)pos_scale, inv_freq[j], &cos_out[i * (D / 2) + j],
+                  &sin_out[i * (D / 2) + j]);
+}
+
+void oracle_cos_sin(const int32_t* pos, int64_t npos, int32_t D, double theta,
+                    float* cos_out, float* sin_out) {
+  oracle_cos_sin_ex(pos, npos, D, theta, 1.0, cos_out, sin_out);
 }
 
 /* ---- R3: token -> (sequence id, position), by walking the sequences ------------ */
@@ -128,30 +143,52 @@ static int64_t used_len(const int32_t* cu, const int32_t* seqused, int32_t s) {
   return len < 0 ? 0 : len;
 }
 
+/* Position after the per-sequence offset (R7), or -1 when it leaves [0, 2^31). */
+static int32_t shifted(int64_t p, const int32_t* seq_offsets, int32_t s) {
+  int64_t q = p + (seq_offsets ? (int64_t)seq_offsets[s] : 0);
+  return (q < 0 || q > 2147483647LL) ? -1 : (int32_t)q;
+}
+
 /* pos_out[t] / seq_out[t] = position and sequence of token t, or -1 / -1 for a
- * token that is left untouched. Either output may be NULL. */
-void oracle_positions(const int32_t* cu, int32_t num_seqs, const int32_t* seqused, int64_t T,
-                      int32_t* pos_out, int32_t* seq_out) {
+ * token that is left untouched. Either output may be NULL. With position_ids the
+ * sequence ids are all -1. */
+void oracle_positions_ex(const int32_t* cu, int32_t num_seqs, const int32_t* seqused,
+                         const int32_t* seq_offsets, const int32_t* position_ids, int64_t T,
+                         int32_t* pos_out, int32_t* seq_out) {
   for (int64_t t = 0; t < T; ++t) {
     if (pos_out) pos_out[t] = -1;
     if (seq_out) seq_out[t] = -1;
+  }
+  if (position_ids) {
+    for (int64_t t = 0; t < T; ++t)
+      if (pos_out) pos_out[t] = position_ids[t] < 0 ? -1 : position_ids[t];
+    return;
   }
   for (int32_t s = 0; s < num_seqs; ++s) {
     int64_t len = used_len(cu, seqused, s);
     for (int64_t p = 0; p < len; ++p) {
       int64_t t = (int64_t)cu[s] + p;
       if (t < 0 || t >= T) continue;
-      if (pos_out) pos_out[t] = (int32_t)p;
+      int32_t pe = shifted(p, seq_offsets, s);
+      if (pe < 0) continue;
+      if (pos_out) pos_out[t] = pe;
       if (seq_out) seq_out[t] = s;
     }
   }
 }
 
+void oracle_positions(const int32_t* cu, int32_t num_seqs, const int32_t* seqused, int64_t T,
+                      int32_t* pos_out, int32_t* seq_out) {
+  oracle_positions_ex(cu, num_seqs, seqused, NULL, NULL, T, pos_out, seq_out);
+}
+
 /* Position of one token, or -1 if untouched: the same walk, stopped at t. */
-static int32_t position_of(const int32_t* cu, int32_t num_seqs, const int32_t* seqused, int64_t t) {
+static int32_t position_of(const int32_t* cu, int32_t num_seqs, const int32_t* seqused,
+                           const int32_t* seq_offsets, const int32_t* position_ids, int64_t t) {
+  if (position_ids) return position_ids[t] < 0 ? -1 : position_ids[t];
   for (int32_t s = 0; s < num_seqs; ++s) {
     int64_t p = t - (int64_t)cu[s];
-    if (p >= 0 && p < used_len(cu, seqused, s)) return (int32_t)p;
+    if (p >= 0 && p < used_len(cu, seqused, s)) return shifted(p, seq_offsets, s);
   }
   return -1;
 }
@@ -188,13 +225,15 @@ static int check_args(int32_t dtype, int32_t H, int32_t D) {
 /* Apply the rotation to a whole packed tensor x[T, H, D] (one of Q, K, dQ, dK).
  * y[T, H, D] receives the fp32 result; untouched tokens receive their input value.
  * Parallel over the positions of each sequence (nthreads <= 0: one thread). */
-int32_t oracle_rope(int32_t dtype, const void* x, float* y, int64_t T, int32_t H, int32_t D,
-                    const int32_t* cu, int32_t num_seqs, const int32_t* seqused, double theta,
-                    int32_t dir, int32_t nthreads) {
+int32_t oracle_rope_ex(int32_t dtype, const void* x, float* y, int64_t T, int32_t H, int32_t D,
+                       const int32_t* cu, int32_t num_seqs, const int32_t* seqused,
+                       const int32_t* seq_offsets, const int32_t* position_ids, double theta,
+                       double pos_scale, int32_t dir, int32_t nthreads) {
   if (check_args(dtype, H, D) || T < 0 || num_seqs < 0) return -1;
   if (nthreads <= 0) nthreads = 1;
   float inv_freq[1024];
   oracle_inv_freq(theta, D, inv_freq);
+  const float scale = (float)pos_scale;
   int64_t row_elems = (int64_t)H * D;
 
   /* Start from the input: tokens outside every sequence keep their value. */
@@ -203,14 +242,31 @@ int32_t oracle_rope(int32_t dtype, const void* x, float* y, int64_t T, int32_t H
     for (int32_t h = 0; h < H; ++h)
       copy_row(dtype, x, t * row_elems + (int64_t)h * D, y + t * row_elems + (int64_t)h * D, D);
 
+  if (position_ids) { /* R7: explicit positions */
+#pragma omp parallel for num_threads(nthreads) schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+      int32_t pe = position_ids[t];
+      if (pe < 0) continue;
+      float cs[1024], sn[1024];
+      for (int32_t j = 0; j < D / 2; ++j) cos_sin_one(pe, scale, inv_freq[j], &cs[j], &sn[j]);
+      for (int32_t h = 0; h < H; ++h) {
+        int64_t off = t * row_elems + (int64_t)h * D;
+        rotate_row(dtype, x, off, y + off, D, cs, sn, dir);
+      }
+    }
+    return 0;
+  }
+
   for (int32_t s = 0; s < num_seqs; ++s) {
     int64_t len = used_len(cu, seqused, s);
 #pragma omp parallel for num_threads(nthreads) schedule(static)
     for (int64_t p = 0; p < len; ++p) {
       int64_t t = (int64_t)cu[s] + p;
       if (t < 0 || t >= T) continue;
+      int32_t pe = shifted(p, seq_offsets, s);
+      if (pe < 0) continue;
       float cs[1024], sn[1024];
-      for (int32_t j = 0; j < D / 2; ++j) cos_sin_one((int32_t)p, inv_freq[j], &cs[j], &sn[j]);
+      for (int32_t j = 0; j < D / 2; ++j) cos_sin_one(pe, scale, inv_freq[j], &cs[j], &sn[j]);
       for (int32_t h = 0; h < H; ++h) {
         int64_t off = t * row_elems + (int64_t)h * D;
         rotate_row(dtype, x, off, y + off, D, cs, sn, dir);
@@ -220,23 +276,33 @@ int32_t oracle_rope(int32_t dtype, const void* x, float* y, int64_t T, int32_t H
   return 0;
 }
 
+int32_t oracle_rope(int32_t dtype, const void* x, float* y, int64_t T, int32_t H, int32_t D,
+                    const int32_t* cu, int32_t num_seqs, const int32_t* seqused, double theta,
+                    int32_t dir, int32_t nthreads) {
+  return oracle_rope_ex(dtype, x, y, T, H, D, cu, num_seqs, seqused, NULL, NULL, theta, 1.0, dir,
+                        nthreads);
+}
+
 /* Same result for a list of tokens only. x_rows[n, H, D] holds the input rows of
  * tokens[0..n) (gathered by the caller); y_rows[n, H, D] receives their outputs.
  * The position of each token is found by walking the sequences. */
-int32_t oracle_rope_rows(int32_t dtype, const void* x_rows, float* y_rows, const int64_t* tokens,
-                         int64_t n, int32_t H, int32_t D, const int32_t* cu, int32_t num_seqs,
-                         const int32_t* seqused, double theta, int32_t dir, int32_t nthreads) {
+int32_t oracle_rope_rows_ex(int32_t dtype, const void* x_rows, float* y_rows,
+                            const int64_t* tokens, int64_t n, int32_t H, int32_t D,
+                            const int32_t* cu, int32_t num_seqs, const int32_t* seqused,
+                            const int32_t* seq_offsets, const int32_t* position_ids,
+                            double theta, double pos_scale, int32_t dir, int32_t nthreads) {
   if (check_args(dtype, H, D) || n < 0 || num_seqs < 0) return -1;
   if (nthreads <= 0) nthreads = 1;
   float inv_freq[1024];
   oracle_inv_freq(theta, D, inv_freq);
+  const float scale = (float)pos_scale;
   int64_t row_elems = (int64_t)H * D;
 #pragma omp parallel for num_threads(nthreads) schedule(dynamic, 16)
   for (int64_t i = 0; i < n; ++i) {
-    int32_t p = position_of(cu, num_seqs, seqused, tokens[i]);
+    int32_t p = position_of(cu, num_seqs, seqused, seq_offsets, position_ids, tokens[i]);
     float cs[1024], sn[1024];
     if (p >= 0)
-      for (int32_t j = 0; j < D / 2; ++j) cos_sin_one(p, inv_freq[j], &cs[j], &sn[j]);
+      for (int32_t j = 0; j < D / 2; ++j) cos_sin_one(p, scale, inv_freq[j], &cs[j], &sn[j]);
     for (int32_t h = 0; h < H; ++h) {
       int64_t off = i * row_elems + (int64_t)h * D;
       if (p >= 0)
@@ -246,6 +312,13 @@ int32_t oracle_rope_rows(int32_t dtype, const void* x_rows, float* y_rows, const
     }
   }
   return 0;
+}
+
+int32_t oracle_rope_rows(int32_t dtype, const void* x_rows, float* y_rows, const int64_t* tokens,
+                         int64_t n, int32_t H, int32_t D, const int32_t* cu, int32_t num_seqs,
+                         const int32_t* seqused, double theta, int32_t dir, int32_t nthreads) {
+  return oracle_rope_rows_ex(dtype, x_rows, y_rows, tokens, n, H, D, cu, num_seqs, seqused, NULL,
+                             NULL, theta, 1.0, dir, nthreads);
 }
 
 /* ---- comparison helpers ------------------------------------------------------ */

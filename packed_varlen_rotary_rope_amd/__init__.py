@@ -20,8 +20,9 @@ import os
 import torch
 
 __all__ = [
-    "RopeError", "qk_fwd_", "qk_bwd_", "qk_apply_", "positions", "cos_sin", "inv_freq",
-    "abi_version", "LIB_PATH", "INDEX_AUTO", "INDEX_32", "INDEX_64",
+    "RopeError", "qk_fwd_", "qk_bwd_", "qk_apply_", "qk_apply_ex_", "qk_fwd_pos_", "qk_bwd_pos_",
+    "positions", "cos_sin", "inv_freq", "abi_version", "LIB_PATH", "INDEX_AUTO", "INDEX_32",
+    "INDEX_64",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librope_qk.so")
@@ -48,11 +49,18 @@ def _load() -> ctypes.CDLL:
     lib.rope_qk_fwd.argtypes = qk + [vp]
     lib.rope_qk_bwd.argtypes = qk + [vp]
     lib.rope_qk_apply.argtypes = qk + [i32, i32, i32, vp]
+    lib.rope_qk_apply_ex.argtypes = [vp, vp, i64, i32, i32, i32, vp, i32, vp, vp, vp, dbl, dbl,
+                                     i32, i32, i32, i32, vp]
+    lib.rope_qk_fwd_pos.argtypes = [vp, vp, i64, i32, i32, i32, vp, dbl, i32, vp]
+    lib.rope_qk_bwd_pos.argtypes = [vp, vp, i64, i32, i32, i32, vp, dbl, i32, vp]
     lib.rope_positions.argtypes = [vp, i32, vp, i64, vp, vp, vp]
+    lib.rope_positions_ex.argtypes = [vp, i32, vp, vp, vp, i64, vp, vp, vp]
     lib.rope_cos_sin.argtypes = [vp, i64, i32, dbl, vp, vp, vp]
+    lib.rope_cos_sin_ex.argtypes = [vp, i64, i32, dbl, dbl, vp, vp, vp]
     lib.rope_inv_freq.argtypes = [dbl, i32, vp]
-    for name in ("rope_qk_fwd", "rope_qk_bwd", "rope_qk_apply", "rope_positions", "rope_cos_sin",
-                 "rope_inv_freq", "rope_abi_version"):
+    for name in ("rope_qk_fwd", "rope_qk_bwd", "rope_qk_apply", "rope_qk_apply_ex",
+                 "rope_qk_fwd_pos", "rope_qk_bwd_pos", "rope_positions", "rope_positions_ex",
+                 "rope_cos_sin", "rope_cos_sin_ex", "rope_inv_freq", "rope_abi_version"):
         getattr(lib, name).restype = i32
     lib.rope_status_str.argtypes = [i32]
     lib.rope_status_str.restype = ctypes.c_char_p
@@ -88,6 +96,19 @@ def _index_tensor(t, name: str, device: torch.device):
     return t
 
 
+def _qk_tensors(q, k):
+    if q.device.type != "cuda" or k.device != q.device:
+        raise TypeError("q and k must be on the same GPU")
+    if q.dtype != k.dtype or q.dtype not in _DTYPE_CODE:
+        raise TypeError("q and k must share one dtype: float32, bfloat16 or float16")
+    if q.dim() != 3 or k.dim() != 3 or q.shape[0] != k.shape[0] or q.shape[2] != k.shape[2]:
+        raise ValueError("expected q[T, Hq, D] and k[T, Hkv, D]")
+    if not (q.is_contiguous() and k.is_contiguous()):
+        raise ValueError("q and k must be contiguous (rotation is in place)")
+    T, Hq, D = q.shape
+    return T, Hq, k.shape[1], D
+
+
 def _qk_args(q, k, cu_seqlens, seqused):
     if q.device.type != "cuda" or k.device != q.device:
         raise TypeError("q and k must be on the same GPU")
@@ -118,6 +139,57 @@ def qk_apply_(q, k, cu_seqlens, theta: float, direction: int = 1, seqused=None,
     return q, k
 
 
+def qk_apply_ex_(q, k, theta: float, direction: int = 1, cu_seqlens=None, seqused=None,
+                 seq_offsets=None, position_ids=None, pos_scale: float = 1.0,
+                 index_mode: int = INDEX_AUTO, tokens_per_wave: int = 0):
+    """The general form: positions from `position_ids` (int32[T], negative = untouched)
+    or from `cu_seqlens` (+ optional `seqused`, `seq_offsets`), angles with linear
+    position interpolation by `pos_scale` (>= 1). In place; returns (q, k)."""
+    T, Hq, Hkv, D = _qk_tensors(q, k)
+    cu = _index_tensor(cu_seqlens, "cu_seqlens", q.device)
+    su = _index_tensor(seqused, "seqused", q.device)
+    so = _index_tensor(seq_offsets, "seq_offsets", q.device)
+    pid = _index_tensor(position_ids, "position_ids", q.device)
+    if pid is None and cu is None:
+        raise ValueError("give cu_seqlens or position_ids")
+    if pid is not None and pid.numel() != T:
+        raise ValueError("position_ids must have one entry per token")
+    num_seqs = 0 if cu is None else cu.numel() - 1
+    for name, t in (("seqused", su), ("seq_offsets", so)):
+        if t is not None and t.numel() != num_seqs:
+            raise ValueError(f"{name} must have one entry per sequence")
+    st = _lib.rope_qk_apply_ex(_ptr(q), _ptr(k), T, Hq, Hkv, D, _ptr(cu), num_seqs, _ptr(su),
+                               _ptr(so), _ptr(pid), float(theta), float(pos_scale),
+                               _DTYPE_CODE[q.dtype], int(direction), int(index_mode),
+                               int(tokens_per_wave), _stream(q.device))
+    _check(st, "rope_qk_apply_ex")
+    return q, k
+
+
+def qk_fwd_pos_(q, k, position_ids, theta: float):
+    """Forward RoPE in place with explicit positions (int32[T]; negative = untouched)."""
+    T, Hq, Hkv, D = _qk_tensors(q, k)
+    pid = _index_tensor(position_ids, "position_ids", q.device)
+    if pid.numel() != T:
+        raise ValueError("position_ids must have one entry per token")
+    st = _lib.rope_qk_fwd_pos(_ptr(q), _ptr(k), T, Hq, Hkv, D, _ptr(pid), float(theta),
+                              _DTYPE_CODE[q.dtype], _stream(q.device))
+    _check(st, "rope_qk_fwd_pos")
+    return q, k
+
+
+def qk_bwd_pos_(dq, dk, position_ids, theta: float):
+    """Backward RoPE in place with explicit positions (int32[T]; negative = untouched)."""
+    T, Hq, Hkv, D = _qk_tensors(dq, dk)
+    pid = _index_tensor(position_ids, "position_ids", dq.device)
+    if pid.numel() != T:
+        raise ValueError("position_ids must have one entry per token")
+    st = _lib.rope_qk_bwd_pos(_ptr(dq), _ptr(dk), T, Hq, Hkv, D, _ptr(pid), float(theta),
+                              _DTYPE_CODE[dq.dtype], _stream(dq.device))
+    _check(st, "rope_qk_bwd_pos")
+    return dq, dk
+
+
 def qk_fwd_(q, k, cu_seqlens, theta: float, seqused=None):
     """Forward RoPE on q and k in place (one launch). Returns (q, k)."""
     T, Hq, Hkv, D, cu, num_seqs, su = _qk_args(q, k, cu_seqlens, seqused)
@@ -136,27 +208,31 @@ def qk_bwd_(dq, dk, cu_seqlens, theta: float, seqused=None):
     return dq, dk
 
 
-def positions(cu_seqlens, T: int, seqused=None):
+def positions(cu_seqlens, T: int, seqused=None, seq_offsets=None, position_ids=None):
     """(pos, seq) int32[T] on the GPU as the kernels compute them; -1 = untouched."""
-    device = cu_seqlens.device
+    ref = cu_seqlens if cu_seqlens is not None else position_ids
+    device = ref.device
     cu = _index_tensor(cu_seqlens, "cu_seqlens", device)
     su = _index_tensor(seqused, "seqused", device)
+    so = _index_tensor(seq_offsets, "seq_offsets", device)
+    pid = _index_tensor(position_ids, "position_ids", device)
     pos = torch.empty(int(T), dtype=torch.int32, device=device)
     seq = torch.empty(int(T), dtype=torch.int32, device=device)
-    st = _lib.rope_positions(_ptr(cu), cu.numel() - 1, _ptr(su), int(T), _ptr(pos), _ptr(seq),
-                             _stream(device))
-    _check(st, "rope_positions")
+    num_seqs = 0 if cu is None else cu.numel() - 1
+    st = _lib.rope_positions_ex(_ptr(cu), num_seqs, _ptr(su), _ptr(so), _ptr(pid), int(T),
+                                _ptr(pos), _ptr(seq), _stream(device))
+    _check(st, "rope_positions_ex")
     return pos, seq
 
 
-def cos_sin(pos, D: int, theta: float):
+def cos_sin(pos, D: int, theta: float, pos_scale: float = 1.0):
     """fp32 (cos, sin) [n, D/2] for the int32 positions `pos` (on the GPU)."""
     p = _index_tensor(pos, "pos", pos.device)
     c = torch.empty((p.numel(), D // 2), dtype=torch.float32, device=p.device)
     s = torch.empty_like(c)
-    st = _lib.rope_cos_sin(_ptr(p), p.numel(), int(D), float(theta), _ptr(c), _ptr(s),
-                           _stream(p.device))
-    _check(st, "rope_cos_sin")
+    st = _lib.rope_cos_sin_ex(_ptr(p), p.numel(), int(D), float(theta), float(pos_scale), _ptr(c),
+                              _ptr(s), _stream(p.device))
+    _check(st, "rope_cos_sin_ex")
     return c, s
 
 

@@ -57,10 +57,23 @@ struct RopeParams {
   int32_t nc;   // chunks per half row: (D/2) / VEC
   int32_t tpw;  // tokens per wave
   float sin_sign;
+  float pos_scale;  // linear position interpolation: positions divided by this (1 = none)
 };
 
 struct CosSinParams {
   float inv_freq[kMaxHalf];
+  float pos_scale;
+};
+
+// Where a token's position comes from: explicit position ids, or its offset in its
+// cu_seqlens sequence (optionally cut by seqused and shifted by a per-sequence
+// offset, as a context-parallel shard of a longer sequence needs).
+struct PosSource {
+  const int32_t* cu;
+  const int32_t* seqused;
+  const int32_t* seq_offsets;
+  const int32_t* position_ids;
+  int32_t num_seqs;
 };
 
 // ---- a1: token -> (sequence, position) [U-Pack] ------------------------------------
@@ -91,9 +104,35 @@ __device__ inline int32_t token_position(const int32_t* __restrict__ cu, int32_t
   return (int32_t)p;
 }
 
-// ---- a3: the angle, one fp32 multiply --------------------------------------------
-__device__ inline float rope_angle(int32_t pos, float inv_freq_j) {
-  return __fmul_rn((float)pos, inv_freq_j);
+// Position of token t from any source, or -1 (untouched). With explicit ids a
+// negative id leaves the token untouched; with per-sequence offsets a shifted
+// position outside [0, 2^31) does.
+__device__ inline int32_t resolve_position(const PosSource& ps, int64_t t, int32_t* seq_out) {
+  if (ps.position_ids != nullptr) {
+    *seq_out = -1;
+    const int32_t p = ps.position_ids[t];
+    return p < 0 ? -1 : p;
+  }
+  const int32_t p = token_position(ps.cu, ps.num_seqs, ps.seqused, t, seq_out);
+  if (p < 0 || ps.seq_offsets == nullptr) return p;
+  const int64_t shifted = (int64_t)p + (int64_t)ps.seq_offsets[*seq_out];
+  if (shifted < 0 || shifted > (int64_t)INT32_MAX) {
+    *seq_out = -1;
+    return -1;
+  }
+  return (int32_t)shifted;
+}
+
+// ---- a3: the angle --------------------------------------------------------------
+// fp32(pos) * inv_freq[j], one fp32 multiply; with linear position interpolation
+// by a factor s, the position is first divided by s in fp32 (correctly rounded),
+// so that position s*p gets exactly the angles of position p.
+__device__ inline float scaled_position(int32_t pos, float pos_scale) {
+  const float fp = (float)pos;
+  return pos_scale == 1.0f ? fp : __fdiv_rn(fp, pos_scale);
+}
+__device__ inline float rope_angle(float scaled_pos, float inv_freq_j) {
+  return __fmul_rn(scaled_pos, inv_freq_j);
 }
 
 // ---- storage <-> fp32 -------------------------------------------------------------
@@ -281,9 +320,7 @@ __device__ inline T* token_row0(T* p, int64_t t, int32_t H, int32_t D) {
 // ---- the fused QK kernel (a1..a7) ---------------------------------------------------
 template <typename T, int VEC, bool LONG_INDEX>
 __global__ __launch_bounds__(kBlock) void rope_qk_kernel(T* __restrict__ q, T* __restrict__ k,
-                                                         const int32_t* __restrict__ cu,
-                                                         const int32_t* __restrict__ seqused,
-                                                         const RopeParams p) {
+                                                         const PosSource ps, const RopeParams p) {
   __shared__ float lds_cs[kWaves][kMaxHalf];
   __shared__ float lds_sn[kWaves][kMaxHalf];
   const int lane = threadIdx.x & 63;
@@ -308,8 +345,9 @@ __global__ __launch_bounds__(kBlock) void rope_qk_kernel(T* __restrict__ q, T* _
     const int64_t t = t_begin + it;
     if (t >= p.T) break;
     int32_t seq;
-    const int32_t pos = token_position(cu, p.num_seqs, seqused, t, &seq);  // wave-uniform
+    const int32_t pos = resolve_position(ps, t, &seq);  // wave-uniform
     if (pos < 0) continue;
+    const float spos = scaled_position(pos, p.pos_scale);
 
     // a3: this token's fp32 cos/sin table, each (token, frequency) computed once.
 #pragma unroll
@@ -317,7 +355,7 @@ __global__ __launch_bounds__(kBlock) void rope_qk_kernel(T* __restrict__ q, T* _
       const uint32_t j = (uint32_t)lane + 64u * i;
       if (j < half) {
         float sn, cs;
-        rope_trig::sincos_f32_cr(rope_angle(pos, f[i]), sn, cs);
+        rope_trig::sincos_f32_cr(rope_angle(spos, f[i]), sn, cs);
         lds_cs[wave][j] = cs;
         lds_sn[wave][j] = sn * p.sin_sign;  // backward: R transposed = sin negated
       }
@@ -349,15 +387,13 @@ __global__ __launch_bounds__(kBlock) void rope_qk_kernel(T* __restrict__ q, T* _
 }
 
 // ---- export hooks (same device functions) --------------------------------------------
-__global__ __launch_bounds__(kBlock) void rope_positions_kernel(const int32_t* __restrict__ cu,
-                                                                int32_t num_seqs,
-                                                                const int32_t* __restrict__ seqused,
-                                                                int64_t T, int32_t* pos_out,
+__global__ __launch_bounds__(kBlock) void rope_positions_kernel(const PosSource ps, int64_t T,
+                                                                int32_t* pos_out,
                                                                 int32_t* seq_out) {
   const int64_t t = (int64_t)blockIdx.x * kBlock + threadIdx.x;
   if (t >= T) return;
   int32_t seq;
-  const int32_t pos = token_position(cu, num_seqs, seqused, t, &seq);
+  const int32_t pos = resolve_position(ps, t, &seq);
   if (pos_out) pos_out[t] = pos;
   if (seq_out) seq_out[t] = seq;
 }
@@ -371,7 +407,8 @@ __global__ __launch_bounds__(kBlock) void rope_cos_sin_kernel(const int32_t* __r
   const int64_t i = idx / half;
   const int32_t j = (int32_t)(idx - i * half);
   float s, c;
-  rope_trig::sincos_f32_cr(rope_angle(positions[i], p.inv_freq[j]), s, c);
+  rope_trig::sincos_f32_cr(rope_angle(scaled_position(positions[i], p.pos_scale), p.inv_freq[j]),
+                           s, c);
   cos_out[idx] = c;
   sin_out[idx] = s;
 }
@@ -386,6 +423,8 @@ void host_inv_freq(double theta, int32_t D, float* out) {
 
 bool valid_theta(double theta) { return isfinite(theta) && theta >= 1.0; }
 bool valid_D(int32_t D) { return D >= 2 && D <= 2 * kMaxHalf && (D & 1) == 0; }
+// Linear position interpolation factor, applied in fp32: finite and >= 1.
+bool valid_scale(double s) { return isfinite(s) && (float)s >= 1.0f && isfinite((float)s); }
 
 int32_t elem_size(int32_t dtype) { return dtype == ROPE_F32 ? 4 : 2; }
 
@@ -402,16 +441,16 @@ int32_t chunk_bytes(int32_t D, int32_t esize, const void* q, const void* k) {
 }
 
 template <typename T, int VEC>
-int32_t launch_vec(void* q, void* k, const int32_t* cu, const int32_t* seqused,
-                   const RopeParams& p, bool long_index, unsigned blocks, hipStream_t stream) {
+int32_t launch_vec(void* q, void* k, const PosSource& ps, const RopeParams& p, bool long_index,
+                   unsigned blocks, hipStream_t stream) {
   T* qt = static_cast<T*>(q);
   T* kt = static_cast<T*>(k);
   if (long_index)
     hipLaunchKernelGGL((rope_qk_kernel<T, VEC, true>), dim3(blocks), dim3(kBlock), 0, stream, qt,
-                       kt, cu, seqused, p);
+                       kt, ps, p);
   else
     hipLaunchKernelGGL((rope_qk_kernel<T, VEC, false>), dim3(blocks), dim3(kBlock), 0, stream, qt,
-                       kt, cu, seqused, p);
+                       kt, ps, p);
   return hipGetLastError() == hipSuccess ? ROPE_OK : ROPE_ELAUNCH;
 }
 
@@ -426,20 +465,20 @@ int32_t auto_tokens_per_wave(int64_t T) {
 }
 
 template <typename T>
-int32_t launch_typed(void* q, void* k, const int32_t* cu, const int32_t* seqused, RopeParams& p,
-                     int32_t bytes, bool long_index, hipStream_t stream) {
+int32_t launch_typed(void* q, void* k, const PosSource& ps, RopeParams& p, int32_t bytes,
+                     bool long_index, hipStream_t stream) {
   const int32_t vec = bytes / (int32_t)sizeof(T);
   p.nc = (p.D / 2) / vec;
   const int64_t waves = (p.T + p.tpw - 1) / p.tpw;
   const int64_t blocks = (waves + kWaves - 1) / kWaves;
   if (blocks > kMaxBlocksX) return ROPE_EINVAL;
   switch (vec) {
-    case 1: return launch_vec<T, 1>(q, k, cu, seqused, p, long_index, (unsigned)blocks, stream);
-    case 2: return launch_vec<T, 2>(q, k, cu, seqused, p, long_index, (unsigned)blocks, stream);
-    case 4: return launch_vec<T, 4>(q, k, cu, seqused, p, long_index, (unsigned)blocks, stream);
+    case 1: return launch_vec<T, 1>(q, k, ps, p, long_index, (unsigned)blocks, stream);
+    case 2: return launch_vec<T, 2>(q, k, ps, p, long_index, (unsigned)blocks, stream);
+    case 4: return launch_vec<T, 4>(q, k, ps, p, long_index, (unsigned)blocks, stream);
     default:
       if constexpr (sizeof(T) == 2)
-        return launch_vec<T, 8>(q, k, cu, seqused, p, long_index, (unsigned)blocks, stream);
+        return launch_vec<T, 8>(q, k, ps, p, long_index, (unsigned)blocks, stream);
       return ROPE_EINVAL;
   }
 }
@@ -448,22 +487,26 @@ int32_t launch_typed(void* q, void* k, const int32_t* cu, const int32_t* seqused
 
 extern "C" {
 
-int32_t rope_qk_apply(void* q, void* k, int64_t T, int32_t Hq, int32_t Hkv, int32_t D,
-                      const int32_t* cu_seqlens, int32_t num_seqs, const int32_t* seqused,
-                      double theta, int32_t dtype, int32_t direction, int32_t index_mode,
-                      int32_t tokens_per_wave, void* stream) {
+int32_t rope_qk_apply_ex(void* q, void* k, int64_t T, int32_t Hq, int32_t Hkv, int32_t D,
+                         const int32_t* cu_seqlens, int32_t num_seqs, const int32_t* seqused,
+                         const int32_t* seq_offsets, const int32_t* position_ids, double theta,
+                         double pos_scale, int32_t dtype, int32_t direction, int32_t index_mode,
+                         int32_t tokens_per_wave, void* stream) {
   if (dtype != ROPE_F32 && dtype != ROPE_BF16 && dtype != ROPE_F16) return ROPE_EUNSUPPORTED;
   if (T < 0 || T > ((int64_t)1 << 40)) return ROPE_EINVAL;
   if (Hq < 0 || Hkv < 0 || Hq > kMaxHeads || Hkv > kMaxHeads) return ROPE_EINVAL;
-  if (!valid_D(D) || !valid_theta(theta)) return ROPE_EINVAL;
+  if (!valid_D(D) || !valid_theta(theta) || !valid_scale(pos_scale)) return ROPE_EINVAL;
   if (num_seqs < 0 || num_seqs == INT32_MAX) return ROPE_EINVAL;
   if (direction != 1 && direction != -1) return ROPE_EINVAL;
   if (index_mode < ROPE_INDEX_AUTO || index_mode > ROPE_INDEX_64) return ROPE_EINVAL;
   if (tokens_per_wave < 0 || tokens_per_wave > kMaxTokensPerWave) return ROPE_EINVAL;
   const int32_t H = Hq + Hkv;
   if (T > 0 && H == 0) return ROPE_EINVAL;
-  if (T == 0 || num_seqs == 0) return ROPE_OK;  // nothing is rotated
-  if (cu_seqlens == nullptr) return ROPE_EINVAL;
+  if (T == 0) return ROPE_OK;
+  if (position_ids == nullptr) {
+    if (num_seqs == 0) return ROPE_OK;  // nothing is rotated
+    if (cu_seqlens == nullptr) return ROPE_EINVAL;
+  }
   if ((Hq > 0 && q == nullptr) || (Hkv > 0 && k == nullptr)) return ROPE_EINVAL;
 
   const bool needs_long = T * (int64_t)H * (int64_t)D >= ((int64_t)1 << 31);
@@ -478,61 +521,110 @@ int32_t rope_qk_apply(void* q, void* k, int64_t T, int32_t Hq, int32_t Hkv, int3
   p.D = D;
   p.tpw = tokens_per_wave == 0 ? auto_tokens_per_wave(T) : tokens_per_wave;
   p.sin_sign = direction > 0 ? 1.0f : -1.0f;
+  p.pos_scale = (float)pos_scale;
   host_inv_freq(theta, D, p.inv_freq);
+
+  PosSource ps;
+  ps.position_ids = position_ids;
+  ps.cu = position_ids ? nullptr : cu_seqlens;
+  ps.seqused = position_ids ? nullptr : seqused;
+  ps.seq_offsets = position_ids ? nullptr : seq_offsets;
+  ps.num_seqs = position_ids ? 0 : num_seqs;
 
   void* qp = Hq > 0 ? q : nullptr;
   void* kp = Hkv > 0 ? k : nullptr;
   const int32_t bytes = chunk_bytes(D, elem_size(dtype), qp, kp);
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (dtype) {
-    case ROPE_F32: return launch_typed<float>(qp, kp, cu_seqlens, seqused, p, bytes, long_index, s);
-    case ROPE_BF16: return launch_typed<__bf16>(qp, kp, cu_seqlens, seqused, p, bytes, long_index, s);
-    default: return launch_typed<_Float16>(qp, kp, cu_seqlens, seqused, p, bytes, long_index, s);
+    case ROPE_F32: return launch_typed<float>(qp, kp, ps, p, bytes, long_index, s);
+    case ROPE_BF16: return launch_typed<__bf16>(qp, kp, ps, p, bytes, long_index, s);
+    default: return launch_typed<_Float16>(qp, kp, ps, p, bytes, long_index, s);
   }
+}
+
+int32_t rope_qk_apply(void* q, void* k, int64_t T, int32_t Hq, int32_t Hkv, int32_t D,
+                      const int32_t* cu_seqlens, int32_t num_seqs, const int32_t* seqused,
+                      double theta, int32_t dtype, int32_t direction, int32_t index_mode,
+                      int32_t tokens_per_wave, void* stream) {
+  return rope_qk_apply_ex(q, k, T, Hq, Hkv, D, cu_seqlens, num_seqs, seqused, nullptr, nullptr,
+                          theta, 1.0, dtype, direction, index_mode, tokens_per_wave, stream);
 }
 
 int32_t rope_qk_fwd(void* q, void* k, int64_t T, int32_t Hq, int32_t Hkv, int32_t D,
                     const int32_t* cu_seqlens, int32_t num_seqs, const int32_t* seqused,
                     double theta, int32_t dtype, void* stream) {
-  return rope_qk_apply(q, k, T, Hq, Hkv, D, cu_seqlens, num_seqs, seqused, theta, dtype, +1,
-                       ROPE_INDEX_AUTO, 0, stream);
+  return rope_qk_apply_ex(q, k, T, Hq, Hkv, D, cu_seqlens, num_seqs, seqused, nullptr, nullptr,
+                          theta, 1.0, dtype, +1, ROPE_INDEX_AUTO, 0, stream);
 }
 
 int32_t rope_qk_bwd(void* dq, void* dk, int64_t T, int32_t Hq, int32_t Hkv, int32_t D,
                     const int32_t* cu_seqlens, int32_t num_seqs, const int32_t* seqused,
                     double theta, int32_t dtype, void* stream) {
-  return rope_qk_apply(dq, dk, T, Hq, Hkv, D, cu_seqlens, num_seqs, seqused, theta, dtype, -1,
-                       ROPE_INDEX_AUTO, 0, stream);
+  return rope_qk_apply_ex(dq, dk, T, Hq, Hkv, D, cu_seqlens, num_seqs, seqused, nullptr, nullptr,
+                          theta, 1.0, dtype, -1, ROPE_INDEX_AUTO, 0, stream);
+}
+
+int32_t rope_qk_fwd_pos(void* q, void* k, int64_t T, int32_t Hq, int32_t Hkv, int32_t D,
+                        const int32_t* position_ids, double theta, int32_t dtype, void* stream) {
+  if (T > 0 && position_ids == nullptr) return ROPE_EINVAL;
+  return rope_qk_apply_ex(q, k, T, Hq, Hkv, D, nullptr, 0, nullptr, nullptr, position_ids, theta,
+                          1.0, dtype, +1, ROPE_INDEX_AUTO, 0, stream);
+}
+
+int32_t rope_qk_bwd_pos(void* dq, void* dk, int64_t T, int32_t Hq, int32_t Hkv, int32_t D,
+                        const int32_t* position_ids, double theta, int32_t dtype, void* stream) {
+  if (T > 0 && position_ids == nullptr) return ROPE_EINVAL;
+  return rope_qk_apply_ex(dq, dk, T, Hq, Hkv, D, nullptr, 0, nullptr, nullptr, position_ids, theta,
+                          1.0, dtype, -1, ROPE_INDEX_AUTO, 0, stream);
+}
+
+int32_t rope_positions_ex(const int32_t* cu_seqlens, int32_t num_seqs, const int32_t* seqused,
+                          const int32_t* seq_offsets, const int32_t* position_ids, int64_t T,
+                          int32_t* pos_out, int32_t* seq_out, void* stream) {
+  if (T < 0 || T > ((int64_t)1 << 40)) return ROPE_EINVAL;
+  if (num_seqs < 0 || num_seqs == INT32_MAX) return ROPE_EINVAL;
+  if (T == 0 || (pos_out == nullptr && seq_out == nullptr)) return ROPE_OK;
+  if (position_ids == nullptr && num_seqs > 0 && cu_seqlens == nullptr) return ROPE_EINVAL;
+  const int64_t blocks = (T + kBlock - 1) / kBlock;
+  if (blocks > kMaxBlocksX) return ROPE_EINVAL;
+  PosSource ps;
+  ps.position_ids = position_ids;
+  ps.cu = position_ids ? nullptr : cu_seqlens;
+  ps.seqused = position_ids ? nullptr : seqused;
+  ps.seq_offsets = position_ids ? nullptr : seq_offsets;
+  ps.num_seqs = position_ids ? 0 : num_seqs;
+  hipLaunchKernelGGL(rope_positions_kernel, dim3((unsigned)blocks), dim3(kBlock), 0,
+                     static_cast<hipStream_t>(stream), ps, T, pos_out, seq_out);
+  return hipGetLastError() == hipSuccess ? ROPE_OK : ROPE_ELAUNCH;
 }
 
 int32_t rope_positions(const int32_t* cu_seqlens, int32_t num_seqs, const int32_t* seqused,
                        int64_t T, int32_t* pos_out, int32_t* seq_out, void* stream) {
-  if (T < 0 || T > ((int64_t)1 << 40)) return ROPE_EINVAL;
-  if (num_seqs < 0 || num_seqs == INT32_MAX) return ROPE_EINVAL;
-  if (T == 0 || (pos_out == nullptr && seq_out == nullptr)) return ROPE_OK;
-  if (cu_seqlens == nullptr) return ROPE_EINVAL;
-  const int64_t blocks = (T + kBlock - 1) / kBlock;
-  if (blocks > kMaxBlocksX) return ROPE_EINVAL;
-  hipLaunchKernelGGL(rope_positions_kernel, dim3((unsigned)blocks), dim3(kBlock), 0,
-                     static_cast<hipStream_t>(stream), cu_seqlens, num_seqs, seqused, T, pos_out,
-                     seq_out);
-  return hipGetLastError() == hipSuccess ? ROPE_OK : ROPE_ELAUNCH;
+  if (num_seqs > 0 && cu_seqlens == nullptr) return ROPE_EINVAL;
+  return rope_positions_ex(cu_seqlens, num_seqs, seqused, nullptr, nullptr, T, pos_out, seq_out,
+                           stream);
 }
 
-int32_t rope_cos_sin(const int32_t* positions, int64_t n, int32_t D, double theta,
-                     float* cos_out, float* sin_out, void* stream) {
-  if (!valid_D(D) || !valid_theta(theta)) return ROPE_EINVAL;
+int32_t rope_cos_sin_ex(const int32_t* positions, int64_t n, int32_t D, double theta,
+                        double pos_scale, float* cos_out, float* sin_out, void* stream) {
+  if (!valid_D(D) || !valid_theta(theta) || !valid_scale(pos_scale)) return ROPE_EINVAL;
   if (n < 0 || n > ((int64_t)1 << 34)) return ROPE_EINVAL;
   if (n == 0) return ROPE_OK;
   if (positions == nullptr || cos_out == nullptr || sin_out == nullptr) return ROPE_EINVAL;
   CosSinParams p;
   host_inv_freq(theta, D, p.inv_freq);
+  p.pos_scale = (float)pos_scale;
   const int32_t half = D / 2;
   const int64_t blocks = (n * half + kBlock - 1) / kBlock;
   if (blocks > kMaxBlocksX) return ROPE_EINVAL;
   hipLaunchKernelGGL(rope_cos_sin_kernel, dim3((unsigned)blocks), dim3(kBlock), 0,
                      static_cast<hipStream_t>(stream), positions, n, half, p, cos_out, sin_out);
   return hipGetLastError() == hipSuccess ? ROPE_OK : ROPE_ELAUNCH;
+}
+
+int32_t rope_cos_sin(const int32_t* positions, int64_t n, int32_t D, double theta,
+                     float* cos_out, float* sin_out, void* stream) {
+  return rope_cos_sin_ex(positions, n, D, theta, 1.0, cos_out, sin_out, stream);
 }
 
 int32_t rope_inv_freq(double theta, int32_t D, float* out) {

@@ -339,6 +339,96 @@ def check_round_bf16(o):
     assert np.array_equal(got, ref)
 
 
+# ---------------------------------------------------------------------------- NEXT rows:
+# explicit position ids, per-sequence offsets, linear position interpolation.
+
+def check_position_ids_match_cu_positions(o):
+    """Explicit ids equal to the hand-written per-sample positions (golden fixture)
+    give the cu_seqlens result bit for bit; negative ids leave their token alone."""
+    with open(os.path.join(GOLDEN, "positions_tiny_packed.txt")) as fh:
+        pos = [ln.split() for ln in fh if ln.startswith("pos")][0]
+    ids = np.array([int(v) for v in pos[1:]], dtype=np.int32)
+    rng = np.random.default_rng(30)
+    x = random_bf16(rng, (64, 3, 16))
+    for direction in (1, -1):
+        a = o.rope(x, [0, 5, 22, 25, 64], 1e6, direction, "bf16")
+        b = o.rope(x, None, 1e6, direction, "bf16", position_ids=ids)
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    ids2 = ids.copy()
+    ids2[[3, 40, 63]] = -1
+    b = o.rope(x, None, 1e6, 1, "bf16", position_ids=ids2)
+    xf = bf16_bits_to_f32(x)
+    for t in (3, 40, 63):
+        assert np.array_equal(b[t].view(np.uint32), xf[t].view(np.uint32))
+    pos_out, seq_out = o.positions(None, 64, position_ids=ids2)
+    assert pos_out.tolist() == [(-1 if t in (3, 40, 63) else int(ids[t])) for t in range(64)]
+    assert np.all(seq_out == -1)
+
+
+def check_position_ids_hand_values(o):
+    # D = 4, theta = 1e4: e0 with id 1 -> [cos 1, 0, sin 1, 0]; e1 with id 100 -> the
+    # fp32 angle 100 * 0.01f is exactly 1 -> [0, cos 1, 0, sin 1].
+    x = np.zeros((2, 1, 4), dtype=np.float32)
+    x[0, 0, 0] = 1.0
+    x[1, 0, 1] = 1.0
+    y = o.rope(x, None, 1e4, 1, position_ids=[1, 100])
+    c1, s1 = np.float32(math.cos(1.0)), np.float32(math.sin(1.0))
+    assert y[0, 0].tolist() == [c1, 0.0, s1, 0.0] and y[1, 0].tolist() == [0.0, c1, 0.0, s1], y
+
+
+def check_seq_offsets_shard_invariant(o):
+    """A long sequence cut into shards, each rotated with the global position of its
+    first token as offset, gives exactly the unsharded result (sequence/context
+    parallelism needs nothing else from RoPE)."""
+    rng = np.random.default_rng(31)
+    L = 97
+    x = random_bf16(rng, (L, 2, 32))
+    full = o.rope(x, [0, L], 1e6, 1, "bf16")
+    cuts = [0, 20, 21, 60, L]
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        part = o.rope(np.ascontiguousarray(x[a:b]), [0, b - a], 1e6, 1, "bf16", seq_offsets=[a])
+        assert np.array_equal(part.view(np.uint32), full[a:b].view(np.uint32)), (a, b)
+    # Two packed shards of two different sequences in one call.
+    both = np.concatenate([x[20:60], x[60:L]])
+    y = o.rope(both, [0, 40, 40 + L - 60], 1e6, 1, "bf16", seq_offsets=[20, 60])
+    assert np.array_equal(y.view(np.uint32), full[20:L].view(np.uint32))
+    # A negative shifted position leaves its token untouched.
+    pos, seq = o.positions([0, 4], 4, seq_offsets=[-2])
+    assert pos.tolist() == [-1, -1, 0, 1] and seq.tolist() == [-1, -1, 0, 0]
+
+
+def check_pos_scale_page_example(o):
+    """With factor 4, position 100000 is treated as position 25000 (TRL guide, YaRN
+    section): same cos/sin bit for bit, and the scaled rotation of positions 4p
+    equals the unscaled rotation of positions p."""
+    c4, s4 = o.cos_sin([100000], 128, 1e6, pos_scale=4.0)
+    c1, s1 = o.cos_sin([25000], 128, 1e6)
+    assert np.array_equal(c4.view(np.uint32), c1.view(np.uint32))
+    assert np.array_equal(s4.view(np.uint32), s1.view(np.uint32))
+    rng = np.random.default_rng(32)
+    x = random_bf16(rng, (50, 2, 16))
+    p = np.arange(50, dtype=np.int32) * 37
+    a = o.rope(x, None, 1e4, 1, "bf16", position_ids=4 * p, pos_scale=4.0)
+    b = o.rope(x, None, 1e4, 1, "bf16", position_ids=p)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def check_pos_scale_mpmath(o):
+    """Scaled angle = fp32(fp32(pos) / fp32(factor)) * inv_freq, one rounding per step;
+    cos/sin correctly rounded (mpmath)."""
+    D, theta = 64, 5e5
+    f = ref_inv_freq(theta, D)
+    plist = [1, 3, 7, 999, 40961, 163839, 524287]
+    for factor in (1.5, 2.5, 4.0):
+        c, s = o.cos_sin(plist, D, theta, pos_scale=factor)
+        for i, p in enumerate(plist):
+            sp = np.float32(np.float32(p) / np.float32(factor))
+            for j in range(D // 2):
+                a = mpmath.mpf(float(np.float32(sp * f[j])))
+                assert c[i, j] == rn_f32(mpmath.cos(a)), (factor, p, j)
+                assert s[i, j] == rn_f32(mpmath.sin(a)), (factor, p, j)
+
+
 ALL_CHECKS = [
     check_inv_freq_closed_form,
     check_inv_freq_mpmath,
@@ -358,4 +448,9 @@ ALL_CHECKS = [
     check_exact_rounding,
     check_rows_match_full,
     check_round_bf16,
+    check_position_ids_match_cu_positions,
+    check_position_ids_hand_values,
+    check_seq_offsets_shard_invariant,
+    check_pos_scale_page_example,
+    check_pos_scale_mpmath,
 ]

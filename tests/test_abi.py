@@ -94,6 +94,35 @@ def test_validation(kw, expect):
     assert apply(**kw) == expect
 
 
+def apply_ex(**kw):
+    a = dict(q=FAKE, k=FAKE, T=16, Hq=4, Hkv=2, D=128, cu=FAKE, num_seqs=2, seqused=None,
+             offsets=None, ids=None, theta=1e4, scale=1.0, dtype=1, direction=1, index_mode=0,
+             tpw=0, stream=None)
+    a.update(kw)
+    return rope._lib.rope_qk_apply_ex(a["q"], a["k"], a["T"], a["Hq"], a["Hkv"], a["D"], a["cu"],
+                                      a["num_seqs"], a["seqused"], a["offsets"], a["ids"],
+                                      a["theta"], a["scale"], a["dtype"], a["direction"],
+                                      a["index_mode"], a["tpw"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(scale=0.5), EINVAL),
+    (dict(scale=float("nan")), EINVAL),
+    (dict(scale=float("inf")), EINVAL),
+    (dict(scale=1e300), EINVAL),  # not finite once rounded to fp32
+    (dict(scale=-4.0), EINVAL),
+    (dict(cu=None, ids=None), EINVAL),
+    (dict(ids=FAKE, theta=0.0), EINVAL),
+    (dict(ids=FAKE, D=3), EINVAL),
+    (dict(ids=FAKE, q=None), EINVAL),
+    (dict(dtype=9, ids=FAKE), EUNSUPPORTED),
+    (dict(T=0, q=None, k=None, cu=None, ids=None), OK),
+    (dict(num_seqs=0, cu=None), OK),
+])
+def test_validation_ex(kw, expect):
+    assert apply_ex(**kw) == expect
+
+
 def test_fwd_bwd_positions_cos_sin_validation():
     lib = rope._lib
     args = (FAKE, FAKE, 16, 4, 2, 127, FAKE, 2, None, 1e4, 1, None)
@@ -108,6 +137,13 @@ def test_fwd_bwd_positions_cos_sin_validation():
     assert lib.rope_cos_sin(None, 4, 8, 1e4, FAKE, FAKE, None) == EINVAL
     assert lib.rope_cos_sin(FAKE, 0, 8, 1e4, FAKE, FAKE, None) == OK
     assert lib.rope_inv_freq(1e4, 8, None) == EINVAL
+    assert lib.rope_qk_fwd_pos(FAKE, FAKE, 16, 4, 2, 128, None, 1e4, 1, None) == EINVAL
+    assert lib.rope_qk_bwd_pos(FAKE, FAKE, 16, 4, 2, 127, FAKE, 1e4, 1, None) == EINVAL
+    assert lib.rope_qk_fwd_pos(None, None, 0, 4, 2, 128, None, 1e4, 1, None) == OK
+    assert lib.rope_positions_ex(None, 2, None, None, None, 16, FAKE, FAKE, None) == EINVAL
+    assert lib.rope_positions_ex(None, 0, None, None, None, 0, FAKE, FAKE, None) == OK
+    assert lib.rope_cos_sin_ex(FAKE, 4, 8, 1e4, 0.9, FAKE, FAKE, None) == EINVAL
+    assert lib.rope_cos_sin_ex(FAKE, 0, 8, 1e4, 2.0, FAKE, FAKE, None) == OK
 
 
 @pytest.mark.parametrize("theta,D", [(1e4, 16), (1e6, 128), (1e4, 128), (5e5, 64), (1e6, 80),

@@ -348,3 +348,107 @@ def test_binding_rejects_bad_tensors(rope):
     with pytest.raises(rope.RopeError):
         rope.qk_fwd_(torch.zeros(4, 2, 7, dtype=torch.bfloat16, device=DEV),
                      torch.zeros(4, 1, 7, dtype=torch.bfloat16, device=DEV), cu, 1e4)
+
+
+# ---------------------------------------------------------------- NEXT rows: explicit
+# position ids, per-sequence offsets, linear position interpolation
+
+def test_position_ids_parity(rope):
+    """Explicit per-token positions (negative = untouched), forward and backward, on the
+    Qwen3-4B-shaped batch, against the oracle."""
+    w = workloads.get("qwen3_4b_packed")
+    print("[parity] position_ids on qwen3_4b_packed", flush=True)
+    rng = np.random.default_rng(77)
+    ids = rng.integers(0, 40960, w.T).astype(np.int32)
+    ids[rng.choice(w.T, 500, replace=False)] = -1
+    ids[:5] = [0, 1, 2, 40959, 2 ** 31 - 1]
+    host = make_host(w, canary_untouched=False)
+    dev = {k: v.to(DEV) for k, v in host.items()}
+    pid = torch.from_numpy(ids).to(DEV)
+    rope.qk_fwd_pos_(dev["q"], dev["k"], pid, w.theta)
+    rope.qk_bwd_pos_(dev["dq"], dev["dk"], pid, w.theta)
+    torch.cuda.synchronize()
+    touched = ids >= 0
+    for what, direction in (("q", 1), ("k", 1), ("dq", -1), ("dk", -1)):
+        x = bits(host[what])
+        ref = oracle.rope(x, None, w.theta, direction, "bf16", nthreads=NTHREADS, position_ids=ids)
+        assert_parity("bf16", bits(dev[what]), ref, x, touched, f"ids:{what}")
+    pos, seq = rope.positions(None, w.T, position_ids=pid)
+    rpos, rseq = oracle.positions(None, w.T, position_ids=ids)
+    assert np.array_equal(pos.cpu().numpy(), rpos) and np.array_equal(seq.cpu().numpy(), rseq)
+
+
+def test_seq_offsets_context_parallel_shards(rope):
+    """The 524288-token sequence cut into 4 shards of 131072 tokens (one rank's share of
+    4-way context parallelism), each rotated alone with the global position of its first
+    token as offset: bit-identical to the unsharded result, forward and backward, and
+    sampled rows of the last shard against the oracle."""
+    w = workloads.get("long_ctx_512k")
+    print("[parity] long_ctx_512k as 4 context-parallel shards", flush=True)
+    q0 = workloads.make_tensor(w.shape("q"), w.seed("q"), "bf16", device=DEV, chunk_rows=32768)
+    k0 = workloads.make_tensor(w.shape("k"), w.seed("k"), "bf16", device=DEV, chunk_rows=32768)
+    cu = torch.from_numpy(w.cu_seqlens).to(DEV)
+    for direction in (1, -1):
+        qf, kf = q0.clone(), k0.clone()
+        rope.qk_apply_(qf, kf, cu, w.theta, direction)
+        qs, ks = q0.clone(), k0.clone()
+        n = w.T // 4
+        for r in range(4):
+            a = r * n
+            cu_r = torch.tensor([0, n], dtype=torch.int32, device=DEV)
+            off = torch.tensor([a], dtype=torch.int32, device=DEV)
+            rope.qk_apply_ex_(qs[a:a + n], ks[a:a + n], w.theta, direction, cu_seqlens=cu_r,
+                              seq_offsets=off)
+        torch.cuda.synchronize()
+        assert torch.equal(qs.view(torch.int16), qf.view(torch.int16)), direction
+        assert torch.equal(ks.view(torch.int16), kf.view(torch.int16)), direction
+        del qs, ks
+    # Sampled rows of the last shard, as that rank computes them (qf holds the last
+    # direction of the loop: the backward), against the oracle.
+    tokens = np.arange(3 * n, 3 * n + 64)
+    tok_dev = torch.from_numpy(tokens).to(DEV)
+    x = bits(q0.index_select(0, tok_dev))
+    ref = oracle.rope_rows(x, tokens - 3 * n, [0, n], w.theta, -1, "bf16", None, NTHREADS,
+                           seq_offsets=[3 * n])
+    assert_parity("bf16", bits(qf.index_select(0, tok_dev)), ref, x, np.ones(64, bool), "cp:q")
+    del q0, k0, qf, kf
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("pos_scale", [4.0, 2.5])
+def test_pos_scale_parity(rope, pos_scale):
+    """Linear position interpolation on the Qwen3-8B packed batch (bf16) against the
+    oracle, and the cos/sin export at that factor bit for bit."""
+    w = workloads.get("qwen3_8b_packed")
+    print(f"[parity] pos_scale={pos_scale} on qwen3_8b_packed", flush=True)
+    host = make_host(w, canary_untouched=False)
+    dev = {k: v.to(DEV) for k, v in host.items()}
+    cu = torch.from_numpy(w.cu_seqlens).to(DEV)
+    rope.qk_apply_ex_(dev["q"], dev["k"], w.theta, 1, cu_seqlens=cu, pos_scale=pos_scale)
+    rope.qk_apply_ex_(dev["dq"], dev["dk"], w.theta, -1, cu_seqlens=cu, pos_scale=pos_scale)
+    torch.cuda.synchronize()
+    touched = np.ones(w.T, dtype=bool)
+    for what, direction in (("q", 1), ("k", 1), ("dq", -1), ("dk", -1)):
+        x = bits(host[what])
+        ref = oracle.rope(x, w.cu_seqlens, w.theta, direction, "bf16", nthreads=NTHREADS,
+                          pos_scale=pos_scale)
+        assert_parity("bf16", bits(dev[what]), ref, x, touched, f"scale:{what}")
+    pos = np.arange(0, 163840, 7, dtype=np.int32)
+    c, s = rope.cos_sin(torch.from_numpy(pos).to(DEV), 128, 1e6, pos_scale)
+    rc, rs = oracle.cos_sin(pos, 128, 1e6, pos_scale)
+    assert np.array_equal(c.cpu().numpy().view(np.uint32), rc.view(np.uint32))
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+
+
+def test_positions_export_offsets(rope):
+    cases = [([0, 5, 22, 25, 64], None, [100, 0, -3, 7], 64),
+             ([2, 2, 5, 9], [0, 2, 9], [0, 5, -1], 11),
+             ([0, 10], None, [2 ** 31 - 5], 10)]
+    for cu_l, su_l, off_l, T in cases:
+        cu = torch.tensor(cu_l, dtype=torch.int32, device=DEV)
+        su = None if su_l is None else torch.tensor(su_l, dtype=torch.int32, device=DEV)
+        off = torch.tensor(off_l, dtype=torch.int32, device=DEV)
+        pos, seq = rope.positions(cu, T, su, seq_offsets=off)
+        rpos, rseq = oracle.positions(cu_l, T, su_l, seq_offsets=off_l)
+        assert np.array_equal(pos.cpu().numpy(), rpos), (cu_l, off_l)
+        assert np.array_equal(seq.cpu().numpy(), rseq), (cu_l, off_l)

@@ -34,12 +34,24 @@ MUTATIONS = [
     ("cos_fp32_libm", "*c = (float)cosl((long double)angle);", "*c = cosf(angle);"),
     ("rotation_in_fp32", "double y1 = x1 * c - x2 * s;",
      "double y1 = (double)((float)x1 * (float)c - (float)x2 * (float)s);"),
-    ("positions_not_reset", "cos_sin_one((int32_t)p, inv_freq[j], &cs[j], &sn[j]);",
-     "cos_sin_one((int32_t)t, inv_freq[j], &cs[j], &sn[j]);"),
-    ("positions_from_1", "if (pos_out) pos_out[t] = (int32_t)p;", "if (pos_out) pos_out[t] = (int32_t)p + 1;"),
+    ("positions_not_reset", "int32_t pe = shifted(p, seq_offsets, s);\n      if (pe < 0) continue;\n      float cs",
+     "int32_t pe = shifted(t, seq_offsets, s);\n      if (pe < 0) continue;\n      float cs"),
+    ("positions_from_1", "if (pos_out) pos_out[t] = pe;", "if (pos_out) pos_out[t] = pe + 1;"),
     ("seqused_ignored", "if (seqused && (int64_t)seqused[s] < len) len = seqused[s];", ""),
-    ("row_walk_off_by_one", "if (p >= 0 && p < used_len(cu, seqused, s)) return (int32_t)p;",
-     "if (p >= 0 && p <= used_len(cu, seqused, s)) return (int32_t)p;"),
+    ("row_walk_off_by_one", "if (p >= 0 && p < used_len(cu, seqused, s)) return shifted(p, seq_offsets, s);",
+     "if (p >= 0 && p <= used_len(cu, seqused, s)) return shifted(p, seq_offsets, s);"),
+    ("offset_sign", "int64_t q = p + (seq_offsets ? (int64_t)seq_offsets[s] : 0);",
+     "int64_t q = p - (seq_offsets ? (int64_t)seq_offsets[s] : 0);"),
+    ("offset_ignored", "int64_t q = p + (seq_offsets ? (int64_t)seq_offsets[s] : 0);", "int64_t q = p;"),
+    ("negative_shift_kept", "return (q < 0 || q > 2147483647LL) ? -1 : (int32_t)q;",
+     "return (q < 0) ? (int32_t)(-q) : (int32_t)q;"),
+    ("scale_multiplies", "if (scale != 1.0f) p = p / scale;", "if (scale != 1.0f) p = p * scale;"),
+    ("scale_ignored", "if (scale != 1.0f) p = p / scale;", ""),
+    ("scale_in_double", "float angle = p * inv_freq_j;",
+     "float angle = (float)((double)pos / (double)scale * (double)inv_freq_j);"),
+    ("ids_off_by_one", "int32_t pe = position_ids[t];", "int32_t pe = position_ids[t] + 1;"),
+    ("ids_negative_rotated", "int32_t pe = position_ids[t];\n      if (pe < 0) continue;",
+     "int32_t pe = position_ids[t] < 0 ? -position_ids[t] : position_ids[t];\n      if (pe < 0) continue;"),
     ("bf16_ties_not_even", "if (rest > 0x8000u || (rest == 0x8000u && (keep & 1u))) keep += 1u;",
      "if (rest >= 0x8000u) keep += 1u;"),
     ("bf16_truncates", "if (rest > 0x8000u || (rest == 0x8000u && (keep & 1u))) keep += 1u;", ""),
