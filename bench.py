@@ -186,6 +186,15 @@ def write_traffic_summary(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, 
     print("\n".join(lines))
 
 
+def packed_position_ids(w: workloads.Workload) -> np.ndarray:
+    """Per-token positions of the packed batch (0..len-1 per sequence; -1 for rows
+    outside every sequence): the position_ids a 1-D packing collator would emit."""
+    ids = np.full(w.T, -1, dtype=np.int32)
+    for s0, n in zip(w.cu_seqlens[:-1], w.lengths):
+        ids[s0:s0 + n] = np.arange(n, dtype=np.int32)
+    return ids
+
+
 def make_sets(w, nsets, dev):
     cu = torch.from_numpy(w.cu_seqlens).to(dev)
     su = None if w.seqused is None else torch.from_numpy(w.seqused).to(dev)
@@ -231,6 +240,83 @@ def copy_calibration(gib: float, reps: int):
                       "reps": reps}))
 
 
+def compare_unfused(rope, w, cu, su, sets, nsets, args, stream):
+    """Fused in-place QK-RoPE against unfused variants built from the same kernel, on
+    the same buffers: one step = forward on (Q, K) + backward on (dQ, dK).
+      fused            one launch per pass, in place (the library's path)
+      separate         Q and K in two launches per pass, in place
+      separate_clone   clone Q and K (out-of-place result), two launches on the clones
+      transpose_clone  per tensor: contiguous transpose to [H, T, D], rotate with
+                       explicit per-row positions, contiguous transpose back
+    Prints one JSON line with per-step times and ratios to fused."""
+    dev = sets[0]["q"].device
+    empty = {}
+
+    def no_heads(x, like):
+        key = (x, like.dtype)
+        if key not in empty:
+            empty[key] = torch.empty((w.T, 0, w.D), dtype=like.dtype, device=dev)
+        return empty[key]
+
+    ids_np = packed_position_ids(w)
+    ids_by_h = {}
+
+    def head_major_ids(H):
+        if H not in ids_by_h:
+            ids_by_h[H] = torch.from_numpy(np.tile(ids_np, H)).to(dev)
+        return ids_by_h[H]
+
+    def fused(s, qn, kn, d):
+        rope.qk_apply_(s[qn], s[kn], cu, w.theta, d, seqused=su)
+
+    def separate(s, qn, kn, d):
+        rope.qk_apply_(s[qn], no_heads("k", s[kn]), cu, w.theta, d, seqused=su)
+        rope.qk_apply_(no_heads("q", s[qn]), s[kn], cu, w.theta, d, seqused=su)
+
+    def separate_clone(s, qn, kn, d):
+        q2 = s[qn].clone()
+        rope.qk_apply_(q2, no_heads("k", q2), cu, w.theta, d, seqused=su)
+        k2 = s[kn].clone()
+        rope.qk_apply_(no_heads("q", k2), k2, cu, w.theta, d, seqused=su)
+        return q2, k2
+
+    def transpose_clone(s, qn, kn, d):
+        out = []
+        for name in (qn, kn):
+            x = s[name]
+            H = x.shape[1]
+            xt = x.transpose(0, 1).contiguous().view(H * w.T, 1, w.D)
+            rope.qk_apply_ex_(xt, torch.empty((H * w.T, 0, w.D), dtype=x.dtype, device=dev),
+                              w.theta, d, position_ids=head_major_ids(H))
+            out.append(xt.view(H, w.T, w.D).transpose(0, 1).contiguous())
+        return out
+
+    variants = {"fused": fused, "separate": separate, "separate_clone": separate_clone,
+                "transpose_clone": transpose_clone}
+    res = {}
+    for name, fn in variants.items():
+        def step(i):
+            s = sets[i % nsets]
+            fn(s, "q", "k", 1)
+            fn(s, "dq", "dk", -1)
+        for i in range(args.warmup):
+            step(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(i)
+        torch.cuda.synchronize()
+        res[name] = (time.perf_counter() - t0) / args.steps * 1e6
+    out = {
+        "compare": "fused in-place QK-RoPE vs unfused variants (fwd+bwd step)",
+        "workload": w.name, "T": w.T, "valid_tokens": w.valid_tokens, "Hq": w.Hq, "Hkv": w.Hkv,
+        "D": w.D, "dtype": w.dtype, "steps": args.steps,
+        "us_per_step": {k: round(v, 2) for k, v in res.items()},
+        "speedup_of_fused": {k: round(v / res["fused"], 3) for k, v in res.items()},
+    }
+    print(json.dumps(out))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -238,6 +324,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="qwen3_4b_packed", choices=workloads.names())
     ap.add_argument("--tokens-per-wave", type=int, default=0, help="0: library default")
+    ap.add_argument("--positions", default="cu", choices=["cu", "ids", "shards4"],
+                    help="position source: cu_seqlens; explicit per-token ids; or the batch "
+                         "cut into 4 token shards, each launched with per-sequence offsets")
+    ap.add_argument("--pos-scale", type=float, default=1.0,
+                    help="linear position interpolation factor (>= 1)")
+    ap.add_argument("--compare", action="store_true",
+                    help="time fused in-place QK-RoPE against unfused variants, then exit")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="timed oracle work for cpu_baseline (0 disables it)")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
@@ -277,15 +370,50 @@ def main():
     tpw = args.tokens_per_wave
 
     stream = torch.cuda.current_stream(dev).cuda_stream  # the stream the library launches on
+    if args.compare:
+        return compare_unfused(rope, w, cu, su, sets, nsets, args, stream)
+
+    pid = None
+    shards = None
+    if args.positions == "ids":
+        pid = torch.from_numpy(packed_position_ids(w)).to(dev)
+    elif args.positions == "shards4":
+        if su is not None:
+            raise SystemExit("--positions shards4 needs a fully packed workload (no seqused)")
+        # 4 token ranges; a sequence crossing a cut continues in the next shard with
+        # the global position of its first token there as offset.
+        bounds = [w.T * r // 4 for r in range(5)]
+        shards = []
+        cu_np = w.cu_seqlens.astype(np.int64)
+        for a, b in zip(bounds[:-1], bounds[1:]):
+            starts = np.clip(cu_np[:-1], a, b)
+            ends = np.clip(cu_np[1:], a, b)
+            keep = ends > starts
+            cu_r = np.concatenate([[0], np.cumsum((ends - starts)[keep])]).astype(np.int32)
+            off_r = (starts - cu_np[:-1])[keep].astype(np.int32)
+            shards.append((a, b, torch.from_numpy(cu_r).to(dev), torch.from_numpy(off_r).to(dev)))
+
+    def launch(qt, kt, direction):
+        if shards is not None:
+            for a, b, cu_r, off_r in shards:
+                rope.qk_apply_ex_(qt[a:b], kt[a:b], w.theta, direction, cu_seqlens=cu_r,
+                                  seq_offsets=off_r, pos_scale=args.pos_scale,
+                                  tokens_per_wave=tpw)
+        elif pid is not None or args.pos_scale != 1.0:
+            rope.qk_apply_ex_(qt, kt, w.theta, direction, cu_seqlens=None if pid is not None else cu,
+                              seqused=None if pid is not None else su, position_ids=pid,
+                              pos_scale=args.pos_scale, tokens_per_wave=tpw)
+        else:
+            rope.qk_apply_(qt, kt, cu, w.theta, direction, seqused=su, tokens_per_wave=tpw)
 
     def step(s, ev=None):
         if ev is not None:
             ev[0].record(stream)
-        rope.qk_apply_(s["q"], s["k"], cu, w.theta, 1, seqused=su, tokens_per_wave=tpw)
+        launch(s["q"], s["k"], 1)
         if ev is not None:
             ev[1].record(stream)
             ev[2].record(stream)
-        rope.qk_apply_(s["dq"], s["dk"], cu, w.theta, -1, seqused=su, tokens_per_wave=tpw)
+        launch(s["dq"], s["dk"], -1)
         if ev is not None:
             ev[3].record(stream)
 
@@ -333,6 +461,7 @@ def main():
             "T": w.T, "valid_tokens": w.valid_tokens, "num_seqs": w.num_seqs,
             "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D, "theta": w.theta,
             "buffer_sets": nsets, "tokens_per_wave": tpw or "auto",
+            "positions": args.positions, "pos_scale": args.pos_scale,
         },
         "step_hbm_GBps": 2 * bpl * args.steps / elapsed / 1e9,
         "roofline": {
