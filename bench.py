@@ -195,11 +195,24 @@ def packed_position_ids(w: workloads.Workload) -> np.ndarray:
     return ids
 
 
-def make_sets(w, nsets, dev):
+def make_sets(w, nsets, dev, layout="contiguous"):
+    """nsets independent buffer sets {q, k, dq, dk}. With layout "qkv" the four are
+    [T, H, D] views into fused projection outputs [T, (Hq + 2 Hkv) D] (and their
+    gradients), as a model's QKV projection produces them; V stays untouched."""
     cu = torch.from_numpy(w.cu_seqlens).to(dev)
     su = None if w.seqused is None else torch.from_numpy(w.seqused).to(dev)
     sets = []
     for i in range(nsets):
+        if layout == "qkv":
+            s = {}
+            for fwd, grad in (("q", "k"), ("dq", "dk")):
+                buf = workloads.make_tensor((w.T, (w.Hq + 2 * w.Hkv) * w.D),
+                                            w.seed(fwd) + 100 * i, w.dtype, device=dev,
+                                            chunk_rows=65536)
+                s[fwd] = buf[:, :w.Hq * w.D].view(w.T, w.Hq, w.D)
+                s[grad] = buf[:, w.Hq * w.D:(w.Hq + w.Hkv) * w.D].view(w.T, w.Hkv, w.D)
+            sets.append(s)
+            continue
         sets.append({what: workloads.make_tensor(w.shape(what), w.seed(what) + 100 * i, w.dtype,
                                                  device=dev, chunk_rows=65536)
                      for what in ("q", "k", "dq", "dk")})
@@ -329,6 +342,8 @@ def main():
                          "cut into 4 token shards, each launched with per-sequence offsets")
     ap.add_argument("--pos-scale", type=float, default=1.0,
                     help="linear position interpolation factor (>= 1)")
+    ap.add_argument("--layout", default="contiguous", choices=["contiguous", "qkv"],
+                    help="qkv: Q/K (and dQ/dK) are strided views into fused QKV buffers")
     ap.add_argument("--compare", action="store_true",
                     help="time fused in-place QK-RoPE against unfused variants, then exit")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -366,11 +381,13 @@ def main():
     # Enough sets that a buffer is touched again only after >= 8x the Infinity
     # Cache's capacity of other traffic: no launch can be served from it.
     nsets = max(2, math.ceil(8 * INFINITY_CACHE_BYTES / set_bytes))
-    cu, su, sets = make_sets(w, nsets, dev)
+    cu, su, sets = make_sets(w, nsets, dev, args.layout)
     tpw = args.tokens_per_wave
 
     stream = torch.cuda.current_stream(dev).cuda_stream  # the stream the library launches on
     if args.compare:
+        if args.layout != "contiguous":
+            raise SystemExit("--compare measures contiguous Q/K only")
         return compare_unfused(rope, w, cu, su, sets, nsets, args, stream)
 
     pid = None
@@ -399,7 +416,7 @@ def main():
                 rope.qk_apply_ex_(qt[a:b], kt[a:b], w.theta, direction, cu_seqlens=cu_r,
                                   seq_offsets=off_r, pos_scale=args.pos_scale,
                                   tokens_per_wave=tpw)
-        elif pid is not None or args.pos_scale != 1.0:
+        elif pid is not None or args.pos_scale != 1.0 or args.layout == "qkv":
             rope.qk_apply_ex_(qt, kt, w.theta, direction, cu_seqlens=None if pid is not None else cu,
                               seqused=None if pid is not None else su, position_ids=pid,
                               pos_scale=args.pos_scale, tokens_per_wave=tpw)
@@ -462,6 +479,7 @@ def main():
             "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D, "theta": w.theta,
             "buffer_sets": nsets, "tokens_per_wave": tpw or "auto",
             "positions": args.positions, "pos_scale": args.pos_scale,
+            "layout": args.layout,
         },
         "step_hbm_GBps": 2 * bpl * args.steps / elapsed / 1e9,
         "roofline": {

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define ROPE_QK_ABI_VERSION 1
+#define ROPE_QK_ABI_VERSION 2
 
 /* Storage dtype of Q and K (computation is fp32 in every case). */
 typedef enum rope_dtype { ROPE_F32 = 0, ROPE_BF16 = 1, ROPE_F16 = 2 } rope_dtype;
@@ -132,8 +132,19 @@ int32_t rope_qk_apply(void* q, void* k, int64_t T, int32_t Hq, int32_t Hkv, int3
  *                position s*p rotates exactly like position p (TRL guide
  *                "Entrainement au-dela de 1 M de jetons", YaRN section: with factor 4,
  *                position 100000 is treated as position 25000). 1 = no scaling.
+ *  q_token_stride, k_token_stride
+ *                elements from one token's first head to the next token's (0 = Hq*D
+ *                resp. Hkv*D, a contiguous [T, H, D] tensor). Heads of one token stay
+ *                contiguous; a larger stride lets q and k be views into a fused QKV
+ *                projection output [T, (Hq + 2*Hkv)*D], rotated in place with V and
+ *                any gaps untouched. q and k must not overlap. A stride below H*D
+ *                (tokens would overlap) or with T*stride above 2^48 elements is
+ *                ROPE_EINVAL. The widest access the library uses is the largest of
+ *                16/8/4 bytes that divides the half row, both base addresses and both
+ *                strides in bytes.
  * Other arguments as in rope_qk_apply. */
 int32_t rope_qk_apply_ex(void* q, void* k, int64_t T, int32_t Hq, int32_t Hkv, int32_t D,
+                         int64_t q_token_stride, int64_t k_token_stride,
                          const int32_t* cu_seqlens, int32_t num_seqs, const int32_t* seqused,
                          const int32_t* seq_offsets, const int32_t* position_ids, double theta,
                          double pos_scale, int32_t dtype, int32_t direction, int32_t index_mode,

@@ -49,8 +49,8 @@ def _load() -> ctypes.CDLL:
     lib.rope_qk_fwd.argtypes = qk + [vp]
     lib.rope_qk_bwd.argtypes = qk + [vp]
     lib.rope_qk_apply.argtypes = qk + [i32, i32, i32, vp]
-    lib.rope_qk_apply_ex.argtypes = [vp, vp, i64, i32, i32, i32, vp, i32, vp, vp, vp, dbl, dbl,
-                                     i32, i32, i32, i32, vp]
+    lib.rope_qk_apply_ex.argtypes = [vp, vp, i64, i32, i32, i32, i64, i64, vp, i32, vp, vp, vp,
+                                     dbl, dbl, i32, i32, i32, i32, vp]
     lib.rope_qk_fwd_pos.argtypes = [vp, vp, i64, i32, i32, i32, vp, dbl, i32, vp]
     lib.rope_qk_bwd_pos.argtypes = [vp, vp, i64, i32, i32, i32, vp, dbl, i32, vp]
     lib.rope_positions.argtypes = [vp, i32, vp, i64, vp, vp, vp]
@@ -96,17 +96,29 @@ def _index_tensor(t, name: str, device: torch.device):
     return t
 
 
-def _qk_tensors(q, k):
+def _qk_tensors(q, k, strided: bool = False):
     if q.device.type != "cuda" or k.device != q.device:
         raise TypeError("q and k must be on the same GPU")
     if q.dtype != k.dtype or q.dtype not in _DTYPE_CODE:
         raise TypeError("q and k must share one dtype: float32, bfloat16 or float16")
     if q.dim() != 3 or k.dim() != 3 or q.shape[0] != k.shape[0] or q.shape[2] != k.shape[2]:
         raise ValueError("expected q[T, Hq, D] and k[T, Hkv, D]")
-    if not (q.is_contiguous() and k.is_contiguous()):
+    if not strided and not (q.is_contiguous() and k.is_contiguous()):
         raise ValueError("q and k must be contiguous (rotation is in place)")
     T, Hq, D = q.shape
     return T, Hq, k.shape[1], D
+
+
+def _token_stride(x, name: str) -> int:
+    """Token stride of a [T, H, D] view whose heads are contiguous within a token
+    (0 when the view is contiguous, meaning H * D)."""
+    T, H, D = x.shape
+    if x.is_contiguous() or x.numel() == 0:
+        return 0
+    if (D > 1 and x.stride(2) != 1) or (H > 1 and x.stride(1) != D):
+        raise ValueError(f"{name}: the heads of a token must be contiguous "
+                         "(stride(2) == 1 and stride(1) == D)")
+    return 0 if T == 1 else x.stride(0)
 
 
 def _qk_args(q, k, cu_seqlens, seqused):
@@ -144,8 +156,13 @@ def qk_apply_ex_(q, k, theta: float, direction: int = 1, cu_seqlens=None, sequse
                  index_mode: int = INDEX_AUTO, tokens_per_wave: int = 0):
     """The general form: positions from `position_ids` (int32[T], negative = untouched)
     or from `cu_seqlens` (+ optional `seqused`, `seq_offsets`), angles with linear
-    position interpolation by `pos_scale` (>= 1). In place; returns (q, k)."""
-    T, Hq, Hkv, D = _qk_tensors(q, k)
+    position interpolation by `pos_scale` (>= 1). In place; returns (q, k).
+
+    q and k may be strided views, e.g. slices of a fused QKV projection output
+    [T, (Hq + 2 Hkv) * D] viewed as [T, H, D], as long as the heads of each token
+    are contiguous; they must not overlap."""
+    T, Hq, Hkv, D = _qk_tensors(q, k, strided=True)
+    qs, ks = _token_stride(q, "q"), _token_stride(k, "k")
     cu = _index_tensor(cu_seqlens, "cu_seqlens", q.device)
     su = _index_tensor(seqused, "seqused", q.device)
     so = _index_tensor(seq_offsets, "seq_offsets", q.device)
@@ -158,8 +175,8 @@ def qk_apply_ex_(q, k, theta: float, direction: int = 1, cu_seqlens=None, sequse
     for name, t in (("seqused", su), ("seq_offsets", so)):
         if t is not None and t.numel() != num_seqs:
             raise ValueError(f"{name} must have one entry per sequence")
-    st = _lib.rope_qk_apply_ex(_ptr(q), _ptr(k), T, Hq, Hkv, D, _ptr(cu), num_seqs, _ptr(su),
-                               _ptr(so), _ptr(pid), float(theta), float(pos_scale),
+    st = _lib.rope_qk_apply_ex(_ptr(q), _ptr(k), T, Hq, Hkv, D, qs, ks, _ptr(cu), num_seqs,
+                               _ptr(su), _ptr(so), _ptr(pid), float(theta), float(pos_scale),
                                _DTYPE_CODE[q.dtype], int(direction), int(index_mode),
                                int(tokens_per_wave), _stream(q.device))
     _check(st, "rope_qk_apply_ex")

@@ -54,6 +54,7 @@ struct RopeParams {
   int64_t T;
   int32_t num_seqs;
   int32_t Hq, Hkv, D;
+  int64_t q_stride, k_stride;  // elements between consecutive tokens of Q / K
   int32_t nc;   // chunks per half row: (D/2) / VEC
   int32_t tpw;  // tokens per wave
   float sin_sign;
@@ -307,14 +308,16 @@ __device__ inline void rotate_rows_general(T* __restrict__ row0, int H, uint32_t
   }
 }
 
-// First row of token t in a [T, H, D] tensor. [U-int64]: with LONG_INDEX the
-// offset is formed in 64 bits; without it, in 32 bits, which the host selects only
-// when every offset of the launch fits. t is wave-uniform, so either way this is
-// scalar arithmetic; per-lane offsets below it are 32-bit (H * D < 2^22).
+// First row of token t in a [T, H, D] tensor whose tokens are `stride` elements
+// apart (H * D when contiguous; more for a view into a fused QKV buffer).
+// [U-int64]: with LONG_INDEX the offset is formed in 64 bits; without it, in 32
+// bits, which the host selects only when every offset of the launch fits. t is
+// wave-uniform, so either way this is scalar arithmetic; per-lane offsets below
+// it are 32-bit (H * D < 2^22).
 template <typename T, bool LONG_INDEX>
-__device__ inline T* token_row0(T* p, int64_t t, int32_t H, int32_t D) {
-  if (LONG_INDEX) return p + t * (int64_t)H * (int64_t)D;
-  return p + (uint32_t)((uint32_t)t * (uint32_t)H * (uint32_t)D);
+__device__ inline T* token_row0(T* p, int64_t t, int64_t stride) {
+  if (LONG_INDEX) return p + t * stride;
+  return p + (uint32_t)((uint32_t)t * (uint32_t)stride);
 }
 
 // ---- the fused QK kernel (a1..a7) ---------------------------------------------------
@@ -363,8 +366,8 @@ __global__ __launch_bounds__(kBlock) void rope_qk_kernel(T* __restrict__ q, T* _
     wave_lds_sync();
 
     // a4/a5: Q rows then K rows of this token, in place.
-    T* qrow = token_row0<T, LONG_INDEX>(q, t, p.Hq, p.D);
-    T* krow = token_row0<T, LONG_INDEX>(k, t, p.Hkv, p.D);
+    T* qrow = token_row0<T, LONG_INDEX>(q, t, p.q_stride);
+    T* krow = token_row0<T, LONG_INDEX>(k, t, p.k_stride);
     if (step_c == 0) {
       if (lane < step_r * nc) {
         float cs[VEC], sn[VEC];
@@ -428,13 +431,15 @@ bool valid_scale(double s) { return isfinite(s) && (float)s >= 1.0f && isfinite(
 
 int32_t elem_size(int32_t dtype) { return dtype == ROPE_F32 ? 4 : 2; }
 
-// Widest chunk (<= 16 bytes) that divides a half row and keeps every access aligned.
-int32_t chunk_bytes(int32_t D, int32_t esize, const void* q, const void* k) {
+// Widest chunk (<= 16 bytes) that divides a half row and keeps every access
+// aligned: the base pointers and the token strides must be multiples of it too.
+int32_t chunk_bytes(int32_t D, int32_t esize, const void* q, const void* k, int64_t q_stride,
+                    int64_t k_stride) {
   const int64_t half_bytes = (int64_t)(D / 2) * esize;
   for (int32_t b = 16; b > esize; b >>= 1) {
     if (half_bytes % b) continue;
-    if (q && ((uintptr_t)q % b)) continue;
-    if (k && ((uintptr_t)k % b)) continue;
+    if (q && (((uintptr_t)q % b) || (q_stride * esize) % b)) continue;
+    if (k && (((uintptr_t)k % b) || (k_stride * esize) % b)) continue;
     return b;
   }
   return esize;
@@ -488,6 +493,7 @@ int32_t launch_typed(void* q, void* k, const PosSource& ps, RopeParams& p, int32
 extern "C" {
 
 int32_t rope_qk_apply_ex(void* q, void* k, int64_t T, int32_t Hq, int32_t Hkv, int32_t D,
+                         int64_t q_token_stride, int64_t k_token_stride,
                          const int32_t* cu_seqlens, int32_t num_seqs, const int32_t* seqused,
                          const int32_t* seq_offsets, const int32_t* position_ids, double theta,
                          double pos_scale, int32_t dtype, int32_t direction, int32_t index_mode,
@@ -509,7 +515,17 @@ int32_t rope_qk_apply_ex(void* q, void* k, int64_t T, int32_t Hq, int32_t Hkv, i
   }
   if ((Hq > 0 && q == nullptr) || (Hkv > 0 && k == nullptr)) return ROPE_EINVAL;
 
-  const bool needs_long = T * (int64_t)H * (int64_t)D >= ((int64_t)1 << 31);
+  const int64_t qs = q_token_stride == 0 ? (int64_t)Hq * D : q_token_stride;
+  const int64_t ks = k_token_stride == 0 ? (int64_t)Hkv * D : k_token_stride;
+  if (qs < (int64_t)Hq * D || ks < (int64_t)Hkv * D) return ROPE_EINVAL;  // tokens overlap
+  // T * stride is formed only after these bounds rule out overflow (T <= 2^40).
+  const int64_t span_max = (int64_t)1 << 48;
+  if ((Hq > 0 && qs > span_max / T) || (Hkv > 0 && ks > span_max / T)) return ROPE_EINVAL;
+
+  // [U-int64] 64-bit offsets exactly when some offset of the launch needs them.
+  const int64_t lim = (int64_t)1 << 31;
+  const bool needs_long = T * (int64_t)H * (int64_t)D >= lim || (Hq > 0 && T * qs >= lim) ||
+                          (Hkv > 0 && T * ks >= lim);
   if (index_mode == ROPE_INDEX_32 && needs_long) return ROPE_EINVAL;
   const bool long_index = needs_long || index_mode == ROPE_INDEX_64;
 
@@ -519,6 +535,8 @@ int32_t rope_qk_apply_ex(void* q, void* k, int64_t T, int32_t Hq, int32_t Hkv, i
   p.Hq = Hq;
   p.Hkv = Hkv;
   p.D = D;
+  p.q_stride = qs;
+  p.k_stride = ks;
   p.tpw = tokens_per_wave == 0 ? auto_tokens_per_wave(T) : tokens_per_wave;
   p.sin_sign = direction > 0 ? 1.0f : -1.0f;
   p.pos_scale = (float)pos_scale;
@@ -533,7 +551,7 @@ int32_t rope_qk_apply_ex(void* q, void* k, int64_t T, int32_t Hq, int32_t Hkv, i
 
   void* qp = Hq > 0 ? q : nullptr;
   void* kp = Hkv > 0 ? k : nullptr;
-  const int32_t bytes = chunk_bytes(D, elem_size(dtype), qp, kp);
+  const int32_t bytes = chunk_bytes(D, elem_size(dtype), qp, kp, qs, ks);
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (dtype) {
     case ROPE_F32: return launch_typed<float>(qp, kp, ps, p, bytes, long_index, s);
@@ -546,36 +564,37 @@ int32_t rope_qk_apply(void* q, void* k, int64_t T, int32_t Hq, int32_t Hkv, int3
                       const int32_t* cu_seqlens, int32_t num_seqs, const int32_t* seqused,
                       double theta, int32_t dtype, int32_t direction, int32_t index_mode,
                       int32_t tokens_per_wave, void* stream) {
-  return rope_qk_apply_ex(q, k, T, Hq, Hkv, D, cu_seqlens, num_seqs, seqused, nullptr, nullptr,
-                          theta, 1.0, dtype, direction, index_mode, tokens_per_wave, stream);
+  return rope_qk_apply_ex(q, k, T, Hq, Hkv, D, 0, 0, cu_seqlens, num_seqs, seqused, nullptr,
+                          nullptr, theta, 1.0, dtype, direction, index_mode, tokens_per_wave,
+                          stream);
 }
 
 int32_t rope_qk_fwd(void* q, void* k, int64_t T, int32_t Hq, int32_t Hkv, int32_t D,
                     const int32_t* cu_seqlens, int32_t num_seqs, const int32_t* seqused,
                     double theta, int32_t dtype, void* stream) {
-  return rope_qk_apply_ex(q, k, T, Hq, Hkv, D, cu_seqlens, num_seqs, seqused, nullptr, nullptr,
-                          theta, 1.0, dtype, +1, ROPE_INDEX_AUTO, 0, stream);
+  return rope_qk_apply_ex(q, k, T, Hq, Hkv, D, 0, 0, cu_seqlens, num_seqs, seqused, nullptr,
+                          nullptr, theta, 1.0, dtype, +1, ROPE_INDEX_AUTO, 0, stream);
 }
 
 int32_t rope_qk_bwd(void* dq, void* dk, int64_t T, int32_t Hq, int32_t Hkv, int32_t D,
                     const int32_t* cu_seqlens, int32_t num_seqs, const int32_t* seqused,
                     double theta, int32_t dtype, void* stream) {
-  return rope_qk_apply_ex(dq, dk, T, Hq, Hkv, D, cu_seqlens, num_seqs, seqused, nullptr, nullptr,
-                          theta, 1.0, dtype, -1, ROPE_INDEX_AUTO, 0, stream);
+  return rope_qk_apply_ex(dq, dk, T, Hq, Hkv, D, 0, 0, cu_seqlens, num_seqs, seqused, nullptr,
+                          nullptr, theta, 1.0, dtype, -1, ROPE_INDEX_AUTO, 0, stream);
 }
 
 int32_t rope_qk_fwd_pos(void* q, void* k, int64_t T, int32_t Hq, int32_t Hkv, int32_t D,
                         const int32_t* position_ids, double theta, int32_t dtype, void* stream) {
   if (T > 0 && position_ids == nullptr) return ROPE_EINVAL;
-  return rope_qk_apply_ex(q, k, T, Hq, Hkv, D, nullptr, 0, nullptr, nullptr, position_ids, theta,
-                          1.0, dtype, +1, ROPE_INDEX_AUTO, 0, stream);
+  return rope_qk_apply_ex(q, k, T, Hq, Hkv, D, 0, 0, nullptr, 0, nullptr, nullptr, position_ids,
+                          theta, 1.0, dtype, +1, ROPE_INDEX_AUTO, 0, stream);
 }
 
 int32_t rope_qk_bwd_pos(void* dq, void* dk, int64_t T, int32_t Hq, int32_t Hkv, int32_t D,
                         const int32_t* position_ids, double theta, int32_t dtype, void* stream) {
   if (T > 0 && position_ids == nullptr) return ROPE_EINVAL;
-  return rope_qk_apply_ex(dq, dk, T, Hq, Hkv, D, nullptr, 0, nullptr, nullptr, position_ids, theta,
-                          1.0, dtype, -1, ROPE_INDEX_AUTO, 0, stream);
+  return rope_qk_apply_ex(dq, dk, T, Hq, Hkv, D, 0, 0, nullptr, 0, nullptr, nullptr, position_ids,
+                          theta, 1.0, dtype, -1, ROPE_INDEX_AUTO, 0, stream);
 }
 
 int32_t rope_positions_ex(const int32_t* cu_seqlens, int32_t num_seqs, const int32_t* seqused,

@@ -11,6 +11,7 @@ import sys
 import mpmath
 import numpy as np
 import pytest
+import torch
 
 import oracle
 import packed_varlen_rotary_rope_amd as rope
@@ -44,7 +45,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert rope.abi_version() == 1
+    assert rope.abi_version() == 2
     lib = rope._lib
     for st in (0, -1, -2, -3):
         assert lib.rope_status_str(st).decode().startswith("ROPE_")
@@ -95,14 +96,14 @@ def test_validation(kw, expect):
 
 
 def apply_ex(**kw):
-    a = dict(q=FAKE, k=FAKE, T=16, Hq=4, Hkv=2, D=128, cu=FAKE, num_seqs=2, seqused=None,
-             offsets=None, ids=None, theta=1e4, scale=1.0, dtype=1, direction=1, index_mode=0,
-             tpw=0, stream=None)
+    a = dict(q=FAKE, k=FAKE, T=16, Hq=4, Hkv=2, D=128, qs=0, ks=0, cu=FAKE, num_seqs=2,
+             seqused=None, offsets=None, ids=None, theta=1e4, scale=1.0, dtype=1, direction=1,
+             index_mode=0, tpw=0, stream=None)
     a.update(kw)
-    return rope._lib.rope_qk_apply_ex(a["q"], a["k"], a["T"], a["Hq"], a["Hkv"], a["D"], a["cu"],
-                                      a["num_seqs"], a["seqused"], a["offsets"], a["ids"],
-                                      a["theta"], a["scale"], a["dtype"], a["direction"],
-                                      a["index_mode"], a["tpw"], a["stream"])
+    return rope._lib.rope_qk_apply_ex(a["q"], a["k"], a["T"], a["Hq"], a["Hkv"], a["D"], a["qs"],
+                                      a["ks"], a["cu"], a["num_seqs"], a["seqused"], a["offsets"],
+                                      a["ids"], a["theta"], a["scale"], a["dtype"],
+                                      a["direction"], a["index_mode"], a["tpw"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,expect", [
@@ -118,6 +119,13 @@ def apply_ex(**kw):
     (dict(dtype=9, ids=FAKE), EUNSUPPORTED),
     (dict(T=0, q=None, k=None, cu=None, ids=None), OK),
     (dict(num_seqs=0, cu=None), OK),
+    (dict(qs=-1), EINVAL),
+    (dict(qs=4 * 128 - 1), EINVAL),             # consecutive q tokens would overlap
+    (dict(ks=2 * 128 - 2), EINVAL),
+    (dict(qs=1 << 45), EINVAL),                 # 16 tokens span 2^49 elements
+    (dict(ks=1 << 45), EINVAL),
+    (dict(qs=1 << 28, index_mode=1), EINVAL),   # 32-bit offsets asked for, 64 needed
+    (dict(Hq=0, q=None, qs=-1), EINVAL),
 ])
 def test_validation_ex(kw, expect):
     assert apply_ex(**kw) == expect
@@ -168,3 +176,19 @@ def test_trig_constants_regenerate():
     mpmath.mp.prec = 300
     err = sum(mpmath.mpf(p) for p in parts) - mpmath.pi / 2
     assert abs(err) < mpmath.mpf(2) ** -150
+
+
+def test_token_stride_of_views():
+    """Token strides the binding derives from [T, H, D] views (host-only logic)."""
+    T, Hq, Hkv, D = 5, 4, 2, 8
+    qkv = torch.zeros(T, (Hq + 2 * Hkv) * D)
+    q = qkv[:, :Hq * D].view(T, Hq, D)
+    k = qkv[:, Hq * D:(Hq + Hkv) * D].view(T, Hkv, D)
+    assert rope._token_stride(q, "q") == (Hq + 2 * Hkv) * D
+    assert rope._token_stride(k, "k") == (Hq + 2 * Hkv) * D
+    assert rope._token_stride(torch.zeros(T, Hq, D), "q") == 0
+    assert rope._token_stride(q[:1], "q") == 0          # one token: stride unused
+    with pytest.raises(ValueError):
+        rope._token_stride(torch.zeros(T, D, Hq).transpose(1, 2), "q")
+    with pytest.raises(ValueError):
+        rope._token_stride(torch.zeros(T, Hq, 2 * D)[:, :, ::2], "q")

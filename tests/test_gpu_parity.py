@@ -452,3 +452,112 @@ def test_positions_export_offsets(rope):
         rpos, rseq = oracle.positions(cu_l, T, su_l, seq_offsets=off_l)
         assert np.array_equal(pos.cpu().numpy(), rpos), (cu_l, off_l)
         assert np.array_equal(seq.cpu().numpy(), rseq), (cu_l, off_l)
+
+
+# ---------------------------------------------------------------- strided (fused QKV) views
+
+def _qkv_views(qkv: torch.Tensor, Hq: int, Hkv: int, D: int, lead: int = 0):
+    """q, k, v views [T, H, D] into a fused projection output [T, width] whose
+    columns are [lead gap | Q | K | V | trailing gap]."""
+    T = qkv.shape[0]
+    q = qkv[:, lead:lead + Hq * D].view(T, Hq, D)
+    k = qkv[:, lead + Hq * D:lead + (Hq + Hkv) * D].view(T, Hkv, D)
+    v = qkv[:, lead + (Hq + Hkv) * D:lead + (Hq + 2 * Hkv) * D].view(T, Hkv, D)
+    return q, k, v
+
+
+@pytest.mark.parametrize("direction", [1, -1])
+def test_fused_qkv_views_qwen3_8b(rope, direction):
+    """Q and K rotated in place as views into the fused QKV output of the Qwen3-8B
+    packed batch (token stride (32 + 2*8) * 128): bit-identical to rotating
+    contiguous copies, V untouched, and against the oracle."""
+    w = workloads.get("qwen3_8b_packed")
+    Hq, Hkv, D = w.Hq, w.Hkv, w.D
+    print(f"[parity] fused qkv views qwen3_8b_packed direction={direction}", flush=True)
+    qkv0 = workloads.make_tensor((w.T, (Hq + 2 * Hkv) * D), 9100, "bf16", device=DEV)
+    qkv = qkv0.clone()
+    q, k, v = _qkv_views(qkv, Hq, Hkv, D)
+    assert not q.is_contiguous() and q.stride(0) == (Hq + 2 * Hkv) * D
+    qc, kc = q.contiguous(), k.contiguous()
+    cu = torch.from_numpy(w.cu_seqlens).to(DEV)
+    rope.qk_apply_ex_(q, k, w.theta, direction, cu_seqlens=cu)
+    rope.qk_apply_(qc, kc, cu, w.theta, direction)
+    torch.cuda.synchronize()
+    assert torch.equal(q.contiguous().view(torch.int16), qc.view(torch.int16))
+    assert torch.equal(k.contiguous().view(torch.int16), kc.view(torch.int16))
+    _, _, v0 = _qkv_views(qkv0, Hq, Hkv, D)
+    assert torch.equal(v.view(torch.int16), v0.view(torch.int16)), "V changed"
+    q0, k0, _ = _qkv_views(qkv0, Hq, Hkv, D)
+    touched = np.ones(w.T, dtype=bool)
+    for what, x0, got in (("q", q0, q), ("k", k0, k)):
+        x = bits(x0)
+        ref = oracle.rope(x, w.cu_seqlens, w.theta, direction, "bf16", nthreads=NTHREADS)
+        assert_parity("bf16", bits(got), ref, x, touched, f"qkv:{what}")
+
+
+@pytest.mark.parametrize("dtype,D,Hq,Hkv,lead,tail", [
+    (torch.float32, 64, 3, 1, 0, 2),     # stride 8 bytes past a 16-byte multiple
+    (torch.float32, 96, 2, 2, 1, 0),     # base 4 bytes off: 4-byte accesses
+    (torch.float16, 128, 5, 1, 0, 3),    # odd stride in 2-byte words
+    (torch.bfloat16, 256, 4, 2, 8, 8),   # gaps on both sides, 16-byte aligned
+    (torch.bfloat16, 2, 3, 1, 1, 1),     # smallest head dimension
+])
+def test_strided_views_ragged(rope, dtype, D, Hq, Hkv, lead, tail):
+    """Views with leading/trailing gaps and strides that force narrower accesses, on a
+    ragged batch with an empty sequence and a token tail: parity with the oracle,
+    gaps and V bit-for-bit untouched."""
+    name = {torch.float32: "f32", torch.bfloat16: "bf16", torch.float16: "f16"}[dtype]
+    lengths = [37, 0, 129, 1, 64]
+    cu_h = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    T = int(cu_h[-1]) + 5  # tokens past the last sequence are left untouched
+    width = lead + (Hq + 2 * Hkv) * D + tail
+    print(f"[parity] strided views {name} D={D} Hq={Hq} Hkv={Hkv} lead={lead} tail={tail}",
+          flush=True)
+    qkv0 = workloads.make_tensor((T, width), 9200 + D, name, device=DEV)
+    qkv = qkv0.clone()
+    q, k, _ = _qkv_views(qkv, Hq, Hkv, D, lead)
+    cu = torch.from_numpy(cu_h).to(DEV)
+    rope.qk_apply_ex_(q, k, 1e4, 1, cu_seqlens=cu)
+    torch.cuda.synchronize()
+    q0, k0, _ = _qkv_views(qkv0, Hq, Hkv, D, lead)
+    pos, _ = oracle.positions(cu_h, T)
+    touched = pos >= 0
+    for what, x0, got in (("q", q0, q), ("k", k0, k)):
+        x = bits(x0)
+        ref = oracle.rope(x, cu_h, 1e4, 1, name, nthreads=NTHREADS)
+        assert_parity(name, bits(got), ref, x, touched, f"strided:{what}")
+    # everything outside the Q and K views is unchanged
+    mask = torch.ones(width, dtype=torch.bool, device=DEV)
+    mask[lead:lead + (Hq + Hkv) * D] = False
+    word = _word(dtype)
+    assert torch.equal(qkv.view(word)[:, mask], qkv0.view(word)[:, mask])
+
+
+def test_stride_forces_64bit_offsets(rope):
+    """A token stride that takes offsets past 2^31 elements while T*H*D stays small:
+    the library must switch to 64-bit offsets by itself. 8192 tokens, one head each,
+    2^18 elements apart (a 4 GiB bf16 buffer); the result matches the oracle."""
+    T, D, stride = 8192, 128, 1 << 18
+    print("[parity] 64-bit offsets from a large token stride", flush=True)
+    buf = torch.zeros((T, stride), dtype=torch.bfloat16, device=DEV)
+    vals = workloads.make_tensor((T, 2, D), 9300, "bf16", device=DEV)
+    buf[:, :D] = vals[:, 0]
+    buf[:, stride - D:] = vals[:, 1]
+    q = buf[:, :D].view(T, 1, D)
+    k = buf[:, stride - D:].view(T, 1, D)
+    assert q.stride(0) == stride and T * stride >= 1 << 31
+    lengths = [1000, 4000, 3192]
+    cu_h = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    rope.qk_apply_ex_(q, k, 1e6, 1, cu_seqlens=torch.from_numpy(cu_h).to(DEV))
+    with pytest.raises(rope.RopeError):
+        rope.qk_apply_ex_(q, k, 1e6, 1, cu_seqlens=torch.from_numpy(cu_h).to(DEV),
+                          index_mode=rope.INDEX_32)
+    torch.cuda.synchronize()
+    touched = np.ones(T, dtype=bool)
+    for what, x0, got in (("q", vals[:, :1], q), ("k", vals[:, 1:], k)):
+        x = bits(x0)
+        ref = oracle.rope(x, cu_h, 1e6, 1, "bf16", nthreads=NTHREADS)
+        assert_parity("bf16", bits(got), ref, x, touched, f"stride64:{what}")
+    assert torch.count_nonzero(buf[:, D:stride - D]).item() == 0
+    del buf
+    torch.cuda.empty_cache()
