@@ -1,4 +1,5 @@
-"""Build the CPU oracle (plain C, gcc) into oracle/librope_oracle.so.
+"""Build the CPU oracles (plain C, gcc): oracle/librope_oracle.so (QK rotary
+embedding) and oracle/libglu_oracle.so (SwiGLU / GeGLU).
 
 Test infrastructure: building the checker is not using it.
 """
@@ -10,6 +11,8 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "rope_oracle.c")
 LIB_PATH = os.path.join(HERE, "librope_oracle.so")
+GLU_SRC = os.path.join(HERE, "glu_oracle.c")
+GLU_LIB_PATH = os.path.join(HERE, "libglu_oracle.so")
 
 # -ffp-contract=off: every product and sum is rounded as written (no FMA).
 CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off", "-Wall"]
@@ -23,5 +26,12 @@ def build(src: str = SRC, out: str = LIB_PATH) -> str:
     return out
 
 
+def build_all() -> None:
+    build(SRC, LIB_PATH)
+    build(GLU_SRC, GLU_LIB_PATH)
+
+
 if __name__ == "__main__":
-    print(build())
+    build_all()
+    print(LIB_PATH)
+    print(GLU_LIB_PATH)
