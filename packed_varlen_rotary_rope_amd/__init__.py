@@ -22,7 +22,7 @@ import torch
 __all__ = [
     "RopeError", "qk_fwd_", "qk_bwd_", "qk_apply_", "qk_apply_ex_", "qk_fwd_pos_", "qk_bwd_pos_",
     "positions", "cos_sin", "inv_freq", "abi_version", "LIB_PATH", "INDEX_AUTO", "INDEX_32",
-    "INDEX_64",
+    "INDEX_64", "glu_fwd", "glu_bwd", "GLU_KINDS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librope_qk.so")
@@ -58,9 +58,12 @@ def _load() -> ctypes.CDLL:
     lib.rope_cos_sin.argtypes = [vp, i64, i32, dbl, vp, vp, vp]
     lib.rope_cos_sin_ex.argtypes = [vp, i64, i32, dbl, dbl, vp, vp, vp]
     lib.rope_inv_freq.argtypes = [dbl, i32, vp]
+    lib.glu_fwd.argtypes = [i32, vp, vp, vp, i64, i64, i64, i64, i32, i32, vp]
+    lib.glu_bwd.argtypes = [i32, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, vp]
     for name in ("rope_qk_fwd", "rope_qk_bwd", "rope_qk_apply", "rope_qk_apply_ex",
                  "rope_qk_fwd_pos", "rope_qk_bwd_pos", "rope_positions", "rope_positions_ex",
-                 "rope_cos_sin", "rope_cos_sin_ex", "rope_inv_freq", "rope_abi_version"):
+                 "rope_cos_sin", "rope_cos_sin_ex", "rope_inv_freq", "rope_abi_version",
+                 "glu_fwd", "glu_bwd"):
         getattr(lib, name).restype = i32
     lib.rope_status_str.argtypes = [i32]
     lib.rope_status_str.restype = ctypes.c_char_p
@@ -258,3 +261,78 @@ def inv_freq(theta: float, D: int) -> torch.Tensor:
     out = torch.empty(D // 2, dtype=torch.float32)
     _check(_lib.rope_inv_freq(float(theta), int(D), out.data_ptr()), "rope_inv_freq")
     return out
+
+
+# ---------------------------------------------------------------- SwiGLU / GeGLU
+
+GLU_KINDS = {"swiglu": 0, "geglu": 1, "geglu_tanh": 2}
+
+
+def _rows(x, name: str):
+    """(rows, cols, row stride) of a 2-D CUDA tensor with contiguous columns."""
+    if x.device.type != "cuda" or x.dtype not in _DTYPE_CODE:
+        raise TypeError(f"{name}: expected a float32, bfloat16 or float16 CUDA tensor")
+    if x.dim() != 2:
+        raise ValueError(f"{name}: expected a 2-D [rows, cols] tensor")
+    rows, cols = x.shape
+    if cols > 1 and x.stride(1) != 1:
+        raise ValueError(f"{name}: columns must be contiguous")
+    return rows, cols, (x.stride(0) if rows > 1 else cols)
+
+
+def _glu_group(tensors, names):
+    """Shape and one shared row stride for tensors that the C ABI lays out alike."""
+    dims = [_rows(t, n) for t, n in zip(tensors, names)]
+    rows, cols, stride = dims[0]
+    for (r, c, st), n in zip(dims[1:], names[1:]):
+        if (r, c) != (rows, cols):
+            raise ValueError(f"{n}: shape differs from {names[0]}")
+        if st != stride and rows > 1:
+            raise ValueError(f"{n}: row stride differs from {names[0]}")
+    dtype = tensors[0].dtype
+    if any(t.dtype != dtype or t.device != tensors[0].device for t in tensors):
+        raise TypeError("all tensors must share one dtype and device")
+    return rows, cols, stride
+
+
+def glu_fwd(kind: str, e, g, out=None, index_mode: int = INDEX_AUTO):
+    """h = act(e) * g for act = silu ("swiglu"), exact gelu ("geglu") or tanh gelu
+    ("geglu_tanh"), one launch on the current stream. e and g: [rows, cols] with
+    contiguous columns and one row stride (two dense tensors, or the two halves of
+    a fused gate/up output). out: a [rows, cols] tensor (new and dense if None; it
+    may be e or g itself). Returns out."""
+    rows, cols, in_stride = _glu_group([e, g], ["e", "g"])
+    if out is None:
+        out = torch.empty((rows, cols), dtype=e.dtype, device=e.device)
+    orows, ocols, out_stride = _rows(out, "out")
+    if (orows, ocols) != (rows, cols) or out.dtype != e.dtype or out.device != e.device:
+        raise ValueError("out: shape, dtype or device differs from e")
+    st = _lib.glu_fwd(GLU_KINDS[kind], _ptr(e), _ptr(g), _ptr(out), rows, cols, in_stride,
+                      out_stride, _DTYPE_CODE[e.dtype], int(index_mode), _stream(e.device))
+    _check(st, "glu_fwd")
+    return out
+
+
+def glu_bwd(kind: str, dh, e, g, de=None, dg=None, index_mode: int = INDEX_AUTO):
+    """de = dh * g * act'(e), dg = dh * act(e), one launch. de and dg take the
+    layout of e and g (new tensors with e's strides if None; pass de=e, dg=g to
+    update the inputs in place). Returns (de, dg)."""
+    rows, cols, in_stride = _glu_group([e, g], ["e", "g"])
+    hrows, hcols, out_stride = _rows(dh, "dh")
+    if (hrows, hcols) != (rows, cols) or dh.dtype != e.dtype or dh.device != e.device:
+        raise ValueError("dh: shape, dtype or device differs from e")
+    if de is None and dg is None and in_stride == 2 * cols and \
+            g.data_ptr() == e.data_ptr() + cols * e.element_size():
+        # e and g are the halves of one fused gate/up output: so are de and dg
+        buf = torch.empty((rows, 2 * cols), dtype=e.dtype, device=e.device)
+        de, dg = buf[:, :cols], buf[:, cols:]
+    if de is None:
+        de = torch.empty_strided((rows, cols), (in_stride, 1), dtype=e.dtype, device=e.device)
+    if dg is None:
+        dg = torch.empty_strided((rows, cols), (in_stride, 1), dtype=e.dtype, device=e.device)
+    _glu_group([e, g, de, dg], ["e", "g", "de", "dg"])
+    st = _lib.glu_bwd(GLU_KINDS[kind], _ptr(dh), _ptr(e), _ptr(g), _ptr(de), _ptr(dg), rows, cols,
+                      in_stride, out_stride, _DTYPE_CODE[e.dtype], int(index_mode),
+                      _stream(e.device))
+    _check(st, "glu_bwd")
+    return de, dg

@@ -1,4 +1,5 @@
-"""Build the HIP library librope_qk.so for gfx950 with hipcc (in-tree).
+"""Build the HIP library librope_qk.so (QK-RoPE and SwiGLU/GeGLU kernels) for
+gfx950 with hipcc (in-tree).
 
 Usage: python -m packed_varlen_rotary_rope_amd.build
 """
@@ -9,7 +10,7 @@ import subprocess
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "rope_qk.hip")
+SRCS = [os.path.join(PKG, "csrc", "rope_qk.hip"), os.path.join(PKG, "csrc", "glu.hip")]
 LIB_PATH = os.path.join(PKG, "librope_qk.so")
 ARCH = "gfx950"
 
@@ -35,7 +36,7 @@ def hipcc() -> str:
 
 def build(extra_flags=(), out: str = LIB_PATH) -> str:
     tmp = out + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, *extra_flags, "-o", tmp, SRC]
+    cmd = [hipcc(), *HIPCC_FLAGS, *extra_flags, "-o", tmp, *SRCS]
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
     return out

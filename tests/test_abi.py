@@ -18,7 +18,7 @@ import packed_varlen_rotary_rope_amd as rope
 from oracle_checks import ref_inv_freq
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "rope_qk.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("rope_qk.h", "glu.h")]
 CSRC = os.path.join(ROOT, "packed_varlen_rotary_rope_amd", "csrc")
 
 OK, EINVAL, EUNSUPPORTED = 0, -1, -2
@@ -26,14 +26,19 @@ FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: every call below fails va
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    return re.findall(r"^\s*(?:int32_t|const char\*)\s+(rope_\w+)\s*\(", text, re.M)
+    names = []
+    for header in HEADERS:
+        text = open(header).read()
+        names += re.findall(r"^\s*(?:int32_t|const char\*)\s+((?:rope|glu)_\w+)\s*\(", text,
+                            re.M)
+    return names
 
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
     assert set(names) >= {"rope_qk_fwd", "rope_qk_bwd", "rope_qk_apply", "rope_positions",
-                          "rope_cos_sin", "rope_inv_freq", "rope_status_str", "rope_abi_version"}
+                          "rope_cos_sin", "rope_inv_freq", "rope_status_str", "rope_abi_version",
+                          "glu_fwd", "glu_bwd"}
     out = subprocess.run(["nm", "-D", "--defined-only", rope.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
@@ -178,6 +183,37 @@ def test_trig_constants_regenerate():
     assert abs(err) < mpmath.mpf(2) ** -150
 
 
+def test_glu_constants_regenerate():
+    """glu_constants.h is what its generator writes; the roots it holds are roots of
+    the derivatives written independently here (mpmath, literal definitions)."""
+    sys.path.insert(0, CSRC)
+    try:
+        import gen_glu_constants as gen
+    finally:
+        sys.path.remove(CSRC)
+    text = open(os.path.join(CSRC, "glu_constants.h")).read()
+    assert text == gen.generate()
+    mpmath.mp.dps = 40
+
+    def silu(x):
+        return x / (1 + mpmath.exp(-x))
+
+    def gelu(x):
+        return x * (1 + mpmath.erf(x / mpmath.sqrt(2))) / 2
+
+    def gelu_tanh(x):
+        k = mpmath.sqrt(2 / mpmath.pi)
+        return x / 2 * (1 + mpmath.tanh(k * (x + mpmath.mpf("0.044715") * x ** 3)))
+
+    for name, f in (("Silu", silu), ("Gelu", gelu), ("GeluTanh", gelu_tanh)):
+        # the literals are fp32 values: round the parsed decimal back to fp32
+        hi = float(np.float32(re.search(r"k%sRootHi = ([^f]+)f;" % name, text).group(1)))
+        lo = float(np.float32(re.search(r"k%sRootLo = ([^f]+)f;" % name, text).group(1)))
+        root = mpmath.mpf(hi) + mpmath.mpf(lo)
+        slope = mpmath.diff(f, root, 2)
+        assert abs(mpmath.diff(f, root) / slope) < 1e-13, name  # |root error| < 1e-13
+
+
 def test_token_stride_of_views():
     """Token strides the binding derives from [T, H, D] views (host-only logic)."""
     T, Hq, Hkv, D = 5, 4, 2, 8
@@ -192,3 +228,46 @@ def test_token_stride_of_views():
         rope._token_stride(torch.zeros(T, D, Hq).transpose(1, 2), "q")
     with pytest.raises(ValueError):
         rope._token_stride(torch.zeros(T, Hq, 2 * D)[:, :, ::2], "q")
+
+
+# ---------------------------------------------------------------- SwiGLU / GeGLU validation
+
+def glu(bwd=False, **kw):
+    a = dict(kind=0, dh=FAKE, e=FAKE, g=FAKE, out0=FAKE, out1=FAKE, rows=16, cols=64, ins=0,
+             outs=0, dtype=1, index_mode=0, stream=None)
+    a.update(kw)
+    if bwd:
+        return rope._lib.glu_bwd(a["kind"], a["dh"], a["e"], a["g"], a["out0"], a["out1"],
+                                 a["rows"], a["cols"], a["ins"], a["outs"], a["dtype"],
+                                 a["index_mode"], a["stream"])
+    return rope._lib.glu_fwd(a["kind"], a["e"], a["g"], a["out0"], a["rows"], a["cols"], a["ins"],
+                             a["outs"], a["dtype"], a["index_mode"], a["stream"])
+
+
+@pytest.mark.parametrize("bwd", [False, True])
+@pytest.mark.parametrize("kw,expect", [
+    (dict(kind=3), EINVAL),
+    (dict(kind=-1), EINVAL),
+    (dict(dtype=5), EUNSUPPORTED),
+    (dict(rows=-1), EINVAL),
+    (dict(cols=-1), EINVAL),
+    (dict(ins=63), EINVAL),                       # rows would overlap
+    (dict(outs=10), EINVAL),
+    (dict(ins=-64), EINVAL),
+    (dict(e=None), EINVAL),
+    (dict(g=None), EINVAL),
+    (dict(out0=None), EINVAL),
+    (dict(index_mode=3), EINVAL),
+    (dict(rows=1 << 20, ins=1 << 29), EINVAL),    # span 2^49 elements
+    (dict(rows=1 << 16, cols=1 << 16, index_mode=1), EINVAL),  # 2^32 elements need 64 bits
+    (dict(rows=0), OK),
+    (dict(cols=0), OK),
+    (dict(rows=0, e=None, g=None, out0=None, out1=None, dh=None), OK),
+])
+def test_glu_validation(bwd, kw, expect):
+    assert glu(bwd, **kw) == expect
+
+
+def test_glu_bwd_needs_its_extra_pointers():
+    assert glu(True, dh=None) == EINVAL
+    assert glu(True, out1=None) == EINVAL

@@ -23,7 +23,8 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-__all__ = ["Workload", "WORKLOADS", "get", "make_tensor", "names"]
+__all__ = ["Workload", "WORKLOADS", "get", "make_tensor", "names", "GluWorkload",
+           "GLU_WORKLOADS", "glu_get", "glu_names"]
 
 
 @dataclass(frozen=True)
@@ -153,6 +154,56 @@ def names() -> list:
 
 def get(name: str) -> Workload:
     return WORKLOADS[name]()
+
+
+# ---------------------------------------------------------------- SwiGLU / GeGLU inputs
+#
+# The gated MLP activation runs on [tokens, intermediate] tensors: e (gate
+# projection), g (up projection) and, in the backward, dh (upstream gradient),
+# each N(0, 1) from its own seed: e 6000+k, g 7000+k, dh 8000+k. Token counts are
+# those of the packed RoPE batches; the intermediate sizes are the published
+# Qwen3 model configurations (4B: 9728, 8B: 12288). The 524288-token case is the
+# pages' 500K-context run, where 2^31-element offsets are exceeded.
+
+@dataclass(frozen=True)
+class GluWorkload:
+    name: str
+    number: int
+    rows: int  # tokens
+    cols: int  # intermediate size
+    dtype: str
+    description: str = ""
+
+    @property
+    def elements(self) -> int:
+        return self.rows * self.cols
+
+    @property
+    def elem_bytes(self) -> int:
+        return 4 if self.dtype == "f32" else 2
+
+    def seed(self, what: str) -> int:
+        return {"e": 6000, "g": 7000, "dh": 8000}[what] + self.number
+
+
+GLU_WORKLOADS = {
+    "glu_tiny": GluWorkload("glu_tiny", 11, 37, 40, "f32",
+                            "37 rows x 40 columns, fp32 (oracle in milliseconds)"),
+    "glu_qwen3_4b": GluWorkload("glu_qwen3_4b", 12, 16384, 9728, "bf16",
+                                "16384 tokens x 9728 (Qwen3-4B MLP), bf16"),
+    "glu_qwen3_8b": GluWorkload("glu_qwen3_8b", 13, 8554, 12288, "bf16",
+                                "8554 tokens x 12288 (Qwen3-8B MLP), bf16"),
+    "glu_long_512k": GluWorkload("glu_long_512k", 14, 524288, 9728, "bf16",
+                                 "524288 tokens x 9728, bf16: 5.1e9 elements, 64-bit offsets"),
+}
+
+
+def glu_names() -> list:
+    return list(GLU_WORKLOADS)
+
+
+def glu_get(name: str) -> GluWorkload:
+    return GLU_WORKLOADS[name]
 
 
 _TORCH_DTYPES = {"f32": "float32", "bf16": "bfloat16", "f16": "float16"}
