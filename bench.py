@@ -44,12 +44,16 @@ KERNEL_SRC = os.path.join(ROOT, "packed_varlen_rotary_rope_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "rope_qk_qwen3_4b_packed_traffic.txt")
 
 
+# The sources rope_qk_kernel is compiled from: a traffic summary taken on other
+# sources does not describe the kernel being timed.
+ROPE_SOURCES = ["rope_qk.hip", "storage.h", "cr_sincos.h", "trig_constants.h"]
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for name in sorted(os.listdir(KERNEL_SRC)):
-        if name.endswith((".hip", ".h")):
-            with open(os.path.join(KERNEL_SRC, name), "rb") as fh:
-                h.update(name.encode() + b"\0" + fh.read())
+    for name in ROPE_SOURCES:
+        with open(os.path.join(KERNEL_SRC, name), "rb") as fh:
+            h.update(name.encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]
 
 
@@ -330,12 +334,105 @@ def compare_unfused(rope, w, cu, su, sets, nsets, args, stream):
     print(json.dumps(out))
 
 
+GLU_METRIC = "SwiGLU/GeGLU fwd+bwd tokens/s and achieved HBM GB/s (% of peak)"
+
+
+def bench_glu(args) -> None:
+    """One step = glu_fwd (e, g -> h) + glu_bwd (dh, e, g -> de, dg), out of place,
+    on [tokens, intermediate] tensors resident in HBM; buffer sets rotate so no
+    launch is served from the Infinity Cache. Prints one JSON line; the roofline is
+    that of the backward (5 streams, the longer launch), the forward's is beside it."""
+    import packed_varlen_rotary_rope_amd as rope
+
+    w = workloads.glu_get(args.workload)
+    dev = torch.device("cuda:0")
+    n = w.elements
+    set_bytes = 6 * n * w.elem_bytes
+    nsets = max(2, math.ceil(8 * INFINITY_CACHE_BYTES / set_bytes))
+    sets = []
+    for i in range(nsets):
+        st = {k: workloads.make_tensor((w.rows, w.cols), w.seed(k) + 100 * i, w.dtype, device=dev,
+                                       chunk_rows=8192) for k in ("e", "g", "dh")}
+        for k in ("h", "de", "dg"):
+            st[k] = torch.empty((w.rows, w.cols), dtype=st["e"].dtype, device=dev)
+        sets.append(st)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    kind = args.glu
+
+    def step(s, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        rope.glu_fwd(kind, s["e"], s["g"], out=s["h"])
+        if ev is not None:
+            ev[1].record(stream)
+            ev[2].record(stream)
+        rope.glu_bwd(kind, s["dh"], s["e"], s["g"], de=s["de"], dg=s["dg"])
+        if ev is not None:
+            ev[3].record(stream)
+
+    for i in range(args.warmup):
+        step(sets[i % nsets])
+    events = {i: [HipEvent() for _ in range(4)] for i in range(0, args.steps, EVENT_EVERY)}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(sets[i % nsets], events.get(i))
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    fwd_us = float(np.mean([ev[0].elapsed_ms(ev[1]) for ev in events.values()])) * 1e3
+    bwd_us = float(np.mean([ev[2].elapsed_ms(ev[3]) for ev in events.values()])) * 1e3
+    fwd_bytes, bwd_bytes = 3 * n * w.elem_bytes, 5 * n * w.elem_bytes
+    achieved = bwd_bytes / (bwd_us * 1e-6) / 1e9
+    out = {
+        "metric": GLU_METRIC,
+        "value": w.rows * args.steps / elapsed,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": elapsed / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) e, g, dh)",
+        "config": {"workload": w.name, "rows": w.rows, "cols": w.cols, "kind": kind,
+                   "buffer_sets": nsets},
+        "roofline": {
+            "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS, "traffic": None, "kernel": "glu_kernel (backward)",
+            "bytes_per_launch": bwd_bytes, "avg_launch_us": bwd_us,
+        },
+        "forward": {"bytes_per_launch": fwd_bytes, "avg_launch_us": fwd_us,
+                    "achieved_GBps": fwd_bytes / (fwd_us * 1e-6) / 1e9},
+    }
+    if args.cpu_seconds > 0:
+        from oracle import glu as glu_oracle
+
+        rows = max(1, min(w.rows, 256))
+        host = {k: workloads.host_bits(workloads.make_tensor((rows, w.cols), w.seed(k), w.dtype))
+                for k in ("e", "g", "dh")}
+        nthreads = max(1, min(16, len(os.sched_getaffinity(0))))
+        total, reps = 0.0, 0
+        while total < args.cpu_seconds and reps < 1000:
+            total += glu_oracle.seconds(kind, host["e"], host["g"], host["dh"], w.dtype, nthreads)
+            reps += 1
+        out["cpu_baseline"] = {
+            "value": rows * reps / total, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
+            "sample": f"{reps} fwd+bwd passes over {rows} of the {w.rows} rows "
+                      f"({w.cols} columns), {total:.1f} s timed",
+        }
+    print(json.dumps(out))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="qwen3_4b_packed", choices=workloads.names())
+    ap.add_argument("--workload", default=None,
+                    choices=workloads.names() + workloads.glu_names(),
+                    help="default: qwen3_4b_packed (glu_qwen3_4b with --glu)")
     ap.add_argument("--tokens-per-wave", type=int, default=0, help="0: library default")
     ap.add_argument("--positions", default="cu", choices=["cu", "ids", "shards4"],
                     help="position source: cu_seqlens; explicit per-token ids; or the batch "
@@ -344,6 +441,8 @@ def main():
                     help="linear position interpolation factor (>= 1)")
     ap.add_argument("--layout", default="contiguous", choices=["contiguous", "qkv"],
                     help="qkv: Q/K (and dQ/dK) are strided views into fused QKV buffers")
+    ap.add_argument("--glu", default=None, choices=["swiglu", "geglu", "geglu_tanh"],
+                    help="time the SwiGLU/GeGLU kernels instead (workload: a glu_* name)")
     ap.add_argument("--compare", action="store_true",
                     help="time fused in-place QK-RoPE against unfused variants, then exit")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -372,6 +471,14 @@ def main():
     if args.copy_calibration > 0:
         copy_calibration(args.copy_calibration, 5)
         return
+    if args.glu:
+        args.workload = args.workload or "glu_qwen3_4b"
+        if args.workload not in workloads.glu_names():
+            raise SystemExit("--glu takes a glu_* workload")
+        return bench_glu(args)
+    args.workload = args.workload or "qwen3_4b_packed"
+    if args.workload not in workloads.names():
+        raise SystemExit("glu_* workloads need --glu")
 
     import packed_varlen_rotary_rope_amd as rope
 

@@ -19,13 +19,16 @@
 // a lane splits it into (row, chunk in row) with one division.
 //
 // Accuracy. sigmoid comes from one exp of -|z| (no overflow, no cancellation:
-// sigmoid(z) = 1/(1+t) or t/(1+t), t = exp(-|z|)); Phi(e) = erfc(-e/sqrt 2)/2
-// keeps its relative accuracy in the negative tail. The derivative act'(e) has a
-// root e0 where its direct formula cancels; within |e - e0| <= 1/4 it is taken
-// from a degree-10 Taylor polynomial around e0 (glu_constants.h). Every output is
-// then within a few fp32 ulps of the exact value, plus the conditioning of the
-// tail (about e^2 ulps for the erfc and tanh forms), before its one rounding to
-// the storage dtype.
+// sigmoid(z) = 1/(1+t) or t/(1+t), t = exp(-|z|)); Phi(e) comes from
+// erfc(|e|/sqrt 2)/2 = s exp(-e^2/2) R(s), s = 1/(2 sqrt 2 + |e|), with a fitted
+// polynomial R and an exactly split exponent, so it keeps its relative accuracy
+// in the negative tail and shares its exp with the density. The derivative act'(e) has a
+// root e0 where its direct formula cancels; near e0 it is taken from a Taylor
+// polynomial around e0 (glu_constants.h). With fp32 storage every output is then
+// within a few fp32 ulps of the exact value (plus, for the tanh form, the
+// conditioning of its tail: about |2u(e)| ulps). With bf16 / f16 storage shorter
+// polynomials are used, whose errors (below 2^-16 relative) stay far under half a
+// 16-bit ulp; either way each output is rounded once to the storage dtype.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -52,34 +55,95 @@ struct GluShape {
 
 // ---- activations in fp32 -----------------------------------------------------------
 
+// exp(y) for -150 <= y <= 0 (Cody-Waite style): y log2(e) = n + f with n an
+// integer and |f| <= 1/2, exp(y) = 2^f 2^n. The product y log2(e) is carried as
+// ph + pl (FMA split, log2(e) itself in two parts), so f = (ph - n) + pl is exact
+// to far below an ulp; 2^f is one v_exp_f32 (1 ulp on [-1/2, 1/2]) and the
+// scaling by 2^n one ldexp, which also rounds the subnormal results correctly.
+__device__ inline float exp_nonpos(float y) {
+  const float ph = y * kLog2e;
+  const float pl = __builtin_fmaf(y, kLog2eLo, __builtin_fmaf(y, kLog2e, -ph));
+  const float n = __builtin_rintf(ph);
+  const float f = (ph - n) + pl;
+  return __builtin_amdgcn_ldexpf(__builtin_amdgcn_exp2f(f), (int)n);
+}
+
 // sigmoid(z) and 1 - sigmoid(z) from t = exp(-|z|): 1/(1+t) and t/(1+t), each the
-// larger or the smaller by the sign of z. rcp is within 1 ulp.
+// larger or the smaller by the sign of z. rcp is within 1 ulp. exp(-150) is 0 in
+// fp32, so larger |z| are capped there.
 __device__ inline void sigmoid_pair(float z, float& s, float& sc) {
-  const float t = expf(-fabsf(z));
+  const float t = exp_nonpos(fmaxf(-fabsf(z), -150.0f));
   const float r = __builtin_amdgcn_rcpf(1.0f + t);
   const float small = t * r;
   s = z >= 0.0f ? r : small;
   sc = z >= 0.0f ? small : r;
 }
 
-// act'(e0 + d) near the root e0 of the derivative: d * sum_{k<K} a[k] d^k.
-__device__ inline float root_poly(float e, float root_hi, float root_lo, const float (&a)[kRootDegree],
-                                  float direct) {
-  const float d = (e - root_hi) - root_lo;  // e - root_hi is exact inside the window
-  float p = a[kRootDegree - 1];
+// Phi(e) and exp(-e^2/2) with one exp. With s = 1/(2 sqrt(2) + |e|),
+// erfc(|e|/sqrt 2)/2 = s exp(-e^2/2) R(s) for a fitted polynomial R
+// (glu_constants.h). Phi(e) is that half-erfc for e < 0 and 1 minus it
+// otherwise. |e| is capped at 16, where Phi is 0 or 1 in fp32 and exp(-e^2/2) is
+// 0, so nothing overflows. FULL (fp32 storage): the degree-8 R, and e^2 split into
+// its rounded value and the exact rounding error (FMA) so that the exponent
+// carries no rounding of its own; otherwise the degree-6 R and the rounded e^2,
+// whose errors (below 2^-16 relative) vanish in the 16-bit rounding.
+template <bool FULL>
+__device__ inline void normal_cdf_gauss(float e, float& cdf, float& gauss) {
+  const float ec = fminf(fmaxf(e, -16.0f), 16.0f);
+  const float s = __builtin_amdgcn_rcpf(kPhiShift + fabsf(ec));
+  float r;
+  if constexpr (FULL) {
+    r = kPhiPoly[kPhiDegree];
 #pragma unroll
-  for (int k = kRootDegree - 2; k >= 0; --k) p = __builtin_fmaf(p, d, a[k]);
-  return fabsf(d) <= kRootWindow ? p * d : direct;
+    for (int k = kPhiDegree - 1; k >= 0; --k) r = __builtin_fmaf(r, s, kPhiPoly[k]);
+  } else {
+    r = kPhiPoly16[kPhiDegree16];
+#pragma unroll
+    for (int k = kPhiDegree16 - 1; k >= 0; --k) r = __builtin_fmaf(r, s, kPhiPoly16[k]);
+  }
+  const float sq = ec * ec;
+  const float g0 = exp_nonpos(-0.5f * sq);
+  if constexpr (FULL) {
+    const float sq_err = __builtin_fmaf(ec, ec, -sq);  // e^2 = sq + sq_err exactly
+    gauss = __builtin_fmaf(-0.5f * sq_err, g0, g0);   // exp(-sq/2) * (1 - sq_err/2)
+  } else {
+    gauss = g0;
+  }
+  const float half_erfc = s * gauss * r;
+  cdf = e < 0.0f ? half_erfc : 1.0f - half_erfc;
 }
 
-template <int KIND>
+// act'(e0 + d) near the root e0 of the derivative: d * sum_k a[k] d^k, where the
+// direct formula cancels. FULL: degree 10 for |d| <= 1/4; otherwise degree 5 for
+// |d| <= 1/8 (outside it the direct formula loses at most a factor 8 to
+// cancellation, far below a 16-bit ulp).
+template <bool FULL, int N16, int N>
+__device__ inline float root_poly(float e, float root_hi, float root_lo, const float (&a16)[N16],
+                                  const float (&a)[N], float direct) {
+  const float d = (e - root_hi) - root_lo;  // e - root_hi is exact inside the window
+  if constexpr (FULL) {
+    float p = a[N - 1];
+#pragma unroll
+    for (int k = N - 2; k >= 0; --k) p = __builtin_fmaf(p, d, a[k]);
+    return fabsf(d) <= kRootWindow ? p * d : direct;
+  } else {
+    float p = a16[N16 - 1];
+#pragma unroll
+    for (int k = N16 - 2; k >= 0; --k) p = __builtin_fmaf(p, d, a16[k]);
+    return fabsf(d) <= kRootWindow16 ? p * d : direct;
+  }
+}
+
+template <int KIND, bool FULL>
 __device__ inline float act_fwd(float e) {
   if constexpr (KIND == GLU_SWIGLU) {
     float s, sc;
     sigmoid_pair(e, s, sc);
     return e * s;
   } else if constexpr (KIND == GLU_GEGLU) {
-    return e * (0.5f * erfcf(-e * kInvSqrt2));
+    float cdf, gauss;
+    normal_cdf_gauss<FULL>(e, cdf, gauss);
+    return e * cdf;
   } else {
     // 2u = e (A + B e^2); |e| > 64 gives the same sigmoid (0 or 1) without overflow
     const float ec = fminf(fmaxf(e, -64.0f), 64.0f);
@@ -91,7 +155,7 @@ __device__ inline float act_fwd(float e) {
 }
 
 // act(e) and act'(e) together (the backward needs both).
-template <int KIND>
+template <int KIND, bool FULL>
 __device__ inline void act_bwd(float e, float& a, float& da) {
   if constexpr (KIND == GLU_SWIGLU) {
     float s, sc;
@@ -99,14 +163,15 @@ __device__ inline void act_bwd(float e, float& a, float& da) {
     a = e * s;
     // s (1 + e (1 - s))
     const float direct = s * __builtin_fmaf(e, sc, 1.0f);
-    da = root_poly(e, kSiluRootHi, kSiluRootLo, kSiluPoly, direct);
+    da = root_poly<FULL>(e, kSiluRootHi, kSiluRootLo, kSiluPoly16, kSiluPoly, direct);
   } else if constexpr (KIND == GLU_GEGLU) {
-    const float cdf = 0.5f * erfcf(-e * kInvSqrt2);
-    const float pdf = expf(-0.5f * e * e) * kInvSqrt2Pi;
+    float cdf, gauss;
+    normal_cdf_gauss<FULL>(e, cdf, gauss);
+    const float pdf = gauss * kInvSqrt2Pi;
     a = e * cdf;
     // Phi + e phi
     const float direct = __builtin_fmaf(e, pdf, cdf);
-    da = root_poly(e, kGeluRootHi, kGeluRootLo, kGeluPoly, direct);
+    da = root_poly<FULL>(e, kGeluRootHi, kGeluRootLo, kGeluPoly16, kGeluPoly, direct);
   } else {
     const float ec = fminf(fmaxf(e, -64.0f), 64.0f);
     const float e2 = ec * ec;
@@ -117,7 +182,8 @@ __device__ inline void act_bwd(float e, float& a, float& da) {
     a = e * s;
     // s (1 + e z' (1 - s))
     const float direct = s * __builtin_fmaf(ec * zp, sc, 1.0f);
-    da = root_poly(e, kGeluTanhRootHi, kGeluTanhRootLo, kGeluTanhPoly, direct);
+    da = root_poly<FULL>(e, kGeluTanhRootHi, kGeluTanhRootLo, kGeluTanhPoly16, kGeluTanhPoly,
+                         direct);
   }
 }
 
@@ -130,6 +196,7 @@ template <typename T, int VEC, int KIND, bool BWD, bool DENSE, typename Index>
 __global__ __launch_bounds__(kBlock) void glu_kernel(const T* dh, const T* e, const T* g, T* out0,
                                                      T* out1, const GluShape s) {
   using C = Chunk<T, VEC>;
+  constexpr bool kFull = sizeof(T) == 4;  // fp32 storage: full-length polynomials
   const Index n = (Index)s.n_chunks;
   const Index step = (Index)gridDim.x * (Index)(kBlock * kUnroll);
   for (Index base = (Index)blockIdx.x * (Index)(kBlock * kUnroll); base < n; base += step) {
@@ -160,7 +227,7 @@ __global__ __launch_bounds__(kBlock) void glu_kernel(const T* dh, const T* e, co
         if constexpr (!BWD) {
           float h[VEC];
 #pragma unroll
-          for (int j = 0; j < VEC; ++j) h[j] = act_fwd<KIND>(to_f32(ce[u].v[j])) * to_f32(cg[u].v[j]);
+          for (int j = 0; j < VEC; ++j) h[j] = act_fwd<KIND, kFull>(to_f32(ce[u].v[j])) * to_f32(cg[u].v[j]);
           C ch;
           narrow(h, ch);
           store_chunk<T, VEC>(out0 + out_off[u], ch);
@@ -169,7 +236,7 @@ __global__ __launch_bounds__(kBlock) void glu_kernel(const T* dh, const T* e, co
 #pragma unroll
           for (int j = 0; j < VEC; ++j) {
             float a, da;
-            act_bwd<KIND>(to_f32(ce[u].v[j]), a, da);
+            act_bwd<KIND, kFull>(to_f32(ce[u].v[j]), a, da);
             const float up = to_f32(cd[u].v[j]);
             de[j] = up * to_f32(cg[u].v[j]) * da;
             dg[j] = up * a;
