@@ -44,14 +44,18 @@ KERNEL_SRC = os.path.join(ROOT, "packed_varlen_rotary_rope_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "rope_qk_qwen3_4b_packed_traffic.txt")
 
 
-# The sources rope_qk_kernel is compiled from: a traffic summary taken on other
+# The sources each kernel is compiled from: a traffic summary taken on other
 # sources does not describe the kernel being timed.
 ROPE_SOURCES = ["rope_qk.hip", "storage.h", "cr_sincos.h", "trig_constants.h"]
+GLU_SOURCES = ["glu.hip", "storage.h", "glu_constants.h"]
+GLU_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "glu_swiglu_qwen3_4b_traffic.txt")
+# bf16, 16-byte chunks, SwiGLU, dense, 32-bit offsets: forward and backward instances
+GLU_KERNEL_KEYS = {"fwd": "glu_kernelIDF16bLi8ELi0ELb0ELb1Ej", "bwd": "glu_kernelIDF16bLi8ELi0ELb1ELb1Ej"}
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources=ROPE_SOURCES) -> str:
     h = hashlib.sha256()
-    for name in ROPE_SOURCES:
+    for name in sources:
         with open(os.path.join(KERNEL_SRC, name), "rb") as fh:
             h.update(name.encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]
@@ -62,19 +66,19 @@ def algorithmic_bytes_per_launch(w: workloads.Workload) -> int:
     return 2 * w.valid_tokens * (w.Hq + w.Hkv) * w.D * w.elem_bytes
 
 
-def read_traffic(bytes_per_launch: int):
-    """HBM bytes per launch from the committed PMC summary, if it matches this source."""
-    if not os.path.exists(TRAFFIC_FILE):
+def read_traffic(path: str = TRAFFIC_FILE, sources=ROPE_SOURCES, field="hbm_bytes_per_launch"):
+    """HBM bytes per launch from a committed PMC summary, if it matches the sources."""
+    if not os.path.exists(path):
         return None
     kv = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         m = re.match(r"^\s*([a-z_0-9]+)\s*[:=]\s*(\S+)", line)
         if m:
             kv[m.group(1)] = m.group(2)
-    if kv.get("kernel_source_sha256_16") != kernel_source_hash():
+    if kv.get("kernel_source_sha256_16") != kernel_source_hash(sources):
         return None
     try:
-        return int(float(kv["hbm_bytes_per_launch"]))
+        return int(float(kv[field]))
     except (KeyError, ValueError):
         return None
 
@@ -139,15 +143,13 @@ def _dispatch_means(csv_path: str) -> dict:
     return {k: (sum(v) / len(v), len(v)) for k, v in acc.items()}
 
 
-def write_traffic_summary(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, command: str):
-    """HBM bytes per launch of the rope kernel from two PMC passes (FETCH_SIZE, then
-    WRITE_SIZE), each scaled by what the same counter reads for a plain 1 GiB device
-    copy (written and read once), as a small text summary that main() reads back."""
-    w = workloads.get("qwen3_4b_packed")
-    bpl = algorithmic_bytes_per_launch(w)
+def _pmc_scaled(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, key):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the kernel whose name contains
+    key, and the same counters for a plain 1 GiB device copy (written and read
+    once), which give the scale from counter units to bytes."""
     copy_bytes = 2 ** 30
 
-    def kernel(means, key):
+    def kernel(means):
         hits = [(k, v) for k, v in means.items() if key in k]
         if not hits:
             raise SystemExit(f"no dispatch of {key} in the counter file")
@@ -156,38 +158,77 @@ def write_traffic_summary(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, 
     def copy_kernel(means):
         return max(means.items(), key=lambda kv: kv[1][0])[1]  # the 1 GiB copy dominates
 
-    f_k, nf = kernel(_dispatch_means(fetch_csv), "rope_qk_kernel")
-    w_k, nw = kernel(_dispatch_means(write_csv), "rope_qk_kernel")
+    f_k, nf = kernel(_dispatch_means(fetch_csv))
+    w_k, nw = kernel(_dispatch_means(write_csv))
     f_c, _ = copy_kernel(_dispatch_means(copy_fetch_csv))
     w_c, _ = copy_kernel(_dispatch_means(copy_write_csv))
     f_scale = copy_bytes / (f_c * 1024.0)
     w_scale = copy_bytes / (w_c * 1024.0)
-    read_b = f_k * 1024.0 * f_scale
-    write_b = w_k * 1024.0 * w_scale
-    lines = [
+    return {"f_k": f_k, "w_k": w_k, "nf": nf, "nw": nw, "f_c": f_c, "w_c": w_c,
+            "f_scale": f_scale, "w_scale": w_scale, "read": f_k * 1024.0 * f_scale,
+            "write": w_k * 1024.0 * w_scale}
+
+
+def _pmc_lines(m, bpl, prefix=""):
+    return [
+        f"{prefix}fetch_kib_per_dispatch: {m['f_k']:.1f}",
+        f"{prefix}write_kib_per_dispatch: {m['w_k']:.1f}",
+        f"{prefix}dispatches_counted: {m['nf']} {m['nw']}",
+        f"{prefix}hbm_read_bytes_per_launch: {m['read']:.0f}",
+        f"{prefix}hbm_write_bytes_per_launch: {m['write']:.0f}",
+        f"{prefix}hbm_bytes_per_launch: {m['read'] + m['write']:.0f}",
+        f"{prefix}algorithmic_bytes_per_launch: {bpl}",
+        f"{prefix}traffic_over_algorithmic: {(m['read'] + m['write']) / bpl:.4f}",
+    ]
+
+
+def _write_summary(path, header, lines):
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w") as fh:
+        fh.write("\n".join(header + lines) + "\n")
+    print("\n".join(header + lines))
+
+
+def write_traffic_summary(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, command: str):
+    """HBM bytes per launch of the rope kernel from two PMC passes (FETCH_SIZE, then
+    WRITE_SIZE), each scaled by what the same counter reads for a plain 1 GiB device
+    copy, as a small text summary that main() reads back."""
+    w = workloads.get("qwen3_4b_packed")
+    m = _pmc_scaled(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, "rope_qk_kernel")
+    header = [
         "# HBM traffic of rope_qk_kernel (bf16, D=128, Hq=32, Hkv=8) on the qwen3_4b_packed",
         "# workload (T=16384), one launch = forward or backward over Q and K.",
         "# Two rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE) over the same bench",
         "# command, each counter scaled by its reading for a plain 1 GiB device copy.",
         f"# commands: {command}",
-        f"fetch_kib_per_dispatch: {f_k:.1f}",
-        f"write_kib_per_dispatch: {w_k:.1f}",
-        f"dispatches_counted: {nf} {nw}",
-        f"copy_fetch_kib_for_1GiB: {f_c:.1f}",
-        f"copy_write_kib_for_1GiB: {w_c:.1f}",
-        f"fetch_scale: {f_scale:.5f}",
-        f"write_scale: {w_scale:.5f}",
-        f"hbm_read_bytes_per_launch: {read_b:.0f}",
-        f"hbm_write_bytes_per_launch: {write_b:.0f}",
-        f"hbm_bytes_per_launch: {read_b + write_b:.0f}",
-        f"algorithmic_bytes_per_launch: {bpl}",
-        f"traffic_over_algorithmic: {(read_b + write_b) / bpl:.4f}",
-        f"kernel_source_sha256_16: {kernel_source_hash()}",
+        f"copy_fetch_kib_for_1GiB: {m['f_c']:.1f}",
+        f"copy_write_kib_for_1GiB: {m['w_c']:.1f}",
+        f"fetch_scale: {m['f_scale']:.5f}",
+        f"write_scale: {m['w_scale']:.5f}",
     ]
-    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
-    with open(TRAFFIC_FILE, "w") as fh:
-        fh.write("\n".join(lines) + "\n")
-    print("\n".join(lines))
+    lines = _pmc_lines(m, algorithmic_bytes_per_launch(w))
+    lines.append(f"kernel_source_sha256_16: {kernel_source_hash(ROPE_SOURCES)}")
+    _write_summary(TRAFFIC_FILE, header, lines)
+
+
+def write_glu_traffic_summary(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, command: str):
+    """The same for the SwiGLU forward and backward kernels on glu_qwen3_4b."""
+    w = workloads.glu_get("glu_qwen3_4b")
+    header = [
+        "# HBM traffic of glu_kernel (SwiGLU, bf16, 16-byte chunks, dense) on the",
+        "# glu_qwen3_4b workload (16384 x 9728): forward reads e, g and writes h;",
+        "# backward reads dh, e, g and writes de, dg.",
+        "# Two rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE) over the same bench",
+        "# command, each counter scaled by its reading for a plain 1 GiB device copy.",
+        f"# commands: {command}",
+    ]
+    lines = []
+    for name, per_elem in (("fwd", 3), ("bwd", 5)):
+        m = _pmc_scaled(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv,
+                        GLU_KERNEL_KEYS[name])
+        lines += _pmc_lines(m, per_elem * w.elements * w.elem_bytes, prefix=f"{name}_")
+    lines.append(f"kernel_source_sha256_16: {kernel_source_hash(GLU_SOURCES)}")
+    _write_summary(GLU_TRAFFIC_FILE, header, lines)
 
 
 def packed_position_ids(w: workloads.Workload) -> np.ndarray:
@@ -400,7 +441,10 @@ def bench_glu(args) -> None:
                    "buffer_sets": nsets},
         "roofline": {
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBPS, "traffic": None, "kernel": "glu_kernel (backward)",
+            "frac": achieved / HBM_PEAK_GBPS,
+            "traffic": (read_traffic(GLU_TRAFFIC_FILE, GLU_SOURCES, "bwd_hbm_bytes_per_launch")
+                        if kind == "swiglu" and w.name == "glu_qwen3_4b" else None),
+            "kernel": "glu_kernel (backward)",
             "bytes_per_launch": bwd_bytes, "avg_launch_us": bwd_us,
         },
         "forward": {"bytes_per_launch": fwd_bytes, "avg_launch_us": fwd_us,
@@ -453,10 +497,13 @@ def main():
                     metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                     help="write the PMC traffic summary from rocprofv3 counter CSVs, then exit")
     ap.add_argument("--traffic-command", default="", help="commands recorded in that summary")
+    ap.add_argument("--traffic-kernel", default="rope", choices=["rope", "glu"],
+                    help="which kernel's summary --traffic-summary writes")
     args = ap.parse_args()
 
     if args.traffic_summary:
-        write_traffic_summary(*args.traffic_summary, command=args.traffic_command)
+        writer = write_glu_traffic_summary if args.traffic_kernel == "glu" else write_traffic_summary
+        writer(*args.traffic_summary, command=args.traffic_command)
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -565,7 +612,7 @@ def main():
     tokens_per_step = w.valid_tokens
     value = tokens_per_step * args.steps / elapsed
     ms_per_step = elapsed / args.steps * 1e3
-    traffic = read_traffic(bpl)
+    traffic = read_traffic() if w.name == "qwen3_4b_packed" else None
 
     out = {
         "metric": METRIC,
