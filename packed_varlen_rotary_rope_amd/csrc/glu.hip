@@ -190,9 +190,9 @@ __device__ inline void act_bwd(float e, float& a, float& da) {
 // ---- the kernel ------------------------------------------------------------------------
 
 // [U-int64]: Index is uint32_t when every offset of the launch is below 2^31 (the
-// host checks), int64_t otherwise.
+// host checks), int64_t otherwise. No __restrict__: an output may be the memory
+// of one of the inputs (in place).
 template <typename T, int VEC, int KIND, bool BWD, bool DENSE, typename Index>
-// No __restrict__: an output may be the memory of one of the inputs (in place).
 __global__ __launch_bounds__(kBlock) void glu_kernel(const T* dh, const T* e, const T* g, T* out0,
                                                      T* out1, const GluShape s) {
   using C = Chunk<T, VEC>;

@@ -1,0 +1,179 @@
+"""GPU tests of the autograd entry points (packed_varlen_rotary_rope_amd.functional)
+and of HIP-graph capture and replay of the kernels.
+
+Autograd: gradients through rope_qk / glu / glu_fused equal, bit for bit, the
+direct backward launches on the same upstream gradients, and agree with the
+oracle. Graphs: a captured forward+backward, replayed several times with eager
+work and synchronizations in between, gives every time the bits of the eager
+launches on the same inputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from oracle import glu as glu_oracle
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import packed_varlen_rotary_rope_amd as m
+    import packed_varlen_rotary_rope_amd.functional as F
+    return m, F
+
+
+def bits16(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("inplace_backward", [False, True])
+def test_rope_autograd_matches_direct_launches(lib, inplace_backward):
+    """loss = <rope(q), wq> + <rope(k), wk>: dL/dq is the backward rotation of wq,
+    so q's gradient must equal qk_bwd_ applied to wq (bit for bit), and the oracle's
+    backward of wq (1 bf16 ulp)."""
+    rope, F = lib
+    w = workloads.get("qwen3_8b_packed")
+    print(f"[autograd] rope_qk inplace_backward={inplace_backward}", flush=True)
+    q0 = workloads.make_tensor(w.shape("q"), 31, "bf16", device=DEV).requires_grad_()
+    k0 = workloads.make_tensor(w.shape("k"), 32, "bf16", device=DEV).requires_grad_()
+    wq = workloads.make_tensor(w.shape("q"), 33, "bf16", device=DEV)
+    wk = workloads.make_tensor(w.shape("k"), 34, "bf16", device=DEV)
+    cu = torch.from_numpy(w.cu_seqlens).to(DEV)
+    q, k = q0 * 1, k0 * 1  # non-leaf inputs, as projection outputs are
+    qr, kr = F.rope_qk(q, k, cu, w.theta, inplace_backward=inplace_backward)
+    ((qr.float() * wq.float()).sum() + (kr.float() * wk.float()).sum()).backward()
+    # forward result equals the direct launch
+    qd, kd = q0.detach().clone(), k0.detach().clone()
+    rope.qk_fwd_(qd, kd, cu, w.theta)
+    gq, gk = wq.clone(), wk.clone()
+    rope.qk_bwd_(gq, gk, cu, w.theta)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits16(qr), bits16(qd)) and np.array_equal(bits16(kr), bits16(kd))
+    assert np.array_equal(bits16(q0.grad), bits16(gq))
+    assert np.array_equal(bits16(k0.grad), bits16(gk))
+    ref = oracle.rope(bits16(wq), w.cu_seqlens, w.theta, -1, "bf16", nthreads=8)
+    got = bits16(q0.grad).astype(np.int64)
+    want = oracle.round_bf16(ref).astype(np.int64)
+
+    def ordered(b):
+        return np.where(b & 0x8000, -(b & 0x7FFF), b)
+
+    assert int(np.abs(ordered(got) - ordered(want)).max()) <= 1
+
+
+def test_rope_autograd_shared_gradient_is_not_clobbered(lib):
+    """out = rope(q) + x: autograd hands the same gradient tensor to both operands;
+    the default backward must leave x's gradient unrotated."""
+    rope, F = lib
+    T, H, D = 64, 2, 32
+    cu = torch.tensor([0, 40, 64], dtype=torch.int32, device=DEV)
+    q0 = torch.randn(T, H, D, device=DEV, requires_grad=True)
+    x = torch.randn(T, H, D, device=DEV, requires_grad=True)
+    k = torch.zeros(T, 0, D, device=DEV)
+    qr, _ = F.rope_qk(q0 * 1, k, cu, 1e4)
+    upstream = torch.randn(T, H, D, device=DEV)
+    (qr + x).backward(upstream)
+    torch.cuda.synchronize()
+    assert torch.equal(x.grad, upstream)
+    expect = upstream.clone()
+    rope.qk_bwd_(expect, torch.zeros(T, 0, D, device=DEV), cu, 1e4)
+    assert torch.equal(q0.grad, expect)
+
+
+@pytest.mark.parametrize("kind", ["swiglu", "geglu", "geglu_tanh"])
+def test_glu_autograd(lib, kind):
+    """glu and glu_fused: forward and gradients equal the direct launches bit for
+    bit, and the fused gradient is one buffer whose halves are de and dg."""
+    rope, F = lib
+    rows, cols = 513, 1024
+    print(f"[autograd] glu {kind}", flush=True)
+    gu = workloads.make_tensor((rows, 2 * cols), 41, "bf16", device=DEV).requires_grad_()
+    e0 = workloads.make_tensor((rows, cols), 42, "bf16", device=DEV).requires_grad_()
+    g0 = workloads.make_tensor((rows, cols), 43, "bf16", device=DEV).requires_grad_()
+    dh = workloads.make_tensor((rows, cols), 44, "bf16", device=DEV)
+    h = F.glu(kind, e0, g0)
+    h.backward(dh)
+    hf = F.glu_fused(kind, gu)
+    hf.backward(dh)
+    h_ref = rope.glu_fwd(kind, e0.detach(), g0.detach())
+    de_ref, dg_ref = rope.glu_bwd(kind, dh, e0.detach(), g0.detach())
+    e1, g1 = gu.detach()[:, :cols], gu.detach()[:, cols:]
+    hf_ref = rope.glu_fwd(kind, e1, g1)
+    def1, dgf1 = rope.glu_bwd(kind, dh, e1, g1)
+    torch.cuda.synchronize()
+    for a, b in ((h, h_ref), (e0.grad, de_ref), (g0.grad, dg_ref), (hf, hf_ref),
+                 (gu.grad[:, :cols], def1), (gu.grad[:, cols:], dgf1)):
+        assert np.array_equal(bits16(a), bits16(b))
+    # and the oracle agrees with the autograd gradient of e (1 bf16 ulp)
+    ref_de, _ = glu_oracle.bwd(kind, bits16(dh), bits16(e0), bits16(g0), "bf16", 8)
+    want = glu_oracle.round_to("bf16", ref_de).astype(np.int64)
+    got = bits16(e0.grad).astype(np.int64)
+
+    def ordered(b):
+        return np.where(b & 0x8000, -(b & 0x7FFF), b)
+
+    assert int(np.abs(ordered(got) - ordered(want)).max()) <= 1
+
+
+def test_graph_capture_replay(lib):
+    """RoPE forward + backward and SwiGLU forward + backward captured in one HIP
+    graph on static buffers; four replays, each after fresh inputs are copied in
+    and with eager launches and synchronizations between replays, each equal bit
+    for bit to eager launches on the same inputs."""
+    rope, F = lib
+    w = workloads.get("qwen3_4b_packed")
+    cu = torch.from_numpy(w.cu_seqlens).to(DEV)
+    rows, cols = 2048, 4096
+    static = {n: torch.empty(w.shape(n), dtype=torch.bfloat16, device=DEV)
+              for n in ("q", "k", "dq", "dk")}
+    ge, gg, gdh = (torch.empty((rows, cols), dtype=torch.bfloat16, device=DEV) for _ in range(3))
+    gh = torch.empty_like(ge)
+    gde, gdg = torch.empty_like(ge), torch.empty_like(ge)
+
+    def body():
+        rope.qk_fwd_(static["q"], static["k"], cu, w.theta)
+        rope.qk_bwd_(static["dq"], static["dk"], cu, w.theta)
+        rope.glu_fwd("swiglu", ge, gg, out=gh)
+        rope.glu_bwd("swiglu", gdh, ge, gg, de=gde, dg=gdg)
+
+    # warm up on a side stream, as torch requires before capture
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        body()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        body()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        print(f"[graph] replay {rep}", flush=True)
+        inputs = {n: workloads.make_tensor(w.shape(n), 500 + 10 * rep + i, "bf16", device=DEV)
+                  for i, n in enumerate(("q", "k", "dq", "dk"))}
+        ins = [workloads.make_tensor((rows, cols), 600 + 10 * rep + i, "bf16", device=DEV)
+               for i in range(3)]
+        for n in static:
+            static[n].copy_(inputs[n])
+        for dst, src in zip((ge, gg, gdh), ins):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        graph.replay()
+        # eager reference on separate copies, with its own synchronizations
+        eager = {n: t.clone() for n, t in inputs.items()}
+        rope.qk_fwd_(eager["q"], eager["k"], cu, w.theta)
+        rope.qk_bwd_(eager["dq"], eager["dk"], cu, w.theta)
+        h = rope.glu_fwd("swiglu", ins[0], ins[1])
+        de, dg = rope.glu_bwd("swiglu", ins[2], ins[0], ins[1])
+        torch.cuda.synchronize()
+        for n in static:
+            assert np.array_equal(bits16(static[n]), bits16(eager[n])), (rep, n)
+        for a, b in ((gh, h), (gde, de), (gdg, dg)):
+            assert np.array_equal(bits16(a), bits16(b)), rep
