@@ -399,15 +399,16 @@ def bench_glu(args) -> None:
         sets.append(st)
     stream = torch.cuda.current_stream(dev).cuda_stream
     kind = args.glu
+    index_mode = {"auto": rope.INDEX_AUTO, "64": rope.INDEX_64}[args.index]
 
     def step(s, ev=None):
         if ev is not None:
             ev[0].record(stream)
-        rope.glu_fwd(kind, s["e"], s["g"], out=s["h"])
+        rope.glu_fwd(kind, s["e"], s["g"], out=s["h"], index_mode=index_mode)
         if ev is not None:
             ev[1].record(stream)
             ev[2].record(stream)
-        rope.glu_bwd(kind, s["dh"], s["e"], s["g"], de=s["de"], dg=s["dg"])
+        rope.glu_bwd(kind, s["dh"], s["e"], s["g"], de=s["de"], dg=s["dg"], index_mode=index_mode)
         if ev is not None:
             ev[3].record(stream)
 
@@ -438,7 +439,7 @@ def bench_glu(args) -> None:
         "dtype": w.dtype,
         "data": "synthetic (seeded N(0,1) e, g, dh)",
         "config": {"workload": w.name, "rows": w.rows, "cols": w.cols, "kind": kind,
-                   "buffer_sets": nsets},
+                   "buffer_sets": nsets, "index": args.index},
         "roofline": {
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
@@ -485,6 +486,8 @@ def main():
                     help="linear position interpolation factor (>= 1)")
     ap.add_argument("--layout", default="contiguous", choices=["contiguous", "qkv"],
                     help="qkv: Q/K (and dQ/dK) are strided views into fused QKV buffers")
+    ap.add_argument("--index", default="auto", choices=["auto", "64"],
+                    help="64: force the 64-bit offset specialization (auto: 64-bit only when needed)")
     ap.add_argument("--glu", default=None, choices=["swiglu", "geglu", "geglu_tanh"],
                     help="time the SwiGLU/GeGLU kernels instead (workload: a glu_* name)")
     ap.add_argument("--compare", action="store_true",
@@ -564,18 +567,22 @@ def main():
             off_r = (starts - cu_np[:-1])[keep].astype(np.int32)
             shards.append((a, b, torch.from_numpy(cu_r).to(dev), torch.from_numpy(off_r).to(dev)))
 
+    index_mode = {"auto": rope.INDEX_AUTO, "64": rope.INDEX_64}[args.index]
+
     def launch(qt, kt, direction):
         if shards is not None:
             for a, b, cu_r, off_r in shards:
                 rope.qk_apply_ex_(qt[a:b], kt[a:b], w.theta, direction, cu_seqlens=cu_r,
                                   seq_offsets=off_r, pos_scale=args.pos_scale,
-                                  tokens_per_wave=tpw)
+                                  tokens_per_wave=tpw, index_mode=index_mode)
         elif pid is not None or args.pos_scale != 1.0 or args.layout == "qkv":
             rope.qk_apply_ex_(qt, kt, w.theta, direction, cu_seqlens=None if pid is not None else cu,
                               seqused=None if pid is not None else su, position_ids=pid,
-                              pos_scale=args.pos_scale, tokens_per_wave=tpw)
+                              pos_scale=args.pos_scale, tokens_per_wave=tpw,
+                              index_mode=index_mode)
         else:
-            rope.qk_apply_(qt, kt, cu, w.theta, direction, seqused=su, tokens_per_wave=tpw)
+            rope.qk_apply_(qt, kt, cu, w.theta, direction, seqused=su, tokens_per_wave=tpw,
+                           index_mode=index_mode)
 
     def step(s, ev=None):
         if ev is not None:
@@ -633,7 +640,7 @@ def main():
             "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D, "theta": w.theta,
             "buffer_sets": nsets, "tokens_per_wave": tpw or "auto",
             "positions": args.positions, "pos_scale": args.pos_scale,
-            "layout": args.layout,
+            "layout": args.layout, "index": args.index,
         },
         "step_hbm_GBps": 2 * bpl * args.steps / elapsed / 1e9,
         "roofline": {

@@ -189,66 +189,82 @@ __device__ inline void act_bwd(float e, float& a, float& da) {
 
 // ---- the kernel ------------------------------------------------------------------------
 
+// One step of a lane: chunks base + u*kBlock + lane, u < kUnroll. CHECKED = false
+// when the whole step is in range (every step but the last): then the loads of all
+// kUnroll chunks are unconditional and go out back to back, before any math; a
+// per-chunk bounds branch would make the compiler wait for each chunk's loads
+// before issuing the next chunk's.
+template <typename T, int VEC, int KIND, bool BWD, bool DENSE, bool CHECKED, typename Index>
+__device__ __attribute__((always_inline)) inline void glu_step(const T* dh, const T* e, const T* g,
+                                                               T* out0, T* out1, const GluShape& s,
+                                                               Index base, Index n) {
+  using C = Chunk<T, VEC>;
+  constexpr bool kFull = sizeof(T) == 4;  // fp32 storage: full-length polynomials
+  C ce[kUnroll], cg[kUnroll], cd[kUnroll];
+  Index in_off[kUnroll], out_off[kUnroll];
+  bool live[kUnroll];
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const Index c = base + (Index)(u * kBlock) + (Index)threadIdx.x;
+    live[u] = !CHECKED || c < n;
+    const Index cc = live[u] ? c : (Index)0;  // chunk 0 always exists: a safe dummy
+    if constexpr (DENSE) {
+      in_off[u] = cc * VEC;
+      out_off[u] = cc * VEC;
+    } else {
+      const Index row = cc / (Index)s.chunks_per_row;
+      const Index col = (cc - row * (Index)s.chunks_per_row) * VEC;
+      in_off[u] = row * (Index)s.in_stride + col;
+      out_off[u] = row * (Index)s.out_stride + col;
+    }
+    ce[u] = load_chunk<T, VEC>(e + in_off[u]);
+    cg[u] = load_chunk<T, VEC>(g + in_off[u]);
+    if constexpr (BWD) cd[u] = load_chunk<T, VEC>(dh + out_off[u]);
+  }
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    if constexpr (!BWD) {
+      float h[VEC];
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) h[j] = act_fwd<KIND, kFull>(to_f32(ce[u].v[j])) * to_f32(cg[u].v[j]);
+      C ch;
+      narrow(h, ch);
+      if (live[u]) store_chunk<T, VEC>(out0 + out_off[u], ch);
+    } else {
+      float de[VEC], dg[VEC];
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) {
+        float a, da;
+        act_bwd<KIND, kFull>(to_f32(ce[u].v[j]), a, da);
+        const float up = to_f32(cd[u].v[j]);
+        de[j] = up * to_f32(cg[u].v[j]) * da;
+        dg[j] = up * a;
+      }
+      C cde, cdg;
+      narrow(de, cde);
+      narrow(dg, cdg);
+      if (live[u]) {
+        store_chunk<T, VEC>(out0 + in_off[u], cde);
+        store_chunk<T, VEC>(out1 + in_off[u], cdg);
+      }
+    }
+  }
+}
+
 // [U-int64]: Index is uint32_t when every offset of the launch is below 2^31 (the
 // host checks), int64_t otherwise. No __restrict__: an output may be the memory
 // of one of the inputs (in place).
 template <typename T, int VEC, int KIND, bool BWD, bool DENSE, typename Index>
 __global__ __launch_bounds__(kBlock) void glu_kernel(const T* dh, const T* e, const T* g, T* out0,
                                                      T* out1, const GluShape s) {
-  using C = Chunk<T, VEC>;
-  constexpr bool kFull = sizeof(T) == 4;  // fp32 storage: full-length polynomials
   const Index n = (Index)s.n_chunks;
-  const Index step = (Index)gridDim.x * (Index)(kBlock * kUnroll);
-  for (Index base = (Index)blockIdx.x * (Index)(kBlock * kUnroll); base < n; base += step) {
-    C ce[kUnroll], cg[kUnroll], cd[kUnroll];
-    Index in_off[kUnroll], out_off[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const Index c = base + (Index)(u * kBlock) + (Index)threadIdx.x;
-      if (c < n) {
-        if constexpr (DENSE) {
-          in_off[u] = c * VEC;
-          out_off[u] = c * VEC;
-        } else {
-          const Index row = c / (Index)s.chunks_per_row;
-          const Index col = (c - row * (Index)s.chunks_per_row) * VEC;
-          in_off[u] = row * (Index)s.in_stride + col;
-          out_off[u] = row * (Index)s.out_stride + col;
-        }
-        ce[u] = load_chunk<T, VEC>(e + in_off[u]);
-        cg[u] = load_chunk<T, VEC>(g + in_off[u]);
-        if constexpr (BWD) cd[u] = load_chunk<T, VEC>(dh + out_off[u]);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const Index c = base + (Index)(u * kBlock) + (Index)threadIdx.x;
-      if (c < n) {
-        if constexpr (!BWD) {
-          float h[VEC];
-#pragma unroll
-          for (int j = 0; j < VEC; ++j) h[j] = act_fwd<KIND, kFull>(to_f32(ce[u].v[j])) * to_f32(cg[u].v[j]);
-          C ch;
-          narrow(h, ch);
-          store_chunk<T, VEC>(out0 + out_off[u], ch);
-        } else {
-          float de[VEC], dg[VEC];
-#pragma unroll
-          for (int j = 0; j < VEC; ++j) {
-            float a, da;
-            act_bwd<KIND, kFull>(to_f32(ce[u].v[j]), a, da);
-            const float up = to_f32(cd[u].v[j]);
-            de[j] = up * to_f32(cg[u].v[j]) * da;
-            dg[j] = up * a;
-          }
-          C cde, cdg;
-          narrow(de, cde);
-          narrow(dg, cdg);
-          store_chunk<T, VEC>(out0 + in_off[u], cde);
-          store_chunk<T, VEC>(out1 + in_off[u], cdg);
-        }
-      }
-    }
+  const Index per_step = (Index)(kBlock * kUnroll);
+  const Index step = (Index)gridDim.x * per_step;
+  for (Index base = (Index)blockIdx.x * per_step; base < n; base += step) {
+    if (n - base >= per_step)  // wave-uniform: the whole step is in range
+      glu_step<T, VEC, KIND, BWD, DENSE, false>(dh, e, g, out0, out1, s, base, n);
+    else
+      glu_step<T, VEC, KIND, BWD, DENSE, true>(dh, e, g, out0, out1, s, base, n);
   }
 }
 
