@@ -378,6 +378,44 @@ def compare_unfused(rope, w, cu, su, sets, nsets, args, stream):
 GLU_METRIC = "SwiGLU/GeGLU fwd+bwd tokens/s and achieved HBM GB/s (% of peak)"
 
 
+def compare_glu_unfused(rope, w, kind, sets, nsets, args) -> None:
+    """The library's fused GLU kernels against the same math as PyTorch eager ops
+    (activation, product, and autograd for the backward), on the same buffers:
+    wall time per forward and per backward. Context only: the unfused form moves
+    intermediates through HBM."""
+    act = {"swiglu": torch.nn.functional.silu,
+           "geglu": lambda x: torch.nn.functional.gelu(x, approximate="none"),
+           "geglu_tanh": lambda x: torch.nn.functional.gelu(x, approximate="tanh")}[kind]
+
+    def timed(fn):
+        for i in range(args.warmup):
+            fn(sets[i % nsets])
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            fn(sets[i % nsets])
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / args.steps * 1e6
+
+    def torch_bwd(s):
+        e = s["e"].detach().requires_grad_()
+        g = s["g"].detach().requires_grad_()
+        h = act(e) * g
+        torch.autograd.grad(h, (e, g), s["dh"])
+
+    res = {
+        "fused_fwd_us": timed(lambda s: rope.glu_fwd(kind, s["e"], s["g"], out=s["h"])),
+        "fused_bwd_us": timed(lambda s: rope.glu_bwd(kind, s["dh"], s["e"], s["g"], de=s["de"],
+                                                     dg=s["dg"])),
+        "torch_fwd_us": timed(lambda s: act(s["e"]) * s["g"]),
+        "torch_fwd_bwd_us": timed(torch_bwd),
+    }
+    res["speedup_fwd"] = res["torch_fwd_us"] / res["fused_fwd_us"]
+    res["speedup_fwd_bwd"] = res["torch_fwd_bwd_us"] / (res["fused_fwd_us"] + res["fused_bwd_us"])
+    print(json.dumps({"compare": f"glu {kind} fused vs torch eager", "workload": w.name,
+                      "dtype": w.dtype, **res}))
+
+
 def bench_glu(args) -> None:
     """One step = glu_fwd (e, g -> h) + glu_bwd (dh, e, g -> de, dg), out of place,
     on [tokens, intermediate] tensors resident in HBM; buffer sets rotate so no
@@ -412,6 +450,8 @@ def bench_glu(args) -> None:
         if ev is not None:
             ev[3].record(stream)
 
+    if args.compare:
+        return compare_glu_unfused(rope, w, kind, sets, nsets, args)
     for i in range(args.warmup):
         step(sets[i % nsets])
     events = {i: [HipEvent() for _ in range(4)] for i in range(0, args.steps, EVENT_EVERY)}
@@ -491,7 +531,7 @@ def main():
     ap.add_argument("--glu", default=None, choices=["swiglu", "geglu", "geglu_tanh"],
                     help="time the SwiGLU/GeGLU kernels instead (workload: a glu_* name)")
     ap.add_argument("--compare", action="store_true",
-                    help="time fused in-place QK-RoPE against unfused variants, then exit")
+                    help="time the fused kernels against unfused variants, then exit")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="timed oracle work for cpu_baseline (0 disables it)")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",

@@ -1,16 +1,19 @@
-"""Fused, in-place, packed variable-length QK rotary position embedding (RoPE)
-for AMD Instinct MI355X (gfx950).
+"""Fused, in-place, packed variable-length QK rotary position embedding (RoPE),
+and the SwiGLU / GeGLU MLP activations, for AMD Instinct MI355X (gfx950).
 
-Thin Python binding over the C ABI of ``include/rope_qk.h`` (librope_qk.so,
-built from ``csrc/rope_qk.hip``). This module only checks tensor metadata and
-marshals pointers, sizes and the current HIP stream; every step of the
-computation runs in the library's HIP kernels. There is no CPU fallback: if
-the library is missing, importing this package raises.
+Thin Python binding over the C ABI of ``include/rope_qk.h`` and ``include/glu.h``
+(librope_qk.so, built from ``csrc/rope_qk.hip`` and ``csrc/glu.hip``). This module
+only checks tensor metadata and marshals pointers, sizes and the current HIP
+stream; every step of the computation runs in the library's HIP kernels. There is
+no CPU fallback: if the library is missing, importing this package raises.
+Differentiable wrappers live in ``packed_varlen_rotary_rope_amd.functional``.
 
-The operation follows the Unsloth page "Entrainement des LLM 3 fois plus rapide
+The operations follow the Unsloth page "Entrainement des LLM 3 fois plus rapide
 avec les noyaux Unsloth + le packing" (section "Kernel Triton QK RoPE fusionne
 avec packing": one in-place kernel for Q and K, rotate_half form, backward =
-sin negated; section "Packing non contamine": positions restart per sample).
+sin negated; section "Packing non contamine": positions restart per sample;
+section "Indexage int64 pour les kernels Triton": SwiGLU / GeGLU kernels with a
+64-bit offset specialization).
 """
 from __future__ import annotations
 
@@ -125,21 +128,15 @@ def _token_stride(x, name: str) -> int:
 
 
 def _qk_args(q, k, cu_seqlens, seqused):
-    if q.device.type != "cuda" or k.device != q.device:
-        raise TypeError("q and k must be on the same GPU")
-    if q.dtype != k.dtype or q.dtype not in _DTYPE_CODE:
-        raise TypeError("q and k must share one dtype: float32, bfloat16 or float16")
-    if q.dim() != 3 or k.dim() != 3 or q.shape[0] != k.shape[0] or q.shape[2] != k.shape[2]:
-        raise ValueError("expected q[T, Hq, D] and k[T, Hkv, D]")
-    if not (q.is_contiguous() and k.is_contiguous()):
-        raise ValueError("q and k must be contiguous (rotation is in place)")
+    T, Hq, Hkv, D = _qk_tensors(q, k)
+    if cu_seqlens is None:
+        raise ValueError("cu_seqlens is required")
     cu = _index_tensor(cu_seqlens, "cu_seqlens", q.device)
     su = _index_tensor(seqused, "seqused", q.device)
     num_seqs = cu.numel() - 1
     if su is not None and su.numel() != num_seqs:
         raise ValueError("seqused must have one entry per sequence")
-    T, Hq, D = q.shape
-    return T, Hq, k.shape[1], D, cu, num_seqs, su
+    return T, Hq, Hkv, D, cu, num_seqs, su
 
 
 def qk_apply_(q, k, cu_seqlens, theta: float, direction: int = 1, seqused=None,
