@@ -272,7 +272,7 @@ def cpu_baseline(w, budget_s: float, nthreads: int):
     host = {what: workloads.host_bits(workloads.make_tensor(w.shape(what), w.seed(what), w.dtype))
             for what in ("q", "k", "dq", "dk")}
     total, reps = 0.0, 0
-    while total < budget_s and reps < 100:
+    while total < budget_s and reps < 10000:
         total += oracle.fwd_bwd_seconds(host["q"], host["k"], host["dq"], host["dk"],
                                         w.cu_seqlens, w.theta, w.dtype, w.seqused, nthreads)
         reps += 1
@@ -499,7 +499,7 @@ def bench_glu(args) -> None:
                 for k in ("e", "g", "dh")}
         nthreads = max(1, min(16, len(os.sched_getaffinity(0))))
         total, reps = 0.0, 0
-        while total < args.cpu_seconds and reps < 1000:
+        while total < args.cpu_seconds and reps < 100000:
             total += glu_oracle.seconds(kind, host["e"], host["g"], host["dh"], w.dtype, nthreads)
             reps += 1
         out["cpu_baseline"] = {
