@@ -264,18 +264,39 @@ def make_sets(w, nsets, dev, layout="contiguous"):
     return cu, su, sets
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _timed_reps(fn, budget_s: float, cap: int):
+    total, reps = 0.0, 0
+    while total < budget_s and reps < cap:
+        total += fn()
+        reps += 1
+    return reps, total
+
+
 def cpu_baseline(w, budget_s: float, nthreads: int):
     """The oracle, as it stands, on the same workload: whole fwd+bwd passes over the
-    batch, repeated until about budget_s seconds of work have been timed."""
+    batch, repeated until about budget_s seconds of work have been timed on
+    nthreads host threads, then a quarter of that on one thread."""
     import oracle
 
     host = {what: workloads.host_bits(workloads.make_tensor(w.shape(what), w.seed(what), w.dtype))
             for what in ("q", "k", "dq", "dk")}
-    total, reps = 0.0, 0
-    while total < budget_s and reps < 10000:
-        total += oracle.fwd_bwd_seconds(host["q"], host["k"], host["dq"], host["dk"],
-                                        w.cu_seqlens, w.theta, w.dtype, w.seqused, nthreads)
-        reps += 1
+
+    def one(threads):
+        return lambda: oracle.fwd_bwd_seconds(host["q"], host["k"], host["dq"], host["dk"],
+                                              w.cu_seqlens, w.theta, w.dtype, w.seqused, threads)
+
+    reps, total = _timed_reps(one(nthreads), budget_s, 10000)
+    reps1, total1 = _timed_reps(one(1), budget_s / 4, 10000)
     return {
         "value": w.valid_tokens * reps / total,
         "unit": "tokens/s",
@@ -283,6 +304,8 @@ def cpu_baseline(w, budget_s: float, nthreads: int):
         "kind": "oracle",
         "sample": f"{reps} full fwd+bwd passes over the {w.name} batch "
                   f"({w.valid_tokens} tokens, Q/K/dQ/dK), {total:.1f} s timed",
+        "value_1_core": w.valid_tokens * reps1 / total1,
+        "cpu_model": cpu_model(),
     }
 
 
@@ -461,8 +484,9 @@ def bench_glu(args) -> None:
         step(sets[i % nsets], events.get(i))
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    fwd_us = float(np.mean([ev[0].elapsed_ms(ev[1]) for ev in events.values()])) * 1e3
-    bwd_us = float(np.mean([ev[2].elapsed_ms(ev[3]) for ev in events.values()])) * 1e3
+    fwd_all = [ev[0].elapsed_ms(ev[1]) * 1e3 for ev in events.values()]
+    bwd_all = [ev[2].elapsed_ms(ev[3]) * 1e3 for ev in events.values()]
+    fwd_us, bwd_us = float(np.mean(fwd_all)), float(np.mean(bwd_all))
     fwd_bytes, bwd_bytes = 3 * n * w.elem_bytes, 5 * n * w.elem_bytes
     achieved = bwd_bytes / (bwd_us * 1e-6) / 1e9
     out = {
@@ -487,8 +511,11 @@ def bench_glu(args) -> None:
                         if kind == "swiglu" and w.name == "glu_qwen3_4b" else None),
             "kernel": "glu_kernel (backward)",
             "bytes_per_launch": bwd_bytes, "avg_launch_us": bwd_us,
+            "min_launch_us": float(np.min(bwd_all)), "median_launch_us": float(np.median(bwd_all)),
         },
         "forward": {"bytes_per_launch": fwd_bytes, "avg_launch_us": fwd_us,
+                    "min_launch_us": float(np.min(fwd_all)),
+                    "median_launch_us": float(np.median(fwd_all)),
                     "achieved_GBps": fwd_bytes / (fwd_us * 1e-6) / 1e9},
     }
     if args.cpu_seconds > 0:
@@ -498,14 +525,18 @@ def bench_glu(args) -> None:
         host = {k: workloads.host_bits(workloads.make_tensor((rows, w.cols), w.seed(k), w.dtype))
                 for k in ("e", "g", "dh")}
         nthreads = max(1, min(16, len(os.sched_getaffinity(0))))
-        total, reps = 0.0, 0
-        while total < args.cpu_seconds and reps < 100000:
-            total += glu_oracle.seconds(kind, host["e"], host["g"], host["dh"], w.dtype, nthreads)
-            reps += 1
+
+        def one(threads):
+            return lambda: glu_oracle.seconds(kind, host["e"], host["g"], host["dh"], w.dtype,
+                                              threads)
+
+        reps, total = _timed_reps(one(nthreads), args.cpu_seconds, 100000)
+        reps1, total1 = _timed_reps(one(1), args.cpu_seconds / 4, 100000)
         out["cpu_baseline"] = {
             "value": rows * reps / total, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
             "sample": f"{reps} fwd+bwd passes over {rows} of the {w.rows} rows "
                       f"({w.cols} columns), {total:.1f} s timed",
+            "value_1_core": rows * reps1 / total1, "cpu_model": cpu_model(),
         }
     print(json.dumps(out))
 
@@ -694,6 +725,7 @@ def main():
             "bytes_per_launch": bpl,
             "avg_launch_us": avg_launch_s * 1e6,
             "min_launch_us": float(np.min(launch_ms)) * 1e3,
+            "median_launch_us": float(np.median(launch_ms)) * 1e3,
         },
     }
     if args.cpu_seconds > 0:
