@@ -104,7 +104,7 @@ def check_all(rope, kind, dtype, e, g, dh, what):
 # ---------------------------------------------------------------- whole workloads
 
 @pytest.mark.parametrize("kind", KINDS)
-@pytest.mark.parametrize("name", ["glu_tiny", "glu_qwen3_8b"])
+@pytest.mark.parametrize("name", ["glu_tiny", "glu_qwen3_8b", "glu_qwen3_4b"])
 def test_glu_workload_parity(rope, name, kind):
     w = workloads.glu_get(name)
     print(f"[glu parity] {name} {kind}", flush=True)
