@@ -271,3 +271,17 @@ def test_glu_validation(bwd, kw, expect):
 def test_glu_bwd_needs_its_extra_pointers():
     assert glu(True, dh=None) == EINVAL
     assert glu(True, out1=None) == EINVAL
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    """Without the built library the package refuses to import: there is no CPU
+    fallback. A copy of the package without its .so is imported in a subprocess."""
+    import shutil
+    pkg = os.path.join(ROOT, "packed_varlen_rotary_rope_amd")
+    dst = tmp_path / "packed_varlen_rotary_rope_amd"
+    shutil.copytree(pkg, dst, ignore=shutil.ignore_patterns("*.so", "__pycache__", "csrc"))
+    assert not any(p.suffix == ".so" for p in dst.iterdir())
+    r = subprocess.run([sys.executable, "-c", "import packed_varlen_rotary_rope_amd"],
+                       cwd=tmp_path, capture_output=True, text=True)
+    assert r.returncode != 0
+    assert "ImportError" in r.stderr and "no fallback" in r.stderr.lower()
