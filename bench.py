@@ -61,6 +61,15 @@ def kernel_source_hash(sources=ROPE_SOURCES) -> str:
     return h.hexdigest()[:16]
 
 
+def rope_kernel_name(w: workloads.Workload, tokens_per_wave: int) -> str:
+    """The kernel the library picks for this call: row groups by default, one wave
+    per token when the caller sets tokens per wave or passes seqused (padded)."""
+    nc = max(1, (w.D // 2) // (16 // w.elem_bytes))
+    if tokens_per_wave == 0 and w.seqused is None and 64 % nc == 0:
+        return "rope_qk_group_kernel"
+    return "rope_qk_kernel"
+
+
 def algorithmic_bytes_per_launch(w: workloads.Workload) -> int:
     """One read and one write of every rotated element of Q and K (or dQ and dK)."""
     return 2 * w.valid_tokens * (w.Hq + w.Hkv) * w.D * w.elem_bytes
@@ -194,10 +203,10 @@ def write_traffic_summary(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, 
     WRITE_SIZE), each scaled by what the same counter reads for a plain 1 GiB device
     copy, as a small text summary that main() reads back."""
     w = workloads.get("qwen3_4b_packed")
-    m = _pmc_scaled(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, "rope_qk_kernel")
+    m = _pmc_scaled(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, "rope_qk_group_kernel")
     header = [
-        "# HBM traffic of rope_qk_kernel (bf16, D=128, Hq=32, Hkv=8) on the qwen3_4b_packed",
-        "# workload (T=16384), one launch = forward or backward over Q and K.",
+        "# HBM traffic of rope_qk_group_kernel (bf16, D=128, Hq=32, Hkv=8) on the",
+        "# qwen3_4b_packed workload (T=16384), one launch = forward or backward over Q and K.",
         "# Two rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE) over the same bench",
         "# command, each counter scaled by its reading for a plain 1 GiB device copy.",
         f"# commands: {command}",
@@ -544,8 +553,8 @@ def bench_glu(args) -> None:
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default=None,
                     choices=workloads.names() + workloads.glu_names(),
                     help="default: qwen3_4b_packed (glu_qwen3_4b with --glu)")
@@ -721,7 +730,7 @@ def main():
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
             "traffic": traffic,
-            "kernel": "rope_qk_kernel",
+            "kernel": rope_kernel_name(w, tpw),
             "bytes_per_launch": bpl,
             "avg_launch_us": avg_launch_s * 1e6,
             "min_launch_us": float(np.min(launch_ms)) * 1e3,

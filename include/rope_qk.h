@@ -104,10 +104,16 @@ int32_t rope_qk_bwd(void* dq, void* dk, int64_t T, int32_t Hq, int32_t Hkv, int3
  *  direction        +1 forward, -1 backward (anything else: ROPE_EINVAL)
  *  index_mode       a rope_index_mode; ROPE_INDEX_32 is rejected (ROPE_EINVAL)
  *                   when the tensors need 64-bit offsets
- *  tokens_per_wave  launch geometry: each 64-lane wave rotates this many consecutive
- *                   tokens, one at a time, all Q and K heads of each (0 = chosen by
- *                   the library from T; 1..1024 otherwise). Results do not depend
- *                   on it.
+ *  tokens_per_wave  launch geometry. 0: the library's default, one 64-lane
+ *                   workgroup per token and group of consecutive head rows (8 rows
+ *                   for D = 128 in bf16), which evaluates the token's cos/sin once
+ *                   per group; one wave per token instead when seqused is given
+ *                   (padded layouts skip many rows, which that geometry passes over
+ *                   more cheaply) or when the row layout or the grid size rules the
+ *                   row groups out. 1..1024: each 64-lane wave rotates this many
+ *                   consecutive tokens, one at a time, all Q and K heads of each,
+ *                   evaluating each token's cos/sin once. Results do not depend on
+ *                   it.
  * Other arguments as in rope_qk_fwd. */
 int32_t rope_qk_apply(void* q, void* k, int64_t T, int32_t Hq, int32_t Hkv, int32_t D,
                       const int32_t* cu_seqlens, int32_t num_seqs, const int32_t* seqused,
