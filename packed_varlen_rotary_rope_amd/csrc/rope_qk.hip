@@ -37,6 +37,7 @@
 
 #include "../../include/rope_qk.h"
 #include "cr_sincos.h"
+#include "fast_div.h"
 #include "storage.h"
 
 namespace {
@@ -62,6 +63,10 @@ struct RopeParams {
   int32_t tpw;  // tokens per wave
   float sin_sign;
   float pos_scale;  // linear position interpolation: positions divided by this (1 = none)
+  // row-group kernel only, set by the host when it launches that kernel
+  uint32_t gq, gk;           // row groups of Q and of K per token
+  uint32_t nc_shift;         // log2(nc); nc divides 64
+  fastdiv::FastDiv groups;   // division by gq + gk
 };
 
 struct CosSinParams {
@@ -84,15 +89,18 @@ struct PosSource {
 // Sequence s is the last index with cu[s] <= t (upper bound minus one). The token
 // is rotated if 0 <= s < num_seqs and, with seqused, t - cu[s] < seqused[s].
 // Returns the position, or -1 for an untouched token (then *seq_out = -1).
+// I is the token index type: int32_t where every token index of the launch fits
+// (the search then compares in 32 bits), int64_t otherwise.
+template <typename I>
 __device__ inline int32_t token_position(const int32_t* __restrict__ cu, int32_t num_seqs,
-                                         const int32_t* __restrict__ seqused, int64_t t,
+                                         const int32_t* __restrict__ seqused, I t,
                                          int32_t* seq_out) {
   int32_t first = 0;
   int32_t count = num_seqs + 1;
   while (count > 0) {
     const int32_t step = count >> 1;
     const int32_t it = first + step;
-    if ((int64_t)cu[it] <= t) {
+    if ((I)cu[it] <= t) {
       first = it + 1;
       count -= step + 1;
     } else {
@@ -102,7 +110,7 @@ __device__ inline int32_t token_position(const int32_t* __restrict__ cu, int32_t
   const int32_t s = first - 1;
   *seq_out = -1;
   if (s < 0 || s >= num_seqs) return -1;
-  const int64_t p = t - (int64_t)cu[s];
+  const int64_t p = (int64_t)t - (int64_t)cu[s];
   if (seqused != nullptr && p >= (int64_t)seqused[s]) return -1;
   *seq_out = s;
   return (int32_t)p;
@@ -111,7 +119,8 @@ __device__ inline int32_t token_position(const int32_t* __restrict__ cu, int32_t
 // Position of token t from any source, or -1 (untouched). With explicit ids a
 // negative id leaves the token untouched; with per-sequence offsets a shifted
 // position outside [0, 2^31) does.
-__device__ inline int32_t resolve_position(const PosSource& ps, int64_t t, int32_t* seq_out) {
+template <typename I>
+__device__ inline int32_t resolve_position(const PosSource& ps, I t, int32_t* seq_out) {
   if (ps.position_ids != nullptr) {
     *seq_out = -1;
     const int32_t p = ps.position_ids[t];
@@ -354,25 +363,25 @@ __global__ __launch_bounds__(64) void rope_qk_group_kernel(T* __restrict__ q, T*
   __shared__ float lds_sn[kMaxHalf];
   using C = Chunk<T, VEC>;
   const int lane = threadIdx.x;
-  const int nc = p.nc;
-  const int step_r = 64 / nc;
-  const int gq = (p.Hq + step_r - 1) / step_r;
-  const int groups = gq + (p.Hkv + step_r - 1) / step_r;
-  const int64_t t = (int64_t)blockIdx.x / groups;
-  const int g = (int)((int64_t)blockIdx.x - t * groups);
+  // Workgroup -> (token, row group) with host-made constants: a multiply and a
+  // shift instead of integer divisions, so the wave reaches its loads sooner.
+  const uint32_t ns = p.nc_shift;
+  const uint32_t gq = p.gq;
+  const uint32_t t = fastdiv::div(blockIdx.x, p.groups);  // < 2^26
+  const uint32_t g = blockIdx.x - t * (gq + p.gk);
   int32_t seq;
-  const int32_t pos = resolve_position(ps, t, &seq);  // wave-uniform
+  const int32_t pos = resolve_position(ps, (int32_t)t, &seq);  // wave-uniform
   if (pos < 0) return;
   const uint32_t D = (uint32_t)p.D;
   const uint32_t half = D >> 1;
 
   // a4/a5 loads: this lane's row of the group, and its chunk of the row halves
-  const int c = lane % nc;
+  const int c = lane & ((1 << ns) - 1);
   const bool in_q = g < gq;
-  const int r = (in_q ? g : g - gq) * step_r + lane / nc;
+  const int r = (int)(((in_q ? g : g - gq) << (6 - ns)) + ((uint32_t)lane >> ns));
   const bool live = r < (in_q ? p.Hq : p.Hkv);
-  T* row = in_q ? token_row0<T, LONG_INDEX>(q, t, p.q_stride)
-                : token_row0<T, LONG_INDEX>(k, t, p.k_stride);
+  T* row = in_q ? token_row0<T, LONG_INDEX>(q, (int64_t)t, p.q_stride)
+                : token_row0<T, LONG_INDEX>(k, (int64_t)t, p.k_stride);
   row += (uint32_t)(live ? r : 0) * D + (uint32_t)(c * VEC);
   C lo, hi;
   if (live) {
@@ -463,17 +472,34 @@ int32_t chunk_bytes(int32_t D, int32_t esize, const void* q, const void* k, int6
   return esize;
 }
 
+// Workgroups of the row-group kernel resident per CU. Unrestricted, its 64-lane
+// workgroups (48 VGPRs) fill every wave slot of a CU; fewer in flight move data
+// faster. The cap is set by reserving LDS the kernel does not use: each workgroup
+// asks for lds_per_cu / cap bytes in all. Measured on MI355X (bf16, D = 128,
+// back-to-back launches on the same buffers): a cap of 28 gains 1% on the
+// 16384-token batch with 32 + 8 heads and costs at most 0.3% on the other packed
+// batches; from 2^19 workgroups on, a cap of 24 gains 3-8% over no cap (524288
+// tokens with 32 + 8 heads: 1660 vs 1798 us; 28 reaches 1715) and within 1% of the
+// best cap for 64 + 8 heads.
+constexpr uint32_t kLdsPerCU = 160 * 1024;
+constexpr uint32_t kGroupStaticLds = 2 * kMaxHalf * sizeof(float);
+uint32_t group_dynamic_lds(unsigned group_blocks) {
+  const uint32_t cap = group_blocks >= (1u << 19) ? 24 : 28;
+  return kLdsPerCU / cap - kGroupStaticLds;
+}
+
 template <typename T, int VEC>
 int32_t launch_vec(void* q, void* k, const PosSource& ps, const RopeParams& p, bool long_index,
                    unsigned blocks, unsigned group_blocks, hipStream_t stream) {
   T* qt = static_cast<T*>(q);
   T* kt = static_cast<T*>(k);
   if (group_blocks > 0) {
+    const uint32_t lds = group_dynamic_lds(group_blocks);
     if (long_index)
-      hipLaunchKernelGGL((rope_qk_group_kernel<T, VEC, true>), dim3(group_blocks), dim3(64), 0,
+      hipLaunchKernelGGL((rope_qk_group_kernel<T, VEC, true>), dim3(group_blocks), dim3(64), lds,
                          stream, qt, kt, ps, p);
     else
-      hipLaunchKernelGGL((rope_qk_group_kernel<T, VEC, false>), dim3(group_blocks), dim3(64), 0,
+      hipLaunchKernelGGL((rope_qk_group_kernel<T, VEC, false>), dim3(group_blocks), dim3(64), lds,
                          stream, qt, kt, ps, p);
     return hipGetLastError() == hipSuccess ? ROPE_OK : ROPE_ELAUNCH;
   }
@@ -507,6 +533,7 @@ int64_t group_grid(const RopeParams& p, bool geometry_chosen, bool padded) {
   const int step_r = 64 / p.nc;
   const int64_t groups = (p.Hq + step_r - 1) / step_r + (p.Hkv + step_r - 1) / step_r;
   const int64_t blocks = p.T * groups;
+  // < 2^26 workgroups: the dispatch limit, and the range of fastdiv::div
   return blocks <= (int64_t)0xffffffffu / 64 ? blocks : 0;
 }
 
@@ -516,6 +543,14 @@ int32_t launch_typed(void* q, void* k, const PosSource& ps, RopeParams& p, int32
   const int32_t vec = bytes / (int32_t)sizeof(T);
   p.nc = (p.D / 2) / vec;
   const int64_t group_blocks = group_grid(p, geometry_chosen, ps.seqused != nullptr);
+  if (group_blocks > 0) {
+    const int step_r = 64 / p.nc;
+    p.gq = (uint32_t)((p.Hq + step_r - 1) / step_r);
+    p.gk = (uint32_t)((p.Hkv + step_r - 1) / step_r);
+    p.nc_shift = 0;
+    while ((1 << p.nc_shift) < p.nc) ++p.nc_shift;
+    p.groups = fastdiv::make(p.gq + p.gk);
+  }
   if (group_blocks == 0 && !geometry_chosen) p.tpw = auto_tokens_per_wave(p.T);
   const int64_t waves = (p.T + p.tpw - 1) / p.tpw;
   const int64_t blocks = (waves + kWaves - 1) / kWaves;

@@ -285,3 +285,60 @@ def test_missing_library_fails_loudly(tmp_path):
                        cwd=tmp_path, capture_output=True, text=True)
     assert r.returncode != 0
     assert "ImportError" in r.stderr and "no fallback" in r.stderr.lower()
+
+
+FAST_DIV_CHECK = r"""
+#include <stdio.h>
+#include <stdlib.h>
+#include "fast_div.h"
+using namespace fastdiv;
+static uint64_t state = 88172645463325252ull;
+static uint32_t rnd(void) { state ^= state << 13; state ^= state >> 7; state ^= state << 17; return (uint32_t)state; }
+static int check(uint32_t n, uint32_t d, FastDiv f) {
+  if (div(n, f) != n / d) { printf("n=%u d=%u got %u\n", n, d, div(n, f)); return 1; }
+  return 0;
+}
+int main(void) {
+  const uint32_t top = (1u << kMaxDividendBits) - 1;
+  int bad = 0;
+  /* every divisor a launch can have (row groups per token <= 2 * 4096), near every
+     multiple of d that the edges of the range hold, and at random */
+  for (uint32_t d = 1; d <= 8192 && !bad; ++d) {
+    const FastDiv f = make(d);
+    if (f.mul == 0) return 2;
+    for (uint32_t j = 0; j < 64; ++j) {
+      const uint64_t m = (uint64_t)j * d, m2 = (uint64_t)(top / d - j) * d;
+      for (int e = -1; e <= 1; ++e) {
+        if ((int64_t)m + e >= 0 && m + e <= top) bad |= check((uint32_t)(m + e), d, f);
+        if ((int64_t)m2 + e >= 0 && m2 + e <= top) bad |= check((uint32_t)(m2 + e), d, f);
+      }
+    }
+    for (int i = 0; i < 2000; ++i) bad |= check(rnd() & top, d, f);
+  }
+  /* exhaustively for a few divisors, and for large ones at random */
+  const uint32_t some[] = {3, 5, 7, 9, 10, 17, 40, 72, 4097};
+  for (uint32_t d : some) {
+    const FastDiv f = make(d);
+    for (uint32_t n = 0; n <= top && !bad; ++n) bad |= check(n, d, f);
+  }
+  for (int i = 0; i < 200000 && !bad; ++i) {
+    const uint32_t d = 1 + (rnd() & 0x7ffffffe);
+    bad |= check(rnd() & top, d, make(d));
+  }
+  printf(bad ? "FAIL\n" : "ok\n");
+  return bad;
+}
+"""
+
+
+def test_fast_division_constants(tmp_path):
+    """The row-group kernel maps a workgroup index to (token, row group) as
+    (n * mul) >> shift with host-made constants (fastdiv::make): equal to n / d for
+    every divisor a launch can have, checked near range edges, at random and
+    exhaustively over all n < 2^26 for a few divisors."""
+    src = tmp_path / "fast_div_check.cpp"
+    src.write_text(FAST_DIV_CHECK)
+    exe = tmp_path / "fast_div_check"
+    subprocess.run(["g++", "-O2", "-std=c++17", "-I", CSRC, "-o", str(exe), str(src)], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0 and out.stdout.strip() == "ok", out.stdout
