@@ -46,7 +46,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "rope_qk_qwen3_4b_packed_traffic.t
 
 # The sources each kernel is compiled from: a traffic summary taken on other
 # sources does not describe the kernel being timed.
-ROPE_SOURCES = ["rope_qk.hip", "storage.h", "cr_sincos.h", "trig_constants.h"]
+ROPE_SOURCES = ["rope_qk.hip", "storage.h", "cr_sincos.h", "trig_constants.h", "fast_div.h"]
 GLU_SOURCES = ["glu.hip", "storage.h", "glu_constants.h"]
 GLU_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "glu_swiglu_qwen3_4b_traffic.txt")
 # bf16, 16-byte chunks, SwiGLU, dense, 32-bit offsets: forward and backward instances
