@@ -369,25 +369,41 @@ __global__ __launch_bounds__(64) void rope_qk_group_kernel(T* __restrict__ q, T*
   const uint32_t gq = p.gq;
   const uint32_t t = fastdiv::div(blockIdx.x, p.groups);  // < 2^26
   const uint32_t g = blockIdx.x - t * (gq + p.gk);
-  int32_t seq;
-  const int32_t pos = resolve_position(ps, (int32_t)t, &seq);  // wave-uniform
-  if (pos < 0) return;
   const uint32_t D = (uint32_t)p.D;
   const uint32_t half = D >> 1;
 
-  // a4/a5 loads: this lane's row of the group, and its chunk of the row halves
+  // a4/a5 addresses: this lane's row of the group, and its chunk of the row
+  // halves. Lanes past the last row of a partial group address row 0 of the
+  // same token and tensor (valid memory) and store nothing.
   const int c = lane & ((1 << ns) - 1);
   const bool in_q = g < gq;
   const int r = (int)(((in_q ? g : g - gq) << (6 - ns)) + ((uint32_t)lane >> ns));
   const bool live = r < (in_q ? p.Hq : p.Hkv);
   T* row = in_q ? token_row0<T, LONG_INDEX>(q, (int64_t)t, p.q_stride)
                 : token_row0<T, LONG_INDEX>(k, (int64_t)t, p.k_stride);
-  row += (uint32_t)(live ? r : 0) * D + (uint32_t)(c * VEC);
-  C lo, hi;
-  if (live) {
-    lo = load_chunk<T, VEC>(row);
-    hi = load_chunk<T, VEC>(row + half);
-  }
+  // r * D < 2^22: a 24-bit multiply. (A full 32-bit multiply-add becomes
+  // v_mad_u64_u32 with an undefined high addend, which the register allocator
+  // may place in a register a pending load writes, forcing a wait on it.)
+  row += __umul24((uint32_t)(live ? r : 0), D) + (uint32_t)(c * VEC);
+
+  // Vector-memory loads complete in issue order, so the order of issue below is
+  // what lets the cos/sin evaluation overlap the row loads: this lane's inverse
+  // frequencies first (from the argument struct, which holds all kMaxHalf
+  // entries, so no condition is needed; entries past D/2 go unused), then the
+  // position search (scalar loads), then the two row loads, unconditionally, so
+  // that the wait for the frequencies needs no wait for the rows. The schedule
+  // barriers keep the compiler from interleaving these phases.
+  __builtin_amdgcn_sched_barrier(0);
+  float f[kMaxHalf / 64];
+#pragma unroll
+  for (int i = 0; i < kMaxHalf / 64; ++i) f[i] = p.inv_freq[(uint32_t)lane + 64u * i];
+  __builtin_amdgcn_sched_barrier(0);
+  int32_t seq;
+  const int32_t pos = resolve_position(ps, (int32_t)t, &seq);  // wave-uniform
+  if (pos < 0) return;
+  C lo = load_chunk<T, VEC>(row);
+  C hi = load_chunk<T, VEC>(row + half);
+  __builtin_amdgcn_sched_barrier(0);
 
   // a3: the token's fp32 cos/sin table
   const float spos = scaled_position(pos, p.pos_scale);
@@ -396,7 +412,7 @@ __global__ __launch_bounds__(64) void rope_qk_group_kernel(T* __restrict__ q, T*
     const uint32_t j = (uint32_t)lane + 64u * i;
     if (j < half) {
       float sn, cs;
-      rope_trig::sincos_f32_cr(rope_angle(spos, p.inv_freq[j]), sn, cs);
+      rope_trig::sincos_f32_cr(rope_angle(spos, f[i]), sn, cs);
       lds_cs[j] = cs;
       lds_sn[j] = sn * p.sin_sign;  // backward: R transposed = sin negated
     }
@@ -473,18 +489,20 @@ int32_t chunk_bytes(int32_t D, int32_t esize, const void* q, const void* k, int6
 }
 
 // Workgroups of the row-group kernel resident per CU. Unrestricted, its 64-lane
-// workgroups (48 VGPRs) fill every wave slot of a CU; fewer in flight move data
-// faster. The cap is set by reserving LDS the kernel does not use: each workgroup
-// asks for lds_per_cu / cap bytes in all. Measured on MI355X (bf16, D = 128,
-// back-to-back launches on the same buffers): a cap of 28 gains 1% on the
-// 16384-token batch with 32 + 8 heads and costs at most 0.3% on the other packed
-// batches; from 2^19 workgroups on, a cap of 24 gains 3-8% over no cap (524288
-// tokens with 32 + 8 heads: 1660 vs 1798 us; 28 reaches 1715) and within 1% of the
-// best cap for 64 + 8 heads.
+// workgroups fill every wave slot of a CU (32); fewer in flight move data faster.
+// The cap is set by reserving LDS the kernel does not use: each workgroup asks
+// for lds_per_cu / cap bytes in all. Measured on MI355X (bf16, D = 128,
+// back-to-back launches on the same buffers, caps 16-32): 24 is within 0.5% of
+// the best cap on every batch below 2^19 workgroups (Qwen3-4B batch 51.8 us vs
+// 53.0 uncapped) and on launches of the 64 + 8 head shape of any length;
+// launches of 2^19 workgroups or more where K has at least a fifth of the row
+// groups (32 + 8 heads) do best at 20 (524288 tokens: 1652 us vs 1686 at 24 and
+// 1796 uncapped; 131072 and 262144 tokens: 0.5-1% better than 24).
 constexpr uint32_t kLdsPerCU = 160 * 1024;
 constexpr uint32_t kGroupStaticLds = 2 * kMaxHalf * sizeof(float);
-uint32_t group_dynamic_lds(unsigned group_blocks) {
-  const uint32_t cap = group_blocks >= (1u << 19) ? 24 : 28;
+uint32_t group_dynamic_lds(unsigned group_blocks, uint32_t gq, uint32_t gk) {
+  const bool long_kv_heavy = group_blocks >= (1u << 19) && 5 * gk >= gq + gk;
+  const uint32_t cap = long_kv_heavy ? 20 : 24;
   return kLdsPerCU / cap - kGroupStaticLds;
 }
 
@@ -494,7 +512,7 @@ int32_t launch_vec(void* q, void* k, const PosSource& ps, const RopeParams& p, b
   T* qt = static_cast<T*>(q);
   T* kt = static_cast<T*>(k);
   if (group_blocks > 0) {
-    const uint32_t lds = group_dynamic_lds(group_blocks);
+    const uint32_t lds = group_dynamic_lds(group_blocks, p.gq, p.gk);
     if (long_index)
       hipLaunchKernelGGL((rope_qk_group_kernel<T, VEC, true>), dim3(group_blocks), dim3(64), lds,
                          stream, qt, kt, ps, p);
