@@ -44,7 +44,7 @@ class RopeError(RuntimeError):
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is not built; run `python -m packed_varlen_rotary_rope_amd.build` "
+            f"{LIB_PATH} is not built; run `python packed_varlen_rotary_rope_amd/build.py` "
             "(hipcc, gfx950). There is no fallback implementation.")
     lib = ctypes.CDLL(LIB_PATH)
     i32, i64, dbl, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_double, ctypes.c_void_p

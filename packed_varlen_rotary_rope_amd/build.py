@@ -1,7 +1,8 @@
 """Build the HIP library librope_qk.so (QK-RoPE and SwiGLU/GeGLU kernels) for
 gfx950 with hipcc (in-tree).
 
-Usage: python -m packed_varlen_rotary_rope_amd.build
+Usage: python packed_varlen_rotary_rope_amd/build.py  (run as a script: importing the
+package itself needs the library this builds)
 """
 from __future__ import annotations
 

@@ -287,6 +287,22 @@ def test_missing_library_fails_loudly(tmp_path):
     assert "ImportError" in r.stderr and "no fallback" in r.stderr.lower()
 
 
+def test_build_entry_loads_builder_without_library(tmp_path):
+    """A fresh checkout has no library yet: the build entry point must reach the
+    builder without importing the package (whose import needs the library)."""
+    import shutil
+    pkg = os.path.join(ROOT, "packed_varlen_rotary_rope_amd")
+    shutil.copytree(pkg, tmp_path / "packed_varlen_rotary_rope_amd",
+                    ignore=shutil.ignore_patterns("*.so", "__pycache__", "csrc"))
+    shutil.copy(os.path.join(ROOT, "__graft_entry__.py"), tmp_path)
+    code = ("import sys, __graft_entry__ as g; m = g._load_lib_builder(); "
+            "assert 'packed_varlen_rotary_rope_amd' not in sys.modules; "
+            "print(m.ARCH, len(m.SRCS))")
+    r = subprocess.run([sys.executable, "-c", code], cwd=tmp_path, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.split() == ["gfx950", "2"]
+
+
 FAST_DIV_CHECK = r"""
 #include <stdio.h>
 #include <stdlib.h>
