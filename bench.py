@@ -240,6 +240,63 @@ def write_glu_traffic_summary(fetch_csv, write_csv, copy_fetch_csv, copy_write_c
     _write_summary(GLU_TRAFFIC_FILE, header, lines)
 
 
+def trace_summary_path(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"rope_qk_{workload}_kernel_trace.txt")
+
+
+def write_trace_summary(trace_csv: str, workload: str, command: str) -> None:
+    """Per-launch durations of the RoPE kernel from a rocprofv3 --kernel-trace CSV
+    (one row per dispatch), with the algorithmic bandwidth they give, as a small
+    text summary under profiles/."""
+    import csv
+    w = workloads.get(workload)
+    durs, names, shape = [], set(), None
+    with open(trace_csv) as fh:
+        for row in csv.DictReader(fh):
+            if "rope_qk" not in row["Kernel_Name"]:
+                continue
+            durs.append((int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3)
+            names.add(row["Kernel_Name"])
+            shape = (row["Grid_Size_X"], row["Workgroup_Size_X"], row["VGPR_Count"],
+                     row["LDS_Block_Size"])
+    if not durs:
+        raise SystemExit(f"no rope_qk dispatch in {trace_csv}")
+    d = np.array(durs)
+    bpl = algorithmic_bytes_per_launch(w)
+
+    def rate(us):
+        gbps = bpl / (us * 1e-6) / 1e9
+        return f"{us:.2f} us -> {gbps:.0f} GB/s = {100 * gbps / HBM_PEAK_GBPS:.1f}% of 8 TB/s"
+
+    seq = "padded rows skipped via seqused" if w.seqused is not None else "packed"
+    header = [
+        f"# rocprofv3 kernel trace: RoPE kernel on the {w.name} workload",
+        f"# (T={w.T} rows, {w.valid_tokens} valid tokens in {len(w.cu_seqlens) - 1} sequences, "
+        f"{seq}; Hq={w.Hq}, Hkv={w.Hkv}, D={w.D}, {w.dtype}, theta={w.theta:g})",
+        "# every timed step = forward(Q, K) + backward(dQ, dK), one launch each;",
+        "# buffer sets rotate so that no launch is served from the Infinity Cache",
+        f"# command (R = repository root, on one MI355X): {command}",
+        "",
+    ]
+    lines = [
+        "kernel: " + ", ".join(sorted(names)),
+        f"grid_threads, workgroup, vgprs, static_lds_bytes: {', '.join(shape)}",
+    ]
+    if any("group_kernel" in n for n in names):
+        lines += ["(rocprofv3's LDS column is the kernel's static LDS only: the dynamic LDS the",
+                  " row-group launch reserves to cap residency per CU is allocated but not shown)"]
+    lines += [
+        f"dispatches: {len(d)} (warmup included)",
+        f"algorithmic_bytes_per_launch: {bpl} (one read + one write of every rotated element)",
+        f"average: {rate(float(d.mean()))}",
+        f"median:  {rate(float(np.median(d)))}",
+        f"minimum: {rate(float(d.min()))}",
+        f"maximum: {float(d.max()):.2f} us",
+        f"valid_tokens_per_s_at_average: {w.valid_tokens / (float(d.mean()) * 1e-6):.4g} per launch",
+    ]
+    _write_summary(trace_summary_path(workload), header, lines)
+
+
 def packed_position_ids(w: workloads.Workload) -> np.ndarray:
     """Per-token positions of the packed batch (0..len-1 per sequence; -1 for rows
     outside every sequence): the position_ids a 1-D packing collator would emit."""
@@ -582,7 +639,16 @@ def main():
     ap.add_argument("--traffic-command", default="", help="commands recorded in that summary")
     ap.add_argument("--traffic-kernel", default="rope", choices=["rope", "glu"],
                     help="which kernel's summary --traffic-summary writes")
+    ap.add_argument("--trace-summary", default=None, metavar="KERNEL_TRACE_CSV",
+                    help="write profiles/rope_qk_<workload>_kernel_trace.txt from a rocprofv3 "
+                         "--kernel-trace CSV of a run on --workload, then exit")
+    ap.add_argument("--trace-command", default="", help="command recorded in that summary")
     args = ap.parse_args()
+
+    if args.trace_summary:
+        write_trace_summary(args.trace_summary, args.workload or "qwen3_4b_packed",
+                            args.trace_command)
+        return
 
     if args.traffic_summary:
         writer = write_glu_traffic_summary if args.traffic_kernel == "glu" else write_traffic_summary
