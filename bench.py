@@ -12,8 +12,11 @@ HBM, as a training step would.
 
 Prints ONE JSON line (rank 0). `value` is tokens/s of whole steps (wall clock
 around K steps, bracketed by synchronize). `roofline` uses the kernel's average
-launch duration from HIP events (timing-only, no system fence) recorded on the
-launch stream around both launches of every 4th step of the timed region; `traffic` comes from the committed rocprofv3 PMC
+launch duration: the GPU time of the timed region, from one pair of HIP events
+(timing-only, no system fence) recorded on the launch stream around it, divided
+by its 2K launches (gaps between launches included). Per-launch minimum and
+median come from events around single launches in a sampling pass after the
+timed region. `traffic` comes from the committed rocprofv3 PMC
 summary when it was taken on the current kernel source, else null.
 `cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
 """
@@ -745,23 +748,35 @@ def main():
         step(sets[i % nsets])
     torch.cuda.synchronize()
 
-    # Per-launch HIP events, on the launch stream, around both launches of every
-    # EVENT_EVERY-th step of the timed region (fewer event packets between kernels).
-    events = {i: [HipEvent() for _ in range(4)] for i in range(0, args.steps, EVENT_EVERY)}
+    # The timed region: K steps back to back, bracketed by synchronize (wall clock)
+    # and by one pair of HIP events on the launch stream (GPU time). Nothing else is
+    # enqueued between the launches.
+    region = [HipEvent(), HipEvent()]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    region[0].record(stream)
     for i in range(args.steps):
-        step(sets[i % nsets], events.get(i))
+        step(sets[i % nsets])
+    region[1].record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-
-    launch_ms = []
-    for ev in events.values():
-        launch_ms.append(ev[0].elapsed_ms(ev[1]))
-        launch_ms.append(ev[2].elapsed_ms(ev[3]))
-    avg_launch_s = float(np.mean(launch_ms)) / 1e3
+    region_s = region[0].elapsed_ms(region[1]) / 1e3
+    # Average duration of one pass (forward or backward: one launch, or one per
+    # shard with --positions shards4), gaps between launches included.
+    avg_launch_s = region_s / (2 * args.steps)
     bpl = algorithmic_bytes_per_launch(w)
     achieved = bpl / avg_launch_s / 1e9
+
+    # Sampled per-launch durations, after the timed region: HIP events around both
+    # launches of each of up to 250 further steps (context: minimum and median).
+    events = [[HipEvent() for _ in range(4)] for _ in range(min(250, args.steps))]
+    for i, ev in enumerate(events):
+        step(sets[i % nsets], ev)
+    torch.cuda.synchronize()
+    launch_ms = []
+    for ev in events:
+        launch_ms.append(ev[0].elapsed_ms(ev[1]))
+        launch_ms.append(ev[2].elapsed_ms(ev[3]))
     tokens_per_step = w.valid_tokens
     value = tokens_per_step * args.steps / elapsed
     ms_per_step = elapsed / args.steps * 1e3
@@ -799,8 +814,11 @@ def main():
             "kernel": rope_kernel_name(w, tpw),
             "bytes_per_launch": bpl,
             "avg_launch_us": avg_launch_s * 1e6,
-            "min_launch_us": float(np.min(launch_ms)) * 1e3,
-            "median_launch_us": float(np.median(launch_ms)) * 1e3,
+            "timing": "HIP events around the timed region / (2 x steps)",
+            "sampled_launches": len(launch_ms),
+            "sampled_avg_launch_us": float(np.mean(launch_ms)) * 1e3,
+            "sampled_median_launch_us": float(np.median(launch_ms)) * 1e3,
+            "sampled_min_launch_us": float(np.min(launch_ms)) * 1e3,
         },
     }
     if args.cpu_seconds > 0:
