@@ -243,6 +243,94 @@ def write_glu_traffic_summary(fetch_csv, write_csv, copy_fetch_csv, copy_write_c
     _write_summary(GLU_TRAFFIC_FILE, header, lines)
 
 
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "rope_qk_cos_sin_fly_vs_table_counters.txt")
+CU_COUNT, SIMDS_PER_CU, XCDS = 256, 4, 8
+
+
+def _kernel_counters(run_dir: str) -> dict:
+    """Mean per-dispatch value of every counter in the rocprofv3 --pmc CSVs under
+    run_dir (one pass per subfolder), over the dispatches of the RoPE kernel."""
+    import csv
+    import glob
+    acc = {}
+    for path in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as fh:
+            for row in csv.DictReader(fh):
+                if "rope_qk" in row["Kernel_Name"]:
+                    acc.setdefault(row["Counter_Name"], []).append(float(row["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def _kernel_durations_us(run_dir: str) -> np.ndarray:
+    import csv
+    import glob
+    d = []
+    for path in glob.glob(os.path.join(run_dir, "**", "*kernel_trace.csv"), recursive=True):
+        with open(path) as fh:
+            for row in csv.DictReader(fh):
+                if "rope_qk" in row["Kernel_Name"]:
+                    d.append((int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3)
+    return np.array(d)
+
+
+def write_counters_summary(fly_dir, table_dir, copy_fetch_csv, copy_write_csv, command):
+    """Counters of the row-group kernel on the Qwen3-4B batch with cos/sin evaluated in
+    the kernel (fly) and read from a cos/sin cache (table): instruction mix per wave,
+    VALU issue, wave lifetime, HBM bytes (scaled by a 1 GiB device copy's readings)
+    and per-launch time from kernel traces of the same commands."""
+    w = workloads.get("qwen3_4b_packed")
+    bpl = algorithmic_bytes_per_launch(w)
+    copy_bytes = 2 ** 30
+    f_c = max(v[0] for v in _dispatch_means(copy_fetch_csv).values())
+    w_c = max(v[0] for v in _dispatch_means(copy_write_csv).values())
+    f_scale, w_scale = copy_bytes / (f_c * 1024.0), copy_bytes / (w_c * 1024.0)
+    runs = {"fly": _kernel_counters(fly_dir), "table": _kernel_counters(table_dir)}
+    times = {"fly": _kernel_durations_us(fly_dir), "table": _kernel_durations_us(table_dir)}
+    simds = CU_COUNT * SIMDS_PER_CU
+
+    def row(name, fn, fmt="{:.4g}"):
+        vals = {m: fn(runs[m], times[m]) for m in runs}
+        ratio = vals["table"] / vals["fly"] if vals["fly"] else float("nan")
+        return f"{name:44s} {fmt.format(vals['fly']):>14s} {fmt.format(vals['table']):>14s}   x{ratio:.3f}"
+
+    per_wave = lambda k: (lambda c, t: c[k] / c["SQ_WAVES"])
+    lines = [
+        f"{'quantity (per launch of the RoPE kernel)':44s} {'fly':>14s} {'table':>14s}   table/fly",
+        row("kernel duration, kernel trace (us)", lambda c, t: float(t.mean()), "{:.2f}"),
+        row("waves (SQ_WAVES)", lambda c, t: c["SQ_WAVES"], "{:.0f}"),
+        row("VALU instructions per wave", per_wave("SQ_INSTS_VALU"), "{:.1f}"),
+        row("  of which fp64 FMA", per_wave("SQ_INSTS_VALU_FMA_F64"), "{:.1f}"),
+        row("SALU instructions per wave", per_wave("SQ_INSTS_SALU"), "{:.1f}"),
+        row("scalar memory instructions per wave", per_wave("SQ_INSTS_SMEM"), "{:.1f}"),
+        row("LDS instructions per wave", per_wave("SQ_INSTS_LDS"), "{:.1f}"),
+        row("vector memory reads per wave", per_wave("SQ_INSTS_VMEM_RD"), "{:.1f}"),
+        row("vector memory writes per wave", per_wave("SQ_INSTS_VMEM_WR"), "{:.1f}"),
+        row("LDS bank conflict cycles", lambda c, t: c["SQ_LDS_BANK_CONFLICT"], "{:.0f}"),
+        row("VALU busy, % of SIMD issue cycles",
+            lambda c, t: 100.0 * 4 * c["SQ_ACTIVE_INST_VALU"] / (simds * c["GRBM_GUI_ACTIVE"] / XCDS),
+            "{:.1f}"),
+        row("wave lifetime (SQ_WAVE_CYCLES / SQ_WAVES)", per_wave("SQ_WAVE_CYCLES"), "{:.0f}"),
+        row("cycles waiting per wave (SQ_WAIT_INST_ANY)", per_wave("SQ_WAIT_INST_ANY"), "{:.0f}"),
+        row("HBM read bytes (FETCH_SIZE x scale)",
+            lambda c, t: c["FETCH_SIZE"] * 1024.0 * f_scale, "{:.4g}"),
+        row("HBM write bytes (WRITE_SIZE x scale)",
+            lambda c, t: c["WRITE_SIZE"] * 1024.0 * w_scale, "{:.4g}"),
+        f"algorithmic bytes per launch: {bpl} (one read + one write of Q and K)",
+        f"FETCH_SIZE scale {f_scale:.5f}, WRITE_SIZE scale {w_scale:.5f} (1 GiB device copy)",
+    ]
+    header = [
+        "# cos/sin in the kernel (fly) versus from a cos/sin cache (table): counters of the",
+        "# row-group kernel on the qwen3_4b_packed workload (T=16384, Hq=32, Hkv=8, D=128,",
+        "# bf16, theta=1e6). Both give bit-identical results (the cache is written by the",
+        "# library's own cos/sin export). Counter values are per dispatch, summed over the",
+        "# chip; VALU busy takes 4 cycles per wave64 VALU instruction (SQ_ACTIVE_INST_VALU",
+        "# counts instructions issued) against 1024 SIMDs x GRBM_GUI_ACTIVE / 8 XCDs cycles.",
+        f"# commands (R = repository root, M = fly or table): {command}",
+        "",
+    ]
+    _write_summary(COUNTERS_FILE, header, lines)
+
+
 def trace_summary_path(workload: str) -> str:
     return os.path.join(ROOT, "profiles", f"rope_qk_{workload}_kernel_trace.txt")
 
@@ -628,6 +716,9 @@ def main():
                     help="qkv: Q/K (and dQ/dK) are strided views into fused QKV buffers")
     ap.add_argument("--index", default="auto", choices=["auto", "64"],
                     help="64: force the 64-bit offset specialization (auto: 64-bit only when needed)")
+    ap.add_argument("--cos-sin", default="fly", choices=["fly", "table"],
+                    help="fly: cos/sin evaluated in the kernel (default); table: read from a "
+                         "cos/sin cache made once with the library's export (rope_qk_apply_table)")
     ap.add_argument("--glu", default=None, choices=["swiglu", "geglu", "geglu_tanh"],
                     help="time the SwiGLU/GeGLU kernels instead (workload: a glu_* name)")
     ap.add_argument("--compare", action="store_true",
@@ -646,7 +737,15 @@ def main():
                     help="write profiles/rope_qk_<workload>_kernel_trace.txt from a rocprofv3 "
                          "--kernel-trace CSV of a run on --workload, then exit")
     ap.add_argument("--trace-command", default="", help="command recorded in that summary")
+    ap.add_argument("--counters-summary", nargs=4, default=None,
+                    metavar=("FLY_DIR", "TABLE_DIR", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="write the cos/sin fly-vs-table counter summary from rocprofv3 "
+                         "--pmc and --kernel-trace output folders, then exit")
     args = ap.parse_args()
+
+    if args.counters_summary:
+        write_counters_summary(*args.counters_summary, command=args.trace_command)
+        return
 
     if args.trace_summary:
         write_trace_summary(args.trace_summary, args.workload or "qwen3_4b_packed",
@@ -718,8 +817,23 @@ def main():
 
     index_mode = {"auto": rope.INDEX_AUTO, "64": rope.INDEX_64}[args.index]
 
+    tables = None
+    if args.cos_sin == "table":
+        if shards is not None or args.pos_scale != 1.0:
+            raise SystemExit("--cos-sin table times the cu_seqlens / ids position sources, "
+                             "unscaled")
+        # The cos/sin cache a caller would keep: every position of the batch, made
+        # once by the library's own export, outside the timed region.
+        rows = int(max(w.lengths))
+        tables = rope.cos_sin(torch.arange(rows, dtype=torch.int32, device=dev), w.D, w.theta)
+
     def launch(qt, kt, direction):
-        if shards is not None:
+        if tables is not None:
+            rope.qk_apply_table_(qt, kt, tables[0], tables[1], direction,
+                                 cu_seqlens=None if pid is not None else cu,
+                                 seqused=None if pid is not None else su, position_ids=pid,
+                                 tokens_per_wave=tpw, index_mode=index_mode)
+        elif shards is not None:
             for a, b, cu_r, off_r in shards:
                 rope.qk_apply_ex_(qt[a:b], kt[a:b], w.theta, direction, cu_seqlens=cu_r,
                                   seq_offsets=off_r, pos_scale=args.pos_scale,
@@ -780,7 +894,11 @@ def main():
     tokens_per_step = w.valid_tokens
     value = tokens_per_step * args.steps / elapsed
     ms_per_step = elapsed / args.steps * 1e3
-    traffic = read_traffic() if w.name == "qwen3_4b_packed" else None
+    # the PMC traffic summary covers the default configuration of this workload only
+    default_config = (args.positions == "cu" and args.pos_scale == 1.0 and tpw == 0
+                      and args.layout == "contiguous" and args.index == "auto"
+                      and args.cos_sin == "fly")
+    traffic = read_traffic() if w.name == "qwen3_4b_packed" and default_config else None
 
     out = {
         "metric": METRIC,
@@ -801,7 +919,7 @@ def main():
             "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D, "theta": w.theta,
             "buffer_sets": nsets, "tokens_per_wave": tpw or "auto",
             "positions": args.positions, "pos_scale": args.pos_scale,
-            "layout": args.layout, "index": args.index,
+            "layout": args.layout, "index": args.index, "cos_sin": args.cos_sin,
         },
         "step_hbm_GBps": 2 * bpl * args.steps / elapsed / 1e9,
         "roofline": {

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define ROPE_QK_ABI_VERSION 2
+#define ROPE_QK_ABI_VERSION 3
 
 /* Storage dtype of Q and K (computation is fp32 in every case). */
 typedef enum rope_dtype { ROPE_F32 = 0, ROPE_BF16 = 1, ROPE_F16 = 2 } rope_dtype;
@@ -155,6 +155,30 @@ int32_t rope_qk_apply_ex(void* q, void* k, int64_t T, int32_t Hq, int32_t Hkv, i
                          const int32_t* seq_offsets, const int32_t* position_ids, double theta,
                          double pos_scale, int32_t dtype, int32_t direction, int32_t index_mode,
                          int32_t tokens_per_wave, void* stream);
+
+/* rope_qk_apply_ex with caller-supplied cos/sin tables instead of theta: a
+ * cos/sin cache computed once and reused across calls, or the tables of a RoPE
+ * variant whose frequencies this library does not generate. The rotation, its
+ * backward (sin negated), the pairing, the positions and the untouched tokens
+ * are those of rope_qk_apply_ex (Unsloth page, fused QK RoPE section; positions
+ * per "Packing non contamine").
+ *  cos_tab, sin_tab  device float[tab_rows * (D/2)], row-major: row p holds the
+ *                    cos / sin of position p for frequencies j < D/2 (the layout
+ *                    rope_cos_sin writes for positions 0 .. tab_rows-1). Read only.
+ *  tab_rows          rows of both tables, >= 1. A token whose position is >=
+ *                    tab_rows is left untouched (no row exists for it).
+ * There is no theta or pos_scale: the tables already hold the angles' cos/sin.
+ * Rotating with the tables rope_cos_sin writes for (theta, D) gives results bit
+ * for bit equal to rope_qk_apply_ex with that theta and pos_scale 1.
+ * Errors: ROPE_EINVAL if either table is NULL or tab_rows < 1, otherwise as in
+ * rope_qk_apply_ex. Other arguments as in rope_qk_apply_ex. */
+int32_t rope_qk_apply_table(void* q, void* k, int64_t T, int32_t Hq, int32_t Hkv, int32_t D,
+                            int64_t q_token_stride, int64_t k_token_stride,
+                            const int32_t* cu_seqlens, int32_t num_seqs, const int32_t* seqused,
+                            const int32_t* seq_offsets, const int32_t* position_ids,
+                            const float* cos_tab, const float* sin_tab, int32_t tab_rows,
+                            int32_t dtype, int32_t direction, int32_t index_mode,
+                            int32_t tokens_per_wave, void* stream);
 
 /* Forward / backward RoPE with explicit positions: position_ids is a device
  * int32[T] (required when T > 0); negative ids leave their token untouched.

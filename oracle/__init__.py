@@ -58,6 +58,9 @@ class Oracle:
         lib.oracle_rope_rows.argtypes = [i32, vp, vp, vp, i64, i32, i32, vp, i32, vp, dbl, i32,
                                          i32]
         lib.oracle_rope_rows.restype = i32
+        lib.oracle_rope_table.argtypes = [i32, vp, vp, i64, i32, i32, vp, i32, vp, vp, vp, vp, vp,
+                                          i64, i32]
+        lib.oracle_rope_table.restype = i32
         lib.oracle_round_bf16.argtypes = [vp, vp, i64]
         lib.oracle_round_bf16.restype = None
         lib.oracle_fwd_bwd_seconds.argtypes = [i32, vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, i32,
@@ -112,6 +115,27 @@ class Oracle:
                                      float(pos_scale), int(direction), int(nthreads))
         if rc != 0:
             raise ValueError("oracle_rope_ex rejected its arguments")
+        return y
+
+    def rope_table(self, x: np.ndarray, cu_seqlens, cos_tab, sin_tab, direction: int = 1,
+                   dtype: str = "f32", seqused=None, seq_offsets=None,
+                   position_ids=None) -> np.ndarray:
+        """Rotate x[T, H, D] with cos/sin from tables [rows, D/2] (row p = position p);
+        positions without a row are untouched. Returns the fp32 result."""
+        xs = _storage(x, dtype)
+        T, H, D = xs.shape
+        ct = np.ascontiguousarray(cos_tab, dtype=np.float32)
+        st = np.ascontiguousarray(sin_tab, dtype=np.float32)
+        if ct.shape != st.shape or ct.ndim != 2 or ct.shape[1] != D // 2:
+            raise ValueError("cos_tab and sin_tab must both be [rows, D/2]")
+        cu, su, so, pid = (_i32(a) for a in (cu_seqlens, seqused, seq_offsets, position_ids))
+        num_seqs = 0 if cu is None else cu.size - 1
+        y = np.empty((T, H, D), dtype=np.float32)
+        rc = self.lib.oracle_rope_table(_DTYPES[dtype], _ptr(xs), _ptr(y), T, H, D, _ptr(cu),
+                                        num_seqs, _ptr(su), _ptr(so), _ptr(pid), _ptr(ct),
+                                        _ptr(st), ct.shape[0], int(direction))
+        if rc != 0:
+            raise ValueError("oracle_rope_table rejected its arguments")
         return y
 
     def rope_rows(self, x_rows: np.ndarray, tokens, cu_seqlens, theta: float, direction: int = 1,
@@ -192,6 +216,12 @@ def rope_rows(x_rows, tokens, cu_seqlens, theta, direction=1, dtype="f32", sequs
               nthreads=1, seq_offsets=None, position_ids=None, pos_scale=1.0):
     return default().rope_rows(x_rows, tokens, cu_seqlens, theta, direction, dtype, seqused,
                                nthreads, seq_offsets, position_ids, pos_scale)
+
+
+def rope_table(x, cu_seqlens, cos_tab, sin_tab, direction=1, dtype="f32", seqused=None,
+               seq_offsets=None, position_ids=None):
+    return default().rope_table(x, cu_seqlens, cos_tab, sin_tab, direction, dtype, seqused,
+                                seq_offsets, position_ids)
 
 
 def round_bf16(y):

@@ -46,6 +46,10 @@
  *  R8 linear position interpolation by a factor f >= 1 (TRL guide, YaRN section:
  *     with factor 4, position 100000 is treated as 25000): the fp32 position is
  *     divided by the fp32 factor (one rounding) before the angle multiply.
+ *  R9 caller-supplied cos/sin tables: row p of each table holds the fp32 cos /
+ *     sin of position p for every frequency; the rotation (R2, R6) uses them as
+ *     given, sin negated backward; a token whose position has no row is
+ *     untouched.
  *
  * Parity pins: every function here is checked against something other than
  * itself in tests/test_oracle_pins.py (closed forms, mpmath, the block matrix R
@@ -271,6 +275,32 @@ int32_t oracle_rope_ex(int32_t dtype, const void* x, float* y, int64_t T, int32_
         int64_t off = t * row_elems + (int64_t)h * D;
         rotate_row(dtype, x, off, y + off, D, cs, sn, dir);
       }
+    }
+  }
+  return 0;
+}
+
+/* R9: the same rotation with cos/sin taken from tables cos_tab / sin_tab
+ * [tab_rows, D/2] (row p = position p) instead of from theta. Positions and
+ * untouched tokens as in oracle_rope_ex; a position >= tab_rows is untouched.
+ * One thread, one token at a time. */
+int32_t oracle_rope_table(int32_t dtype, const void* x, float* y, int64_t T, int32_t H,
+                          int32_t D, const int32_t* cu, int32_t num_seqs, const int32_t* seqused,
+                          const int32_t* seq_offsets, const int32_t* position_ids,
+                          const float* cos_tab, const float* sin_tab, int64_t tab_rows,
+                          int32_t dir) {
+  if (check_args(dtype, H, D) || T < 0 || num_seqs < 0 || tab_rows < 1) return -1;
+  int64_t row_elems = (int64_t)H * D;
+  int32_t half = D / 2;
+  for (int64_t t = 0; t < T; ++t) {
+    int32_t pe = position_of(cu, num_seqs, seqused, seq_offsets, position_ids, t);
+    for (int32_t h = 0; h < H; ++h) {
+      int64_t off = t * row_elems + (int64_t)h * D;
+      if (pe < 0 || pe >= tab_rows)
+        copy_row(dtype, x, off, y + off, D);
+      else
+        rotate_row(dtype, x, off, y + off, D, cos_tab + (int64_t)pe * half,
+                   sin_tab + (int64_t)pe * half, dir);
     }
   }
   return 0;

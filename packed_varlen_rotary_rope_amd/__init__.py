@@ -23,7 +23,8 @@ import os
 import torch
 
 __all__ = [
-    "RopeError", "qk_fwd_", "qk_bwd_", "qk_apply_", "qk_apply_ex_", "qk_fwd_pos_", "qk_bwd_pos_",
+    "RopeError", "qk_fwd_", "qk_bwd_", "qk_apply_", "qk_apply_ex_", "qk_apply_table_",
+    "qk_fwd_pos_", "qk_bwd_pos_",
     "positions", "cos_sin", "inv_freq", "abi_version", "LIB_PATH", "INDEX_AUTO", "INDEX_32",
     "INDEX_64", "glu_fwd", "glu_bwd", "GLU_KINDS",
 ]
@@ -54,6 +55,8 @@ def _load() -> ctypes.CDLL:
     lib.rope_qk_apply.argtypes = qk + [i32, i32, i32, vp]
     lib.rope_qk_apply_ex.argtypes = [vp, vp, i64, i32, i32, i32, i64, i64, vp, i32, vp, vp, vp,
                                      dbl, dbl, i32, i32, i32, i32, vp]
+    lib.rope_qk_apply_table.argtypes = [vp, vp, i64, i32, i32, i32, i64, i64, vp, i32, vp, vp, vp,
+                                        vp, vp, i32, i32, i32, i32, i32, vp]
     lib.rope_qk_fwd_pos.argtypes = [vp, vp, i64, i32, i32, i32, vp, dbl, i32, vp]
     lib.rope_qk_bwd_pos.argtypes = [vp, vp, i64, i32, i32, i32, vp, dbl, i32, vp]
     lib.rope_positions.argtypes = [vp, i32, vp, i64, vp, vp, vp]
@@ -63,7 +66,7 @@ def _load() -> ctypes.CDLL:
     lib.rope_inv_freq.argtypes = [dbl, i32, vp]
     lib.glu_fwd.argtypes = [i32, vp, vp, vp, i64, i64, i64, i64, i32, i32, vp]
     lib.glu_bwd.argtypes = [i32, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, vp]
-    for name in ("rope_qk_fwd", "rope_qk_bwd", "rope_qk_apply", "rope_qk_apply_ex",
+    for name in ("rope_qk_fwd", "rope_qk_bwd", "rope_qk_apply", "rope_qk_apply_ex", "rope_qk_apply_table",
                  "rope_qk_fwd_pos", "rope_qk_bwd_pos", "rope_positions", "rope_positions_ex",
                  "rope_cos_sin", "rope_cos_sin_ex", "rope_inv_freq", "rope_abi_version",
                  "glu_fwd", "glu_bwd"):
@@ -163,6 +166,16 @@ def qk_apply_ex_(q, k, theta: float, direction: int = 1, cu_seqlens=None, sequse
     are contiguous; they must not overlap."""
     T, Hq, Hkv, D = _qk_tensors(q, k, strided=True)
     qs, ks = _token_stride(q, "q"), _token_stride(k, "k")
+    cu, num_seqs, su, so, pid = _position_args(q, T, cu_seqlens, seqused, seq_offsets, position_ids)
+    st = _lib.rope_qk_apply_ex(_ptr(q), _ptr(k), T, Hq, Hkv, D, qs, ks, _ptr(cu), num_seqs,
+                               _ptr(su), _ptr(so), _ptr(pid), float(theta), float(pos_scale),
+                               _DTYPE_CODE[q.dtype], int(direction), int(index_mode),
+                               int(tokens_per_wave), _stream(q.device))
+    _check(st, "rope_qk_apply_ex")
+    return q, k
+
+
+def _position_args(q, T, cu_seqlens, seqused, seq_offsets, position_ids):
     cu = _index_tensor(cu_seqlens, "cu_seqlens", q.device)
     su = _index_tensor(seqused, "seqused", q.device)
     so = _index_tensor(seq_offsets, "seq_offsets", q.device)
@@ -175,11 +188,31 @@ def qk_apply_ex_(q, k, theta: float, direction: int = 1, cu_seqlens=None, sequse
     for name, t in (("seqused", su), ("seq_offsets", so)):
         if t is not None and t.numel() != num_seqs:
             raise ValueError(f"{name} must have one entry per sequence")
-    st = _lib.rope_qk_apply_ex(_ptr(q), _ptr(k), T, Hq, Hkv, D, qs, ks, _ptr(cu), num_seqs,
-                               _ptr(su), _ptr(so), _ptr(pid), float(theta), float(pos_scale),
-                               _DTYPE_CODE[q.dtype], int(direction), int(index_mode),
-                               int(tokens_per_wave), _stream(q.device))
-    _check(st, "rope_qk_apply_ex")
+    return cu, num_seqs, su, so, pid
+
+
+def qk_apply_table_(q, k, cos_tab, sin_tab, direction: int = 1, cu_seqlens=None, seqused=None,
+                    seq_offsets=None, position_ids=None, index_mode: int = INDEX_AUTO,
+                    tokens_per_wave: int = 0):
+    """qk_apply_ex_ with caller-supplied cos/sin tables: `cos_tab` and `sin_tab` are
+    float32 [rows, D/2] device tensors whose row p holds the cos / sin of position p
+    (as `cos_sin(torch.arange(rows), D, theta)` returns them). Tokens whose position
+    has no row are left untouched. In place; returns (q, k)."""
+    T, Hq, Hkv, D = _qk_tensors(q, k, strided=True)
+    qs, ks = _token_stride(q, "q"), _token_stride(k, "k")
+    for name, t in (("cos_tab", cos_tab), ("sin_tab", sin_tab)):
+        if (t.dtype != torch.float32 or t.device != q.device or not t.is_contiguous()
+                or t.dim() != 2 or t.shape[1] != D // 2):
+            raise ValueError(f"{name} must be a contiguous float32 [rows, D/2] tensor on "
+                             f"{q.device}")
+    if cos_tab.shape != sin_tab.shape or cos_tab.shape[0] < 1 or cos_tab.shape[0] > 2 ** 31 - 1:
+        raise ValueError("cos_tab and sin_tab must have the same 1 .. 2^31-1 rows")
+    cu, num_seqs, su, so, pid = _position_args(q, T, cu_seqlens, seqused, seq_offsets, position_ids)
+    st = _lib.rope_qk_apply_table(_ptr(q), _ptr(k), T, Hq, Hkv, D, qs, ks, _ptr(cu), num_seqs,
+                                  _ptr(su), _ptr(so), _ptr(pid), _ptr(cos_tab), _ptr(sin_tab),
+                                  int(cos_tab.shape[0]), _DTYPE_CODE[q.dtype], int(direction),
+                                  int(index_mode), int(tokens_per_wave), _stream(q.device))
+    _check(st, "rope_qk_apply_table")
     return q, k
 
 

@@ -67,6 +67,10 @@ struct RopeParams {
   uint32_t gq, gk;           // row groups of Q and of K per token
   uint32_t nc_shift;         // log2(nc); nc divides 64
   fastdiv::FastDiv groups;   // division by gq + gk
+  // caller-supplied cos/sin tables [tab_rows, D/2] (table kernels only)
+  const float* tab_cos;
+  const float* tab_sin;
+  int32_t tab_rows;
 };
 
 struct CosSinParams {
@@ -276,7 +280,9 @@ __device__ inline T* token_row0(T* p, int64_t t, int64_t stride) {
 }
 
 // ---- the fused QK kernel (a1..a7) ---------------------------------------------------
-template <typename T, int VEC, bool LONG_INDEX>
+// TABLE: cos/sin of position p are row p of the caller's tables (a token whose
+// position has no row is left untouched) instead of being evaluated here.
+template <typename T, int VEC, bool LONG_INDEX, bool TABLE>
 __global__ __launch_bounds__(kBlock) void rope_qk_kernel(T* __restrict__ q, T* __restrict__ k,
                                                          const PosSource ps, const RopeParams p) {
   __shared__ float lds_cs[kWaves][kMaxHalf];
@@ -304,18 +310,27 @@ __global__ __launch_bounds__(kBlock) void rope_qk_kernel(T* __restrict__ q, T* _
     if (t >= p.T) break;
     int32_t seq;
     const int32_t pos = resolve_position(ps, t, &seq);  // wave-uniform
-    if (pos < 0) continue;
-    const float spos = scaled_position(pos, p.pos_scale);
+    if (pos < 0 || (TABLE && pos >= p.tab_rows)) continue;
 
     // a3: this token's fp32 cos/sin table, each (token, frequency) computed once.
+    if constexpr (TABLE) {
+      const float* crow = p.tab_cos + (int64_t)pos * half;
+      const float* srow = p.tab_sin + (int64_t)pos * half;
+      for (uint32_t j = (uint32_t)lane; j < half; j += 64) {
+        lds_cs[wave][j] = crow[j];
+        lds_sn[wave][j] = srow[j] * p.sin_sign;
+      }
+    } else {
+      const float spos = scaled_position(pos, p.pos_scale);
 #pragma unroll
-    for (int i = 0; i < kMaxHalf / 64; ++i) {
-      const uint32_t j = (uint32_t)lane + 64u * i;
-      if (j < half) {
-        float sn, cs;
-        rope_trig::sincos_f32_cr(rope_angle(spos, f[i]), sn, cs);
-        lds_cs[wave][j] = cs;
-        lds_sn[wave][j] = sn * p.sin_sign;  // backward: R transposed = sin negated
+      for (int i = 0; i < kMaxHalf / 64; ++i) {
+        const uint32_t j = (uint32_t)lane + 64u * i;
+        if (j < half) {
+          float sn, cs;
+          rope_trig::sincos_f32_cr(rope_angle(spos, f[i]), sn, cs);
+          lds_cs[wave][j] = cs;
+          lds_sn[wave][j] = sn * p.sin_sign;  // backward: R transposed = sin negated
+        }
       }
     }
     wave_lds_sync();
@@ -356,7 +371,8 @@ __global__ __launch_bounds__(kBlock) void rope_qk_kernel(T* __restrict__ q, T* _
 // memory traffic of others, and each wave's reads and writes stay within 2 KB.
 // The cost is evaluating each (token, frequency) cos/sin once per row group of
 // the token instead of once per token. Requires nc to divide 64.
-template <typename T, int VEC, bool LONG_INDEX>
+// TABLE as in rope_qk_kernel.
+template <typename T, int VEC, bool LONG_INDEX, bool TABLE>
 __global__ __launch_bounds__(64) void rope_qk_group_kernel(T* __restrict__ q, T* __restrict__ k,
                                                            const PosSource ps, const RopeParams p) {
   __shared__ float lds_cs[kMaxHalf];
@@ -400,21 +416,30 @@ __global__ __launch_bounds__(64) void rope_qk_group_kernel(T* __restrict__ q, T*
   __builtin_amdgcn_sched_barrier(0);
   int32_t seq;
   const int32_t pos = resolve_position(ps, (int32_t)t, &seq);  // wave-uniform
-  if (pos < 0) return;
+  if (pos < 0 || (TABLE && pos >= p.tab_rows)) return;
   C lo = load_chunk<T, VEC>(row);
   C hi = load_chunk<T, VEC>(row + half);
   __builtin_amdgcn_sched_barrier(0);
 
   // a3: the token's fp32 cos/sin table
-  const float spos = scaled_position(pos, p.pos_scale);
+  if constexpr (TABLE) {
+    const float* crow = p.tab_cos + (int64_t)pos * half;
+    const float* srow = p.tab_sin + (int64_t)pos * half;
+    for (uint32_t j = (uint32_t)lane; j < half; j += 64) {
+      lds_cs[j] = crow[j];
+      lds_sn[j] = srow[j] * p.sin_sign;
+    }
+  } else {
+    const float spos = scaled_position(pos, p.pos_scale);
 #pragma unroll
-  for (int i = 0; i < kMaxHalf / 64; ++i) {
-    const uint32_t j = (uint32_t)lane + 64u * i;
-    if (j < half) {
-      float sn, cs;
-      rope_trig::sincos_f32_cr(rope_angle(spos, f[i]), sn, cs);
-      lds_cs[j] = cs;
-      lds_sn[j] = sn * p.sin_sign;  // backward: R transposed = sin negated
+    for (int i = 0; i < kMaxHalf / 64; ++i) {
+      const uint32_t j = (uint32_t)lane + 64u * i;
+      if (j < half) {
+        float sn, cs;
+        rope_trig::sincos_f32_cr(rope_angle(spos, f[i]), sn, cs);
+        lds_cs[j] = cs;
+        lds_sn[j] = sn * p.sin_sign;  // backward: R transposed = sin negated
+      }
     }
   }
   wave_lds_sync();
@@ -506,7 +531,7 @@ uint32_t group_dynamic_lds(unsigned group_blocks, uint32_t gq, uint32_t gk) {
   return kLdsPerCU / cap - kGroupStaticLds;
 }
 
-template <typename T, int VEC>
+template <typename T, int VEC, bool TABLE>
 int32_t launch_vec(void* q, void* k, const PosSource& ps, const RopeParams& p, bool long_index,
                    unsigned blocks, unsigned group_blocks, hipStream_t stream) {
   T* qt = static_cast<T*>(q);
@@ -514,20 +539,28 @@ int32_t launch_vec(void* q, void* k, const PosSource& ps, const RopeParams& p, b
   if (group_blocks > 0) {
     const uint32_t lds = group_dynamic_lds(group_blocks, p.gq, p.gk);
     if (long_index)
-      hipLaunchKernelGGL((rope_qk_group_kernel<T, VEC, true>), dim3(group_blocks), dim3(64), lds,
-                         stream, qt, kt, ps, p);
+      hipLaunchKernelGGL((rope_qk_group_kernel<T, VEC, true, TABLE>), dim3(group_blocks), dim3(64),
+                         lds, stream, qt, kt, ps, p);
     else
-      hipLaunchKernelGGL((rope_qk_group_kernel<T, VEC, false>), dim3(group_blocks), dim3(64), lds,
-                         stream, qt, kt, ps, p);
+      hipLaunchKernelGGL((rope_qk_group_kernel<T, VEC, false, TABLE>), dim3(group_blocks), dim3(64),
+                         lds, stream, qt, kt, ps, p);
     return hipGetLastError() == hipSuccess ? ROPE_OK : ROPE_ELAUNCH;
   }
   if (long_index)
-    hipLaunchKernelGGL((rope_qk_kernel<T, VEC, true>), dim3(blocks), dim3(kBlock), 0, stream, qt,
-                       kt, ps, p);
+    hipLaunchKernelGGL((rope_qk_kernel<T, VEC, true, TABLE>), dim3(blocks), dim3(kBlock), 0, stream,
+                       qt, kt, ps, p);
   else
-    hipLaunchKernelGGL((rope_qk_kernel<T, VEC, false>), dim3(blocks), dim3(kBlock), 0, stream, qt,
-                       kt, ps, p);
+    hipLaunchKernelGGL((rope_qk_kernel<T, VEC, false, TABLE>), dim3(blocks), dim3(kBlock), 0, stream,
+                       qt, kt, ps, p);
   return hipGetLastError() == hipSuccess ? ROPE_OK : ROPE_ELAUNCH;
+}
+
+template <typename T, int VEC>
+int32_t launch_vec(void* q, void* k, const PosSource& ps, const RopeParams& p, bool long_index,
+                   unsigned blocks, unsigned group_blocks, hipStream_t stream) {
+  return p.tab_cos != nullptr
+             ? launch_vec<T, VEC, true>(q, k, ps, p, long_index, blocks, group_blocks, stream)
+             : launch_vec<T, VEC, false>(q, k, ps, p, long_index, blocks, group_blocks, stream);
 }
 
 // Tokens per wave when the caller does not choose: one. Short-lived waves, one per
@@ -591,16 +624,24 @@ int32_t launch_typed(void* q, void* k, const PosSource& ps, RopeParams& p, int32
 
 extern "C" {
 
-int32_t rope_qk_apply_ex(void* q, void* k, int64_t T, int32_t Hq, int32_t Hkv, int32_t D,
-                         int64_t q_token_stride, int64_t k_token_stride,
-                         const int32_t* cu_seqlens, int32_t num_seqs, const int32_t* seqused,
-                         const int32_t* seq_offsets, const int32_t* position_ids, double theta,
-                         double pos_scale, int32_t dtype, int32_t direction, int32_t index_mode,
-                         int32_t tokens_per_wave, void* stream) {
+// Shared by rope_qk_apply_ex (cos/sin evaluated from theta and pos_scale) and
+// rope_qk_apply_table (tab_cos != NULL: cos/sin read from the caller's tables;
+// theta and pos_scale unused).
+static int32_t apply_impl(void* q, void* k, int64_t T, int32_t Hq, int32_t Hkv, int32_t D,
+                          int64_t q_token_stride, int64_t k_token_stride,
+                          const int32_t* cu_seqlens, int32_t num_seqs, const int32_t* seqused,
+                          const int32_t* seq_offsets, const int32_t* position_ids, double theta,
+                          double pos_scale, const float* tab_cos, const float* tab_sin,
+                          int32_t tab_rows, int32_t dtype, int32_t direction, int32_t index_mode,
+                          int32_t tokens_per_wave, void* stream) {
+  const bool table = tab_cos != nullptr;
   if (dtype != ROPE_F32 && dtype != ROPE_BF16 && dtype != ROPE_F16) return ROPE_EUNSUPPORTED;
   if (T < 0 || T > ((int64_t)1 << 40)) return ROPE_EINVAL;
   if (Hq < 0 || Hkv < 0 || Hq > kMaxHeads || Hkv > kMaxHeads) return ROPE_EINVAL;
-  if (!valid_D(D) || !valid_theta(theta) || !valid_scale(pos_scale)) return ROPE_EINVAL;
+  if (!valid_D(D)) return ROPE_EINVAL;
+  if (table ? (tab_sin == nullptr || tab_rows < 1)
+            : (!valid_theta(theta) || !valid_scale(pos_scale)))
+    return ROPE_EINVAL;
   if (num_seqs < 0 || num_seqs == INT32_MAX) return ROPE_EINVAL;
   if (direction != 1 && direction != -1) return ROPE_EINVAL;
   if (index_mode < ROPE_INDEX_AUTO || index_mode > ROPE_INDEX_64) return ROPE_EINVAL;
@@ -638,8 +679,16 @@ int32_t rope_qk_apply_ex(void* q, void* k, int64_t T, int32_t Hq, int32_t Hkv, i
   p.k_stride = ks;
   p.tpw = tokens_per_wave == 0 ? 1 : tokens_per_wave;  // 0: launch_typed picks the geometry
   p.sin_sign = direction > 0 ? 1.0f : -1.0f;
-  p.pos_scale = (float)pos_scale;
-  host_inv_freq(theta, D, p.inv_freq);
+  p.tab_cos = table ? tab_cos : nullptr;
+  p.tab_sin = table ? tab_sin : nullptr;
+  p.tab_rows = table ? tab_rows : 0;
+  if (table) {
+    p.pos_scale = 1.0f;
+    for (int32_t j = 0; j < kMaxHalf; ++j) p.inv_freq[j] = 0.0f;  // unused
+  } else {
+    p.pos_scale = (float)pos_scale;
+    host_inv_freq(theta, D, p.inv_freq);
+  }
 
   PosSource ps;
   ps.position_ids = position_ids;
@@ -658,6 +707,31 @@ int32_t rope_qk_apply_ex(void* q, void* k, int64_t T, int32_t Hq, int32_t Hkv, i
     case ROPE_BF16: return launch_typed<__bf16>(qp, kp, ps, p, bytes, long_index, chosen, s);
     default: return launch_typed<_Float16>(qp, kp, ps, p, bytes, long_index, chosen, s);
   }
+}
+
+int32_t rope_qk_apply_ex(void* q, void* k, int64_t T, int32_t Hq, int32_t Hkv, int32_t D,
+                         int64_t q_token_stride, int64_t k_token_stride,
+                         const int32_t* cu_seqlens, int32_t num_seqs, const int32_t* seqused,
+                         const int32_t* seq_offsets, const int32_t* position_ids, double theta,
+                         double pos_scale, int32_t dtype, int32_t direction, int32_t index_mode,
+                         int32_t tokens_per_wave, void* stream) {
+  return apply_impl(q, k, T, Hq, Hkv, D, q_token_stride, k_token_stride, cu_seqlens, num_seqs,
+                    seqused, seq_offsets, position_ids, theta, pos_scale, nullptr, nullptr, 0,
+                    dtype, direction, index_mode, tokens_per_wave, stream);
+}
+
+int32_t rope_qk_apply_table(void* q, void* k, int64_t T, int32_t Hq, int32_t Hkv, int32_t D,
+                            int64_t q_token_stride, int64_t k_token_stride,
+                            const int32_t* cu_seqlens, int32_t num_seqs, const int32_t* seqused,
+                            const int32_t* seq_offsets, const int32_t* position_ids,
+                            const float* cos_tab, const float* sin_tab, int32_t tab_rows,
+                            int32_t dtype, int32_t direction, int32_t index_mode,
+                            int32_t tokens_per_wave, void* stream) {
+  if (dtype != ROPE_F32 && dtype != ROPE_BF16 && dtype != ROPE_F16) return ROPE_EUNSUPPORTED;
+  if (cos_tab == nullptr || sin_tab == nullptr || tab_rows < 1) return ROPE_EINVAL;
+  return apply_impl(q, k, T, Hq, Hkv, D, q_token_stride, k_token_stride, cu_seqlens, num_seqs,
+                    seqused, seq_offsets, position_ids, 1.0, 1.0, cos_tab, sin_tab, tab_rows,
+                    dtype, direction, index_mode, tokens_per_wave, stream);
 }
 
 int32_t rope_qk_apply(void* q, void* k, int64_t T, int32_t Hq, int32_t Hkv, int32_t D,

@@ -429,6 +429,75 @@ def check_pos_scale_mpmath(o):
                 assert s[i, j] == rn_f32(mpmath.sin(a)), (factor, p, j)
 
 
+# ------------------------------------------------------- caller-supplied cos/sin tables
+
+def check_table_block_matrix_R(o):
+    """With arbitrary tables (not cos/sin of anything, not on the unit circle), the
+    table rotation is x*C + (x @ R)*S with R, R^T from the page's block form, each
+    token using the table row of its position; positions without a row, and tokens
+    outside every sequence, are untouched."""
+    mats = load_golden_matrices()
+    rng = np.random.default_rng(31)
+    for D in (4, 6):
+        R, RT = mats[("R", D)], mats[("RT", D)]
+        T, H, rows = 14, 2, 5
+        x = rng.standard_normal((T, H, D)).astype(np.float32)
+        cu = np.array([1, 4, 12], dtype=np.int32)   # token 0 and 12, 13 outside
+        pos = [-1, 0, 1, 2, 0, 1, 2, 3, 4, 5, 6, 7, -1, -1]  # rows 5.. do not exist
+        ct = rng.uniform(-1.5, 1.5, (rows, D // 2)).astype(np.float32)
+        st = rng.uniform(-1.5, 1.5, (rows, D // 2)).astype(np.float32)
+        xd = x.astype(np.float64)
+        for direction, M in ((1, R), (-1, RT)):
+            got = o.rope_table(x, cu, ct, st, direction)
+            for t in range(T):
+                p = pos[t]
+                if p < 0 or p >= rows:
+                    assert np.array_equal(got[t].view(np.uint32), x[t].view(np.uint32)), t
+                    continue
+                C, S = full_cos_sin(ct[p:p + 1].astype(np.float64), st[p:p + 1].astype(np.float64))
+                # rotate_half's sign lives in R / R^T: S stays the table's sin both ways
+                ref = (xd[t] * C[0] + (xd[t] @ M) * S[0]).astype(np.float32)
+                assert np.array_equal(got[t].view(np.uint32), ref.view(np.uint32)), (D, direction, t)
+
+
+def check_table_equals_theta(o):
+    """Tables holding the oracle's own cos/sin of positions 0..rows-1 reproduce the
+    theta path bit for bit (packed with seqused, per-sequence offsets, explicit ids)."""
+    rng = np.random.default_rng(32)
+    D, H, theta = 16, 3, 1e6
+    cu = np.array([0, 5, 5, 17, 30], dtype=np.int32)
+    su = np.array([4, 0, 12, 9], dtype=np.int32)
+    so = np.array([3, 0, 100, 7], dtype=np.int32)
+    T = 32
+    pid = rng.integers(-2, 120, T).astype(np.int32)
+    rows = 130
+    ct, st = o.cos_sin(np.arange(rows), D, theta)
+    x = random_bf16(rng, (T, H, D))
+    for direction in (1, -1):
+        for kw in (dict(seqused=su), dict(seq_offsets=so), dict(position_ids=pid)):
+            ref = o.rope(x, cu, theta, direction, "bf16", **kw)
+            got = o.rope_table(x, cu, ct, st, direction, "bf16", **kw)
+            assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), (direction, kw)
+
+
+def check_table_hand_values(o):
+    """cos = 1, sin = 0 is the identity; cos = 0, sin = 1 is rotate_half exactly:
+    forward [x1, x2] -> [-x2, x1], backward -> [x2, -x1]."""
+    rng = np.random.default_rng(33)
+    D, T = 8, 3
+    x = rng.standard_normal((T, 1, D)).astype(np.float32)
+    one, zero = np.ones((1, D // 2), np.float32), np.zeros((1, D // 2), np.float32)
+    cu = [0, T]
+    pid = np.zeros(T, dtype=np.int32)
+    ident = o.rope_table(x, cu, one, zero, 1, position_ids=pid)
+    assert np.array_equal(ident, x)
+    x1, x2 = x[..., : D // 2], x[..., D // 2:]
+    fwd = o.rope_table(x, cu, zero, one, 1, position_ids=pid)
+    bwd = o.rope_table(x, cu, zero, one, -1, position_ids=pid)
+    assert np.array_equal(fwd, np.concatenate([-x2, x1], axis=-1))
+    assert np.array_equal(bwd, np.concatenate([x2, -x1], axis=-1))
+
+
 ALL_CHECKS = [
     check_inv_freq_closed_form,
     check_inv_freq_mpmath,
@@ -453,4 +522,7 @@ ALL_CHECKS = [
     check_seq_offsets_shard_invariant,
     check_pos_scale_page_example,
     check_pos_scale_mpmath,
+    check_table_block_matrix_R,
+    check_table_equals_theta,
+    check_table_hand_values,
 ]

@@ -50,7 +50,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert rope.abi_version() == 2
+    assert rope.abi_version() == 3
     lib = rope._lib
     for st in (0, -1, -2, -3):
         assert lib.rope_status_str(st).decode().startswith("ROPE_")
@@ -134,6 +134,40 @@ def apply_ex(**kw):
 ])
 def test_validation_ex(kw, expect):
     assert apply_ex(**kw) == expect
+
+
+def apply_table(**kw):
+    a = dict(q=FAKE, k=FAKE, T=16, Hq=4, Hkv=2, D=128, qs=0, ks=0, cu=FAKE, num_seqs=2,
+             seqused=None, offsets=None, ids=None, ct=FAKE, st=FAKE, rows=8, dtype=1,
+             direction=1, index_mode=0, tpw=0, stream=None)
+    a.update(kw)
+    return rope._lib.rope_qk_apply_table(a["q"], a["k"], a["T"], a["Hq"], a["Hkv"], a["D"],
+                                         a["qs"], a["ks"], a["cu"], a["num_seqs"], a["seqused"],
+                                         a["offsets"], a["ids"], a["ct"], a["st"], a["rows"],
+                                         a["dtype"], a["direction"], a["index_mode"], a["tpw"],
+                                         a["stream"])
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(ct=None), EINVAL),
+    (dict(st=None), EINVAL),
+    (dict(ct=None, st=None, T=0, q=None, k=None), EINVAL),  # tables are always required
+    (dict(rows=0), EINVAL),
+    (dict(rows=-5), EINVAL),
+    (dict(dtype=5), EUNSUPPORTED),
+    (dict(dtype=5, ct=None), EUNSUPPORTED),
+    (dict(D=130 + 1), EINVAL),
+    (dict(direction=0), EINVAL),
+    (dict(cu=None, ids=None), EINVAL),
+    (dict(q=None), EINVAL),
+    (dict(qs=4 * 128 - 1), EINVAL),
+    (dict(T=0, q=None, k=None, cu=None), OK),
+    (dict(num_seqs=0, cu=None), OK),
+])
+def test_validation_table(kw, expect):
+    """The table entry point validates like rope_qk_apply_ex, plus its tables; it has
+    no theta or scale to check."""
+    assert apply_table(**kw) == expect
 
 
 def test_fwd_bwd_positions_cos_sin_validation():

@@ -561,3 +561,83 @@ def test_stride_forces_64bit_offsets(rope):
     assert torch.count_nonzero(buf[:, D:stride - D]).item() == 0
     del buf
     torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------- cos/sin tables
+
+@pytest.mark.parametrize("name", ["qwen3_4b_packed", "qwen3_8b_padded"])
+def test_table_equals_theta_path(rope, name):
+    """Tables written by the library's cos/sin export (bit-exact with the oracle's)
+    make the table path bit-identical to the theta path: the row-group kernel on the
+    packed batch, the token kernel on the padded layout; forward and backward."""
+    w = workloads.get(name)
+    print(f"[table] {name} theta-table identity", flush=True)
+    host = make_host(w)
+    cu = torch.from_numpy(w.cu_seqlens).to(DEV)
+    su = None if w.seqused is None else torch.from_numpy(w.seqused).to(DEV)
+    rows = int(max(w.lengths))
+    ct, st = rope.cos_sin(torch.arange(rows, dtype=torch.int32, device=DEV), w.D, w.theta)
+    a = {what: t.to(DEV) for what, t in host.items()}
+    b = {what: t.to(DEV) for what, t in host.items()}
+    rope.qk_fwd_(a["q"], a["k"], cu, w.theta, seqused=su)
+    rope.qk_bwd_(a["dq"], a["dk"], cu, w.theta, seqused=su)
+    rope.qk_apply_table_(b["q"], b["k"], ct, st, 1, cu_seqlens=cu, seqused=su)
+    rope.qk_apply_table_(b["dq"], b["dk"], ct, st, -1, cu_seqlens=cu, seqused=su)
+    torch.cuda.synchronize()
+    for what in a:
+        wd = _word(a[what].dtype)
+        assert torch.equal(a[what].view(wd), b[what].view(wd)), f"{name}:{what}"
+
+
+TABLE_CASES = [
+    ("f32", 16, 4, 2, 0, "cu"),
+    ("bf16", 128, 8, 2, 0, "cu"),
+    ("bf16", 128, 8, 2, 3, "cu"),
+    ("f16", 64, 3, 5, 1, "offsets"),
+    ("bf16", 80, 2, 1, 0, "ids"),       # 5 chunks per half row: the general lane layout
+    ("f32", 128, 5, 0, 0, "ids"),       # Q only
+]
+
+
+@pytest.mark.parametrize("dtype,D,Hq,Hkv,tpw,mode", TABLE_CASES)
+def test_table_random_vs_oracle(rope, dtype, D, Hq, Hkv, tpw, mode):
+    """Arbitrary tables (uniform in [-1.5, 1.5], not cos/sin of anything) against the
+    oracle's table rotation. The table has fewer rows than the longest sequence, so
+    the tokens whose position has no row must come back untouched, as must the tokens
+    outside every sequence."""
+    print(f"[table] random {dtype} D={D} Hq={Hq} Hkv={Hkv} tpw={tpw} {mode}", flush=True)
+    rng = np.random.default_rng(D * 7 + Hq)
+    cu_np = np.array([0, 5, 22, 25, 64, 64, 300], dtype=np.int32)
+    T, rows = 310, 150
+    ct = rng.uniform(-1.5, 1.5, (rows, D // 2)).astype(np.float32)
+    st = rng.uniform(-1.5, 1.5, (rows, D // 2)).astype(np.float32)
+    so_np = np.array([3, 0, 140, 9, 0, 2], dtype=np.int32) if mode == "offsets" else None
+    pid_np = rng.integers(-3, rows + 40, T).astype(np.int32) if mode == "ids" else None
+    shapes = {"q": (T, Hq, D), "k": (T, Hkv, D), "dq": (T, Hq, D), "dk": (T, Hkv, D)}
+    host = {what: workloads.make_tensor(shp, 900 + i, dtype)
+            for i, (what, shp) in enumerate(shapes.items())}
+    dev, flats = {}, {}
+    for what, t in host.items():
+        dev[what], flats[what], g = guarded(t)
+    kw = dict(cu_seqlens=torch.from_numpy(cu_np).to(DEV), tokens_per_wave=tpw,
+              seq_offsets=None if so_np is None else torch.from_numpy(so_np).to(DEV),
+              position_ids=None if pid_np is None else torch.from_numpy(pid_np).to(DEV))
+    if mode == "ids":
+        kw["cu_seqlens"] = None
+    ctd, std = torch.from_numpy(ct).to(DEV), torch.from_numpy(st).to(DEV)
+    rope.qk_apply_table_(dev["q"], dev["k"], ctd, std, 1, **kw)
+    rope.qk_apply_table_(dev["dq"], dev["dk"], ctd, std, -1, **kw)
+    torch.cuda.synchronize()
+    cu_o = None if mode == "ids" else cu_np
+    pos, _ = oracle.positions(cu_np if cu_o is not None else None, T, None, seq_offsets=so_np,
+                              position_ids=pid_np)
+    touched = (pos >= 0) & (pos < rows)
+    assert touched.any() and (~touched).any()
+    for what, direction in (("q", 1), ("k", 1), ("dq", -1), ("dk", -1)):
+        if host[what].numel() == 0:
+            continue
+        x = bits(host[what])
+        ref = oracle.rope_table(x, cu_o, ct, st, direction, dtype, seq_offsets=so_np,
+                                position_ids=pid_np)
+        assert_parity(dtype, bits(dev[what]), ref, x, touched, f"table:{what}")
+        assert guards_intact(flats[what], g), f"table:{what}: guard region written"
