@@ -259,6 +259,29 @@ def test_variants_bit_identical(rope, name):
         assert torch.equal(k, k_ref), kw
 
 
+@pytest.mark.parametrize("name", ["qwen3_8b_packed", "qwen3_8b_padded", "qwen3_32b_packed"])
+def test_int64_forced_bit_identical(rope, name):
+    """The 64-bit offset specialization forced on the workloads that select 32-bit
+    offsets by default (the packed and padded comparison batches and the Qwen3-32B
+    shape) gives the same bits, forward and backward."""
+    w = workloads.get(name)
+    cu = torch.from_numpy(w.cu_seqlens).to(DEV)
+    su = None if w.seqused is None else torch.from_numpy(w.seqused).to(DEV)
+    word = torch.int16 if w.dtype != "f32" else torch.int32
+    for direction, (a, b) in ((1, ("q", "k")), (-1, ("dq", "dk"))):
+        print(f"[parity] {name} forced int64, direction {direction}", flush=True)
+        x0 = workloads.make_tensor(w.shape(a), w.seed(a), w.dtype).to(DEV)
+        y0 = workloads.make_tensor(w.shape(b), w.seed(b), w.dtype).to(DEV)
+        xr, yr = x0.clone(), y0.clone()
+        rope.qk_apply_(xr, yr, cu, w.theta, direction, seqused=su)
+        x, y = x0.clone(), y0.clone()
+        rope.qk_apply_(x, y, cu, w.theta, direction, seqused=su, index_mode=rope.INDEX_64)
+        torch.cuda.synchronize()
+        assert torch.equal(x.view(word), xr.view(word)), (name, direction, a)
+        assert torch.equal(y.view(word), yr.view(word)), (name, direction, b)
+        assert not torch.equal(xr.view(word), x0.view(word))  # the launch did rotate
+
+
 # ---------------------------------------------------------------- edge cases
 
 EDGE = [
