@@ -14,23 +14,25 @@
 //            group of heads.
 //
 // Work decomposition (memory-bound: one read and one write of every Q/K element,
-// no MFMA). A wave owns one token at a time (a contiguous run of tpw tokens);
-// its 64 lanes cover (head row, chunk) pairs of that token, where a chunk is
-// VEC consecutive elements of the first half of a head row (16 bytes: VEC = 8
-// for bf16/f16, 4 for fp32) together with the matching VEC elements of the
-// second half, D/2 further on. For D = 128 in bf16 that is 8 rows x 8 chunks per
-// wave step, so each load instruction covers 2 KB of one token's rows. Per token:
-//   1. the wave maps the token to (sequence, position) with a wave-uniform
-//      binary search over cu_seqlens [U-Pack];
-//   2. each lane computes the correctly rounded fp32 cos/sin of one frequency
-//      (D/2 <= 64) or a few, into a per-wave LDS table: every (token, frequency)
-//      pair is evaluated exactly once in the whole launch;
-//   3. the wave walks the token's Q rows, then its K rows, 64/nc rows per step
-//      [U-Group]; each lane loads its two chunks, reads its cos/sin from the
-//      table, rotates in fp32, rounds to the storage dtype, stores in place.
-// The lane that reads a pair (j, j + D/2) is the one that writes it, so the
-// in-place update needs no synchronization between lanes. Loads and stores are
-// non-temporal: the data is streamed once and never reused.
+// no MFMA). A chunk is VEC consecutive elements of the first half of a head row
+// (16 bytes: VEC = 8 for bf16/f16, 4 for fp32) together with the matching VEC
+// elements of the second half, D/2 further on; the lane that loads a chunk pair
+// rotates it and stores it back, so the in-place update needs no synchronization
+// between lanes. Loads and stores are non-temporal: the data is streamed once.
+// Two kernels, one launch per pass either way:
+//  * rope_qk_group_kernel (the default): one 64-lane workgroup per (token, group
+//    of 64/nc head rows), Q's groups then K's; for D = 128 in bf16 a group is 8
+//    rows = 2 KB, one chunk pair per lane. The wave maps its token to (sequence,
+//    position) with a wave-uniform binary search over cu_seqlens [U-Pack],
+//    issues its row loads, evaluates the token's correctly rounded fp32 cos/sin
+//    (one frequency per lane) into a wave-local LDS table while the loads are in
+//    flight, rotates in fp32 and stores.
+//  * rope_qk_kernel: a 64-lane wave walks whole tokens (tokens_per_wave of them),
+//    evaluating each token's cos/sin once and rotating its Q rows then its K rows
+//    [U-Group]; used for padded layouts (seqused), head sizes whose chunk count
+//    does not divide 64, and when the caller chooses tokens per wave.
+// Both take cos/sin from caller-supplied tables instead (TABLE instances) for
+// rope_qk_apply_table.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
