@@ -1,0 +1,125 @@
+"""Host logic of bench.py, on the CPU: the algorithmic byte count, the kernel the
+library picks, and the profile summaries built from rocprofv3 CSV files (small
+synthetic files here; the summaries are written to a temporary folder)."""
+import csv
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+import bench
+import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GROUP = "_ZN12_GLOBAL__N_120rope_qk_group_kernelIDF16bLi8ELb0ELb0EEEvPT_S2_"
+COPY = "__amd_rocclr_copyBuffer"
+
+
+def _counter_csv(path, rows):
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w", newline="") as fh:
+        wr = csv.DictWriter(fh, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+        wr.writeheader()
+        for kernel, counter, value in rows:
+            wr.writerow({"Kernel_Name": kernel, "Counter_Name": counter, "Counter_Value": value})
+
+
+def _trace_csv(path, durations_ns, kernel=GROUP):
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    fields = ["Kernel_Name", "Start_Timestamp", "End_Timestamp", "Grid_Size_X",
+              "Workgroup_Size_X", "VGPR_Count", "LDS_Block_Size"]
+    with open(path, "w", newline="") as fh:
+        wr = csv.DictWriter(fh, fieldnames=fields)
+        wr.writeheader()
+        t = 1000
+        for d in durations_ns:
+            wr.writerow({"Kernel_Name": kernel, "Start_Timestamp": t, "End_Timestamp": t + d,
+                         "Grid_Size_X": 5242880, "Workgroup_Size_X": 64, "VGPR_Count": 24,
+                         "LDS_Block_Size": 2048})
+            wr.writerow({"Kernel_Name": COPY, "Start_Timestamp": t, "End_Timestamp": t + 7,
+                         "Grid_Size_X": 64, "Workgroup_Size_X": 64, "VGPR_Count": 8,
+                         "LDS_Block_Size": 0})
+            t += d + 100
+
+
+def test_algorithmic_bytes():
+    w = workloads.get("qwen3_4b_packed")
+    assert bench.algorithmic_bytes_per_launch(w) == 2 * 16384 * (32 + 8) * 128 * 2 == 335544320
+    p = workloads.get("qwen3_8b_padded")  # only the valid tokens count
+    assert bench.algorithmic_bytes_per_launch(p) == 2 * p.valid_tokens * 40 * 128 * 2
+    assert p.valid_tokens < p.T
+
+
+def test_kernel_choice():
+    assert bench.rope_kernel_name(workloads.get("qwen3_4b_packed"), 0) == "rope_qk_group_kernel"
+    assert bench.rope_kernel_name(workloads.get("qwen3_4b_packed"), 1) == "rope_qk_kernel"
+    assert bench.rope_kernel_name(workloads.get("qwen3_8b_padded"), 0) == "rope_qk_kernel"
+
+
+def test_traffic_summary_and_hash_check(tmp_path, monkeypatch):
+    out = tmp_path / "traffic.txt"
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(out))
+    kib = 1024.0
+    # the copy reads 1 GiB and writes 1 GiB; its counters read half and all of that
+    _counter_csv(str(tmp_path / "cf.csv"), [(COPY, "FETCH_SIZE", 2 ** 30 / kib / 2)])
+    _counter_csv(str(tmp_path / "cw.csv"), [(COPY, "WRITE_SIZE", 2 ** 30 / kib)])
+    half = 335544320 / 2 / kib
+    _counter_csv(str(tmp_path / "f.csv"), [(GROUP, "FETCH_SIZE", half / 2)] * 3)
+    _counter_csv(str(tmp_path / "w.csv"), [(GROUP, "WRITE_SIZE", half)] * 3)
+    bench.write_traffic_summary(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"),
+                                str(tmp_path / "cf.csv"), str(tmp_path / "cw.csv"), "cmd")
+    text = out.read_text()
+    assert "fetch_scale: 2.00000" in text and "write_scale: 1.00000" in text
+    assert "traffic_over_algorithmic: 1.0000" in text
+    assert bench.read_traffic(str(out)) == 335544320
+    # a summary taken on other kernel sources is not used
+    out.write_text(text.replace(bench.kernel_source_hash(bench.ROPE_SOURCES), "0" * 16))
+    assert bench.read_traffic(str(out)) is None
+
+
+def test_trace_summary(tmp_path, monkeypatch):
+    out = tmp_path / "trace.txt"
+    monkeypatch.setattr(bench, "trace_summary_path", lambda workload: str(out))
+    durations = [50000, 52000, 54000, 60000]
+    _trace_csv(str(tmp_path / "t.csv"), durations)
+    bench.write_trace_summary(str(tmp_path / "t.csv"), "qwen3_4b_packed", "cmd")
+    text = out.read_text()
+    assert "dispatches: 4" in text
+    mean = float(np.mean(durations)) / 1e3
+    gbps = 335544320 / (mean * 1e-6) / 1e9
+    assert f"average: {mean:.2f} us -> {gbps:.0f} GB/s" in text
+    assert "minimum: 50.00 us" in text and "maximum: 60.00 us" in text
+    assert "static LDS only" in text
+
+
+def test_counters_summary(tmp_path, monkeypatch):
+    out = tmp_path / "counters.txt"
+    monkeypatch.setattr(bench, "COUNTERS_FILE", str(out))
+    kib = 1024.0
+    _counter_csv(str(tmp_path / "cf.csv"), [(COPY, "FETCH_SIZE", 2 ** 30 / kib / 2)])
+    _counter_csv(str(tmp_path / "cw.csv"), [(COPY, "WRITE_SIZE", 2 ** 30 / kib)])
+    base = {"SQ_WAVES": 1000, "SQ_INSTS_VALU": 200000, "SQ_INSTS_VALU_FMA_F64": 19000,
+            "SQ_INSTS_SALU": 1, "SQ_INSTS_SMEM": 1, "SQ_INSTS_LDS": 5000, "SQ_INSTS_VMEM_RD": 6000,
+            "SQ_INSTS_VMEM_WR": 2000, "SQ_LDS_BANK_CONFLICT": 0, "SQ_ACTIVE_INST_VALU": 256000,
+            "GRBM_GUI_ACTIVE": 8000, "SQ_WAVE_CYCLES": 1000, "SQ_WAIT_INST_ANY": 1,
+            "FETCH_SIZE": 100, "WRITE_SIZE": 100}
+    for mode, valu in (("fly", 256000), ("table", 128000)):
+        vals = dict(base, SQ_ACTIVE_INST_VALU=valu)
+        _counter_csv(str(tmp_path / mode / "pmc1" / "bench_counter_collection.csv"),
+                     [(GROUP, k, v) for k, v in vals.items()] * 2)
+        _trace_csv(str(tmp_path / mode / "trace" / "bench_kernel_trace.csv"), [50000])
+    bench.write_counters_summary(str(tmp_path / "fly"), str(tmp_path / "table"),
+                                 str(tmp_path / "cf.csv"), str(tmp_path / "cw.csv"), "cmd")
+    line = [ln for ln in out.read_text().splitlines() if ln.startswith("VALU busy")][0]
+    # 4 cycles x 256000 instructions over 1024 SIMDs x (8000 / 8) cycles = 100%
+    assert line.split()[-3:] == ["100.0", "50.0", "x0.500"]
+    fetch = [ln for ln in out.read_text().splitlines() if ln.startswith("HBM read")][0]
+    assert "2.048e+05" in fetch  # 100 KiB x scale 2
+
+
+def test_refuses_more_than_one_gpu():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True)
+    assert r.returncode == 2 and "one GPU only" in r.stderr
