@@ -454,6 +454,7 @@ def cpu_baseline(w, budget_s: float, nthreads: int):
 
     reps, total = _timed_reps(one(nthreads), budget_s, 10000)
     reps1, total1 = _timed_reps(one(1), budget_s / 4, 10000)
+    step_bytes = 2 * algorithmic_bytes_per_launch(w)  # the GPU's byte count for fwd + bwd
     return {
         "value": w.valid_tokens * reps / total,
         "unit": "tokens/s",
@@ -461,7 +462,10 @@ def cpu_baseline(w, budget_s: float, nthreads: int):
         "kind": "oracle",
         "sample": f"{reps} full fwd+bwd passes over the {w.name} batch "
                   f"({w.valid_tokens} tokens, Q/K/dQ/dK), {total:.1f} s timed",
+        "seconds_per_pass_pair": total / reps,
+        "GBps": step_bytes * reps / total / 1e9,
         "value_1_core": w.valid_tokens * reps1 / total1,
+        "GBps_1_core": step_bytes * reps1 / total1 / 1e9,
         "cpu_model": cpu_model(),
     }
 
