@@ -5,6 +5,7 @@ Every pass is one launch of the library's kernels on the current stream; this
 module only wires them into torch.autograd (no arithmetic of its own).
 
     q, k = rope_qk(q, k, cu_seqlens, theta)        # in place, returns q and k
+    q, k = rope_qk_table(q, k, cos_tab, sin_tab, cu_seqlens)  # cos/sin from tables
     h = glu("swiglu", e, g)                        # h = silu(e) * g
     h = glu_fused("geglu", gate_up)                # e, g = halves of gate_up
 
@@ -21,7 +22,7 @@ from __future__ import annotations
 
 import torch
 
-from . import glu_bwd, glu_fwd, qk_apply_ex_
+from . import glu_bwd, glu_fwd, qk_apply_ex_, qk_apply_table_
 
 
 class _RopeQK(torch.autograd.Function):
@@ -57,6 +58,40 @@ def rope_qk(q: torch.Tensor, k: torch.Tensor, cu_seqlens=None, theta: float = 10
     in ``qk_apply_ex_``. Returns (q, k), rotated."""
     return _RopeQK.apply(q, k, cu_seqlens, float(theta), seqused, position_ids, seq_offsets,
                          float(pos_scale), bool(inplace_backward))
+
+
+class _RopeQKTable(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, cos_tab, sin_tab, cu_seqlens, seqused, position_ids, seq_offsets,
+                inplace_backward):
+        qk_apply_table_(q, k, cos_tab, sin_tab, 1, cu_seqlens=cu_seqlens, seqused=seqused,
+                        seq_offsets=seq_offsets, position_ids=position_ids)
+        ctx.mark_dirty(q, k)
+        ctx.save_for_backward(cos_tab, sin_tab, cu_seqlens, seqused, position_ids, seq_offsets)
+        ctx.inplace = inplace_backward
+        return q, k
+
+    @staticmethod
+    def backward(ctx, dq, dk):
+        ct, st, cu, su, pid, so = ctx.saved_tensors
+        if not (ctx.inplace and dq.is_contiguous()):
+            dq = dq.clone(memory_format=torch.contiguous_format)
+        if not (ctx.inplace and dk.is_contiguous()):
+            dk = dk.clone(memory_format=torch.contiguous_format)
+        qk_apply_table_(dq, dk, ct, st, -1, cu_seqlens=cu, seqused=su, seq_offsets=so,
+                        position_ids=pid)
+        return dq, dk, None, None, None, None, None, None, None
+
+
+def rope_qk_table(q: torch.Tensor, k: torch.Tensor, cos_tab: torch.Tensor, sin_tab: torch.Tensor,
+                  cu_seqlens=None, seqused=None, position_ids=None, seq_offsets=None,
+                  inplace_backward: bool = False):
+    """rope_qk with cos/sin read from float32 [rows, D/2] tables (row p = position p,
+    as ``qk_apply_table_`` takes them) instead of computed from theta. The tables are
+    constants: they receive no gradient. Tokens whose position has no row pass
+    through unchanged, and so do their gradients."""
+    return _RopeQKTable.apply(q, k, cos_tab, sin_tab, cu_seqlens, seqused, position_ids,
+                              seq_offsets, bool(inplace_backward))
 
 
 class _Glu(torch.autograd.Function):

@@ -68,6 +68,35 @@ def test_rope_autograd_matches_direct_launches(lib, inplace_backward):
     assert int(np.abs(ordered(got) - ordered(want)).max()) <= 1
 
 
+@pytest.mark.parametrize("inplace_backward", [False, True])
+def test_rope_table_autograd_matches_theta_path(lib, inplace_backward):
+    """rope_qk_table with the library's own cos/sin tables gives the outputs and the
+    input gradients of rope_qk, bit for bit; the tables get no gradient."""
+    rope, F = lib
+    w = workloads.get("qwen3_8b_packed")
+    print(f"[autograd] rope_qk_table inplace_backward={inplace_backward}", flush=True)
+    cu = torch.from_numpy(w.cu_seqlens).to(DEV)
+    ct, st = rope.cos_sin(torch.arange(int(max(w.lengths)), dtype=torch.int32, device=DEV), w.D,
+                          w.theta)
+    wq = workloads.make_tensor(w.shape("q"), 43, "bf16", device=DEV)
+    wk = workloads.make_tensor(w.shape("k"), 44, "bf16", device=DEV)
+    outs = []
+    for use_table in (False, True):
+        q0 = workloads.make_tensor(w.shape("q"), 41, "bf16", device=DEV).requires_grad_()
+        k0 = workloads.make_tensor(w.shape("k"), 42, "bf16", device=DEV).requires_grad_()
+        q, k = q0 * 1, k0 * 1
+        if use_table:
+            qr, kr = F.rope_qk_table(q, k, ct, st, cu, inplace_backward=inplace_backward)
+        else:
+            qr, kr = F.rope_qk(q, k, cu, w.theta, inplace_backward=inplace_backward)
+        ((qr.float() * wq.float()).sum() + (kr.float() * wk.float()).sum()).backward()
+        torch.cuda.synchronize()
+        outs.append([bits16(t) for t in (qr, kr, q0.grad, k0.grad)])
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)
+    assert ct.grad is None and st.grad is None
+
+
 def test_rope_autograd_shared_gradient_is_not_clobbered(lib):
     """out = rope(q) + x: autograd hands the same gradient tensor to both operands;
     the default backward must leave x's gradient unrotated."""
