@@ -662,6 +662,7 @@ def bench_glu(args) -> None:
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.dtype,
+        "arithmetic": f"{w.dtype} storage; activation and products in fp32",
         "data": "synthetic (seeded N(0,1) e, g, dh)",
         "config": {"workload": w.name, "rows": w.rows, "cols": w.cols, "kind": kind,
                    "buffer_sets": nsets, "index": args.index},
@@ -916,6 +917,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.dtype,
+        "arithmetic": f"{w.dtype} storage; rotation in fp32 (FMA-compensated), cos/sin "
+                      "correctly rounded to fp32 from fp64 arithmetic",
         "data": "synthetic (seeded N(0,1) Q/K/dQ/dK, seeded length draws)",
         "config": {
             "workload": w.name,
