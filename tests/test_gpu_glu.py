@@ -272,7 +272,8 @@ def test_empty(rope):
 def test_long_context_int64(rope):
     """524288 tokens x 9728 (5.1e9 elements, 2.4 x 2^31): the 64-bit path. SwiGLU
     forward and in-place backward; rows at the start, around the 2^31-element
-    boundary and at the end against the oracle."""
+    boundary, at the end, and every 97th row (a prime stride, so the sampled rows'
+    offsets take every residue of the power-of-two tile sizes) against the oracle."""
     w = workloads.glu_get("glu_long_512k")
     print("[glu parity] glu_long_512k int64 path", flush=True)
     assert w.elements >= 2 ** 31
@@ -283,7 +284,7 @@ def test_long_context_int64(rope):
         rope.glu_fwd("swiglu", e, g, out=h, index_mode=rope.INDEX_32)
     boundary_row = (2 ** 31) // w.cols
     rows = np.unique(np.concatenate([np.arange(0, 4), np.arange(boundary_row - 2, boundary_row + 3),
-                                     np.arange(w.rows - 4, w.rows)]))
+                                     np.arange(w.rows - 4, w.rows), np.arange(0, w.rows, 97)]))
     idx = torch.from_numpy(rows).to(DEV)
     e_s, g_s = words(e.index_select(0, idx)), words(g.index_select(0, idx))
     ev = values(e_s, w.dtype)
