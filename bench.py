@@ -23,6 +23,7 @@ summary when it was taken on the current kernel source, else null.
 from __future__ import annotations
 
 import argparse
+import csv
 import hashlib
 import json
 import math
@@ -388,6 +389,93 @@ def write_trace_summary(trace_csv: str, workload: str, command: str) -> None:
     _write_summary(trace_summary_path(workload), header, lines)
 
 
+GLU_TRACE_FILE = os.path.join(ROOT, "profiles", "glu_qwen3_4b_kernel_trace.txt")
+GLU_KIND_CODES = {"swiglu": 0, "geglu": 1, "geglu_tanh": 2}
+
+
+def write_glu_trace_summary(run_dir: str, command: str) -> None:
+    """Per-launch durations of glu_kernel (bf16, dense, 32-bit offsets) on glu_qwen3_4b
+    for the three kinds, from run_dir/glu_trace_<kind>/*kernel_trace.csv (rocprofv3)
+    beside each kind's bench.py JSON line in run_dir/glu_bench_<kind>.log."""
+    import csv
+    import glob
+    w = workloads.glu_get("glu_qwen3_4b")
+    per = {"forward": 3 * w.elements * w.elem_bytes, "backward": 5 * w.elements * w.elem_bytes}
+    lines = [f"{'kind':11s} {'launch':9s} {'calls':>5s} {'avg_us':>8s} {'min_us':>8s} {'max_us':>8s}"
+             f"  {'avg GB/s (% of 8 TB/s)':24s} bench.py events avg_us (GB/s)"]
+    for kind, code in GLU_KIND_CODES.items():
+        durs = {"forward": [], "backward": []}
+        for path in glob.glob(os.path.join(run_dir, f"glu_trace_{kind}", "**", "*kernel_trace.csv"),
+                              recursive=True):
+            with open(path) as fh:
+                for row in csv.DictReader(fh):
+                    name = row["Kernel_Name"]
+                    for launch, bwd in (("forward", 0), ("backward", 1)):
+                        if f"glu_kernelIDF16bLi8ELi{code}ELb{bwd}ELb1Ej" in name:
+                            durs[launch].append((int(row["End_Timestamp"])
+                                                 - int(row["Start_Timestamp"])) / 1e3)
+        with open(os.path.join(run_dir, f"glu_bench_{kind}.log")) as fh:
+            js = json.loads([ln for ln in fh if ln.startswith("{")][-1])
+        ev = {"forward": js["forward"]["avg_launch_us"], "backward": js["roofline"]["avg_launch_us"]}
+        for launch in ("forward", "backward"):
+            d = np.array(durs[launch])
+            if d.size == 0:
+                raise SystemExit(f"no {kind} {launch} dispatch under {run_dir}")
+            gbps = per[launch] / (d.mean() * 1e-6) / 1e9
+            egbps = per[launch] / (ev[launch] * 1e-6) / 1e9
+            lines.append(f"{kind:11s} {launch:9s} {d.size:5d} {d.mean():8.2f} {d.min():8.2f} "
+                         f"{d.max():8.2f}  {gbps:6.0f} ({100 * gbps / HBM_PEAK_GBPS:4.1f}%)"
+                         f"{'':12s} {ev[launch]:.2f} ({egbps:.0f})")
+    header = [
+        "# rocprofv3 kernel traces: glu_kernel on the glu_qwen3_4b workload (16384 tokens x 9728,",
+        "# the Qwen3-4B MLP width, bf16, N(0,1) e, g, dh; forward (e, g -> h) + backward",
+        "# (dh, e, g -> de, dg) per step, 2 rotating buffer sets of 1.9 GB)",
+        f"# commands (R = repository root, on one MI355X), for K in swiglu geglu geglu_tanh: {command}",
+        f"# algorithmic bytes per launch: forward {per['forward']} (read e, g; write h),",
+        f"#                               backward {per['backward']} (read dh, e, g; write de, dg)",
+        "# Instances: glu_kernel<__bf16, VEC=8, KIND, BWD, DENSE=true, uint32 offsets>; the other",
+        "# kernels in the traces are torch's input generation and copies (not timed).",
+        "",
+    ]
+    _write_summary(GLU_TRACE_FILE, header, lines)
+
+
+GLU_VALU_FILE = os.path.join(ROOT, "profiles", "glu_valu_occupancy.txt")
+
+
+def write_glu_valu_summary(run_dir: str, command: str) -> None:
+    """VALU occupancy of glu_kernel's forward and backward for the three kinds, from one
+    rocprofv3 --pmc pass each (run_dir/<kind>/*counter_collection.csv)."""
+    import glob
+    lines = [f"{'kind':12s} {'pass':8s} {'waves':>8s} {'VALU instr/wave':>16s} {'VALU busy':>10s}"
+             f" {'GRBM cycles/XCD':>16s}"]
+    simds = CU_COUNT * SIMDS_PER_CU
+    for kind, code in GLU_KIND_CODES.items():
+        for launch, bwd in (("forward", 0), ("backward", 1)):
+            acc = {}
+            for path in glob.glob(os.path.join(run_dir, kind, "**", "*counter_collection.csv"),
+                                  recursive=True):
+                with open(path) as fh:
+                    for row in csv.DictReader(fh):
+                        if f"glu_kernelIDF16bLi8ELi{code}ELb{bwd}ELb1Ej" in row["Kernel_Name"]:
+                            acc.setdefault(row["Counter_Name"], []).append(
+                                float(row["Counter_Value"]))
+            m = {k: sum(v) / len(v) for k, v in acc.items()}
+            busy = 100.0 * 4 * m["SQ_ACTIVE_INST_VALU"] / (simds * m["GRBM_GUI_ACTIVE"] / XCDS)
+            lines.append(f"{kind:12s} {launch:8s} {m['SQ_WAVES']:8.0f} "
+                         f"{m['SQ_INSTS_VALU'] / m['SQ_WAVES']:16.0f} {busy:9.1f}% "
+                         f"{m['GRBM_GUI_ACTIVE'] / XCDS:16.0f}")
+    header = [
+        "# VALU occupancy of glu_kernel on the glu_qwen3_4b workload (16384 x 9728 bf16), one",
+        "# rocprofv3 --pmc pass per kind; per-dispatch means over the forward and the backward",
+        "# dispatches. VALU busy = SQ_ACTIVE_INST_VALU x 4 cycles / (1024 SIMDs x",
+        "# GRBM_GUI_ACTIVE / 8 XCDs).",
+        f"# command (R = repository root, on one MI355X), for K in swiglu geglu geglu_tanh: {command}",
+        "",
+    ]
+    _write_summary(GLU_VALU_FILE, header, lines)
+
+
 def packed_position_ids(w: workloads.Workload) -> np.ndarray:
     """Per-token positions of the packed batch (0..len-1 per sequence; -1 for rows
     outside every sequence): the position_ids a 1-D packing collator would emit."""
@@ -742,12 +830,24 @@ def main():
                     help="write profiles/rope_qk_<workload>_kernel_trace.txt from a rocprofv3 "
                          "--kernel-trace CSV of a run on --workload, then exit")
     ap.add_argument("--trace-command", default="", help="command recorded in that summary")
+    ap.add_argument("--glu-trace-summary", default=None, metavar="RUN_DIR",
+                    help="write the GLU kernel-trace summary from RUN_DIR/glu_trace_<kind> and "
+                         "RUN_DIR/glu_bench_<kind>.log, then exit")
+    ap.add_argument("--glu-valu-summary", default=None, metavar="RUN_DIR",
+                    help="write the GLU VALU-occupancy summary from RUN_DIR/<kind> PMC folders, "
+                         "then exit")
     ap.add_argument("--counters-summary", nargs=4, default=None,
                     metavar=("FLY_DIR", "TABLE_DIR", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                     help="write the cos/sin fly-vs-table counter summary from rocprofv3 "
                          "--pmc and --kernel-trace output folders, then exit")
     args = ap.parse_args()
 
+    if args.glu_valu_summary:
+        write_glu_valu_summary(args.glu_valu_summary, args.trace_command)
+        return
+    if args.glu_trace_summary:
+        write_glu_trace_summary(args.glu_trace_summary, args.trace_command)
+        return
     if args.counters_summary:
         write_counters_summary(*args.counters_summary, command=args.trace_command)
         return

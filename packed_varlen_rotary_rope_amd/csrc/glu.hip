@@ -21,14 +21,15 @@
 // Accuracy. sigmoid comes from one exp of -|z| (no overflow, no cancellation:
 // sigmoid(z) = 1/(1+t) or t/(1+t), t = exp(-|z|)); Phi(e) comes from
 // erfc(|e|/sqrt 2)/2 = s exp(-e^2/2) R(s), s = 1/(2 sqrt 2 + |e|), with a fitted
-// polynomial R and an exactly split exponent, so it keeps its relative accuracy
+// polynomial R and (fp32 storage) an exactly split exponent, so it keeps its relative accuracy
 // in the negative tail and shares its exp with the density. The derivative act'(e) has a
 // root e0 where its direct formula cancels; near e0 it is taken from a Taylor
 // polynomial around e0 (glu_constants.h). With fp32 storage every output is then
 // within a few fp32 ulps of the exact value (plus, for the tanh form, the
 // conditioning of its tail: about |2u(e)| ulps). With bf16 / f16 storage shorter
-// polynomials are used, whose errors (below 2^-16 relative) stay far under half a
-// 16-bit ulp; either way each output is rounded once to the storage dtype.
+// polynomials and an unsplit exponent product are used, whose errors (below 2^-16
+// relative) stay far under half a 16-bit ulp; either way each output is rounded
+// once to the storage dtype.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -56,23 +57,33 @@ struct GluShape {
 // ---- activations in fp32 -----------------------------------------------------------
 
 // exp(y) for -150 <= y <= 0 (Cody-Waite style): y log2(e) = n + f with n an
-// integer and |f| <= 1/2, exp(y) = 2^f 2^n. The product y log2(e) is carried as
+// integer and |f| <= 1/2, exp(y) = 2^f 2^n; 2^f is one v_exp_f32 (1 ulp on
+// [-1/2, 1/2]) and the scaling by 2^n one ldexp, which also rounds the subnormal
+// results correctly. FULL (fp32 storage): the product y log2(e) is carried as
 // ph + pl (FMA split, log2(e) itself in two parts), so f = (ph - n) + pl is exact
-// to far below an ulp; 2^f is one v_exp_f32 (1 ulp on [-1/2, 1/2]) and the
-// scaling by 2^n one ldexp, which also rounds the subnormal results correctly.
+// to far below an ulp. Otherwise f = ph - n (exact) and the rounding of ph, at
+// most 2^-24 |ph| <= 2^-16.2 for |y| <= 150, moves the result by under 2^-16.7
+// relative: far below a 16-bit ulp, and the two FMAs and an add are saved.
+template <bool FULL>
 __device__ inline float exp_nonpos(float y) {
   const float ph = y * kLog2e;
-  const float pl = __builtin_fmaf(y, kLog2eLo, __builtin_fmaf(y, kLog2e, -ph));
   const float n = __builtin_rintf(ph);
-  const float f = (ph - n) + pl;
+  float f;
+  if constexpr (FULL) {
+    const float pl = __builtin_fmaf(y, kLog2eLo, __builtin_fmaf(y, kLog2e, -ph));
+    f = (ph - n) + pl;
+  } else {
+    f = ph - n;
+  }
   return __builtin_amdgcn_ldexpf(__builtin_amdgcn_exp2f(f), (int)n);
 }
 
 // sigmoid(z) and 1 - sigmoid(z) from t = exp(-|z|): 1/(1+t) and t/(1+t), each the
 // larger or the smaller by the sign of z. rcp is within 1 ulp. exp(-150) is 0 in
 // fp32, so larger |z| are capped there.
+template <bool FULL>
 __device__ inline void sigmoid_pair(float z, float& s, float& sc) {
-  const float t = exp_nonpos(fmaxf(-fabsf(z), -150.0f));
+  const float t = exp_nonpos<FULL>(fmaxf(-fabsf(z), -150.0f));
   const float r = __builtin_amdgcn_rcpf(1.0f + t);
   const float small = t * r;
   s = z >= 0.0f ? r : small;
@@ -102,7 +113,7 @@ __device__ inline void normal_cdf_gauss(float e, float& cdf, float& gauss) {
     for (int k = kPhiDegree16 - 1; k >= 0; --k) r = __builtin_fmaf(r, s, kPhiPoly16[k]);
   }
   const float sq = ec * ec;
-  const float g0 = exp_nonpos(-0.5f * sq);
+  const float g0 = exp_nonpos<FULL>(-0.5f * sq);
   if constexpr (FULL) {
     const float sq_err = __builtin_fmaf(ec, ec, -sq);  // e^2 = sq + sq_err exactly
     gauss = __builtin_fmaf(-0.5f * sq_err, g0, g0);   // exp(-sq/2) * (1 - sq_err/2)
@@ -138,7 +149,7 @@ template <int KIND, bool FULL>
 __device__ inline float act_fwd(float e) {
   if constexpr (KIND == GLU_SWIGLU) {
     float s, sc;
-    sigmoid_pair(e, s, sc);
+    sigmoid_pair<FULL>(e, s, sc);
     return e * s;
   } else if constexpr (KIND == GLU_GEGLU) {
     float cdf, gauss;
@@ -149,7 +160,7 @@ __device__ inline float act_fwd(float e) {
     const float ec = fminf(fmaxf(e, -64.0f), 64.0f);
     const float z = ec * __builtin_fmaf(kTanhB, ec * ec, kTanhA);
     float s, sc;
-    sigmoid_pair(z, s, sc);
+    sigmoid_pair<FULL>(z, s, sc);
     return e * s;
   }
 }
@@ -159,7 +170,7 @@ template <int KIND, bool FULL>
 __device__ inline void act_bwd(float e, float& a, float& da) {
   if constexpr (KIND == GLU_SWIGLU) {
     float s, sc;
-    sigmoid_pair(e, s, sc);
+    sigmoid_pair<FULL>(e, s, sc);
     a = e * s;
     // s (1 + e (1 - s))
     const float direct = s * __builtin_fmaf(e, sc, 1.0f);
@@ -178,7 +189,7 @@ __device__ inline void act_bwd(float e, float& a, float& da) {
     const float z = ec * __builtin_fmaf(kTanhB, e2, kTanhA);
     const float zp = __builtin_fmaf(kTanhC, e2, kTanhA);
     float s, sc;
-    sigmoid_pair(z, s, sc);
+    sigmoid_pair<FULL>(z, s, sc);
     a = e * s;
     // s (1 + e z' (1 - s))
     const float direct = s * __builtin_fmaf(ec * zp, sc, 1.0f);
