@@ -43,7 +43,6 @@ import workloads  # noqa: E402
 METRIC = "fused QK-RoPE fwd+bwd tokens/s and achieved HBM GB/s (% of peak), packed bf16"
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
 INFINITY_CACHE_BYTES = 256 * 2 ** 20
-EVENT_EVERY = 4
 KERNEL_SRC = os.path.join(ROOT, "packed_varlen_rotary_rope_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "rope_qk_qwen3_4b_packed_traffic.txt")
 
@@ -726,16 +725,38 @@ def bench_glu(args) -> None:
         return compare_glu_unfused(rope, w, kind, sets, nsets, args)
     for i in range(args.warmup):
         step(sets[i % nsets])
-    events = {i: [HipEvent() for _ in range(4)] for i in range(0, args.steps, EVENT_EVERY)}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(sets[i % nsets], events.get(i))
+        step(sets[i % nsets])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    fwd_all = [ev[0].elapsed_ms(ev[1]) * 1e3 for ev in events.values()]
-    bwd_all = [ev[2].elapsed_ms(ev[3]) * 1e3 for ev in events.values()]
-    fwd_us, bwd_us = float(np.mean(fwd_all)), float(np.mean(bwd_all))
+
+    # Per-launch durations after the timed region: forward-only and backward-only runs
+    # of back-to-back launches, each between one pair of HIP events on the launch
+    # stream (average, gaps included), then events around single launches of further
+    # steps (minimum and median).
+    reps = max(8, min(args.steps, 200))
+
+    def region_us(launch):
+        ev = [HipEvent(), HipEvent()]
+        ev[0].record(stream)
+        for i in range(reps):
+            launch(sets[i % nsets])
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        return ev[0].elapsed_ms(ev[1]) * 1e3 / reps
+
+    fwd_us = region_us(lambda st: rope.glu_fwd(kind, st["e"], st["g"], out=st["h"],
+                                              index_mode=index_mode))
+    bwd_us = region_us(lambda st: rope.glu_bwd(kind, st["dh"], st["e"], st["g"], de=st["de"],
+                                              dg=st["dg"], index_mode=index_mode))
+    events = [[HipEvent() for _ in range(4)] for _ in range(min(args.steps, 100))]
+    for i, ev in enumerate(events):
+        step(sets[i % nsets], ev)
+    torch.cuda.synchronize()
+    fwd_all = [ev[0].elapsed_ms(ev[1]) * 1e3 for ev in events]
+    bwd_all = [ev[2].elapsed_ms(ev[3]) * 1e3 for ev in events]
     fwd_bytes, bwd_bytes = 3 * n * w.elem_bytes, 5 * n * w.elem_bytes
     achieved = bwd_bytes / (bwd_us * 1e-6) / 1e9
     out = {
@@ -761,6 +782,7 @@ def bench_glu(args) -> None:
                         if kind == "swiglu" and w.name == "glu_qwen3_4b" else None),
             "kernel": "glu_kernel (backward)",
             "bytes_per_launch": bwd_bytes, "avg_launch_us": bwd_us,
+            "timing": f"HIP events around {reps} back-to-back backward launches / {reps}",
             "min_launch_us": float(np.min(bwd_all)), "median_launch_us": float(np.median(bwd_all)),
         },
         "forward": {"bytes_per_launch": fwd_bytes, "avg_launch_us": fwd_us,
