@@ -834,6 +834,9 @@ def main():
     ap.add_argument("--cos-sin", default="fly", choices=["fly", "table"],
                     help="fly: cos/sin evaluated in the kernel (default); table: read from a "
                          "cos/sin cache made once with the library's export (rope_qk_apply_table)")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay each step from a captured HIP graph instead of launching it "
+                         "eagerly from Python")
     ap.add_argument("--glu", default=None, choices=["swiglu", "geglu", "geglu_tanh"],
                     help="time the SwiGLU/GeGLU kernels instead (workload: a glu_* name)")
     ap.add_argument("--compare", action="store_true",
@@ -992,12 +995,31 @@ def main():
     # The timed region: K steps back to back, bracketed by synchronize (wall clock)
     # and by one pair of HIP events on the launch stream (GPU time). Nothing else is
     # enqueued between the launches.
+    run = step
+    if args.graph:
+        # One HIP graph per buffer set, each holding one step (forward + backward
+        # launches), captured on torch's capture stream; replayed in the same rotation.
+        graphs = []
+        torch.cuda.synchronize()
+        for st in sets:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(st)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        by_set = {id(st): g for st, g in zip(sets, graphs)}
+
+        def run(st):
+            by_set[id(st)].replay()
+
+        for i in range(max(args.warmup, nsets)):
+            run(sets[i % nsets])
     region = [HipEvent(), HipEvent()]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     region[0].record(stream)
     for i in range(args.steps):
-        step(sets[i % nsets])
+        run(sets[i % nsets])
     region[1].record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
@@ -1049,6 +1071,7 @@ def main():
             "buffer_sets": nsets, "tokens_per_wave": tpw or "auto",
             "positions": args.positions, "pos_scale": args.pos_scale,
             "layout": args.layout, "index": args.index, "cos_sin": args.cos_sin,
+            "launch": "hip graph per step" if args.graph else "eager",
         },
         "step_hbm_GBps": 2 * bpl * args.steps / elapsed / 1e9,
         "roofline": {
