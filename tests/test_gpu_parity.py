@@ -669,3 +669,26 @@ def test_table_random_vs_oracle(rope, dtype, D, Hq, Hkv, tpw, mode):
                                 position_ids=pid_np)
         assert_parity(dtype, bits(dev[what]), ref, x, touched, f"table:{what}")
         assert guards_intact(flats[what], g), f"table:{what}: guard region written"
+
+
+def test_table_on_fused_qkv_views(rope):
+    """The table path on Q/K views into a fused QKV buffer [T, (Hq + 2 Hkv) D] gives the
+    bits of the same call on contiguous copies, forward and backward; V is untouched."""
+    w = workloads.get("qwen3_8b_packed")
+    print("[table] fused QKV views", flush=True)
+    T, Hq, Hkv, D = w.T, w.Hq, w.Hkv, w.D
+    cu = torch.from_numpy(w.cu_seqlens).to(DEV)
+    ct, st = rope.cos_sin(torch.arange(int(max(w.lengths)), dtype=torch.int32, device=DEV), D,
+                          w.theta)
+    for direction in (1, -1):
+        buf = workloads.make_tensor((T, (Hq + 2 * Hkv) * D), 77 + direction, "bf16", device=DEV)
+        v0 = buf[:, (Hq + Hkv) * D:].clone()
+        q = buf[:, :Hq * D].view(T, Hq, D)
+        k = buf[:, Hq * D:(Hq + Hkv) * D].view(T, Hkv, D)
+        qc, kc = q.contiguous(), k.contiguous()
+        rope.qk_apply_table_(qc, kc, ct, st, direction, cu_seqlens=cu)
+        rope.qk_apply_table_(q, k, ct, st, direction, cu_seqlens=cu)
+        torch.cuda.synchronize()
+        assert torch.equal(q.contiguous().view(torch.int16), qc.view(torch.int16)), direction
+        assert torch.equal(k.contiguous().view(torch.int16), kc.view(torch.int16)), direction
+        assert torch.equal(buf[:, (Hq + Hkv) * D:].view(torch.int16), v0.view(torch.int16))
