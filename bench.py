@@ -311,6 +311,21 @@ def write_counters_summary(fly_dir, table_dir, copy_fetch_csv, copy_write_csv, c
             "{:.1f}"),
         row("wave lifetime (SQ_WAVE_CYCLES / SQ_WAVES)", per_wave("SQ_WAVE_CYCLES"), "{:.0f}"),
         row("cycles waiting per wave (SQ_WAIT_INST_ANY)", per_wave("SQ_WAIT_INST_ANY"), "{:.0f}"),
+    ]
+    if all("TA_TA_BUSY_sum" in runs[m] for m in runs):
+        per_cu = lambda k: (lambda c, t: 100.0 * c[k] / (CU_COUNT * c["GRBM_GUI_ACTIVE"] / XCDS))
+        lines += [
+            row("TA busy, % of cycles per CU", per_cu("TA_TA_BUSY_sum"), "{:.1f}"),
+            row("TD busy, % of cycles per CU", per_cu("TD_TD_BUSY_sum"), "{:.1f}"),
+            row("TA stalled by the cache, % of cycles",
+                per_cu("TA_DATA_STALLED_BY_TC_CYCLES_sum"), "{:.1f}"),
+            row("TCP stalled on pending data, % of cycles",
+                per_cu("TCP_PENDING_STALL_CYCLES_sum"), "{:.1f}"),
+            row("L2 read latency seen by TCP (cycles/request)",
+                lambda c, t: c["TCP_TCC_READ_REQ_LATENCY_sum"] / c["TCP_TCC_READ_REQ_sum"],
+                "{:.0f}"),
+        ]
+    lines += [
         row("HBM read bytes (FETCH_SIZE x scale)",
             lambda c, t: c["FETCH_SIZE"] * 1024.0 * f_scale, "{:.4g}"),
         row("HBM write bytes (WRITE_SIZE x scale)",
