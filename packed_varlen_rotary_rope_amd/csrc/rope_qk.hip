@@ -580,8 +580,9 @@ int32_t auto_tokens_per_wave(int64_t T) {
 // divide 64, the grid would exceed the dispatch size limit, or seqused marks a
 // padded layout. In the last case many rows are skipped; the row-group kernel
 // spends one workgroup per row group of each skipped token where the token kernel
-// spends one wave per token, and the two measure the same (Qwen3-8B batch padded
-// to 8 x 2048 rows: 32.9 vs 33.0 us), so padded layouts keep the token kernel.
+// spends one wave per token, and it measures slower there (Qwen3-8B batch padded
+// to 8 x 2048 rows: 34.2-34.4 vs 33.1-33.4 us), so padded layouts keep the token
+// kernel.
 int64_t group_grid(const RopeParams& p, bool geometry_chosen, bool padded) {
   if (geometry_chosen || padded || 64 % p.nc != 0) return 0;
   const int step_r = 64 / p.nc;
