@@ -692,3 +692,37 @@ def test_table_on_fused_qkv_views(rope):
         assert torch.equal(q.contiguous().view(torch.int16), qc.view(torch.int16)), direction
         assert torch.equal(k.contiguous().view(torch.int16), kc.view(torch.int16)), direction
         assert torch.equal(buf[:, (Hq + Hkv) * D:].view(torch.int16), v0.view(torch.int16))
+
+
+def test_grid_beyond_one_dispatch(rope):
+    """2^26 + 4099 tokens of the smallest shape (one Q and one K head, D = 2): the
+    row-group grid would exceed one dispatch (2^26 workgroups) and one wave per token
+    would exceed the grid limit, so the library launches waves that walk two tokens
+    each. Sampled rows (ends, sequence boundaries, around every 2^24 tokens, random)
+    against the oracle, forward and backward."""
+    T = (1 << 26) + 4099
+    print(f"[parity] T={T} beyond one dispatch", flush=True)
+    cu_np = np.array([0, 1000, 5_000_000, 40_000_003, T - 7, T], dtype=np.int32)
+    cu = torch.from_numpy(cu_np).to(DEV)
+    theta = 1e4
+    host = {what: workloads.make_tensor((T, 1, 2), 5100 + i, "bf16", device=DEV, chunk_rows=1 << 22)
+            for i, what in enumerate(("q", "k", "dq", "dk"))}
+    rng = np.random.default_rng(5150)
+    marks = np.concatenate([np.arange(m - 3, m + 3) for m in (1 << 24, 2 << 24, 3 << 24, 1 << 26)]
+                           + [np.arange(c - 2, c + 2) for c in cu_np[1:-1]])
+    tokens = np.unique(np.concatenate([np.arange(0, 64), np.arange(T - 64, T), marks,
+                                       rng.integers(0, T, 4096)]))
+    tokens = tokens[(tokens >= 0) & (tokens < T)]
+    tok_dev = torch.from_numpy(tokens).to(DEV)
+    before = {what: bits(t.index_select(0, tok_dev)) for what, t in host.items()}
+    rope.qk_fwd_(host["q"], host["k"], cu, theta)
+    rope.qk_bwd_(host["dq"], host["dk"], cu, theta)
+    torch.cuda.synchronize()
+    touched = np.ones(tokens.size, dtype=bool)
+    for what, direction in (("q", 1), ("k", 1), ("dq", -1), ("dk", -1)):
+        got = bits(host[what].index_select(0, tok_dev))
+        ref = oracle.rope_rows(before[what], tokens, cu_np, theta, direction, "bf16", None,
+                               NTHREADS)
+        assert_parity("bf16", got, ref, before[what], touched, f"big-grid:{what}")
+    del host
+    torch.cuda.empty_cache()
