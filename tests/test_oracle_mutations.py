@@ -55,6 +55,13 @@ MUTATIONS = [
     ("bf16_ties_not_even", "if (rest > 0x8000u || (rest == 0x8000u && (keep & 1u))) keep += 1u;",
      "if (rest >= 0x8000u) keep += 1u;"),
     ("bf16_truncates", "if (rest > 0x8000u || (rest == 0x8000u && (keep & 1u))) keep += 1u;", ""),
+    # caller-supplied cos/sin tables
+    ("table_row_not_scaled", "rotate_row(dtype, x, off, y + off, D, cos_tab + (int64_t)pe * half,",
+     "rotate_row(dtype, x, off, y + off, D, cos_tab + (int64_t)pe,"),
+    ("table_cos_sin_swapped",
+     "cos_tab + (int64_t)pe * half,\n                   sin_tab + (int64_t)pe * half, dir);",
+     "sin_tab + (int64_t)pe * half,\n                   cos_tab + (int64_t)pe * half, dir);"),
+    ("table_last_row_dropped", "if (pe < 0 || pe >= tab_rows)", "if (pe < 0 || pe >= tab_rows - 1)"),
 ]
 
 
