@@ -726,3 +726,39 @@ def test_grid_beyond_one_dispatch(rope):
         assert_parity("bf16", got, ref, before[what], touched, f"big-grid:{what}")
     del host
     torch.cuda.empty_cache()
+
+
+def test_concurrent_streams(rope):
+    """Calls on different streams are independent: two batches rotated concurrently on
+    two streams (default priority) give the bits of the same calls made one after the
+    other on the default stream."""
+    print("[parity] two streams", flush=True)
+    work = []
+    for name in ("qwen3_8b_packed", "qwen3_4b_packed"):
+        w = workloads.get(name)
+        cu = torch.from_numpy(w.cu_seqlens).to(DEV)
+        q = workloads.make_tensor(w.shape("q"), w.seed("q"), w.dtype, device=DEV)
+        k = workloads.make_tensor(w.shape("k"), w.seed("k"), w.dtype, device=DEV)
+        work.append((w, cu, q, k))
+    ref = []
+    for w, cu, q, k in work:
+        qr, kr = q.clone(), k.clone()
+        rope.qk_fwd_(qr, kr, cu, w.theta)
+        rope.qk_bwd_(qr, kr, cu, w.theta)
+        rope.qk_fwd_(qr, kr, cu, w.theta)
+        ref.append((qr, kr))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    got = [(q.clone(), k.clone()) for _, _, q, k in work]
+    torch.cuda.synchronize()
+    for it in range(3):  # forward, backward, forward, interleaved across the streams
+        for (w, cu, _q, _k), (qg, kg), st in zip(work, got, streams):
+            with torch.cuda.stream(st):
+                if it == 1:
+                    rope.qk_bwd_(qg, kg, cu, w.theta)
+                else:
+                    rope.qk_fwd_(qg, kg, cu, w.theta)
+    torch.cuda.synchronize()
+    for (qr, kr), (qg, kg) in zip(ref, got):
+        assert torch.equal(qg.view(torch.int16), qr.view(torch.int16))
+        assert torch.equal(kg.view(torch.int16), kr.view(torch.int16))
