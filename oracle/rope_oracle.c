@@ -53,7 +53,8 @@
  *
  * Parity pins: every function here is checked against something other than
  * itself in tests/test_oracle_pins.py (closed forms, mpmath, the block matrix R
- * built with numpy, complex multiplication, invariants, brute force).
+ * built with numpy, complex multiplication, invariants, brute force; the storage
+ * decodes against the IEEE 754 field layout, all 65536 binary16 words included).
  */
 #include <math.h>
 #include <stdint.h>

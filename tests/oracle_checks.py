@@ -324,6 +324,52 @@ def check_rows_match_full(o):
     assert np.array_equal(rows.view(np.uint32), full[tokens].view(np.uint32))
 
 
+def f16_word_value(w: int):
+    """The value of a binary16 word from the IEEE 754 field layout, written in the
+    textbook form: (-1)^sign * (1 + m/2^10) * 2^(e - 15) for normal words,
+    (-1)^sign * (m/2^10) * 2^-14 for subnormal ones; e = 31 is an infinity (m = 0)
+    or a NaN. Returns (sign, Fraction magnitude) or (sign, "inf") / (sign, "nan")."""
+    sign, e, m = w >> 15, (w >> 10) & 0x1F, w & 0x3FF
+    if e == 0x1F:
+        return sign, ("nan" if m else "inf")
+    if e == 0:
+        return sign, Fraction(m, 2 ** 10) * Fraction(1, 2 ** 14)
+    mag = (1 + Fraction(m, 2 ** 10))
+    return sign, mag * (Fraction(2) ** (e - 15))
+
+
+def check_f16_decode_all_words(o):
+    """Every binary16 word (all 65536, NaNs, infinities, subnormals and -0 included)
+    goes through the oracle's f16 storage path at position 0, where the rotation is
+    the identity: word w in the first half of a D = 2 row (second half +0) must come
+    out as the value its IEEE 754 fields define, and the same in the second half.
+    Checked against the field formula above (exact rationals) and numpy's own
+    binary16 widening. (In the second half the identity is x2*1 + (+0)*0, which
+    turns -0 into +0 under IEEE addition; there only the zero's sign is free.)"""
+    words = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    np_vals = words.view(np.float16).astype(np.float32)
+    ids = np.zeros(words.size, dtype=np.int32)  # every token at position 0
+    for half in (0, 1):
+        x = np.zeros((words.size, 1, 2), dtype=np.uint16)
+        x[:, 0, half] = words
+        y = o.rope(x, None, 1e4, 1, "f16", position_ids=ids)[:, 0, half]
+        assert np.array_equal(np.isnan(y), np.isnan(np_vals)), half
+        ok = ~np.isnan(y) & ((y != 0) | (half == 0))
+        assert np.array_equal(y[ok].view(np.uint32), np_vals[ok].view(np.uint32)), half
+        for w in range(65536):
+            sign, mag = f16_word_value(w)
+            v = float(y[w])
+            if mag == "nan":
+                assert math.isnan(v), hex(w)
+                continue
+            if not (half == 1 and mag == 0):
+                assert math.copysign(1.0, v) == (-1.0 if sign else 1.0), hex(w)
+            if mag == "inf":
+                assert math.isinf(v), hex(w)
+            else:
+                assert Fraction(abs(v)) == mag, (hex(w), v, mag)
+
+
 def check_round_bf16(o):
     import torch
     rng = np.random.default_rng(21)
@@ -517,6 +563,7 @@ ALL_CHECKS = [
     check_exact_rounding,
     check_rows_match_full,
     check_round_bf16,
+    check_f16_decode_all_words,
     check_position_ids_match_cu_positions,
     check_position_ids_hand_values,
     check_seq_offsets_shard_invariant,

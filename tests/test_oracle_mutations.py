@@ -55,6 +55,14 @@ MUTATIONS = [
     ("bf16_ties_not_even", "if (rest > 0x8000u || (rest == 0x8000u && (keep & 1u))) keep += 1u;",
      "if (rest >= 0x8000u) keep += 1u;"),
     ("bf16_truncates", "if (rest > 0x8000u || (rest == 0x8000u && (keep & 1u))) keep += 1u;", ""),
+    # binary16 storage decode
+    ("f16_exponent_bias_off_by_one", "v = ldexp((double)(man | 0x400), exp - 25);",
+     "v = ldexp((double)(man | 0x400), exp - 24);"),
+    ("f16_subnormal_scale", "v = ldexp((double)man, -24);", "v = ldexp((double)man, -25);"),
+    ("f16_implicit_bit_dropped", "v = ldexp((double)(man | 0x400), exp - 25);",
+     "v = ldexp((double)man, exp - 25);"),
+    ("f16_inf_nan_swapped", "v = man ? NAN : INFINITY;", "v = man ? INFINITY : NAN;"),
+    ("f16_sign_dropped", "return (float)(sign ? -v : v);", "return (float)v;"),
     # caller-supplied cos/sin tables
     ("table_row_not_scaled", "rotate_row(dtype, x, off, y + off, D, cos_tab + (int64_t)pe * half,",
      "rotate_row(dtype, x, off, y + off, D, cos_tab + (int64_t)pe,"),
