@@ -970,7 +970,7 @@ def main():
         # The cos/sin cache a caller would keep: every position of the batch, made
         # once by the library's own export, outside the timed region.
         rows = int(max(w.lengths))
-        tables = rope.cos_sin(torch.arange(rows, dtype=torch.int32, device=dev), w.D, w.theta)
+        tables = rope.cos_sin_table(rows, w.D, w.theta, dev)
 
     def launch(qt, kt, direction):
         if tables is not None:

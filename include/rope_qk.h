@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define ROPE_QK_ABI_VERSION 3
+#define ROPE_QK_ABI_VERSION 4
 
 /* Storage dtype of Q and K (computation is fp32 in every case). */
 typedef enum rope_dtype { ROPE_F32 = 0, ROPE_BF16 = 1, ROPE_F16 = 2 } rope_dtype;
@@ -164,7 +164,7 @@ int32_t rope_qk_apply_ex(void* q, void* k, int64_t T, int32_t Hq, int32_t Hkv, i
  * per "Packing non contamine").
  *  cos_tab, sin_tab  device float[tab_rows * (D/2)], row-major: row p holds the
  *                    cos / sin of position p for frequencies j < D/2 (the layout
- *                    rope_cos_sin writes for positions 0 .. tab_rows-1). Read only.
+ *                    rope_cos_sin writes with max_pos = tab_rows). Read only.
  *  tab_rows          rows of both tables, >= 1. A token whose position is >=
  *                    tab_rows is left untouched (no row exists for it).
  * There is no theta or pos_scale: the tables already hold the angles' cos/sin.
@@ -190,7 +190,9 @@ int32_t rope_qk_bwd_pos(void* dq, void* dk, int64_t T, int32_t Hq, int32_t Hkv, 
 
 /* Export of the token -> (position, sequence) map the kernels use (test hook,
  * same device code). pos_out, seq_out: device int32[T] (either may be NULL);
- * -1 for tokens that are left untouched. Validation as in rope_qk_fwd. */
+ * -1 for tokens that are left untouched. With num_seqs == 0 every token is
+ * untouched and cu_seqlens may be NULL (it is not read). Validation as in
+ * rope_qk_fwd. */
 int32_t rope_positions(const int32_t* cu_seqlens, int32_t num_seqs, const int32_t* seqused,
                        int64_t T, int32_t* pos_out, int32_t* seq_out, void* stream);
 
@@ -200,14 +202,26 @@ int32_t rope_positions_ex(const int32_t* cu_seqlens, int32_t num_seqs, const int
                           const int32_t* seq_offsets, const int32_t* position_ids, int64_t T,
                           int32_t* pos_out, int32_t* seq_out, void* stream);
 
-/* Export of the fp32 cos/sin the kernels use (test hook, same device code):
- * for each of the n positions in the device array positions (each >= 0) and each
- * j < D/2, cos_out[i*(D/2) + j] and sin_out[i*(D/2) + j] (device float arrays). */
-int32_t rope_cos_sin(const int32_t* positions, int64_t n, int32_t D, double theta,
-                     float* cos_out, float* sin_out, void* stream);
+/* The fp32 cos/sin the kernels use, as a table (same device code; Unsloth page,
+ * fused QK RoPE section: the cos and sin of the rotation): for every position
+ * p < max_pos and every frequency j < D/2, cos_out[p*(D/2) + j] and
+ * sin_out[p*(D/2) + j] receive the correctly rounded fp32 cos and sin of the
+ * angle fp32(p) * inv_freq[j]. This is the row layout rope_qk_apply_table reads.
+ *  max_pos           rows, >= 0 (0: nothing is written)
+ *  D, theta          as in rope_qk_fwd
+ *  cos_out, sin_out  device float[max_pos * (D/2)], owned by the caller
+ * Returns ROPE_OK, ROPE_EINVAL (max_pos < 0, bad D or theta, a NULL output with
+ * max_pos > 0) or ROPE_ELAUNCH. */
+int32_t rope_cos_sin(int32_t max_pos, int32_t D, double theta, float* cos_out, float* sin_out,
+                     void* stream);
 
-/* rope_cos_sin with linear position interpolation (pos_scale as in rope_qk_apply_ex). */
-int32_t rope_cos_sin_ex(const int32_t* positions, int64_t n, int32_t D, double theta,
+/* The same values for an arbitrary list of positions, with linear position
+ * interpolation: row i is position positions[i] (device int32[n], each >= 0),
+ * angle fp32(fp32(positions[i]) / pos_scale) * inv_freq[j] (pos_scale as in
+ * rope_qk_apply_ex; 1 = none). cos_out, sin_out: device float[n * (D/2)].
+ * Errors as in rope_cos_sin, and ROPE_EINVAL for n < 0, a NULL positions array
+ * with n > 0, or a bad pos_scale. */
+int32_t rope_cos_sin_at(const int32_t* positions, int64_t n, int32_t D, double theta,
                         double pos_scale, float* cos_out, float* sin_out, void* stream);
 
 /* Host-only: the fp32 inverse frequencies theta^(-2j/D), j < D/2, written to the

@@ -25,7 +25,7 @@ import torch
 __all__ = [
     "RopeError", "qk_fwd_", "qk_bwd_", "qk_apply_", "qk_apply_ex_", "qk_apply_table_",
     "qk_fwd_pos_", "qk_bwd_pos_",
-    "positions", "cos_sin", "inv_freq", "abi_version", "LIB_PATH", "INDEX_AUTO", "INDEX_32",
+    "positions", "cos_sin", "cos_sin_table", "inv_freq", "abi_version", "LIB_PATH", "INDEX_AUTO", "INDEX_32",
     "INDEX_64", "glu_fwd", "glu_bwd", "GLU_KINDS",
 ]
 
@@ -61,14 +61,14 @@ def _load() -> ctypes.CDLL:
     lib.rope_qk_bwd_pos.argtypes = [vp, vp, i64, i32, i32, i32, vp, dbl, i32, vp]
     lib.rope_positions.argtypes = [vp, i32, vp, i64, vp, vp, vp]
     lib.rope_positions_ex.argtypes = [vp, i32, vp, vp, vp, i64, vp, vp, vp]
-    lib.rope_cos_sin.argtypes = [vp, i64, i32, dbl, vp, vp, vp]
-    lib.rope_cos_sin_ex.argtypes = [vp, i64, i32, dbl, dbl, vp, vp, vp]
+    lib.rope_cos_sin.argtypes = [i32, i32, dbl, vp, vp, vp]
+    lib.rope_cos_sin_at.argtypes = [vp, i64, i32, dbl, dbl, vp, vp, vp]
     lib.rope_inv_freq.argtypes = [dbl, i32, vp]
     lib.glu_fwd.argtypes = [i32, vp, vp, vp, i64, i64, i64, i64, i32, i32, vp]
     lib.glu_bwd.argtypes = [i32, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, vp]
     for name in ("rope_qk_fwd", "rope_qk_bwd", "rope_qk_apply", "rope_qk_apply_ex", "rope_qk_apply_table",
                  "rope_qk_fwd_pos", "rope_qk_bwd_pos", "rope_positions", "rope_positions_ex",
-                 "rope_cos_sin", "rope_cos_sin_ex", "rope_inv_freq", "rope_abi_version",
+                 "rope_cos_sin", "rope_cos_sin_at", "rope_inv_freq", "rope_abi_version",
                  "glu_fwd", "glu_bwd"):
         getattr(lib, name).restype = i32
     lib.rope_status_str.argtypes = [i32]
@@ -280,9 +280,21 @@ def cos_sin(pos, D: int, theta: float, pos_scale: float = 1.0):
     p = _index_tensor(pos, "pos", pos.device)
     c = torch.empty((p.numel(), D // 2), dtype=torch.float32, device=p.device)
     s = torch.empty_like(c)
-    st = _lib.rope_cos_sin_ex(_ptr(p), p.numel(), int(D), float(theta), float(pos_scale), _ptr(c),
+    st = _lib.rope_cos_sin_at(_ptr(p), p.numel(), int(D), float(theta), float(pos_scale), _ptr(c),
                               _ptr(s), _stream(p.device))
-    _check(st, "rope_cos_sin_ex")
+    _check(st, "rope_cos_sin_at")
+    return c, s
+
+
+def cos_sin_table(max_pos: int, D: int, theta: float, device=None):
+    """fp32 (cos, sin) [max_pos, D/2] for positions 0 .. max_pos-1 on `device`
+    (default: the current GPU): the tables qk_apply_table_ takes."""
+    device = torch.device(device) if device is not None else torch.device(
+        "cuda", torch.cuda.current_device())
+    c = torch.empty((int(max_pos), D // 2), dtype=torch.float32, device=device)
+    s = torch.empty_like(c)
+    _check(_lib.rope_cos_sin(int(max_pos), int(D), float(theta), _ptr(c), _ptr(s),
+                             _stream(device)), "rope_cos_sin")
     return c, s
 
 

@@ -465,12 +465,16 @@ __global__ __launch_bounds__(kBlock) void rope_positions_kernel(const PosSource 
                                                                 int32_t* seq_out) {
   const int64_t t = (int64_t)blockIdx.x * kBlock + threadIdx.x;
   if (t >= T) return;
-  int32_t seq;
-  const int32_t pos = resolve_position(ps, t, &seq);
+  int32_t seq = -1, pos = -1;
+  // With no sequences (and no explicit ids) every token is untouched, and
+  // cu_seqlens may be NULL: it is not read.
+  if (ps.position_ids != nullptr || ps.num_seqs > 0) pos = resolve_position(ps, t, &seq);
   if (pos_out) pos_out[t] = pos;
   if (seq_out) seq_out[t] = seq;
 }
 
+// Row i of the tables is position positions[i], or position i when positions is
+// NULL (the [max_pos, D/2] table of positions 0 .. max_pos-1).
 __global__ __launch_bounds__(kBlock) void rope_cos_sin_kernel(const int32_t* __restrict__ positions,
                                                               int64_t n, int32_t half,
                                                               const CosSinParams p, float* cos_out,
@@ -479,9 +483,9 @@ __global__ __launch_bounds__(kBlock) void rope_cos_sin_kernel(const int32_t* __r
   if (idx >= n * half) return;
   const int64_t i = idx / half;
   const int32_t j = (int32_t)(idx - i * half);
+  const int32_t pos = positions != nullptr ? positions[i] : (int32_t)i;
   float s, c;
-  rope_trig::sincos_f32_cr(rope_angle(scaled_position(positions[i], p.pos_scale), p.inv_freq[j]),
-                           s, c);
+  rope_trig::sincos_f32_cr(rope_angle(scaled_position(pos, p.pos_scale), p.inv_freq[j]), s, c);
   cos_out[idx] = c;
   sin_out[idx] = s;
 }
@@ -801,12 +805,14 @@ int32_t rope_positions(const int32_t* cu_seqlens, int32_t num_seqs, const int32_
                            stream);
 }
 
-int32_t rope_cos_sin_ex(const int32_t* positions, int64_t n, int32_t D, double theta,
-                        double pos_scale, float* cos_out, float* sin_out, void* stream) {
+// Shared by rope_cos_sin (positions == NULL: rows are positions 0 .. n-1) and
+// rope_cos_sin_at.
+static int32_t cos_sin_impl(const int32_t* positions, int64_t n, int32_t D, double theta,
+                            double pos_scale, float* cos_out, float* sin_out, void* stream) {
   if (!valid_D(D) || !valid_theta(theta) || !valid_scale(pos_scale)) return ROPE_EINVAL;
   if (n < 0 || n > ((int64_t)1 << 34)) return ROPE_EINVAL;
   if (n == 0) return ROPE_OK;
-  if (positions == nullptr || cos_out == nullptr || sin_out == nullptr) return ROPE_EINVAL;
+  if (cos_out == nullptr || sin_out == nullptr) return ROPE_EINVAL;
   CosSinParams p;
   host_inv_freq(theta, D, p.inv_freq);
   p.pos_scale = (float)pos_scale;
@@ -818,9 +824,16 @@ int32_t rope_cos_sin_ex(const int32_t* positions, int64_t n, int32_t D, double t
   return hipGetLastError() == hipSuccess ? ROPE_OK : ROPE_ELAUNCH;
 }
 
-int32_t rope_cos_sin(const int32_t* positions, int64_t n, int32_t D, double theta,
-                     float* cos_out, float* sin_out, void* stream) {
-  return rope_cos_sin_ex(positions, n, D, theta, 1.0, cos_out, sin_out, stream);
+int32_t rope_cos_sin(int32_t max_pos, int32_t D, double theta, float* cos_out, float* sin_out,
+                     void* stream) {
+  if (max_pos < 0) return ROPE_EINVAL;
+  return cos_sin_impl(nullptr, max_pos, D, theta, 1.0, cos_out, sin_out, stream);
+}
+
+int32_t rope_cos_sin_at(const int32_t* positions, int64_t n, int32_t D, double theta,
+                        double pos_scale, float* cos_out, float* sin_out, void* stream) {
+  if (n > 0 && positions == nullptr) return ROPE_EINVAL;
+  return cos_sin_impl(positions, n, D, theta, pos_scale, cos_out, sin_out, stream);
 }
 
 int32_t rope_inv_freq(double theta, int32_t D, float* out) {

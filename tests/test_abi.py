@@ -50,7 +50,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert rope.abi_version() == 3
+    assert rope.abi_version() == 4
     lib = rope._lib
     for st in (0, -1, -2, -3):
         assert lib.rope_status_str(st).decode().startswith("ROPE_")
@@ -179,18 +179,24 @@ def test_fwd_bwd_positions_cos_sin_validation():
     assert lib.rope_positions(None, 2, None, 16, FAKE, FAKE, None) == EINVAL
     assert lib.rope_positions(FAKE, 2, None, -5, FAKE, FAKE, None) == EINVAL
     assert lib.rope_positions(FAKE, 2, None, 0, FAKE, FAKE, None) == OK
-    assert lib.rope_cos_sin(FAKE, 4, 7, 1e4, FAKE, FAKE, None) == EINVAL
-    assert lib.rope_cos_sin(FAKE, -1, 8, 1e4, FAKE, FAKE, None) == EINVAL
-    assert lib.rope_cos_sin(None, 4, 8, 1e4, FAKE, FAKE, None) == EINVAL
-    assert lib.rope_cos_sin(FAKE, 0, 8, 1e4, FAKE, FAKE, None) == OK
+    assert lib.rope_cos_sin(4, 7, 1e4, FAKE, FAKE, None) == EINVAL  # odd D
+    assert lib.rope_cos_sin(-1, 8, 1e4, FAKE, FAKE, None) == EINVAL
+    assert lib.rope_cos_sin(4, 8, 0.5, FAKE, FAKE, None) == EINVAL
+    assert lib.rope_cos_sin(4, 8, 1e4, None, FAKE, None) == EINVAL
+    assert lib.rope_cos_sin(4, 8, 1e4, FAKE, None, None) == EINVAL
+    assert lib.rope_cos_sin(0, 8, 1e4, None, None, None) == OK
+    assert lib.rope_cos_sin_at(FAKE, 4, 7, 1e4, 1.0, FAKE, FAKE, None) == EINVAL
+    assert lib.rope_cos_sin_at(FAKE, -1, 8, 1e4, 1.0, FAKE, FAKE, None) == EINVAL
+    assert lib.rope_cos_sin_at(None, 4, 8, 1e4, 1.0, FAKE, FAKE, None) == EINVAL
+    assert lib.rope_cos_sin_at(FAKE, 0, 8, 1e4, 1.0, FAKE, FAKE, None) == OK
     assert lib.rope_inv_freq(1e4, 8, None) == EINVAL
     assert lib.rope_qk_fwd_pos(FAKE, FAKE, 16, 4, 2, 128, None, 1e4, 1, None) == EINVAL
     assert lib.rope_qk_bwd_pos(FAKE, FAKE, 16, 4, 2, 127, FAKE, 1e4, 1, None) == EINVAL
     assert lib.rope_qk_fwd_pos(None, None, 0, 4, 2, 128, None, 1e4, 1, None) == OK
     assert lib.rope_positions_ex(None, 2, None, None, None, 16, FAKE, FAKE, None) == EINVAL
     assert lib.rope_positions_ex(None, 0, None, None, None, 0, FAKE, FAKE, None) == OK
-    assert lib.rope_cos_sin_ex(FAKE, 4, 8, 1e4, 0.9, FAKE, FAKE, None) == EINVAL
-    assert lib.rope_cos_sin_ex(FAKE, 0, 8, 1e4, 2.0, FAKE, FAKE, None) == OK
+    assert lib.rope_cos_sin_at(FAKE, 4, 8, 1e4, 0.9, FAKE, FAKE, None) == EINVAL
+    assert lib.rope_cos_sin_at(FAKE, 0, 8, 1e4, 2.0, FAKE, FAKE, None) == OK
 
 
 @pytest.mark.parametrize("theta,D", [(1e4, 16), (1e6, 128), (1e4, 128), (5e5, 64), (1e6, 80),

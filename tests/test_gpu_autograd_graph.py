@@ -76,8 +76,7 @@ def test_rope_table_autograd_matches_theta_path(lib, inplace_backward):
     w = workloads.get("qwen3_8b_packed")
     print(f"[autograd] rope_qk_table inplace_backward={inplace_backward}", flush=True)
     cu = torch.from_numpy(w.cu_seqlens).to(DEV)
-    ct, st = rope.cos_sin(torch.arange(int(max(w.lengths)), dtype=torch.int32, device=DEV), w.D,
-                          w.theta)
+    ct, st = rope.cos_sin_table(int(max(w.lengths)), w.D, w.theta, DEV)
     wq = workloads.make_tensor(w.shape("q"), 43, "bf16", device=DEV)
     wk = workloads.make_tensor(w.shape("k"), 44, "bf16", device=DEV)
     outs = []

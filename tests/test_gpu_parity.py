@@ -233,12 +233,33 @@ def test_positions_edges(rope):
 @pytest.mark.parametrize("theta,D,maxpos", [(1e4, 16, 64), (1e6, 128, 524288), (1e4, 128, 40000),
                                             (5e5, 64, 70000), (1e6, 80, 20000)])
 def test_cos_sin_export_bit_exact(rope, theta, D, maxpos):
+    """Both exports against the oracle's correctly rounded values: the [max_pos, D/2]
+    table of positions 0 .. max_pos-1, and the same positions as a shuffled list."""
     pos = np.arange(maxpos, dtype=np.int32)
-    c, s = rope.cos_sin(torch.from_numpy(pos).to(DEV), D, theta)
     rc, rs = oracle.cos_sin(pos, D, theta)
-    cb, sb = c.cpu().numpy().view(np.uint32), s.cpu().numpy().view(np.uint32)
-    mism = int((cb != rc.view(np.uint32)).sum() + (sb != rs.view(np.uint32)).sum())
-    assert mism == 0, f"{mism} of {2 * rc.size} cos/sin values differ from the oracle"
+    perm = np.random.default_rng(maxpos).permutation(maxpos).astype(np.int32)
+    tc, ts = rope.cos_sin_table(maxpos, D, theta, DEV)
+    lc, ls = rope.cos_sin(torch.from_numpy(perm).to(DEV), D, theta)
+    for form, c, s, rows in (("table", tc, ts, pos), ("list", lc, ls, perm)):
+        cb, sb = c.cpu().numpy().view(np.uint32), s.cpu().numpy().view(np.uint32)
+        mism = int((cb != rc[rows].view(np.uint32)).sum() + (sb != rs[rows].view(np.uint32)).sum())
+        assert mism == 0, f"{form}: {mism} of {2 * rc.size} cos/sin values differ from the oracle"
+
+
+def test_positions_without_sequences(rope):
+    """num_seqs == 0 with no cu_seqlens (NULL) and no ids: every token is untouched
+    (-1) and nothing is read from the missing array."""
+    T = 1000
+    pos = torch.full((T,), 7, dtype=torch.int32, device=DEV)
+    seq = torch.full((T,), 7, dtype=torch.int32, device=DEV)
+    st = rope._lib.rope_positions_ex(None, 0, None, None, None, T, pos.data_ptr(),
+                                     seq.data_ptr(), torch.cuda.current_stream(DEV).cuda_stream)
+    assert st == 0
+    st = rope._lib.rope_positions(None, 0, None, T, pos.data_ptr(), None,
+                                  torch.cuda.current_stream(DEV).cuda_stream)
+    assert st == 0
+    torch.cuda.synchronize()
+    assert bool(torch.all(pos == -1)) and bool(torch.all(seq == -1))
 
 
 # ---------------------------------------------------------------- launch variants
@@ -604,7 +625,7 @@ def test_table_equals_theta_path(rope, name):
     cu = torch.from_numpy(w.cu_seqlens).to(DEV)
     su = None if w.seqused is None else torch.from_numpy(w.seqused).to(DEV)
     rows = int(max(w.lengths))
-    ct, st = rope.cos_sin(torch.arange(rows, dtype=torch.int32, device=DEV), w.D, w.theta)
+    ct, st = rope.cos_sin_table(rows, w.D, w.theta, DEV)
     a = {what: t.to(DEV) for what, t in host.items()}
     b = {what: t.to(DEV) for what, t in host.items()}
     rope.qk_fwd_(a["q"], a["k"], cu, w.theta, seqused=su)
@@ -678,8 +699,7 @@ def test_table_on_fused_qkv_views(rope):
     print("[table] fused QKV views", flush=True)
     T, Hq, Hkv, D = w.T, w.Hq, w.Hkv, w.D
     cu = torch.from_numpy(w.cu_seqlens).to(DEV)
-    ct, st = rope.cos_sin(torch.arange(int(max(w.lengths)), dtype=torch.int32, device=DEV), D,
-                          w.theta)
+    ct, st = rope.cos_sin_table(int(max(w.lengths)), D, w.theta, DEV)
     for direction in (1, -1):
         buf = workloads.make_tensor((T, (Hq + 2 * Hkv) * D), 77 + direction, "bf16", device=DEV)
         v0 = buf[:, (Hq + Hkv) * D:].clone()
