@@ -34,6 +34,10 @@
 #ifndef ROPE_HD
 #define ROPE_HD __host__ __device__
 #endif
+// A host build may count the fallbacks (the CPU test of this header does).
+#ifndef ROPE_TRIG_ON_FALLBACK
+#define ROPE_TRIG_ON_FALLBACK()
+#endif
 
 namespace rope_trig {
 
@@ -159,6 +163,7 @@ ROPE_HD inline void sincos_f32_cr(float angle, float& s_out, float& c_out) {
   apply_quadrant((int)((int64_t)k & 3), s, c, sx, cx);
   float so = (float)sx, co = (float)cx;
   if (near_f32_boundary(sx) || near_f32_boundary(cx)) {
+    ROPE_TRIG_ON_FALLBACK();
     const sc32 r = sincos_dd_path(x);
     so = r.s;
     co = r.c;
