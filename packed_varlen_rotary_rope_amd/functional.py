@@ -4,19 +4,29 @@ and the SwiGLU / GeGLU activations as differentiable torch functions.
 Every pass is one launch of the library's kernels on the current stream; this
 module only wires them into torch.autograd (no arithmetic of its own).
 
-    q, k = rope_qk(q, k, cu_seqlens, theta)        # in place, returns q and k
+    qkv = rope_qkv(qkv, Hq, Hkv, cu_seqlens, theta)  # fused QKV output, in place
+    q, k = rope_qk(q, k, cu_seqlens, theta)        # returns q and k, rotated
     q, k = rope_qk_table(q, k, cos_tab, sin_tab, cu_seqlens)  # cos/sin from tables
     h = glu("swiglu", e, g)                        # h = silu(e) * g
     h = glu_fused("geglu", gate_up)                # e, g = halves of gate_up
 
-rope_qk rotates its inputs in place (they are marked dirty), so q and k must not
-be leaf tensors that require grad -- in a model they are projection outputs. Its
-backward applies the transposed rotation (sin negated, Unsloth, "Entrainement des
-LLM 3 fois plus rapide...", fused QK RoPE section) to the incoming gradients:
-in place on them when ``inplace_backward=True``, otherwise on a copy, because
-autograd may hand the same gradient tensor to several consumers (an addition
-passes its gradient to both operands), and rotating a shared tensor in place
-would change the other consumer's gradient.
+The RoPE functions rotate in place (their inputs are marked dirty), so the
+inputs must not be leaf tensors that require grad -- in a model they are
+projection outputs. rope_qkv takes the fused projection output [T, (Hq + 2 Hkv)
+* D] (or [T, Hq + 2 Hkv, D]) and rotates its Q and K columns in one strided
+launch, V untouched; it is one in-place output, which autograd accepts also when
+the buffer is a view (e.g. ``(x @ W).view(...)``). rope_qk takes q and k as two
+tensors: autograd cannot mark two outputs of one function dirty when an input is
+a view of another tensor, so a q or k that is such a view and requires grad is
+rotated on a contiguous copy (one extra read and write of it; rope_qkv avoids
+that for fused projections). Either way use the returned tensors.
+
+The backward applies the transposed rotation (sin negated, Unsloth, "Entrainement
+des LLM 3 fois plus rapide...", fused QK RoPE section) to the incoming
+gradients: in place on them when ``inplace_backward=True``, otherwise on a copy,
+because autograd may hand the same gradient tensor to several consumers (an
+addition passes its gradient to both operands), and rotating a shared tensor in
+place would change the other consumer's gradient.
 """
 from __future__ import annotations
 
@@ -49,15 +59,85 @@ class _RopeQK(torch.autograd.Function):
         return dq, dk, None, None, None, None, None, None, None
 
 
+def _own_storage(t: torch.Tensor) -> torch.Tensor:
+    """t itself, or a contiguous copy when t is a view that requires grad (autograd
+    refuses an in-place function with two outputs on such an input)."""
+    if torch.is_grad_enabled() and t.requires_grad and t._is_view():
+        return t.clone(memory_format=torch.contiguous_format)
+    return t
+
+
 def rope_qk(q: torch.Tensor, k: torch.Tensor, cu_seqlens=None, theta: float = 10000.0,
             seqused=None, position_ids=None, seq_offsets=None, pos_scale: float = 1.0,
             inplace_backward: bool = False):
-    """Differentiable in-place RoPE of q [T, Hq, D] and k [T, Hkv, D] (views with
-    contiguous heads, e.g. slices of a fused QKV output, are accepted). Positions
-    come from cu_seqlens (with optional seqused / seq_offsets) or position_ids, as
-    in ``qk_apply_ex_``. Returns (q, k), rotated."""
-    return _RopeQK.apply(q, k, cu_seqlens, float(theta), seqused, position_ids, seq_offsets,
-                         float(pos_scale), bool(inplace_backward))
+    """Differentiable RoPE of q [T, Hq, D] and k [T, Hkv, D] (views with contiguous
+    heads, e.g. slices of a fused QKV output, are accepted), in place unless q or k
+    is a view that requires grad (then on a copy of it; see the module docstring and
+    rope_qkv). Positions come from cu_seqlens (with optional seqused / seq_offsets)
+    or position_ids, as in ``qk_apply_ex_``. Returns (q, k), rotated."""
+    return _RopeQK.apply(_own_storage(q), _own_storage(k), cu_seqlens, float(theta), seqused,
+                         position_ids, seq_offsets, float(pos_scale), bool(inplace_backward))
+
+
+def _qkv_split(qkv: torch.Tensor, Hq: int, Hkv: int):
+    """Q and K views [T, Hq, D] and [T, Hkv, D] of a fused projection output
+    [T, (Hq + 2 Hkv) * D] or [T, Hq + 2 Hkv, D] whose columns are contiguous."""
+    H = Hq + 2 * Hkv
+    if qkv.dim() == 3:
+        if qkv.shape[1] != H:
+            raise ValueError(f"qkv has {qkv.shape[1]} heads, expected Hq + 2 Hkv = {H}")
+        if (qkv.shape[2] > 1 and qkv.stride(2) != 1) or (H > 1 and qkv.stride(1) != qkv.shape[2]):
+            raise ValueError("qkv: the heads of a token must be contiguous")
+        flat = qkv.flatten(1)
+    elif qkv.dim() == 2:
+        if qkv.shape[1] % H:
+            raise ValueError(f"qkv has {qkv.shape[1]} columns, not a multiple of Hq + 2 Hkv = {H}")
+        if qkv.shape[1] > 1 and qkv.stride(1) != 1:
+            raise ValueError("qkv: columns must be contiguous")
+        flat = qkv
+    else:
+        raise ValueError("qkv must be [T, (Hq + 2 Hkv) * D] or [T, Hq + 2 Hkv, D]")
+    D = flat.shape[1] // H
+    q = flat[:, :Hq * D].unflatten(1, (Hq, D))
+    k = flat[:, Hq * D:(Hq + Hkv) * D].unflatten(1, (Hkv, D))
+    return q, k
+
+
+class _RopeQKV(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, qkv, Hq, Hkv, cu_seqlens, theta, seqused, position_ids, seq_offsets,
+                pos_scale, inplace_backward):
+        q, k = _qkv_split(qkv, Hq, Hkv)
+        qk_apply_ex_(q, k, theta, 1, cu_seqlens=cu_seqlens, seqused=seqused,
+                     seq_offsets=seq_offsets, position_ids=position_ids, pos_scale=pos_scale)
+        ctx.mark_dirty(qkv)
+        ctx.save_for_backward(cu_seqlens, seqused, position_ids, seq_offsets)
+        ctx.heads, ctx.theta, ctx.pos_scale = (Hq, Hkv), theta, pos_scale
+        ctx.inplace = inplace_backward
+        return qkv
+
+    @staticmethod
+    def backward(ctx, g):
+        cu, su, pid, so = ctx.saved_tensors
+        if not (ctx.inplace and g.is_contiguous()):
+            g = g.clone(memory_format=torch.contiguous_format)
+        dq, dk = _qkv_split(g, *ctx.heads)
+        qk_apply_ex_(dq, dk, ctx.theta, -1, cu_seqlens=cu, seqused=su, seq_offsets=so,
+                     position_ids=pid, pos_scale=ctx.pos_scale)
+        return g, None, None, None, None, None, None, None, None, None
+
+
+def rope_qkv(qkv: torch.Tensor, num_q_heads: int, num_kv_heads: int, cu_seqlens=None,
+             theta: float = 10000.0, seqused=None, position_ids=None, seq_offsets=None,
+             pos_scale: float = 1.0, inplace_backward: bool = False) -> torch.Tensor:
+    """Differentiable in-place RoPE of the Q and K heads inside a fused QKV projection
+    output qkv [T, (Hq + 2 Hkv) * D] or [T, Hq + 2 Hkv, D] (Q heads, then K, then V;
+    each token's columns contiguous, rows of any stride), one kernel launch per
+    pass; the V heads and their gradient pass through unchanged. qkv may be a view
+    (e.g. ``(x @ W_qkv).view(T, -1, D)``). Positions as in ``rope_qk``. Returns qkv."""
+    return _RopeQKV.apply(qkv, int(num_q_heads), int(num_kv_heads), cu_seqlens, float(theta),
+                          seqused, position_ids, seq_offsets, float(pos_scale),
+                          bool(inplace_backward))
 
 
 class _RopeQKTable(torch.autograd.Function):
@@ -87,11 +167,12 @@ def rope_qk_table(q: torch.Tensor, k: torch.Tensor, cos_tab: torch.Tensor, sin_t
                   cu_seqlens=None, seqused=None, position_ids=None, seq_offsets=None,
                   inplace_backward: bool = False):
     """rope_qk with cos/sin read from float32 [rows, D/2] tables (row p = position p,
-    as ``qk_apply_table_`` takes them) instead of computed from theta. The tables are
+    as ``qk_apply_table_`` takes them) instead of computed from theta (views that
+    require grad are rotated on copies, as in rope_qk). The tables are
     constants: they receive no gradient. Tokens whose position has no row pass
     through unchanged, and so do their gradients."""
-    return _RopeQKTable.apply(q, k, cos_tab, sin_tab, cu_seqlens, seqused, position_ids,
-                              seq_offsets, bool(inplace_backward))
+    return _RopeQKTable.apply(_own_storage(q), _own_storage(k), cos_tab, sin_tab, cu_seqlens,
+                              seqused, position_ids, seq_offsets, bool(inplace_backward))
 
 
 class _Glu(torch.autograd.Function):

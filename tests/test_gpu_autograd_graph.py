@@ -115,6 +115,84 @@ def test_rope_autograd_shared_gradient_is_not_clobbered(lib):
     assert torch.equal(q0.grad, expect)
 
 
+def _projection(T, n_in, n_out, seed):
+    """fp32 input and weight (the products and their backward stay in fp32); the
+    projection output is cast to bf16 by the caller."""
+    x = workloads.make_tensor((T, n_in), seed, "f32", device=DEV).requires_grad_()
+    w = (workloads.make_tensor((n_in, n_out), seed + 1, "f32", device=DEV) * 0.05).contiguous()
+    return x, w
+
+
+def test_rope_qk_on_projection_views(lib):
+    """The usual model code: q = (x @ Wq).view(T, Hq, D), k = (x @ Wk).view(T, Hkv, D),
+    views that require grad. rope_qk returns the rotation of their values, and the
+    gradient reaching each projection output is the backward rotation of the upstream
+    gradient, bit for bit against direct launches."""
+    rope, F = lib
+    w = workloads.get("qwen3_8b_packed")
+    print("[autograd] rope_qk on projection views", flush=True)
+    cu = torch.from_numpy(w.cu_seqlens).to(DEV)
+    x, wq = _projection(w.T, 256, w.Hq * w.D, 51)
+    wk = (workloads.make_tensor((256, w.Hkv * w.D), 53, "f32", device=DEV) * 0.05).contiguous()
+    pq, pk = (x @ wq).to(torch.bfloat16), (x @ wk).to(torch.bfloat16)
+    grads = {}
+    pq.register_hook(lambda g: grads.__setitem__("q", g.detach().clone()))
+    pk.register_hook(lambda g: grads.__setitem__("k", g.detach().clone()))
+    q, k = pq.view(w.T, w.Hq, w.D), pk.view(w.T, w.Hkv, w.D)
+    qr, kr = F.rope_qk(q, k, cu, w.theta)
+    uq = workloads.make_tensor(w.shape("q"), 55, "bf16", device=DEV)
+    uk = workloads.make_tensor(w.shape("k"), 56, "bf16", device=DEV)
+    ((qr.float() * uq.float()).sum() + (kr.float() * uk.float()).sum()).backward()
+    qd = pq.detach().view(w.T, w.Hq, w.D).clone()
+    kd = pk.detach().view(w.T, w.Hkv, w.D).clone()
+    rope.qk_fwd_(qd, kd, cu, w.theta)
+    gq, gk = uq.clone(), uk.clone()
+    rope.qk_bwd_(gq, gk, cu, w.theta)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits16(qr), bits16(qd)) and np.array_equal(bits16(kr), bits16(kd))
+    assert np.array_equal(bits16(grads["q"].view(w.shape("q"))), bits16(gq))
+    assert np.array_equal(bits16(grads["k"].view(w.shape("k"))), bits16(gk))
+    assert x.grad is not None and bool(torch.isfinite(x.grad.float()).all())
+
+
+@pytest.mark.parametrize("shape3,inplace_backward", [(False, False), (True, False), (True, True)])
+def test_rope_qkv_fused_projection(lib, shape3, inplace_backward):
+    """rope_qkv on a fused projection output (x @ Wqkv, viewed as [T, H*D] or
+    [T, Hq+2Hkv, D]): Q and K rotated in place in one launch, V untouched; the
+    gradient into the projection is [bwd(dQ), bwd(dK), dV], bit for bit."""
+    rope, F = lib
+    w = workloads.get("qwen3_8b_packed")
+    print(f"[autograd] rope_qkv shape3={shape3} inplace_backward={inplace_backward}", flush=True)
+    H = w.Hq + 2 * w.Hkv
+    cu = torch.from_numpy(w.cu_seqlens).to(DEV)
+    x, wqkv = _projection(w.T, 256, H * w.D, 61)
+    proj = (x @ wqkv).to(torch.bfloat16)
+    got = {}
+    proj.register_hook(lambda g: got.__setitem__("g", g.detach().clone()))
+    before = proj.detach().clone()
+    qkv = proj.view(w.T, H, w.D) if shape3 else proj.view(w.T, -1)
+    out = F.rope_qkv(qkv, w.Hq, w.Hkv, cu, w.theta, inplace_backward=inplace_backward)
+    assert out.data_ptr() == proj.data_ptr()
+    up = workloads.make_tensor((w.T, H * w.D), 63, "bf16", device=DEV)
+    (out.float() * up.view(out.shape).float()).sum().backward()
+    nq, nk = w.Hq * w.D, w.Hkv * w.D
+    qd = before[:, :nq].contiguous().view(w.shape("q"))
+    kd = before[:, nq:nq + nk].contiguous().view(w.shape("k"))
+    rope.qk_fwd_(qd, kd, cu, w.theta)
+    gq = up[:, :nq].contiguous().view(w.shape("q"))
+    gk = up[:, nq:nq + nk].contiguous().view(w.shape("k"))
+    rope.qk_bwd_(gq, gk, cu, w.theta)
+    torch.cuda.synchronize()
+    o = out.detach().reshape(w.T, -1)
+    assert np.array_equal(bits16(o[:, :nq]), bits16(qd.view(w.T, -1)))
+    assert np.array_equal(bits16(o[:, nq:nq + nk]), bits16(kd.view(w.T, -1)))
+    assert np.array_equal(bits16(o[:, nq + nk:]), bits16(before[:, nq + nk:]))
+    g = got["g"]
+    assert np.array_equal(bits16(g[:, :nq]), bits16(gq.view(w.T, -1)))
+    assert np.array_equal(bits16(g[:, nq:nq + nk]), bits16(gk.view(w.T, -1)))
+    assert np.array_equal(bits16(g[:, nq + nk:]), bits16(up[:, nq + nk:]))
+
+
 @pytest.mark.parametrize("kind", ["swiglu", "geglu", "geglu_tanh"])
 def test_glu_autograd(lib, kind):
     """glu and glu_fused: forward and gradients equal the direct launches bit for
