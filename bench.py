@@ -2,8 +2,12 @@
 
 One step = forward RoPE on (Q, K) plus backward RoPE on (dQ, dK) of one packed
 batch: two launches of the fused kernel, every row of the hot path. Default
-workload: the Qwen3-4B-shaped packed batch (T = 16384 tokens from an 80% short /
-20% long length mix, Hq = 32, Hkv = 8, D = 128, bf16, theta = 1e6).
+workload: the largest one, a single 524288-token sequence (Hq = 32, Hkv = 8,
+D = 128, bf16, theta = 1e6; Q alone holds 2^31 elements, so the 64-bit offset
+instance runs), standing in for the Unsloth page's 500K-token contexts. The same
+JSON line carries per-workload results for the other workloads (region-timed
+launches of the default path, with a torch in-place elementwise reference over
+the same bytes), so one run covers every configuration.
 
 Inputs are synthetic, seeded and resident in HBM before timing starts. Several
 buffer sets are rotated so that the working set between two touches of the
@@ -18,7 +22,8 @@ by its 2K launches (gaps between launches included). Per-launch minimum and
 median come from events around single launches in a sampling pass after the
 timed region. `traffic` comes from the committed rocprofv3 PMC
 summary when it was taken on the current kernel source, else null.
-`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+`cpu_baseline` times the CPU oracle on a bounded sample of the same workload
+(for the 524288-token sequence: the gathered rows of evenly spaced tokens).
 """
 from __future__ import annotations
 
@@ -44,7 +49,17 @@ METRIC = "fused QK-RoPE fwd+bwd tokens/s and achieved HBM GB/s (% of peak), pack
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
 INFINITY_CACHE_BYTES = 256 * 2 ** 20
 KERNEL_SRC = os.path.join(ROOT, "packed_varlen_rotary_rope_amd", "csrc")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "rope_qk_qwen3_4b_packed_traffic.txt")
+HEADLINE_WORKLOAD = "long_ctx_512k"
+# workloads timed beside the headline in the default run (every bf16 and fp32 one)
+SUB_WORKLOADS = ["tiny_packed", "qwen3_4b_packed", "qwen3_8b_packed", "qwen3_8b_padded",
+                 "qwen3_32b_packed", "long_ctx_512k"]
+
+
+def traffic_path(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"rope_qk_{workload}_traffic.txt")
+
+
+TRAFFIC_FILE = traffic_path("qwen3_4b_packed")
 
 
 # The sources each kernel is compiled from: a traffic summary taken on other
@@ -201,15 +216,56 @@ def _write_summary(path, header, lines):
     print("\n".join(header + lines))
 
 
-def write_traffic_summary(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, command: str):
-    """HBM bytes per launch of the rope kernel from two PMC passes (FETCH_SIZE, then
-    WRITE_SIZE), each scaled by what the same counter reads for a plain 1 GiB device
-    copy, as a small text summary that main() reads back."""
-    w = workloads.get("qwen3_4b_packed")
-    m = _pmc_scaled(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, "rope_qk_group_kernel")
+def _counter_means(csv_path: str) -> dict:
+    """{kernel name: {counter: mean per dispatch}} over a rocprofv3 --pmc CSV that may
+    hold several counters per dispatch."""
+    acc = {}
+    with open(csv_path) as fh:
+        for row in csv.DictReader(fh):
+            acc.setdefault(row["Kernel_Name"], {}).setdefault(row["Counter_Name"], []).append(
+                float(row["Counter_Value"]))
+    return {k: {c: sum(v) / len(v) for c, v in d.items()} for k, d in acc.items()}
+
+
+def _pick(means: dict, key: str | None) -> dict:
+    """The counters of the kernel whose name contains key (the largest reading of its
+    first counter, i.e. the 1 GiB copy, when key is None)."""
+    if key is None:
+        return max(means.values(), key=lambda d: next(iter(d.values())))
+    hits = [d for k, d in means.items() if key in k]
+    if not hits:
+        raise SystemExit(f"no dispatch of {key} in the counter file")
+    return hits[0]
+
+
+def ea_bytes(read: dict, write: dict) -> tuple:
+    """HBM read and write bytes from the TCC-to-memory request counts, by the
+    counters' definitions: a read request is 32, 64 or 128 bytes (TCC_EA0_RDREQ counts
+    all, _32B and _128B the two sizes named), a write request 32 or 64 bytes
+    (TCC_EA0_WRREQ all, _64B the large ones). No calibration enters."""
+    rd, r32, r128 = (read[c] for c in ("TCC_EA0_RDREQ_sum", "TCC_EA0_RDREQ_32B_sum",
+                                       "TCC_EA0_RDREQ_128B_sum"))
+    wr, w64 = write["TCC_EA0_WRREQ_sum"], write["TCC_EA0_WRREQ_64B_sum"]
+    return 128 * r128 + 32 * r32 + 64 * (rd - r128 - r32), 64 * w64 + 32 * (wr - w64)
+
+
+def write_traffic_summary(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, command: str,
+                          workload: str = "qwen3_4b_packed", ea=None):
+    """HBM bytes per launch of the workload's default RoPE kernel instance from two PMC
+    passes (FETCH_SIZE, then WRITE_SIZE), each scaled by what the same counter reads
+    for a plain 1 GiB device copy, as a small text summary that main() reads back.
+    With ea = (read CSV, write CSV, copy read CSV, copy write CSV) of two more passes
+    (TCC_EA0_RDREQ/_32B/_128B and TCC_BUBBLE; TCC_EA0_WRREQ/_64B), the bytes are also
+    derived from the request counts by the counters' definitions, uncalibrated."""
+    w = workloads.get(workload)
+    key = rope_kernel_instance(w, needs_long_index(w))
+    m = _pmc_scaled(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, key)
+    bpl = algorithmic_bytes_per_launch(w)
+    seq = "padded rows skipped via seqused" if w.seqused is not None else "packed"
     header = [
-        "# HBM traffic of rope_qk_group_kernel (bf16, D=128, Hq=32, Hkv=8) on the",
-        "# qwen3_4b_packed workload (T=16384), one launch = forward or backward over Q and K.",
+        f"# HBM traffic of the RoPE kernel instance {key}",
+        f"# on the {w.name} workload (T={w.T}, {w.valid_tokens} valid tokens, {seq}; Hq={w.Hq},",
+        f"# Hkv={w.Hkv}, D={w.D}, {w.dtype}), one launch = forward or backward over Q and K.",
         "# Two rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE) over the same bench",
         "# command, each counter scaled by its reading for a plain 1 GiB device copy.",
         f"# commands: {command}",
@@ -218,9 +274,27 @@ def write_traffic_summary(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, 
         f"fetch_scale: {m['f_scale']:.5f}",
         f"write_scale: {m['w_scale']:.5f}",
     ]
-    lines = _pmc_lines(m, algorithmic_bytes_per_launch(w))
+    lines = _pmc_lines(m, bpl)
+    if ea is not None:
+        kr, kw = _pick(_counter_means(ea[0]), key), _pick(_counter_means(ea[1]), key)
+        cr, cw = _pick(_counter_means(ea[2]), None), _pick(_counter_means(ea[3]), None)
+        k_read, k_write = ea_bytes(kr, kw)
+        c_read, c_write = ea_bytes(cr, cw)
+        lines += [
+            "# second counter family: TCC-to-memory request counts x request size (uncalibrated)",
+            f"ea_copy_read_bytes_for_1GiB: {c_read:.0f} (x{c_read / 2 ** 30:.4f})",
+            f"ea_copy_write_bytes_for_1GiB: {c_write:.0f} (x{c_write / 2 ** 30:.4f})",
+            f"ea_read_requests_per_launch: {kr['TCC_EA0_RDREQ_sum']:.0f} "
+            f"(32B {kr['TCC_EA0_RDREQ_32B_sum']:.0f}, 128B {kr['TCC_EA0_RDREQ_128B_sum']:.0f}, "
+            f"TCC_BUBBLE {kr.get('TCC_BUBBLE_sum', float('nan')):.0f})",
+            f"ea_write_requests_per_launch: {kw['TCC_EA0_WRREQ_sum']:.0f} "
+            f"(64B {kw['TCC_EA0_WRREQ_64B_sum']:.0f})",
+            f"ea_hbm_read_bytes_per_launch: {k_read:.0f}",
+            f"ea_hbm_write_bytes_per_launch: {k_write:.0f}",
+            f"ea_traffic_over_algorithmic: {(k_read + k_write) / bpl:.4f}",
+        ]
     lines.append(f"kernel_source_sha256_16: {kernel_source_hash(ROPE_SOURCES)}")
-    _write_summary(TRAFFIC_FILE, header, lines)
+    _write_summary(traffic_path(w.name), header, lines)
 
 
 def write_glu_traffic_summary(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, command: str):
@@ -661,6 +735,223 @@ def compare_unfused(rope, w, cu, su, sets, nsets, args, stream):
     print(json.dumps(out))
 
 
+def rope_kernel_instance(w: workloads.Workload, long_index: bool) -> str:
+    """Mangled-name fragment of the default path's kernel instance for this workload
+    (row-group kernel unless seqused marks a padded layout; dtype, chunk width and
+    index width), as rocprofv3 lists it."""
+    base = rope_kernel_name(w, 0)
+    dt = {"bf16": "DF16b", "f16": "DF16_", "f32": "f"}[w.dtype]
+    vec = 16 // w.elem_bytes
+    return f"{base}I{dt}Li{vec}ELb{int(long_index)}ELb0E"
+
+
+def needs_long_index(w: workloads.Workload) -> bool:
+    return w.T * (w.Hq + w.Hkv) * w.D >= 2 ** 31
+
+
+def region_us(stream: int, launches, n: int) -> float:
+    """Average GPU time per call of launches(i) over n back-to-back calls, from one
+    pair of HIP events on the launch stream (gaps between launches included)."""
+    ev = [HipEvent(), HipEvent()]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for i in range(n):
+        launches(i)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    return ev[0].elapsed_ms(ev[1]) * 1e3 / n
+
+
+def inplace_reference_us(sets, nsets, stream, n: int) -> float:
+    """Per-pass time of a torch in-place elementwise op over the same bytes as one
+    RoPE launch: negate Q, then K (two launches, each one read and one write of its
+    tensor), on the same rotating buffer sets."""
+    def one(i):
+        s = sets[i % nsets]
+        s["q"].neg_()
+        s["k"].neg_()
+    for i in range(min(n, 2 * nsets)):
+        one(i)
+    return region_us(stream, one, n)
+
+
+def time_workload(rope, w: workloads.Workload, dev, n_steps: int, warmup: int) -> dict:
+    """Region-timed default launches (forward + backward per step) of one workload on
+    its own rotating buffer sets, beside the torch in-place reference over the same
+    bytes (fully packed workloads only: a padded layout's valid bytes are not one
+    tensor)."""
+    set_bytes = 2 * w.T * (w.Hq + w.Hkv) * w.D * w.elem_bytes
+    nsets = max(2, math.ceil(8 * INFINITY_CACHE_BYTES / set_bytes))
+    cu, su, sets = make_sets(w, nsets, dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+
+    def step(i):
+        s = sets[i % nsets]
+        rope.qk_apply_(s["q"], s["k"], cu, w.theta, 1, seqused=su)
+        rope.qk_apply_(s["dq"], s["dk"], cu, w.theta, -1, seqused=su)
+
+    for i in range(warmup):
+        step(i)
+    launch_us = region_us(stream, step, n_steps) / 2
+    bpl = algorithmic_bytes_per_launch(w)
+    gbps = bpl / (launch_us * 1e-6) / 1e9
+    out = {
+        "T": w.T, "valid_tokens": w.valid_tokens, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D,
+        "dtype": w.dtype, "kernel": rope_kernel_name(w, 0),
+        "index": "64-bit" if needs_long_index(w) else "32-bit",
+        "bytes_per_launch": bpl, "avg_launch_us": launch_us, "GBps": gbps,
+        "frac": gbps / HBM_PEAK_GBPS,
+        "fwd_bwd_tokens_per_s": w.valid_tokens / (2 * launch_us * 1e-6),
+        "launches_timed": 2 * n_steps,
+    }
+    if w.seqused is None:
+        ref_us = inplace_reference_us(sets, nsets, stream, 2 * n_steps)
+        out["torch_inplace_us"] = ref_us
+        out["torch_inplace_GBps"] = bpl / (ref_us * 1e-6) / 1e9
+        out["frac_of_ceiling"] = ref_us / launch_us
+    del sets
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline_sampled(w: workloads.Workload, sets0: dict, budget_s: float, nthreads: int,
+                         n_tokens: int = 1024) -> dict:
+    """The oracle, as it stands, on evenly spaced tokens of a workload too large to
+    process whole: their rows of Q, K, dQ and dK (copied from the benchmark's first
+    buffer set, the same bits the GPU rotates) go through the oracle's forward and
+    backward, repeated for about budget_s seconds on nthreads threads, then a
+    quarter of that on one thread. tokens/s = sampled tokens per pass pair / time."""
+    import oracle
+
+    tokens = np.unique(np.linspace(0, w.T - 1, n_tokens).astype(np.int64))
+    idx = torch.from_numpy(tokens).to(sets0["q"].device)
+    rows = {what: workloads.host_bits(sets0[what].index_select(0, idx))
+            for what in ("q", "k", "dq", "dk")}
+    timer = oracle.rows_fwd_bwd_timer(rows["q"], rows["k"], rows["dq"], rows["dk"], tokens,
+                                      w.cu_seqlens, w.theta, w.dtype, w.seqused)
+    timer(nthreads)  # first touch of the output buffers, not timed
+    reps, total = _timed_reps(lambda: timer(nthreads), budget_s, 100000)
+    reps1, total1 = _timed_reps(lambda: timer(1), budget_s / 4, 100000)
+    n = tokens.size
+    tok_bytes = 2 * 2 * (w.Hq + w.Hkv) * w.D * w.elem_bytes  # the GPU's count, fwd + bwd
+    return {
+        "value": n * reps / total,
+        "unit": "tokens/s",
+        "cores": nthreads,
+        "kind": "oracle",
+        "sample": f"{n} evenly spaced tokens of the {w.name} workload (T={w.T}): their rows "
+                  f"of Q, K, dQ, dK through the oracle's forward + backward, {reps} passes, "
+                  f"{total:.1f} s timed",
+        "seconds_per_token": total / (reps * n),
+        "GBps": tok_bytes * n * reps / total / 1e9,
+        "value_1_core": n * reps1 / total1,
+        "GBps_1_core": tok_bytes * n * reps1 / total1 / 1e9,
+        "cpu_model": cpu_model(),
+    }
+
+
+SWEEP_TOKENS = [2048, 4096, 8192, 8554, 12288, 16384, 24576, 32768, 65536, 131072, 262144,
+                524288]
+SWEEP_HEADS = (32, 8, 128)  # Hq, Hkv, D: the Qwen3-4B/8B attention shape
+SWEEP_FILE = os.path.join(ROOT, "profiles", "rope_qk_size_sweep.txt")
+
+
+def sweep_workload(T: int) -> workloads.Workload:
+    """One sequence of T tokens in the 32 + 8 head, D = 128, bf16 shape."""
+    Hq, Hkv, D = SWEEP_HEADS
+    return workloads.Workload(f"sweep_{T}", 90, T, Hq, Hkv, D, "bf16", 1e6,
+                              np.array([0, T], dtype=np.int32), description=f"one sequence, T={T}")
+
+
+def linear_fit(x, y):
+    """Least-squares t = t0 + b x; returns (t0, b)."""
+    A = np.stack([np.ones(len(x)), np.asarray(x, dtype=np.float64)], 1)
+    (t0, b), *_ = np.linalg.lstsq(A, np.asarray(y, dtype=np.float64), rcond=None)
+    return float(t0), float(b)
+
+
+def size_sweep(rope, dev, n_steps: int) -> dict:
+    """Region-timed default launches and the torch in-place reference at every size
+    of SWEEP_TOKENS, with t = t0 + b T fitted to each."""
+    rows = []
+    for T in SWEEP_TOKENS:
+        print(f"[sweep] T={T}", file=sys.stderr, flush=True)
+        r = time_workload(rope, sweep_workload(T), dev, n_steps, 20)
+        rows.append({"T": T, "avg_launch_us": r["avg_launch_us"],
+                     "torch_inplace_us": r["torch_inplace_us"], "GBps": r["GBps"],
+                     "index": r["index"]})
+    per_token = 2 * (SWEEP_HEADS[0] + SWEEP_HEADS[1]) * SWEEP_HEADS[2] * 2
+    out = {"sweep": "RoPE launch time vs tokens (one sequence, 32+8 heads, D=128, bf16)",
+           "bytes_per_token": per_token, "rows": rows}
+    for key in ("avg_launch_us", "torch_inplace_us"):
+        t0, b = linear_fit([r["T"] for r in rows], [r[key] for r in rows])
+        out[f"fit_{key}"] = {"t0_us": t0, "us_per_token": b,
+                             "asymptotic_GBps": per_token / (b * 1e-6) / 1e9}
+    return out
+
+
+def write_sweep_summary(run_dir: str, command: str) -> None:
+    """profiles/rope_qk_size_sweep.txt from a rocprofv3 --kernel-trace of bench.py
+    --sweep (run_dir/**/*kernel_trace.csv) and that run's JSON line
+    (run_dir/sweep.json): per size, the RoPE kernel's average dispatch duration
+    (trace) and region timing, torch's in-place reference (region timing), and
+    t = t0 + b T fitted to each."""
+    import glob
+    with open(os.path.join(run_dir, "sweep.json")) as fh:
+        js = json.loads([ln for ln in fh if ln.startswith("{")][-1])
+    Hq, Hkv, D = SWEEP_HEADS
+    groups = -(-Hq // 8) + -(-Hkv // 8)
+    durs = {}
+    for path in glob.glob(os.path.join(run_dir, "**", "*kernel_trace.csv"), recursive=True):
+        with open(path) as fh:
+            for row in csv.DictReader(fh):
+                if "rope_qk_group_kernel" not in row["Kernel_Name"]:
+                    continue
+                T = int(row["Grid_Size_X"]) // (64 * groups)
+                durs.setdefault(T, []).append(
+                    (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3)
+    per_token = js["bytes_per_token"]
+    lines = [f"{'tokens':>8s} {'trace avg us':>13s} {'GB/s':>6s} {'% peak':>7s} "
+             f"{'region us':>10s} {'torch neg_ us':>14s} {'torch GB/s':>10s} {'ratio':>6s} index"]
+    xs, ys = [], []
+    for r in js["rows"]:
+        T = r["T"]
+        d = np.array(durs.get(T, [np.nan]))
+        avg = float(np.mean(d))
+        gb = per_token * T / (avg * 1e-6) / 1e9
+        tgb = per_token * T / (r["torch_inplace_us"] * 1e-6) / 1e9
+        lines.append(f"{T:8d} {avg:13.2f} {gb:6.0f} {100 * gb / HBM_PEAK_GBPS:6.1f}% "
+                     f"{r['avg_launch_us']:10.2f} {r['torch_inplace_us']:14.2f} {tgb:10.0f} "
+                     f"{r['torch_inplace_us'] / avg:6.3f} {r['index']}")
+        if np.isfinite(avg):
+            xs.append(T)
+            ys.append(avg)
+    t0, b = linear_fit(xs, ys)
+    lines += ["",
+              f"fit, RoPE kernel (trace averages): t = {t0:.2f} us + T x {b * 1e3:.4f} ns "
+              f"-> asymptotic {per_token / (b * 1e-6) / 1e9:.0f} GB/s "
+              f"({100 * per_token / (b * 1e-6) / 1e9 / HBM_PEAK_GBPS:.1f}% of 8 TB/s)"]
+    for key, label in (("avg_launch_us", "RoPE kernel (region timing)"),
+                       ("torch_inplace_us", "torch in-place neg_ on Q and K (region timing)")):
+        f = js[f"fit_{key}"]
+        lines.append(f"fit, {label}: t = {f['t0_us']:.2f} us + T x {f['us_per_token'] * 1e3:.4f} "
+                     f"ns -> asymptotic {f['asymptotic_GBps']:.0f} GB/s")
+    for T in (8554, 16384):
+        lines.append(f"at T={T}: fixed part t0 / t = {t0 / (t0 + b * T):.3f}; at the asymptotic "
+                     f"rate the launch would take {b * T:.2f} us "
+                     f"({100 * per_token * T / (b * T * 1e-6) / 1e9 / HBM_PEAK_GBPS:.1f}%)")
+    header = [
+        "# RoPE launch time against token count: one sequence of T tokens, Hq=32, Hkv=8, D=128,",
+        "# bf16, theta=1e6, default launch (row-group kernel; 64-bit offsets at T=524288), each",
+        "# size on its own rotating buffer sets (>= 2 GiB between touches of one buffer); beside",
+        "# it torch's in-place neg_ over the same bytes (Q then K), the achievable-pattern reference.",
+        f"# algorithmic bytes per token and launch: {per_token}",
+        f"# command (R = repository root, on one MI355X): {command}",
+        "",
+    ]
+    _write_summary(SWEEP_FILE, header, lines)
+
+
 GLU_METRIC = "SwiGLU/GeGLU fwd+bwd tokens/s and achieved HBM GB/s (% of peak)"
 
 
@@ -835,7 +1126,16 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default=None,
                     choices=workloads.names() + workloads.glu_names(),
-                    help="default: qwen3_4b_packed (glu_qwen3_4b with --glu)")
+                    help=f"default: {HEADLINE_WORKLOAD} (glu_qwen3_4b with --glu)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time the default launch over a range of token counts (one sequence, "
+                         "32+8 heads) with a torch in-place reference, fit t = t0 + b T, then exit")
+    ap.add_argument("--sweep-summary", default=None, metavar="RUN_DIR",
+                    help="write profiles/rope_qk_size_sweep.txt from RUN_DIR (rocprofv3 kernel "
+                         "trace of --sweep and its JSON line in RUN_DIR/sweep.json), then exit")
+    ap.add_argument("--configs", default="all", choices=["all", "none"],
+                    help="all: also time every other RoPE workload's default launches and put "
+                         "them in the JSON line (per_config); none: the chosen workload only")
     ap.add_argument("--tokens-per-wave", type=int, default=0, help="0: library default")
     ap.add_argument("--positions", default="cu", choices=["cu", "ids", "shards4"],
                     help="position source: cu_seqlens; explicit per-token ids; or the batch "
@@ -864,6 +1164,10 @@ def main():
                     metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                     help="write the PMC traffic summary from rocprofv3 counter CSVs, then exit")
     ap.add_argument("--traffic-command", default="", help="commands recorded in that summary")
+    ap.add_argument("--traffic-ea", nargs=4, default=None,
+                    metavar=("EA_READ_CSV", "EA_WRITE_CSV", "COPY_EA_READ_CSV", "COPY_EA_WRITE_CSV"),
+                    help="with --traffic-summary: also derive bytes from TCC-to-memory request "
+                         "counts (the second counter family)")
     ap.add_argument("--traffic-kernel", default="rope", choices=["rope", "glu"],
                     help="which kernel's summary --traffic-summary writes")
     ap.add_argument("--trace-summary", default=None, metavar="KERNEL_TRACE_CSV",
@@ -882,6 +1186,9 @@ def main():
                          "--pmc and --kernel-trace output folders, then exit")
     args = ap.parse_args()
 
+    if args.sweep_summary:
+        write_sweep_summary(args.sweep_summary, args.trace_command)
+        return
     if args.glu_valu_summary:
         write_glu_valu_summary(args.glu_valu_summary, args.trace_command)
         return
@@ -898,8 +1205,11 @@ def main():
         return
 
     if args.traffic_summary:
-        writer = write_glu_traffic_summary if args.traffic_kernel == "glu" else write_traffic_summary
-        writer(*args.traffic_summary, command=args.traffic_command)
+        if args.traffic_kernel == "glu":
+            write_glu_traffic_summary(*args.traffic_summary, command=args.traffic_command)
+        else:
+            write_traffic_summary(*args.traffic_summary, command=args.traffic_command,
+                                  workload=args.workload or HEADLINE_WORKLOAD, ea=args.traffic_ea)
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -919,13 +1229,16 @@ def main():
         if args.workload not in workloads.glu_names():
             raise SystemExit("--glu takes a glu_* workload")
         return bench_glu(args)
-    args.workload = args.workload or "qwen3_4b_packed"
+    args.workload = args.workload or HEADLINE_WORKLOAD
     if args.workload not in workloads.names():
         raise SystemExit("glu_* workloads need --glu")
 
     import packed_varlen_rotary_rope_amd as rope
 
     dev = torch.device("cuda:0")
+    if args.sweep:
+        print(json.dumps(size_sweep(rope, dev, max(50, min(args.steps, 500)))))
+        return
     w = workloads.get(args.workload)
     set_bytes = 2 * w.T * (w.Hq + w.Hkv) * w.D * w.elem_bytes  # Q, K, dQ, dK
     # Enough sets that a buffer is touched again only after >= 8x the Infinity
@@ -1061,8 +1374,12 @@ def main():
     # the PMC traffic summary covers the default configuration of this workload only
     default_config = (args.positions == "cu" and args.pos_scale == 1.0 and tpw == 0
                       and args.layout == "contiguous" and args.index == "auto"
-                      and args.cos_sin == "fly")
-    traffic = read_traffic() if w.name == "qwen3_4b_packed" and default_config else None
+                      and args.cos_sin == "fly" and not args.graph)
+    traffic = read_traffic(traffic_path(w.name)) if default_config else None
+    # the torch in-place elementwise reference over the same bytes, same buffer sets
+    ref_us = None
+    if w.seqused is None and args.layout == "contiguous":
+        ref_us = inplace_reference_us(sets, nsets, stream, 2 * max(args.steps, 20))
 
     out = {
         "metric": METRIC,
@@ -1106,9 +1423,44 @@ def main():
             "sampled_min_launch_us": float(np.min(launch_ms)) * 1e3,
         },
     }
+    if ref_us is not None:
+        out["roofline"]["frac_of_ceiling"] = ref_us / (avg_launch_s * 1e6)
+        out["roofline"]["ceiling_reference"] = {
+            "op": "torch in-place neg_ on Q, then on K (same bytes as one launch)",
+            "avg_pass_us": ref_us, "GBps": bpl / (ref_us * 1e-6) / 1e9,
+            "frac_of_ceiling": "reference time / RoPE launch time"}
     if args.cpu_seconds > 0:
         nthreads = max(1, min(16, len(os.sched_getaffinity(0))))
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, nthreads)
+        if w.T * (w.Hq + w.Hkv) * w.D > 2 ** 28:  # too large to process whole on the host
+            out["cpu_baseline"] = cpu_baseline_sampled(w, sets[0], args.cpu_seconds, nthreads)
+        else:
+            out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, nthreads)
+    if args.configs == "all" and default_config:
+        del sets, events
+        torch.cuda.empty_cache()
+        per = {}
+        for name in SUB_WORKLOADS:
+            if name == w.name:
+                per[name] = {
+                    "T": w.T, "valid_tokens": w.valid_tokens, "Hq": w.Hq, "Hkv": w.Hkv,
+                    "D": w.D, "dtype": w.dtype, "kernel": rope_kernel_name(w, 0),
+                    "index": "64-bit" if needs_long_index(w) else "32-bit",
+                    "bytes_per_launch": bpl, "avg_launch_us": avg_launch_s * 1e6,
+                    "GBps": achieved, "frac": achieved / HBM_PEAK_GBPS,
+                    "fwd_bwd_tokens_per_s": w.valid_tokens / (2 * avg_launch_s),
+                    "launches_timed": 2 * args.steps, "headline": True}
+                if ref_us is not None:
+                    per[name]["torch_inplace_us"] = ref_us
+                    per[name]["frac_of_ceiling"] = ref_us / (avg_launch_s * 1e6)
+                continue
+            sw = workloads.get(name)
+            print(f"[bench] timing {name}", file=sys.stderr, flush=True)
+            per[name] = time_workload(rope, sw, dev, 200, 20)
+        if "qwen3_8b_padded" in per and "qwen3_8b_packed" in per:
+            pad, pk = per["qwen3_8b_padded"], per["qwen3_8b_packed"]
+            pad["t_over_packed"] = pad["avg_launch_us"] / pk["avg_launch_us"]
+            pad["valid_fraction"] = pad["valid_tokens"] / pad["T"]
+        out["per_config"] = per
     print(json.dumps(out))
 
 

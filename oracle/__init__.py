@@ -76,6 +76,9 @@ class Oracle:
         lib.oracle_rope_rows_ex.argtypes = [i32, vp, vp, vp, i64, i32, i32, vp, i32, vp, vp, vp,
                                             dbl, dbl, i32, i32]
         lib.oracle_rope_rows_ex.restype = i32
+        lib.oracle_rows_fwd_bwd_seconds.argtypes = [i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64,
+                                                    i32, i32, i32, vp, i32, vp, dbl, i32]
+        lib.oracle_rows_fwd_bwd_seconds.restype = dbl
         self.lib = lib
         self.path = path
 
@@ -182,6 +185,28 @@ class Oracle:
         return sec
 
 
+    def rows_fwd_bwd_timer(self, q_rows, k_rows, dq_rows, dk_rows, tokens, cu_seqlens,
+                           theta: float, dtype: str, seqused=None):
+        """A callable(nthreads) -> seconds: the oracle's forward on the gathered rows
+        of q and k plus its backward on those of dq and dk (rows[n, H, D] of the
+        listed tokens), timed inside the C library; outputs are allocated once."""
+        ins = [_storage(a, dtype) for a in (q_rows, k_rows, dq_rows, dk_rows)]
+        outs = [np.empty(a.shape, dtype=np.float32) for a in ins]
+        tok = np.ascontiguousarray(tokens, dtype=np.int64)
+        n, Hq, D = ins[0].shape
+        Hkv = ins[1].shape[1]
+        cu, su = _i32(cu_seqlens), _i32(seqused)
+
+        def run(nthreads: int) -> float:
+            sec = self.lib.oracle_rows_fwd_bwd_seconds(
+                _DTYPES[dtype], *(_ptr(a) for a in ins), *(_ptr(o) for o in outs), _ptr(tok), n,
+                Hq, Hkv, D, _ptr(cu), cu.size - 1, _ptr(su), float(theta), int(nthreads))
+            if sec < 0:
+                raise ValueError("oracle rejected its arguments")
+            return sec
+        return run
+
+
 _default: Oracle | None = None
 
 
@@ -230,3 +255,9 @@ def round_bf16(y):
 
 def fwd_bwd_seconds(q, k, dq, dk, cu_seqlens, theta, dtype, seqused=None, nthreads=1):
     return default().fwd_bwd_seconds(q, k, dq, dk, cu_seqlens, theta, dtype, seqused, nthreads)
+
+
+def rows_fwd_bwd_timer(q_rows, k_rows, dq_rows, dk_rows, tokens, cu_seqlens, theta, dtype,
+                       seqused=None):
+    return default().rows_fwd_bwd_timer(q_rows, k_rows, dq_rows, dk_rows, tokens, cu_seqlens,
+                                        theta, dtype, seqused)

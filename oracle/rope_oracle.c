@@ -388,3 +388,28 @@ double oracle_fwd_bwd_seconds(int32_t dtype, const void* q, const void* k, const
   if (rc) return -1.0;
   return (double)(b.tv_sec - a.tv_sec) + 1e-9 * (double)(b.tv_nsec - a.tv_nsec);
 }
+
+/* The same for a sample of tokens: forward over the gathered rows of Q and K,
+ * backward over those of dQ and dK (oracle_rope_rows each), timed as one unit.
+ * For the CPU baseline on inputs too large to process whole. */
+double oracle_rows_fwd_bwd_seconds(int32_t dtype, const void* q_rows, const void* k_rows,
+                                   const void* dq_rows, const void* dk_rows, float* yq,
+                                   float* yk, float* ydq, float* ydk, const int64_t* tokens,
+                                   int64_t n, int32_t Hq, int32_t Hkv, int32_t D,
+                                   const int32_t* cu, int32_t num_seqs, const int32_t* seqused,
+                                   double theta, int32_t nthreads) {
+  struct timespec a, b;
+  clock_gettime(CLOCK_MONOTONIC, &a);
+  int rc = 0;
+  rc |= oracle_rope_rows(dtype, q_rows, yq, tokens, n, Hq, D, cu, num_seqs, seqused, theta, +1,
+                         nthreads);
+  rc |= oracle_rope_rows(dtype, k_rows, yk, tokens, n, Hkv, D, cu, num_seqs, seqused, theta, +1,
+                         nthreads);
+  rc |= oracle_rope_rows(dtype, dq_rows, ydq, tokens, n, Hq, D, cu, num_seqs, seqused, theta, -1,
+                         nthreads);
+  rc |= oracle_rope_rows(dtype, dk_rows, ydk, tokens, n, Hkv, D, cu, num_seqs, seqused, theta, -1,
+                         nthreads);
+  clock_gettime(CLOCK_MONOTONIC, &b);
+  if (rc) return -1.0;
+  return (double)(b.tv_sec - a.tv_sec) + 1e-9 * (double)(b.tv_nsec - a.tv_nsec);
+}

@@ -58,9 +58,27 @@ def test_kernel_choice():
     assert bench.rope_kernel_name(workloads.get("qwen3_8b_padded"), 0) == "rope_qk_kernel"
 
 
+def test_kernel_instance_names():
+    """The mangled-name fragments the summaries filter rocprofv3 records by."""
+    w5, w2 = workloads.get("long_ctx_512k"), workloads.get("qwen3_4b_packed")
+    assert bench.needs_long_index(w5) and not bench.needs_long_index(w2)
+    assert bench.rope_kernel_instance(w5, True) == "rope_qk_group_kernelIDF16bLi8ELb1ELb0E"
+    assert bench.rope_kernel_instance(w2, False) in GROUP
+    assert bench.rope_kernel_instance(workloads.get("tiny_packed"), False) == \
+        "rope_qk_group_kernelIfLi4ELb0ELb0E"
+    assert bench.rope_kernel_instance(workloads.get("qwen3_8b_padded"), False) == \
+        "rope_qk_kernelIDF16bLi8ELb0ELb0E"
+
+
+def test_linear_fit():
+    T = np.array([1000, 2000, 8000, 64000])
+    t0, b = bench.linear_fit(T, 1.5 + 0.003 * T)
+    assert abs(t0 - 1.5) < 1e-9 and abs(b - 0.003) < 1e-12
+
+
 def test_traffic_summary_and_hash_check(tmp_path, monkeypatch):
     out = tmp_path / "traffic.txt"
-    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(out))
+    monkeypatch.setattr(bench, "traffic_path", lambda workload: str(out))
     kib = 1024.0
     # the copy reads 1 GiB and writes 1 GiB; its counters read half and all of that
     _counter_csv(str(tmp_path / "cf.csv"), [(COPY, "FETCH_SIZE", 2 ** 30 / kib / 2)])
@@ -77,6 +95,71 @@ def test_traffic_summary_and_hash_check(tmp_path, monkeypatch):
     # a summary taken on other kernel sources is not used
     out.write_text(text.replace(bench.kernel_source_hash(bench.ROPE_SOURCES), "0" * 16))
     assert bench.read_traffic(str(out)) is None
+
+
+def test_traffic_summary_request_counts(tmp_path, monkeypatch):
+    """The second counter family: bytes from request counts x request sizes by the
+    counters' definitions (no calibration), for the long-context (64-bit) instance."""
+    out = tmp_path / "traffic.txt"
+    monkeypatch.setattr(bench, "traffic_path", lambda workload: str(out))
+    w = workloads.get("long_ctx_512k")
+    bpl = bench.algorithmic_bytes_per_launch(w)
+    long_k = "_ZN12_GLOBAL__N_120rope_qk_group_kernelIDF16bLi8ELb1ELb0EEEvPT_S2_"
+    kib = 1024.0
+    for name, ctr, val in (("cf", "FETCH_SIZE", 2 ** 30 / kib / 2), ("cw", "WRITE_SIZE", 2 ** 30 / kib)):
+        _counter_csv(str(tmp_path / f"{name}.csv"), [(COPY, ctr, val)])
+    _counter_csv(str(tmp_path / "f.csv"), [(long_k, "FETCH_SIZE", bpl / 2 / kib / 2)])
+    _counter_csv(str(tmp_path / "w.csv"), [(long_k, "WRITE_SIZE", bpl / 2 / kib)])
+    # all reads are 128-byte requests, all writes 64-byte ones
+    def rd(n):
+        return [("TCC_EA0_RDREQ_sum", n), ("TCC_EA0_RDREQ_32B_sum", 0),
+                ("TCC_EA0_RDREQ_128B_sum", n), ("TCC_BUBBLE_sum", 0)]
+    def wr(n):
+        return [("TCC_EA0_WRREQ_sum", n), ("TCC_EA0_WRREQ_64B_sum", n)]
+    _counter_csv(str(tmp_path / "er.csv"), [(long_k, c, v) for c, v in rd(bpl / 2 / 128)]
+                 + [(GROUP, c, 1.0) for c, v in rd(1)])
+    _counter_csv(str(tmp_path / "ew.csv"), [(long_k, c, v) for c, v in wr(bpl / 2 / 64)])
+    _counter_csv(str(tmp_path / "cer.csv"), [(COPY, c, v) for c, v in rd(2 ** 30 / 128)])
+    _counter_csv(str(tmp_path / "cew.csv"), [(COPY, c, v) for c, v in wr(2 ** 30 / 64)])
+    bench.write_traffic_summary(*(str(tmp_path / f"{n}.csv") for n in ("f", "w", "cf", "cw")),
+                                "cmd", workload="long_ctx_512k",
+                                ea=[str(tmp_path / f"{n}.csv") for n in ("er", "ew", "cer", "cew")])
+    text = out.read_text()
+    assert "rope_qk_group_kernelIDF16bLi8ELb1ELb0E" in text
+    assert "traffic_over_algorithmic: 1.0000" in text
+    assert "ea_traffic_over_algorithmic: 1.0000" in text
+    assert "ea_copy_read_bytes_for_1GiB: 1073741824 (x1.0000)" in text
+    assert bench.read_traffic(str(out)) == bpl
+
+
+def test_sweep_summary(tmp_path, monkeypatch):
+    out = tmp_path / "sweep.txt"
+    monkeypatch.setattr(bench, "SWEEP_FILE", str(out))
+    sizes = [2048, 16384, 65536]
+    rows, trace = [], []
+    for T in sizes:
+        us = 1.5 + 0.003 * T
+        rows.append({"T": T, "avg_launch_us": us + 0.1, "torch_inplace_us": 2 + 0.0035 * T,
+                     "GBps": 0.0, "index": "32-bit"})
+        trace.append((T, int(us * 1e3)))
+    js = {"bytes_per_token": 20480, "rows": rows}
+    for key in ("avg_launch_us", "torch_inplace_us"):
+        t0, b = bench.linear_fit(sizes, [r[key] for r in rows])
+        js[f"fit_{key}"] = {"t0_us": t0, "us_per_token": b,
+                            "asymptotic_GBps": 20480 / (b * 1e-6) / 1e9}
+    (tmp_path / "sweep.json").write_text("noise\n" + bench.json.dumps(js) + "\n")
+    fields = ["Kernel_Name", "Start_Timestamp", "End_Timestamp", "Grid_Size_X"]
+    os.makedirs(tmp_path / "tr")
+    with open(tmp_path / "tr" / "x_kernel_trace.csv", "w", newline="") as fh:
+        wr = csv.DictWriter(fh, fieldnames=fields)
+        wr.writeheader()
+        for T, ns in trace:
+            for _ in range(3):
+                wr.writerow({"Kernel_Name": GROUP, "Start_Timestamp": 0, "End_Timestamp": ns,
+                             "Grid_Size_X": T * 5 * 64})
+    bench.write_sweep_summary(str(tmp_path), "cmd")
+    text = out.read_text()
+    assert "fit, RoPE kernel (trace averages): t = 1.50 us + T x 3.0000 ns" in text, text
 
 
 def test_trace_summary(tmp_path, monkeypatch):

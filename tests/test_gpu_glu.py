@@ -114,6 +114,38 @@ def test_glu_workload_parity(rope, name, kind):
     check_all(rope, kind, w.dtype, e, g, dh, name)
 
 
+def f32_ulps(got: np.ndarray, ref: np.ndarray) -> np.ndarray:
+    """|got - ref| in units of the fp32 ulp at the exact value ref (normal range;
+    below it the smallest subnormal step)."""
+    mag = np.maximum(np.abs(ref), 2.0 ** -126)
+    ulp = np.exp2(np.floor(np.log2(mag)) - 23)
+    return np.abs(got.astype(np.float64) - ref) / ulp
+
+
+@pytest.mark.parametrize("kind", KINDS)
+def test_glu_f32_accuracy(rope, kind):
+    """fp32 storage on 4096 x 1024 elements, e ~ N(0, 4^2) (so the tails out to
+    |e| ~ 20 are sampled), against the oracle; reports the worst error in fp32 ulps
+    per |e| band for each output."""
+    rows, cols = 4096, 1024
+    print(f"[glu f32 accuracy] {kind}", flush=True)
+    e = make((rows, cols), 9900, "f32", scale=4.0)
+    g = make((rows, cols), 9901, "f32")
+    dh = make((rows, cols), 9902, "f32")
+    h, de, dg = check_all(rope, kind, "f32", e, g, dh, "f32acc")
+    we, wg, wd = words(e), words(g), words(dh)
+    ref = {"h": glu_oracle.fwd(kind, we, wg, "f32", NTHREADS)}
+    ref["de"], ref["dg"] = glu_oracle.bwd(kind, wd, we, wg, "f32", NTHREADS)
+    ae = np.abs(we.astype(np.float64))
+    bands = [(0, 1), (1, 2), (2, 4), (4, 8), (8, 16), (16, 1e9)]
+    for name, got in (("h", h), ("de", de), ("dg", dg)):
+        u = f32_ulps(words(got), ref[name])
+        worst = [float(u[(ae >= a) & (ae < b)].max()) if ((ae >= a) & (ae < b)).any() else 0.0
+                 for a, b in bands]
+        print(f"[glu f32 ulps] {kind} {name}: " +
+              " ".join(f"|e|in[{a},{b}):{w:.1f}" for (a, b), w in zip(bands, worst)), flush=True)
+
+
 # ---------------------------------------------------------------- edge values
 
 def edge_values(dtype: str) -> np.ndarray:
@@ -269,19 +301,20 @@ def test_empty(rope):
     assert de.shape == (5, 0)
 
 
-def test_long_context_int64(rope):
-    """524288 tokens x 9728 (5.1e9 elements, 2.4 x 2^31): the 64-bit path. SwiGLU
-    forward and in-place backward; rows at the start, around the 2^31-element
+@pytest.mark.parametrize("kind", KINDS)
+def test_long_context_int64(rope, kind):
+    """524288 tokens x 9728 (5.1e9 elements, 2.4 x 2^31): the 64-bit path, for each
+    kind. Forward and in-place backward; rows at the start, around the 2^31-element
     boundary, at the end, and every 97th row (a prime stride, so the sampled rows'
     offsets take every residue of the power-of-two tile sizes) against the oracle."""
     w = workloads.glu_get("glu_long_512k")
-    print("[glu parity] glu_long_512k int64 path", flush=True)
+    print(f"[glu parity] glu_long_512k int64 path {kind}", flush=True)
     assert w.elements >= 2 ** 31
     e = workloads.make_tensor((w.rows, w.cols), w.seed("e"), w.dtype, device=DEV, chunk_rows=32768)
     g = workloads.make_tensor((w.rows, w.cols), w.seed("g"), w.dtype, device=DEV, chunk_rows=32768)
-    h = rope.glu_fwd("swiglu", e, g)
+    h = rope.glu_fwd(kind, e, g)
     with pytest.raises(rope.RopeError):
-        rope.glu_fwd("swiglu", e, g, out=h, index_mode=rope.INDEX_32)
+        rope.glu_fwd(kind, e, g, out=h, index_mode=rope.INDEX_32)
     boundary_row = (2 ** 31) // w.cols
     rows = np.unique(np.concatenate([np.arange(0, 4), np.arange(boundary_row - 2, boundary_row + 3),
                                      np.arange(w.rows - 4, w.rows), np.arange(0, w.rows, 97)]))
@@ -289,14 +322,14 @@ def test_long_context_int64(rope):
     e_s, g_s = words(e.index_select(0, idx)), words(g.index_select(0, idx))
     ev = values(e_s, w.dtype)
     torch.cuda.synchronize()
-    ref_h = glu_oracle.fwd("swiglu", e_s, g_s, w.dtype, NTHREADS)
-    assert_glu_parity(w.dtype, words(h.index_select(0, idx)), ref_h, ev, "long:h")
+    ref_h = glu_oracle.fwd(kind, e_s, g_s, w.dtype, NTHREADS)
+    assert_glu_parity(w.dtype, words(h.index_select(0, idx)), ref_h, ev, f"long:{kind}:h")
     dh = h  # reuse the buffer as the upstream gradient (any values will do)
     d_s = words(dh.index_select(0, idx))
-    rope.glu_bwd("swiglu", dh, e, g, de=e, dg=g)
+    rope.glu_bwd(kind, dh, e, g, de=e, dg=g)
     torch.cuda.synchronize()
-    ref_de, ref_dg = glu_oracle.bwd("swiglu", d_s, e_s, g_s, w.dtype, NTHREADS)
-    assert_glu_parity(w.dtype, words(e.index_select(0, idx)), ref_de, ev, "long:de")
-    assert_glu_parity(w.dtype, words(g.index_select(0, idx)), ref_dg, ev, "long:dg")
+    ref_de, ref_dg = glu_oracle.bwd(kind, d_s, e_s, g_s, w.dtype, NTHREADS)
+    assert_glu_parity(w.dtype, words(e.index_select(0, idx)), ref_de, ev, f"long:{kind}:de")
+    assert_glu_parity(w.dtype, words(g.index_select(0, idx)), ref_dg, ev, f"long:{kind}:dg")
     del e, g, h, dh
     torch.cuda.empty_cache()
