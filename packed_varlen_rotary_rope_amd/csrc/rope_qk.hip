@@ -36,6 +36,7 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+#include <string.h>
 
 #include "../../include/rope_qk.h"
 #include "cr_sincos.h"
@@ -492,10 +493,28 @@ __global__ __launch_bounds__(kBlock) void rope_cos_sin_kernel(const int32_t* __r
 
 // ---- host side -----------------------------------------------------------------------
 
-// a2: inv_freq[j] = theta^(-2j/D), evaluated in extended precision and rounded once.
+// a2: inv_freq[j] = theta^(-2j/D), correctly rounded to fp32.
+// Fast path in double: the exponent -2j/D rounds with a relative error of at most
+// 2^-53, which moves theta^e by at most |ln theta| * 2^-53 relative (< 2^-43.4 for
+// any finite theta), and pow adds under one double ulp: the double result is within
+// about 800 double ulps of the exact value. Rounding it to fp32 therefore gives the
+// correctly rounded result unless it lies within that distance of a binary32
+// midpoint -- its 29 bits below binary32 precision near 0x10000000 -- or below the
+// binary32 normal range; those values (about 1 in 65000) are recomputed in
+// extended precision (powl with a 64-bit-mantissa exponent), as is the whole
+// table on hosts without an 80-bit long double. powl for every entry costs about
+// 0.35 us each, more than a short launch's GPU time.
 void host_inv_freq(double theta, int32_t D, float* out) {
-  for (int32_t j = 0; j < D / 2; ++j)
-    out[j] = (float)powl((long double)theta, -(2.0L * (long double)j) / (long double)D);
+  constexpr int64_t kWindow = 4096;  // double ulps; 5x the error bound above
+  for (int32_t j = 0; j < D / 2; ++j) {
+    const double v = pow(theta, -(2.0 * (double)j) / (double)D);
+    uint64_t u;
+    memcpy(&u, &v, sizeof u);
+    const int64_t low = (int64_t)(u & 0x1fffffffu) - 0x10000000;
+    const bool safe = v >= 0x1p-126 && (low > kWindow || low < -kWindow);
+    out[j] = safe ? (float)v
+                  : (float)powl((long double)theta, -(2.0L * (long double)j) / (long double)D);
+  }
 }
 
 bool valid_theta(double theta) { return isfinite(theta) && theta >= 1.0; }

@@ -208,6 +208,24 @@ def test_host_inv_freq(theta, D):
     assert np.array_equal(got.view(np.uint32), oracle.inv_freq(theta, D).view(np.uint32))
 
 
+def test_host_inv_freq_many_thetas():
+    """The fast host path (double pow, extended precision only near a binary32
+    midpoint) against the oracle (extended precision throughout, itself pinned to
+    mpmath) for 300 random log-uniform theta in [1, 1e12] and every even D up to 512
+    in turn, and against mpmath directly on a sample."""
+    rng = np.random.default_rng(44)
+    thetas = np.concatenate([[1.0, 2.0, 1e4, 5e5, 1e6, 1e7, 8e6, 2.5e5, 1e12],
+                             10.0 ** rng.uniform(0, 12, 300)])
+    Ds = list(range(2, 514, 2))
+    for i, theta in enumerate(thetas):
+        D = Ds[i % len(Ds)] if i >= 9 else 128
+        got = rope.inv_freq(float(theta), D).numpy()
+        assert np.array_equal(got.view(np.uint32), oracle.inv_freq(float(theta), D).view(np.uint32)), \
+            (theta, D)
+        if i % 30 == 0:
+            assert np.array_equal(got.view(np.uint32), ref_inv_freq(float(theta), D).view(np.uint32))
+
+
 def test_trig_constants_regenerate():
     sys.path.insert(0, CSRC)
     try:
