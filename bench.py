@@ -71,6 +71,13 @@ GLU_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "glu_swiglu_qwen3_4b_traffic.t
 GLU_KERNEL_KEYS = {"fwd": "glu_kernelIDF16bLi8ELi0ELb0ELb1Ej", "bwd": "glu_kernelIDF16bLi8ELi0ELb1ELb1Ej"}
 
 
+def glu_instance(code: int, bwd: int) -> str:
+    """Mangled-name fragment of the bf16, 16-byte, dense GLU instance the library runs
+    by default for this kind and pass (the tanh-GeGLU backward takes 64-bit offsets)."""
+    index = "l" if (code == 2 and bwd) else "j"
+    return f"glu_kernelIDF16bLi8ELi{code}ELb{bwd}ELb1E{index}"
+
+
 def kernel_source_hash(sources=ROPE_SOURCES) -> str:
     h = hashlib.sha256()
     for name in sources:
@@ -499,7 +506,7 @@ def write_glu_trace_summary(run_dir: str, command: str) -> None:
                 for row in csv.DictReader(fh):
                     name = row["Kernel_Name"]
                     for launch, bwd in (("forward", 0), ("backward", 1)):
-                        if f"glu_kernelIDF16bLi8ELi{code}ELb{bwd}ELb1Ej" in name:
+                        if glu_instance(code, bwd) in name:
                             durs[launch].append((int(row["End_Timestamp"])
                                                  - int(row["Start_Timestamp"])) / 1e3)
         with open(os.path.join(run_dir, f"glu_bench_{kind}.log")) as fh:
@@ -521,7 +528,8 @@ def write_glu_trace_summary(run_dir: str, command: str) -> None:
         f"# commands (R = repository root, on one MI355X), for K in swiglu geglu geglu_tanh: {command}",
         f"# algorithmic bytes per launch: forward {per['forward']} (read e, g; write h),",
         f"#                               backward {per['backward']} (read dh, e, g; write de, dg)",
-        "# Instances: glu_kernel<__bf16, VEC=8, KIND, BWD, DENSE=true, uint32 offsets>; the other",
+        "# Instances: glu_kernel<__bf16, VEC=8, KIND, BWD, DENSE=true, uint32 offsets (int64 for the",
+        "# tanh-GeGLU backward, the library's default there)>; the other",
         "# kernels in the traces are torch's input generation and copies (not timed).",
         "",
     ]
@@ -545,7 +553,7 @@ def write_glu_valu_summary(run_dir: str, command: str) -> None:
                                   recursive=True):
                 with open(path) as fh:
                     for row in csv.DictReader(fh):
-                        if f"glu_kernelIDF16bLi8ELi{code}ELb{bwd}ELb1Ej" in row["Kernel_Name"]:
+                        if glu_instance(code, bwd) in row["Kernel_Name"]:
                             acc.setdefault(row["Counter_Name"], []).append(
                                 float(row["Counter_Value"]))
             m = {k: sum(v) / len(v) for k, v in acc.items()}

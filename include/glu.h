@@ -35,9 +35,12 @@
  * offsets are needed; ROPE_EUNSUPPORTED for an unknown dtype; ROPE_ELAUNCH if
  * the launch fails. rows*cols == 0 returns ROPE_OK without launching.
  *
- * index_mode (rope_index_mode): ROPE_INDEX_AUTO picks 64-bit offsets exactly when
- * some element offset of the call reaches 2^31; ROPE_INDEX_64 forces them (the
- * results are identical either way).
+ * index_mode (rope_index_mode): ROPE_INDEX_AUTO picks 64-bit offsets when some
+ * element offset of the call reaches 2^31, and otherwise 32-bit offsets, except
+ * for the tanh-GeGLU backward, whose 64-bit instance is the faster one on gfx950
+ * even where every offset fits; ROPE_INDEX_32 forces 32-bit offsets (rejected when
+ * they do not fit) and ROPE_INDEX_64 64-bit ones. The results are identical either
+ * way.
  */
 #ifndef GLU_H
 #define GLU_H

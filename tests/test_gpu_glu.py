@@ -15,6 +15,7 @@ Bars (derived from the fp32 arithmetic of the kernels, written here):
   * layout variants (access width, dense vs strided, 32- vs 64-bit offsets,
     in place): bit-identical to each other.
 """
+import math
 import os
 
 import numpy as np
@@ -114,6 +115,17 @@ def test_glu_workload_parity(rope, name, kind):
     check_all(rope, kind, w.dtype, e, g, dh, name)
 
 
+def f32_tail(kind: str, e: np.ndarray) -> np.ndarray:
+    """The conditioning of each kind's tail for fp32 arithmetic: e^2 for the exact
+    GELU's erfc tail, |2u(e)| = |2 sqrt(2/pi) (e + 0.044715 e^3)| for the tanh form's
+    exp(2u) tail, none for SwiGLU."""
+    if kind == "geglu":
+        return e * e
+    if kind == "geglu_tanh":
+        return np.abs(2 * math.sqrt(2 / math.pi) * (e + 0.044715 * e ** 3))
+    return np.zeros_like(e)
+
+
 def f32_ulps(got: np.ndarray, ref: np.ndarray) -> np.ndarray:
     """|got - ref| in units of the fp32 ulp at the exact value ref (normal range;
     below it the smallest subnormal step)."""
@@ -136,13 +148,18 @@ def test_glu_f32_accuracy(rope, kind):
     we, wg, wd = words(e), words(g), words(dh)
     ref = {"h": glu_oracle.fwd(kind, we, wg, "f32", NTHREADS)}
     ref["de"], ref["dg"] = glu_oracle.bwd(kind, wd, we, wg, "f32", NTHREADS)
-    ae = np.abs(we.astype(np.float64))
+    ev = we.astype(np.float64)
+    ae = np.abs(ev)
+    tail = f32_tail(kind, ev)
     bands = [(0, 1), (1, 2), (2, 4), (4, 8), (8, 16), (16, 1e9)]
     for name, got in (("h", h), ("de", de), ("dg", dg)):
         u = f32_ulps(words(got), ref[name])
         worst = [float(u[(ae >= a) & (ae < b)].max()) if ((ae >= a) & (ae < b)).any() else 0.0
                  for a, b in bands]
-        print(f"[glu f32 ulps] {kind} {name}: " +
+        A = float(u[ae < 2].max())
+        big = (ae >= 2) & (tail > 0)
+        B = float((u[big] / tail[big]).max()) if big.any() else 0.0
+        print(f"[glu f32 ulps] {kind} {name}: A={A:.1f} B={B:.3f} " +
               " ".join(f"|e|in[{a},{b}):{w:.1f}" for (a, b), w in zip(bands, worst)), flush=True)
 
 
@@ -234,8 +251,8 @@ def test_fused_gate_up_layout(rope, kind):
     ("f32", 1001, 1, 0, 0),      # 4-byte chunks
 ])
 def test_layout_variants_bit_identical(rope, dtype, cols, lead, in_pad, out_pad):
-    """Access widths, strides and forced 64-bit offsets all give the dense default's
-    bits; gap elements are never written."""
+    """Access widths, strides and forced 32- or 64-bit offsets all give the dense
+    default's bits; gap elements are never written."""
     rows = 257
     ft = TORCH_DT[dtype]
     print(f"[glu parity] layouts {dtype} cols={cols} lead={lead} pads={in_pad},{out_pad}",
@@ -261,7 +278,7 @@ def test_layout_variants_bit_identical(rope, dtype, cols, lead, in_pad, out_pad)
     g.copy_(g0)
     dh.copy_(d0)
     for kind in KINDS:
-        for mode in (rope.INDEX_AUTO, rope.INDEX_64):
+        for mode in (rope.INDEX_AUTO, rope.INDEX_32, rope.INDEX_64):
             rope.glu_fwd(kind, e, g, out=hv, index_mode=mode)
             de, dg = rope.glu_bwd(kind, dh, e, g, index_mode=mode)
             torch.cuda.synchronize()
