@@ -427,27 +427,102 @@ def write_counters_summary(fly_dir, table_dir, copy_fetch_csv, copy_write_csv, c
     _write_summary(COUNTERS_FILE, header, lines)
 
 
+PADDED_COUNTERS_FILE = os.path.join(ROOT, "profiles", "rope_qk_qwen3_8b_padded_counters.txt")
+
+
+def write_padded_counters_summary(padded_dir, packed_dir, copy_fetch_csv, copy_write_csv,
+                                  command):
+    """Counters of the padded layout's launch (token kernel, 8 x 2048 rows, seqused)
+    beside the packed batch of the same sequences (row-group kernel): waves, their
+    lifetime and instruction mix, memory-unit busy, HBM bytes (scaled by a 1 GiB copy's
+    readings) and kernel-trace durations, per dispatch."""
+    wp, wk = workloads.get("qwen3_8b_padded"), workloads.get("qwen3_8b_packed")
+    bpl = algorithmic_bytes_per_launch(wp)
+    copy_bytes = 2 ** 30
+    f_c = max(v[0] for v in _dispatch_means(copy_fetch_csv).values())
+    w_c = max(v[0] for v in _dispatch_means(copy_write_csv).values())
+    f_scale, w_scale = copy_bytes / (f_c * 1024.0), copy_bytes / (w_c * 1024.0)
+    runs = {"padded": _kernel_counters(padded_dir), "packed": _kernel_counters(packed_dir)}
+    times = {"padded": _kernel_durations_us(padded_dir), "packed": _kernel_durations_us(packed_dir)}
+
+    def row(name, fn, fmt="{:.4g}"):
+        vals = {m: fn(runs[m], times[m]) for m in runs}
+        ratio = vals["padded"] / vals["packed"] if vals["packed"] else float("nan")
+        return (f"{name:46s} {fmt.format(vals['padded']):>12s} {fmt.format(vals['packed']):>12s}"
+                f"   x{ratio:.3f}")
+
+    per_wave = lambda k: (lambda c, t: c[k] / c["SQ_WAVES"])
+    per_cu = lambda k: (lambda c, t: 100.0 * c[k] / (CU_COUNT * c["GRBM_GUI_ACTIVE"] / XCDS))
+    lines = [
+        f"{'quantity (per launch)':46s} {'padded':>12s} {'packed':>12s}   padded/packed",
+        row("kernel duration, kernel trace (us)", lambda c, t: float(t.mean()), "{:.2f}"),
+        row("waves (SQ_WAVES)", lambda c, t: c["SQ_WAVES"], "{:.0f}"),
+        row("wave lifetime, cycles (SQ_WAVE_CYCLES/SQ_WAVES)", per_wave("SQ_WAVE_CYCLES"), "{:.0f}"),
+        row("wave-cycles in all waves (SQ_WAVE_CYCLES)", lambda c, t: c["SQ_WAVE_CYCLES"], "{:.4g}"),
+        row("VALU instructions per wave", per_wave("SQ_INSTS_VALU"), "{:.1f}"),
+        row("scalar memory instructions per wave", per_wave("SQ_INSTS_SMEM"), "{:.1f}"),
+        row("vector memory reads per wave", per_wave("SQ_INSTS_VMEM_RD"), "{:.1f}"),
+        row("vector memory writes per wave", per_wave("SQ_INSTS_VMEM_WR"), "{:.1f}"),
+        row("cycles waiting per wave (SQ_WAIT_INST_ANY)", per_wave("SQ_WAIT_INST_ANY"), "{:.0f}"),
+        row("TA busy, % of cycles per CU", per_cu("TA_TA_BUSY_sum"), "{:.1f}"),
+        row("TA stalled by the cache, % of cycles", per_cu("TA_DATA_STALLED_BY_TC_CYCLES_sum"),
+            "{:.1f}"),
+        row("HBM read bytes (FETCH_SIZE x scale)",
+            lambda c, t: c["FETCH_SIZE"] * 1024.0 * f_scale, "{:.4g}"),
+        row("HBM write bytes (WRITE_SIZE x scale)",
+            lambda c, t: c["WRITE_SIZE"] * 1024.0 * w_scale, "{:.4g}"),
+        f"algorithmic bytes per launch (valid tokens only): {bpl} for both; rows: padded "
+        f"{wp.T}, packed {wk.T} ({wp.valid_tokens} valid)",
+        f"FETCH_SIZE scale {f_scale:.5f}, WRITE_SIZE scale {w_scale:.5f} (1 GiB device copy)",
+    ]
+    header = [
+        "# The padded layout: the same 8 sequences (lengths U{256..2048}, Hq=32, Hkv=8, D=128,",
+        "# bf16) as 8 x 2048 rows with seqused (padded rows skipped; the token kernel, one wave",
+        "# per token) and packed (row-group kernel, 5 waves per token). rocprofv3 --pmc passes",
+        "# (per-dispatch means, summed over the chip) and a kernel trace of each command.",
+        f"# commands (R = repository root, W = qwen3_8b_padded or qwen3_8b_packed): {command}",
+        "",
+    ]
+    _write_summary(PADDED_COUNTERS_FILE, header, lines)
+
+
 def trace_summary_path(workload: str) -> str:
     return os.path.join(ROOT, "profiles", f"rope_qk_{workload}_kernel_trace.txt")
+
+
+def expected_grid_threads(w: workloads.Workload) -> int:
+    """Work-items of the default launch for this workload: one 64-lane workgroup per
+    (token, row group) for the row-group kernel, one 64-lane wave per token for the
+    token kernel (padded layouts)."""
+    vec = 16 // w.elem_bytes
+    nc = max(1, (w.D // 2) // vec)
+    if rope_kernel_name(w, 0) == "rope_qk_group_kernel":
+        rows = 64 // nc
+        return w.T * (-(-w.Hq // rows) + -(-w.Hkv // rows)) * 64
+    return w.T * 64
 
 
 def write_trace_summary(trace_csv: str, workload: str, command: str) -> None:
     """Per-launch durations of the RoPE kernel from a rocprofv3 --kernel-trace CSV
     (one row per dispatch), with the algorithmic bandwidth they give, as a small
-    text summary under profiles/."""
+    text summary under profiles/. Only the dispatches of this workload's default
+    launch count (its kernel instance and grid size), so a trace of the default
+    bench command, which runs every workload, serves each of them."""
     import csv
     w = workloads.get(workload)
+    key = rope_kernel_instance(w, needs_long_index(w))
+    grid = expected_grid_threads(w)
     durs, names, shape = [], set(), None
     with open(trace_csv) as fh:
         for row in csv.DictReader(fh):
-            if "rope_qk" not in row["Kernel_Name"]:
+            if key not in row["Kernel_Name"] or int(row["Grid_Size_X"]) != grid:
                 continue
             durs.append((int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3)
             names.add(row["Kernel_Name"])
             shape = (row["Grid_Size_X"], row["Workgroup_Size_X"], row["VGPR_Count"],
                      row["LDS_Block_Size"])
     if not durs:
-        raise SystemExit(f"no rope_qk dispatch in {trace_csv}")
+        raise SystemExit(f"no dispatch of {key} with {grid} work-items in {trace_csv}")
     d = np.array(durs)
     bpl = algorithmic_bytes_per_launch(w)
 
@@ -1188,6 +1263,10 @@ def main():
     ap.add_argument("--glu-valu-summary", default=None, metavar="RUN_DIR",
                     help="write the GLU VALU-occupancy summary from RUN_DIR/<kind> PMC folders, "
                          "then exit")
+    ap.add_argument("--padded-counters-summary", nargs=4, default=None,
+                    metavar=("PADDED_DIR", "PACKED_DIR", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="write the padded-vs-packed counter summary from rocprofv3 --pmc and "
+                         "--kernel-trace output folders, then exit")
     ap.add_argument("--counters-summary", nargs=4, default=None,
                     metavar=("FLY_DIR", "TABLE_DIR", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                     help="write the cos/sin fly-vs-table counter summary from rocprofv3 "
@@ -1202,6 +1281,9 @@ def main():
         return
     if args.glu_trace_summary:
         write_glu_trace_summary(args.glu_trace_summary, args.trace_command)
+        return
+    if args.padded_counters_summary:
+        write_padded_counters_summary(*args.padded_counters_summary, command=args.trace_command)
         return
     if args.counters_summary:
         write_counters_summary(*args.counters_summary, command=args.trace_command)
