@@ -235,10 +235,14 @@ def _counter_means(csv_path: str) -> dict:
 
 
 def _pick(means: dict, key: str | None) -> dict:
-    """The counters of the kernel whose name contains key (the largest reading of its
-    first counter, i.e. the 1 GiB copy, when key is None)."""
+    """The counters of the kernel whose name contains key; key None means the 1 GiB
+    device copy of --copy-calibration (the runtime's copy kernel, else the kernel with
+    the largest readings: the fill that makes its source reads nothing)."""
     if key is None:
-        return max(means.values(), key=lambda d: next(iter(d.values())))
+        copies = [d for k, d in means.items() if "copyBuffer" in k]
+        if copies:
+            return copies[0]
+        return max(means.values(), key=lambda d: sum(d.values()))
     hits = [d for k, d in means.items() if key in k]
     if not hits:
         raise SystemExit(f"no dispatch of {key} in the counter file")
@@ -510,12 +514,13 @@ def write_trace_summary(trace_csv: str, workload: str, command: str) -> None:
     bench command, which runs every workload, serves each of them."""
     import csv
     w = workloads.get(workload)
-    key = rope_kernel_instance(w, needs_long_index(w))
+    keys = rope_instance_names(w, needs_long_index(w))
+    key = keys[0]
     grid = expected_grid_threads(w)
     durs, names, shape = [], set(), None
     with open(trace_csv) as fh:
         for row in csv.DictReader(fh):
-            if key not in row["Kernel_Name"] or int(row["Grid_Size_X"]) != grid:
+            if not any(k in row["Kernel_Name"] for k in keys) or int(row["Grid_Size_X"]) != grid:
                 continue
             durs.append((int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3)
             names.add(row["Kernel_Name"])
@@ -828,6 +833,15 @@ def rope_kernel_instance(w: workloads.Workload, long_index: bool) -> str:
     return f"{base}I{dt}Li{vec}ELb{int(long_index)}ELb0E"
 
 
+def rope_instance_names(w: workloads.Workload, long_index: bool) -> tuple:
+    """The instance's name as rocprofv3 may list it: mangled, or demangled."""
+    base = rope_kernel_name(w, 0)
+    dt = {"bf16": "__bf16", "f16": "_Float16", "f32": "float"}[w.dtype]
+    vec = 16 // w.elem_bytes
+    demangled = f"{base}<{dt}, {vec}, {str(long_index).lower()}, false>"
+    return rope_kernel_instance(w, long_index), demangled
+
+
 def needs_long_index(w: workloads.Workload) -> bool:
     return w.T * (w.Hq + w.Hkv) * w.D >= 2 ** 31
 
@@ -1009,20 +1023,27 @@ def write_sweep_summary(run_dir: str, command: str) -> None:
         if np.isfinite(avg):
             xs.append(T)
             ys.append(avg)
-    t0, b = linear_fit(xs, ys)
-    lines += ["",
-              f"fit, RoPE kernel (trace averages): t = {t0:.2f} us + T x {b * 1e3:.4f} ns "
-              f"-> asymptotic {per_token / (b * 1e-6) / 1e9:.0f} GB/s "
-              f"({100 * per_token / (b * 1e-6) / 1e9 / HBM_PEAK_GBPS:.1f}% of 8 TB/s)"]
-    for key, label in (("avg_launch_us", "RoPE kernel (region timing)"),
-                       ("torch_inplace_us", "torch in-place neg_ on Q and K (region timing)")):
-        f = js[f"fit_{key}"]
-        lines.append(f"fit, {label}: t = {f['t0_us']:.2f} us + T x {f['us_per_token'] * 1e3:.4f} "
-                     f"ns -> asymptotic {f['asymptotic_GBps']:.0f} GB/s")
+    def fit_line(label, x, y):
+        t0, b = linear_fit(x, y)
+        gb = per_token / (b * 1e-6) / 1e9
+        return t0, b, (f"fit, {label}: t = {t0:.2f} us + T x {b * 1e3:.4f} ns -> incremental "
+                       f"{gb:.0f} GB/s ({100 * gb / HBM_PEAK_GBPS:.1f}% of 8 TB/s)")
+
+    small = [i for i, T in enumerate(xs) if T <= 65536]
+    torch_small = [r for r in js["rows"] if r["T"] <= 65536]
+    t0, b, l_all = fit_line("RoPE kernel, trace averages, all sizes", xs, ys)
+    t0s, bs, l_small = fit_line("RoPE kernel, trace averages, T <= 65536",
+                                [xs[i] for i in small], [ys[i] for i in small])
+    _, _, l_torch = fit_line("torch in-place neg_ on Q and K (two launches), T <= 65536",
+                             [r["T"] for r in torch_small],
+                             [r["torch_inplace_us"] for r in torch_small])
+    lines += ["", l_all, l_small, l_torch]
     for T in (8554, 16384):
-        lines.append(f"at T={T}: fixed part t0 / t = {t0 / (t0 + b * T):.3f}; at the asymptotic "
-                     f"rate the launch would take {b * T:.2f} us "
-                     f"({100 * per_token * T / (b * T * 1e-6) / 1e9 / HBM_PEAK_GBPS:.1f}%)")
+        t = t0s + bs * T
+        lines.append(f"at T={T} (T <= 65536 fit): t = {t:.2f} us, of which the fixed part t0 is "
+                     f"{t0s:.2f} us ({100 * t0s / t:.1f}%); without it the launch would take "
+                     f"{bs * T:.2f} us = {100 * per_token * T / (bs * T * 1e-6) / 1e9 / HBM_PEAK_GBPS:.1f}%"
+                     f" of 8 TB/s")
     header = [
         "# RoPE launch time against token count: one sequence of T tokens, Hq=32, Hkv=8, D=128,",
         "# bf16, theta=1e6, default launch (row-group kernel; 64-bit offsets at T=524288), each",

@@ -119,7 +119,9 @@ def test_traffic_summary_request_counts(tmp_path, monkeypatch):
     _counter_csv(str(tmp_path / "er.csv"), [(long_k, c, v) for c, v in rd(bpl / 2 / 128)]
                  + [(GROUP, c, 1.0) for c, v in rd(1)])
     _counter_csv(str(tmp_path / "ew.csv"), [(long_k, c, v) for c, v in wr(bpl / 2 / 64)])
-    _counter_csv(str(tmp_path / "cer.csv"), [(COPY, c, v) for c, v in rd(2 ** 30 / 128)])
+    fill = "void at::native::vectorized_elementwise_kernel<4, at::native::FillFunctor<float>"
+    _counter_csv(str(tmp_path / "cer.csv"), [(fill, c, v) for c, v in rd(300)]
+                 + [(COPY, c, v) for c, v in rd(2 ** 30 / 128)])
     _counter_csv(str(tmp_path / "cew.csv"), [(COPY, c, v) for c, v in wr(2 ** 30 / 64)])
     bench.write_traffic_summary(*(str(tmp_path / f"{n}.csv") for n in ("f", "w", "cf", "cw")),
                                 "cmd", workload="long_ctx_512k",
@@ -159,7 +161,8 @@ def test_sweep_summary(tmp_path, monkeypatch):
                              "Grid_Size_X": T * 5 * 64})
     bench.write_sweep_summary(str(tmp_path), "cmd")
     text = out.read_text()
-    assert "fit, RoPE kernel (trace averages): t = 1.50 us + T x 3.0000 ns" in text, text
+    assert "fit, RoPE kernel, trace averages, all sizes: t = 1.50 us + T x 3.0000 ns" in text, text
+    assert "fit, RoPE kernel, trace averages, T <= 65536: t = 1.50 us + T x 3.0000 ns" in text
 
 
 def test_trace_summary(tmp_path, monkeypatch):
