@@ -872,11 +872,14 @@ def inplace_reference_us(sets, nsets, stream, n: int) -> float:
     return region_us(stream, one, n)
 
 
-def time_workload(rope, w: workloads.Workload, dev, n_steps: int, warmup: int) -> dict:
+def time_workload(rope, w: workloads.Workload, dev, n_steps: int, warmup: int,
+                  min_warmup_s: float = 0.05, min_timed_s: float = 0.1) -> dict:
     """Region-timed default launches (forward + backward per step) of one workload on
     its own rotating buffer sets, beside the torch in-place reference over the same
     bytes (fully packed workloads only: a padded layout's valid bytes are not one
-    tensor)."""
+    tensor). Warm-up runs at least `warmup` steps and `min_warmup_s` seconds (the
+    GPU's clocks settle after the previous workload), the timed region at least
+    `n_steps` steps and `min_timed_s` seconds."""
     set_bytes = 2 * w.T * (w.Hq + w.Hkv) * w.D * w.elem_bytes
     nsets = max(2, math.ceil(8 * INFINITY_CACHE_BYTES / set_bytes))
     cu, su, sets = make_sets(w, nsets, dev)
@@ -887,8 +890,10 @@ def time_workload(rope, w: workloads.Workload, dev, n_steps: int, warmup: int) -
         rope.qk_apply_(s["q"], s["k"], cu, w.theta, 1, seqused=su)
         rope.qk_apply_(s["dq"], s["dk"], cu, w.theta, -1, seqused=su)
 
-    for i in range(warmup):
+    step_us = region_us(stream, step, 10)
+    for i in range(max(warmup, math.ceil(min_warmup_s * 1e6 / step_us))):
         step(i)
+    n_steps = max(n_steps, math.ceil(min_timed_s * 1e6 / step_us))
     launch_us = region_us(stream, step, n_steps) / 2
     bpl = algorithmic_bytes_per_launch(w)
     gbps = bpl / (launch_us * 1e-6) / 1e9
