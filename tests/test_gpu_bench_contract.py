@@ -1,0 +1,43 @@
+"""bench.py's one-line JSON output on the GPU: the keys the benchmark contract names,
+with consistent values, on a short run of the smallest workloads."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+pytestmark = pytest.mark.gpu
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def run_bench(*args):
+    print(f"[bench contract] bench.py {' '.join(args)}", flush=True)
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *args], capture_output=True,
+                       text=True, timeout=240)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [ln for ln in r.stdout.splitlines() if ln.startswith("{")]
+    assert len(lines) == 1, r.stdout[-2000:]
+    return json.loads(lines[0])
+
+
+def test_bench_json_contract():
+    d = run_bench("--workload", "qwen3_8b_packed", "--steps", "5", "--warmup", "2",
+                  "--cpu-seconds", "0.5")
+    for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
+                "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config",
+                "roofline", "cpu_baseline", "per_config"):
+        assert key in d, key
+    assert d["n_gpus"] == 1 and d["steps"] == 5 and d["warmup"] == 2 and d["dtype"] == "bf16"
+    assert d["config"]["workload"] == "qwen3_8b_packed" and d["value"] > 0
+    r = d["roofline"]
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["peak"] == 8000.0
+    assert abs(r["frac"] - r["achieved"] / r["peak"]) < 1e-9
+    assert abs(r["achieved"] - r["bytes_per_launch"] / (r["avg_launch_us"] * 1e-6) / 1e9) < 1e-6
+    assert 0.3 < r["frac"] < 1.0 and r["frac_of_ceiling"] > 0
+    c = d["cpu_baseline"]
+    assert c["kind"] == "oracle" and c["cores"] >= 1 and c["value"] > 0 and c["sample"]
+    assert set(d["per_config"]) == {"tiny_packed", "qwen3_4b_packed", "qwen3_8b_packed",
+                                    "qwen3_8b_padded", "qwen3_32b_packed", "long_ctx_512k"}
+    assert d["per_config"]["qwen3_8b_packed"].get("headline") is True
+    assert 1.0 < d["per_config"]["qwen3_8b_padded"]["t_over_packed"] < 2.0
