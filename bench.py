@@ -86,11 +86,19 @@ def kernel_source_hash(sources=ROPE_SOURCES) -> str:
     return h.hexdigest()[:16]
 
 
-def rope_kernel_name(w: workloads.Workload, tokens_per_wave: int) -> str:
-    """The kernel the library picks for this call: row groups by default, one wave
-    per token when the caller sets tokens per wave or passes seqused (padded)."""
+def compact_launch(w: workloads.Workload, padded: str = "compact") -> bool:
+    """Whether a padded workload (seqused) is launched compact: rope_qk_apply_padded
+    with cu_valid and the host count of rotated tokens, the grid covering only them."""
+    return w.seqused is not None and padded == "compact"
+
+
+def rope_kernel_name(w: workloads.Workload, tokens_per_wave: int, padded: str = "compact") -> str:
+    """The kernel the library picks for this call: row groups by default and for
+    compact padded launches, one wave per token when the caller sets tokens per wave
+    or passes seqused to the plain entry points."""
     nc = max(1, (w.D // 2) // (16 // w.elem_bytes))
-    if tokens_per_wave == 0 and w.seqused is None and 64 % nc == 0:
+    if tokens_per_wave == 0 and 64 % nc == 0 and (w.seqused is None or
+                                                   compact_launch(w, padded)):
         return "rope_qk_group_kernel"
     return "rope_qk_kernel"
 
@@ -436,7 +444,7 @@ PADDED_COUNTERS_FILE = os.path.join(ROOT, "profiles", "rope_qk_qwen3_8b_padded_c
 
 def write_padded_counters_summary(padded_dir, packed_dir, copy_fetch_csv, copy_write_csv,
                                   command):
-    """Counters of the padded layout's launch (token kernel, 8 x 2048 rows, seqused)
+    """Counters of the padded layout's seqused launch (token kernel, 8 x 2048 rows)
     beside the packed batch of the same sequences (row-group kernel): waves, their
     lifetime and instruction mix, memory-unit busy, HBM bytes (scaled by a 1 GiB copy's
     readings) and kernel-trace durations, per dispatch."""
@@ -481,9 +489,10 @@ def write_padded_counters_summary(padded_dir, packed_dir, copy_fetch_csv, copy_w
     ]
     header = [
         "# The padded layout: the same 8 sequences (lengths U{256..2048}, Hq=32, Hkv=8, D=128,",
-        "# bf16) as 8 x 2048 rows with seqused (padded rows skipped; the token kernel, one wave",
-        "# per token) and packed (row-group kernel, 5 waves per token). rocprofv3 --pmc passes",
-        "# (per-dispatch means, summed over the chip) and a kernel trace of each command.",
+        "# bf16) as 8 x 2048 rows through the seqused launch of the plain entry point (padded",
+        "# rows skipped; the token kernel, one wave per token) and packed (row-group kernel, 5",
+        "# waves per token). rocprofv3 --pmc passes (per-dispatch means, summed over the chip)",
+        "# and a kernel trace of each command.",
         f"# commands (R = repository root, W = qwen3_8b_padded or qwen3_8b_packed): {command}",
         "",
     ]
@@ -494,15 +503,16 @@ def trace_summary_path(workload: str) -> str:
     return os.path.join(ROOT, "profiles", f"rope_qk_{workload}_kernel_trace.txt")
 
 
-def expected_grid_threads(w: workloads.Workload) -> int:
+def expected_grid_threads(w: workloads.Workload, padded: str = "compact") -> int:
     """Work-items of the default launch for this workload: one 64-lane workgroup per
-    (token, row group) for the row-group kernel, one 64-lane wave per token for the
-    token kernel (padded layouts)."""
+    (token, row group) for the row-group kernel (per rotated token only, for a compact
+    padded launch), one 64-lane wave per token for the token kernel."""
     vec = 16 // w.elem_bytes
     nc = max(1, (w.D // 2) // vec)
-    if rope_kernel_name(w, 0) == "rope_qk_group_kernel":
+    if rope_kernel_name(w, 0, padded) == "rope_qk_group_kernel":
         rows = 64 // nc
-        return w.T * (-(-w.Hq // rows) + -(-w.Hkv // rows)) * 64
+        tokens = w.valid_tokens if compact_launch(w, padded) else w.T
+        return tokens * (-(-w.Hq // rows) + -(-w.Hkv // rows)) * 64
     return w.T * 64
 
 
@@ -823,23 +833,29 @@ def compare_unfused(rope, w, cu, su, sets, nsets, args, stream):
     print(json.dumps(out))
 
 
-def rope_kernel_instance(w: workloads.Workload, long_index: bool) -> str:
+def rope_kernel_instance(w: workloads.Workload, long_index: bool, padded: str = "compact") -> str:
     """Mangled-name fragment of the default path's kernel instance for this workload
-    (row-group kernel unless seqused marks a padded layout; dtype, chunk width and
-    index width), as rocprofv3 lists it."""
-    base = rope_kernel_name(w, 0)
+    (kernel, dtype, chunk width, index width, no tables, and for the row-group kernel
+    whether the launch is compact), as rocprofv3 lists it."""
+    base = rope_kernel_name(w, 0, padded)
     dt = {"bf16": "DF16b", "f16": "DF16_", "f32": "f"}[w.dtype]
     vec = 16 // w.elem_bytes
-    return f"{base}I{dt}Li{vec}ELb{int(long_index)}ELb0E"
+    name = f"{base}I{dt}Li{vec}ELb{int(long_index)}ELb0E"
+    if base == "rope_qk_group_kernel":
+        name += f"Lb{int(compact_launch(w, padded))}E"
+    return name
 
 
-def rope_instance_names(w: workloads.Workload, long_index: bool) -> tuple:
+def rope_instance_names(w: workloads.Workload, long_index: bool, padded: str = "compact") -> tuple:
     """The instance's name as rocprofv3 may list it: mangled, or demangled."""
-    base = rope_kernel_name(w, 0)
+    base = rope_kernel_name(w, 0, padded)
     dt = {"bf16": "__bf16", "f16": "_Float16", "f32": "float"}[w.dtype]
     vec = 16 // w.elem_bytes
-    demangled = f"{base}<{dt}, {vec}, {str(long_index).lower()}, false>"
-    return rope_kernel_instance(w, long_index), demangled
+    flags = [str(long_index).lower(), "false"]
+    if base == "rope_qk_group_kernel":
+        flags.append(str(compact_launch(w, padded)).lower())
+    demangled = f"{base}<{dt}, {vec}, {', '.join(flags)}>"
+    return rope_kernel_instance(w, long_index, padded), demangled
 
 
 def needs_long_index(w: workloads.Workload) -> bool:
@@ -872,40 +888,67 @@ def inplace_reference_us(sets, nsets, stream, n: int) -> float:
     return region_us(stream, one, n)
 
 
+def padded_metadata(rope, w: workloads.Workload, cu, su):
+    """cu_valid (the library's prefix kernel, once per batch, as a trainer builds it
+    beside cu_seqlens) and the host count of rotated tokens of a padded workload."""
+    return rope.valid_prefix(cu, su), w.valid_tokens
+
+
 def time_workload(rope, w: workloads.Workload, dev, n_steps: int, warmup: int,
-                  min_warmup_s: float = 0.05, min_timed_s: float = 0.1) -> dict:
+                  min_warmup_s: float = 0.05, min_timed_s: float = 0.1,
+                  padded: str = "compact") -> dict:
     """Region-timed default launches (forward + backward per step) of one workload on
     its own rotating buffer sets, beside the torch in-place reference over the same
     bytes (fully packed workloads only: a padded layout's valid bytes are not one
     tensor). Warm-up runs at least `warmup` steps and `min_warmup_s` seconds (the
     GPU's clocks settle after the previous workload), the timed region at least
-    `n_steps` steps and `min_timed_s` seconds."""
+    `n_steps` steps and `min_timed_s` seconds. A padded workload is launched compact
+    (padded == "compact") and, for comparison, also timed through the seqused launch
+    of the plain entry point."""
     set_bytes = 2 * w.T * (w.Hq + w.Hkv) * w.D * w.elem_bytes
     nsets = max(2, math.ceil(8 * INFINITY_CACHE_BYTES / set_bytes))
     cu, su, sets = make_sets(w, nsets, dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
+    compact = compact_launch(w, padded)
+    if compact:
+        cv, valid = padded_metadata(rope, w, cu, su)
 
-    def step(i):
+    def step_compact(i):
+        s = sets[i % nsets]
+        rope.qk_apply_padded_(s["q"], s["k"], w.theta, 1, cu, su, cv, valid)
+        rope.qk_apply_padded_(s["dq"], s["dk"], w.theta, -1, cu, su, cv, valid)
+
+    def step_plain(i):
         s = sets[i % nsets]
         rope.qk_apply_(s["q"], s["k"], cu, w.theta, 1, seqused=su)
         rope.qk_apply_(s["dq"], s["dk"], cu, w.theta, -1, seqused=su)
 
-    step_us = region_us(stream, step, 10)
-    for i in range(max(warmup, math.ceil(min_warmup_s * 1e6 / step_us))):
-        step(i)
-    n_steps = max(n_steps, math.ceil(min_timed_s * 1e6 / step_us))
-    launch_us = region_us(stream, step, n_steps) / 2
+    def timed(step):
+        step_us = region_us(stream, step, 10)
+        for i in range(max(warmup, math.ceil(min_warmup_s * 1e6 / step_us))):
+            step(i)
+        n = max(n_steps, math.ceil(min_timed_s * 1e6 / step_us))
+        return region_us(stream, step, n) / 2, n
+
+    launch_us, n_steps = timed(step_compact if compact else step_plain)
     bpl = algorithmic_bytes_per_launch(w)
     gbps = bpl / (launch_us * 1e-6) / 1e9
     out = {
         "T": w.T, "valid_tokens": w.valid_tokens, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D,
-        "dtype": w.dtype, "kernel": rope_kernel_name(w, 0),
+        "dtype": w.dtype, "kernel": rope_kernel_name(w, 0, padded),
         "index": "64-bit" if needs_long_index(w) else "32-bit",
         "bytes_per_launch": bpl, "avg_launch_us": launch_us, "GBps": gbps,
         "frac": gbps / HBM_PEAK_GBPS,
         "fwd_bwd_tokens_per_s": w.valid_tokens / (2 * launch_us * 1e-6),
         "launches_timed": 2 * n_steps,
     }
+    if w.seqused is not None:
+        out["padded_launch"] = padded
+        if compact:
+            plain_us, _ = timed(step_plain)
+            out["seqused_launch_us"] = plain_us
+            out["seqused_kernel"] = rope_kernel_name(w, 0, "seqused")
+            out["seqused_frac"] = bpl / (plain_us * 1e-6) / 1e9 / HBM_PEAK_GBPS
     if w.seqused is None:
         ref_us = inplace_reference_us(sets, nsets, stream, 2 * n_steps)
         out["torch_inplace_us"] = ref_us
@@ -1246,6 +1289,11 @@ def main():
                     help="all: also time every other RoPE workload's default launches and put "
                          "them in the JSON line (per_config); none: the chosen workload only")
     ap.add_argument("--tokens-per-wave", type=int, default=0, help="0: library default")
+    ap.add_argument("--padded", default="compact", choices=["compact", "seqused"],
+                    help="padded workloads (seqused): compact launches over the rotated tokens "
+                         "only (rope_qk_apply_padded, with cu_valid made once per batch and "
+                         "the host count of rotated tokens), or the seqused launch of the "
+                         "plain entry point")
     ap.add_argument("--positions", default="cu", choices=["cu", "ids", "shards4"],
                     help="position source: cu_seqlens; explicit per-token ids; or the batch "
                          "cut into 4 token shards, each launched with per-sequence offsets")
@@ -1401,8 +1449,16 @@ def main():
         rows = int(max(w.lengths))
         tables = rope.cos_sin_table(rows, w.D, w.theta, dev)
 
+    compact = compact_launch(w, args.padded) and tpw == 0 and pid is None and shards is None \
+        and tables is None
+    if compact:
+        cv, valid = padded_metadata(rope, w, cu, su)
+
     def launch(qt, kt, direction):
-        if tables is not None:
+        if compact:
+            rope.qk_apply_padded_(qt, kt, w.theta, direction, cu, su, cv, valid,
+                                  pos_scale=args.pos_scale, index_mode=index_mode)
+        elif tables is not None:
             rope.qk_apply_table_(qt, kt, tables[0], tables[1], direction,
                                  cu_seqlens=None if pid is not None else cu,
                                  seqused=None if pid is not None else su, position_ids=pid,
@@ -1519,6 +1575,8 @@ def main():
             "buffer_sets": nsets, "tokens_per_wave": tpw or "auto",
             "positions": args.positions, "pos_scale": args.pos_scale,
             "layout": args.layout, "index": args.index, "cos_sin": args.cos_sin,
+            **({"padded_launch": "compact" if compact else "seqused"}
+               if w.seqused is not None else {}),
             "launch": "hip graph per step" if args.graph else "eager",
         },
         "step_hbm_GBps": 2 * bpl * args.steps / elapsed / 1e9,
@@ -1529,7 +1587,7 @@ def main():
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
             "traffic": traffic,
-            "kernel": rope_kernel_name(w, tpw),
+            "kernel": rope_kernel_name(w, tpw, args.padded if compact else "seqused"),
             "bytes_per_launch": bpl,
             "avg_launch_us": avg_launch_s * 1e6,
             "timing": "HIP events around the timed region / (2 x steps)",
@@ -1559,7 +1617,8 @@ def main():
             if name == w.name:
                 per[name] = {
                     "T": w.T, "valid_tokens": w.valid_tokens, "Hq": w.Hq, "Hkv": w.Hkv,
-                    "D": w.D, "dtype": w.dtype, "kernel": rope_kernel_name(w, 0),
+                    "D": w.D, "dtype": w.dtype,
+                    "kernel": rope_kernel_name(w, 0, args.padded if compact else "seqused"),
                     "index": "64-bit" if needs_long_index(w) else "32-bit",
                     "bytes_per_launch": bpl, "avg_launch_us": avg_launch_s * 1e6,
                     "GBps": achieved, "frac": achieved / HBM_PEAK_GBPS,
@@ -1571,7 +1630,7 @@ def main():
                 continue
             sw = workloads.get(name)
             print(f"[bench] timing {name}", file=sys.stderr, flush=True)
-            per[name] = time_workload(rope, sw, dev, 200, 20)
+            per[name] = time_workload(rope, sw, dev, 200, 20, padded=args.padded)
         if "qwen3_8b_padded" in per and "qwen3_8b_packed" in per:
             pad, pk = per["qwen3_8b_padded"], per["qwen3_8b_packed"]
             pad["t_over_packed"] = pad["avg_launch_us"] / pk["avg_launch_us"]

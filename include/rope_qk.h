@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define ROPE_QK_ABI_VERSION 4
+#define ROPE_QK_ABI_VERSION 5
 
 /* Storage dtype of Q and K (computation is fp32 in every case). */
 typedef enum rope_dtype { ROPE_F32 = 0, ROPE_BF16 = 1, ROPE_F16 = 2 } rope_dtype;
@@ -109,11 +109,11 @@ int32_t rope_qk_bwd(void* dq, void* dk, int64_t T, int32_t Hq, int32_t Hkv, int3
  *                   for D = 128 in bf16), which evaluates the token's cos/sin once
  *                   per group; one wave per token instead when seqused is given
  *                   (padded layouts skip many rows, which that geometry passes over
- *                   more cheaply) or when the row layout or the grid size rules the
- *                   row groups out. 1..1024: each 64-lane wave rotates this many
- *                   consecutive tokens, one at a time, all Q and K heads of each,
- *                   evaluating each token's cos/sin once. Results do not depend on
- *                   it.
+ *                   more cheaply; rope_qk_apply_padded spends nothing on them) or
+ *                   when the row layout or the grid size rules the row groups out.
+ *                   1..1024: each 64-lane wave rotates this many consecutive
+ *                   tokens, one at a time, all Q and K heads of each, evaluating
+ *                   each token's cos/sin once. Results do not depend on it.
  * Other arguments as in rope_qk_fwd. */
 int32_t rope_qk_apply(void* q, void* k, int64_t T, int32_t Hq, int32_t Hkv, int32_t D,
                       const int32_t* cu_seqlens, int32_t num_seqs, const int32_t* seqused,
@@ -180,6 +180,35 @@ int32_t rope_qk_apply_table(void* q, void* k, int64_t T, int32_t Hq, int32_t Hkv
                             int32_t dtype, int32_t direction, int32_t index_mode,
                             int32_t tokens_per_wave, void* stream);
 
+/* rope_qk_apply_ex for a padded layout whose rotated tokens the caller has
+ * counted: the launch covers only those tokens, so padded rows cost no work at
+ * all (Unsloth page, section "Pourquoi le remplissage est-il necessaire et gain
+ * de vitesse mathematique": padding rows are waste; section "Packing non
+ * contamine": positions restart per sample). The tokens rotated, their positions
+ * and the results are those of rope_qk_apply_ex with the same cu_seqlens,
+ * seqused and seq_offsets, bit for bit, whenever cu_valid and valid_tokens match
+ * them; the extra arguments only shape the launch.
+ *  cu_valid      device int32[num_seqs + 1]: cu_valid[0] = 0 and cu_valid[s+1] =
+ *                cu_valid[s] + used(s), used(s) = min(seqused[s], cu_seqlens[s+1]
+ *                - cu_seqlens[s]) clamped at 0 (the sequence length when seqused
+ *                is NULL): the running count of rotated tokens, the same for every
+ *                layer of a batch. rope_valid_prefix writes it.
+ *  valid_tokens  host count of rotated tokens, cu_valid[num_seqs]; 0..T.
+ * When they do not match, memory stays safe and no token is rotated twice or
+ * with a wrong position, but tokens outside the ranges they describe may be
+ * left untouched. Where the row-group geometry does not apply (nc does not
+ * divide 64, or a grid beyond the dispatch limit) the call runs the seqused
+ * launch of rope_qk_apply_ex instead, with the same results.
+ * Errors: ROPE_EINVAL for valid_tokens < 0 or > T, or a NULL cu_valid with
+ * valid_tokens > 0 (valid_tokens == 0 enqueues nothing); otherwise as in
+ * rope_qk_apply_ex. Other arguments as in rope_qk_apply_ex. */
+int32_t rope_qk_apply_padded(void* q, void* k, int64_t T, int32_t Hq, int32_t Hkv, int32_t D,
+                             int64_t q_token_stride, int64_t k_token_stride,
+                             const int32_t* cu_seqlens, int32_t num_seqs, const int32_t* seqused,
+                             const int32_t* cu_valid, int64_t valid_tokens,
+                             const int32_t* seq_offsets, double theta, double pos_scale,
+                             int32_t dtype, int32_t direction, int32_t index_mode, void* stream);
+
 /* Forward / backward RoPE with explicit positions: position_ids is a device
  * int32[T] (required when T > 0); negative ids leave their token untouched.
  * Other arguments as in rope_qk_fwd. */
@@ -201,6 +230,18 @@ int32_t rope_positions(const int32_t* cu_seqlens, int32_t num_seqs, const int32_
 int32_t rope_positions_ex(const int32_t* cu_seqlens, int32_t num_seqs, const int32_t* seqused,
                           const int32_t* seq_offsets, const int32_t* position_ids, int64_t T,
                           int32_t* pos_out, int32_t* seq_out, void* stream);
+
+/* The cu_valid array of rope_qk_apply_padded, on the device: cu_valid_out[0] = 0
+ * and cu_valid_out[s+1] = cu_valid_out[s] + min(seqused[s], cu_seqlens[s+1] -
+ * cu_seqlens[s]), each term clamped at 0 (the length alone when seqused is NULL),
+ * saturated at INT32_MAX. One small launch per batch.
+ *  cu_seqlens     device int32[num_seqs + 1] (not read when num_seqs == 0)
+ *  seqused        device int32[num_seqs] or NULL
+ *  cu_valid_out   device int32[num_seqs + 1], owned by the caller
+ * Returns ROPE_OK, ROPE_EINVAL (num_seqs < 0 or INT32_MAX, a NULL output, or a
+ * NULL cu_seqlens with num_seqs > 0) or ROPE_ELAUNCH. */
+int32_t rope_valid_prefix(const int32_t* cu_seqlens, int32_t num_seqs, const int32_t* seqused,
+                          int32_t* cu_valid_out, void* stream);
 
 /* The fp32 cos/sin the kernels use, as a table (same device code; Unsloth page,
  * fused QK RoPE section: the cos and sin of the rotation): for every position

@@ -24,7 +24,7 @@ import torch
 
 __all__ = [
     "RopeError", "qk_fwd_", "qk_bwd_", "qk_apply_", "qk_apply_ex_", "qk_apply_table_",
-    "qk_fwd_pos_", "qk_bwd_pos_",
+    "qk_apply_padded_", "valid_prefix", "qk_fwd_pos_", "qk_bwd_pos_",
     "positions", "cos_sin", "cos_sin_table", "inv_freq", "abi_version", "LIB_PATH", "INDEX_AUTO", "INDEX_32",
     "INDEX_64", "glu_fwd", "glu_bwd", "GLU_KINDS",
 ]
@@ -59,6 +59,9 @@ def _load() -> ctypes.CDLL:
                                         vp, vp, i32, i32, i32, i32, i32, vp]
     lib.rope_qk_fwd_pos.argtypes = [vp, vp, i64, i32, i32, i32, vp, dbl, i32, vp]
     lib.rope_qk_bwd_pos.argtypes = [vp, vp, i64, i32, i32, i32, vp, dbl, i32, vp]
+    lib.rope_qk_apply_padded.argtypes = [vp, vp, i64, i32, i32, i32, i64, i64, vp, i32, vp, vp,
+                                         i64, vp, dbl, dbl, i32, i32, i32, vp]
+    lib.rope_valid_prefix.argtypes = [vp, i32, vp, vp, vp]
     lib.rope_positions.argtypes = [vp, i32, vp, i64, vp, vp, vp]
     lib.rope_positions_ex.argtypes = [vp, i32, vp, vp, vp, i64, vp, vp, vp]
     lib.rope_cos_sin.argtypes = [i32, i32, dbl, vp, vp, vp]
@@ -67,6 +70,7 @@ def _load() -> ctypes.CDLL:
     lib.glu_fwd.argtypes = [i32, vp, vp, vp, i64, i64, i64, i64, i32, i32, vp]
     lib.glu_bwd.argtypes = [i32, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, vp]
     for name in ("rope_qk_fwd", "rope_qk_bwd", "rope_qk_apply", "rope_qk_apply_ex", "rope_qk_apply_table",
+                 "rope_qk_apply_padded", "rope_valid_prefix",
                  "rope_qk_fwd_pos", "rope_qk_bwd_pos", "rope_positions", "rope_positions_ex",
                  "rope_cos_sin", "rope_cos_sin_at", "rope_inv_freq", "rope_abi_version",
                  "glu_fwd", "glu_bwd"):
@@ -173,6 +177,46 @@ def qk_apply_ex_(q, k, theta: float, direction: int = 1, cu_seqlens=None, sequse
                                int(tokens_per_wave), _stream(q.device))
     _check(st, "rope_qk_apply_ex")
     return q, k
+
+
+def qk_apply_padded_(q, k, theta: float, direction: int, cu_seqlens, seqused, cu_valid,
+                     valid_tokens: int, seq_offsets=None, pos_scale: float = 1.0,
+                     index_mode: int = INDEX_AUTO):
+    """qk_apply_ex_ on a padded layout whose rotated tokens are counted up front:
+    `cu_valid` (int32[B+1] on the GPU, from valid_prefix, once per batch) holds the
+    running count of rotated tokens per sequence and `valid_tokens` (a host int)
+    their total, so the launch covers only those tokens. Same results as
+    qk_apply_ex_ with the same cu_seqlens, seqused and seq_offsets. In place;
+    returns (q, k)."""
+    T, Hq, Hkv, D = _qk_tensors(q, k, strided=True)
+    qs, ks = _token_stride(q, "q"), _token_stride(k, "k")
+    if cu_seqlens is None:
+        raise ValueError("cu_seqlens is required")
+    cu, num_seqs, su, so, _ = _position_args(q, T, cu_seqlens, seqused, seq_offsets, None)
+    cv = _index_tensor(cu_valid, "cu_valid", q.device)
+    if cv is None or cv.numel() != num_seqs + 1:
+        raise ValueError("cu_valid must have num_seqs + 1 entries")
+    st = _lib.rope_qk_apply_padded(_ptr(q), _ptr(k), T, Hq, Hkv, D, qs, ks, _ptr(cu), num_seqs,
+                                   _ptr(su), _ptr(cv), int(valid_tokens), _ptr(so), float(theta),
+                                   float(pos_scale), _DTYPE_CODE[q.dtype], int(direction),
+                                   int(index_mode), _stream(q.device))
+    _check(st, "rope_qk_apply_padded")
+    return q, k
+
+
+def valid_prefix(cu_seqlens, seqused=None):
+    """int32[B+1] on cu_seqlens' GPU: the running count of the tokens each sequence
+    rotates (min(seqused[s], its length)), the cu_valid of qk_apply_padded_."""
+    dev = cu_seqlens.device
+    cu = _index_tensor(cu_seqlens, "cu_seqlens", dev)
+    su = _index_tensor(seqused, "seqused", dev)
+    num_seqs = cu.numel() - 1
+    if num_seqs < 0 or (su is not None and su.numel() != num_seqs):
+        raise ValueError("cu_seqlens needs >= 1 entry and seqused one entry per sequence")
+    out = torch.empty(num_seqs + 1, dtype=torch.int32, device=dev)
+    _check(_lib.rope_valid_prefix(_ptr(cu), num_seqs, _ptr(su), _ptr(out), _stream(dev)),
+           "rope_valid_prefix")
+    return out
 
 
 def _position_args(q, T, cu_seqlens, seqused, seq_offsets, position_ids):

@@ -18,7 +18,8 @@
 // (16 bytes: VEC = 8 for bf16/f16, 4 for fp32) together with the matching VEC
 // elements of the second half, D/2 further on; the lane that loads a chunk pair
 // rotates it and stores it back, so the in-place update needs no synchronization
-// between lanes. Loads and stores are non-temporal: the data is streamed once.
+// between lanes. Loads and stores are non-temporal: the data is streamed once; the
+// row-group kernel's stores also write through L2 at device scope.
 // Two kernels, one launch per pass either way:
 //  * rope_qk_group_kernel (the default): one 64-lane workgroup per (token, group
 //    of 64/nc head rows), Q's groups then K's; for D = 128 in bf16 a group is 8
@@ -89,13 +90,15 @@ struct CosSinParams {
 
 // Where a token's position comes from: explicit position ids, or its offset in its
 // cu_seqlens sequence (optionally cut by seqused and shifted by a per-sequence
-// offset, as a context-parallel shard of a longer sequence needs).
+// offset, as a context-parallel shard of a longer sequence needs). cu_valid is set
+// only for compact launches over a padded layout (compact_position).
 struct PosSource {
   const int32_t* cu;
   const int32_t* seqused;
   const int32_t* seq_offsets;
   const int32_t* position_ids;
   int32_t num_seqs;
+  const int32_t* cu_valid;
 };
 
 // ---- a1: token -> (sequence, position) [U-Pack] ------------------------------------
@@ -147,6 +150,30 @@ __device__ inline int32_t resolve_position(const PosSource& ps, I t, int32_t* se
     return -1;
   }
   return (int32_t)shifted;
+}
+
+// Compact launches over a padded layout count only the rotated tokens: token index
+// v of the launch is the v-th rotated token, sequence by sequence, and
+// cu_valid[s] is the number of rotated tokens before sequence s (the running sum
+// of min(seqused[s], sequence length)). So v lies in the sequence s with the last
+// cu_valid[s] <= v (the search above, over cu_valid), at position p = v -
+// cu_valid[s], in row cu[s] + p. Returns the position and sets *row, or returns -1
+// when v lies past the rotated tokens, or when the metadata puts the row outside
+// sequence s's rotated prefix or outside [0, T): nothing is touched then, so any
+// metadata stays memory-safe, and no row is rotated twice (p is one-to-one in v).
+__device__ inline int32_t compact_position(const PosSource& ps, int32_t v, int64_t T,
+                                           int64_t* row) {
+  int32_t s;
+  const int32_t p = token_position(ps.cu_valid, ps.num_seqs, (const int32_t*)nullptr, v, &s);
+  if (p < 0) return -1;
+  const int64_t start = ps.cu[s];
+  const int64_t r = start + p;
+  if (start < 0 || r >= (int64_t)ps.cu[s + 1] || r >= T) return -1;
+  if (ps.seqused != nullptr && p >= ps.seqused[s]) return -1;
+  *row = r;
+  if (ps.seq_offsets == nullptr) return p;
+  const int64_t shifted = (int64_t)p + (int64_t)ps.seq_offsets[s];
+  return shifted < 0 || shifted > (int64_t)INT32_MAX ? -1 : (int32_t)shifted;
 }
 
 // ---- a3: the angle --------------------------------------------------------------
@@ -368,6 +395,28 @@ __global__ __launch_bounds__(kTokenBlock) void rope_qk_kernel(T* __restrict__ q,
   }
 }
 
+// Streaming store of one chunk written through to memory at device scope (cache
+// policy sc1 + nt on the gfx950 store), so the line does not stay dirty in the
+// XCD's L2. For this in-place update, whose stores follow loads of the same lines,
+// that keeps HBM 1-2% busier than store_chunk on the row-group kernel; the token
+// kernel is 5% slower with it and the out-of-place GLU kernels 1-2% slower, so
+// they keep store_chunk. The compiler has no builtin for these bits on a global
+// store, hence the asm, which the compiler does not see as a store: (1) a store
+// wider than 8 bytes reads its data registers after issue, and gfx950 needs two
+// wait states before a vector instruction may overwrite them, so the asm carries
+// them (s_nop 1); (2) the compiler does not count the store among the wave's
+// outstanding memory operations, so it is used only where the wave issues no
+// further memory operation (the end of the kernel). Other widths use store_chunk.
+template <typename T, int VEC>
+__device__ inline void store_chunk_through(T* p, const Chunk<T, VEC>& c) {
+  if constexpr (sizeof(Chunk<T, VEC>) == 16) {
+    const u32x4 w = __builtin_bit_cast(u32x4, c);
+    asm volatile("global_store_dwordx4 %0, %1, off nt sc1\n\ts_nop 1" : : "v"(p), "v"(w) : "memory");
+  } else {
+    store_chunk<T, VEC>(p, c);
+  }
+}
+
 // ---- the default geometry: one wave per (token, row group) --------------------------
 // A 64-lane workgroup owns one group of step_r = 64 / nc consecutive head rows of
 // one token (Q rows first, then K rows; the last group of each may be partial).
@@ -380,8 +429,9 @@ __global__ __launch_bounds__(kTokenBlock) void rope_qk_kernel(T* __restrict__ q,
 // memory traffic of others, and each wave's reads and writes stay within 2 KB.
 // The cost is evaluating each (token, frequency) cos/sin once per row group of
 // the token instead of once per token. Requires nc to divide 64.
-// TABLE as in rope_qk_kernel.
-template <typename T, int VEC, bool LONG_INDEX, bool TABLE>
+// TABLE as in rope_qk_kernel. COMPACT: the grid covers only the rotated tokens of
+// a padded layout (compact_position), so no workgroup is spent on padded rows.
+template <typename T, int VEC, bool LONG_INDEX, bool TABLE, bool COMPACT>
 __global__ __launch_bounds__(64) void rope_qk_group_kernel(T* __restrict__ q, T* __restrict__ k,
                                                            const PosSource ps, const RopeParams p) {
   __shared__ float lds_cs[kMaxHalf];
@@ -392,7 +442,7 @@ __global__ __launch_bounds__(64) void rope_qk_group_kernel(T* __restrict__ q, T*
   // shift instead of integer divisions, so the wave reaches its loads sooner.
   const uint32_t ns = p.nc_shift;
   const uint32_t gq = p.gq;
-  const uint32_t t = fastdiv::div(blockIdx.x, p.groups);  // < 2^26
+  const uint32_t t = fastdiv::div(blockIdx.x, p.groups);  // < 2^26; COMPACT: rotated-token index
   const uint32_t g = blockIdx.x - t * (gq + p.gk);
   const uint32_t D = (uint32_t)p.D;
   const uint32_t half = D >> 1;
@@ -404,12 +454,15 @@ __global__ __launch_bounds__(64) void rope_qk_group_kernel(T* __restrict__ q, T*
   const bool in_q = g < gq;
   const int r = (int)(((in_q ? g : g - gq) << (6 - ns)) + ((uint32_t)lane >> ns));
   const bool live = r < (in_q ? p.Hq : p.Hkv);
-  T* row = in_q ? token_row0<T, LONG_INDEX>(q, (int64_t)t, p.q_stride)
-                : token_row0<T, LONG_INDEX>(k, (int64_t)t, p.k_stride);
-  // r * D < 2^22: a 24-bit multiply. (A full 32-bit multiply-add becomes
-  // v_mad_u64_u32 with an undefined high addend, which the register allocator
-  // may place in a register a pending load writes, forcing a wait on it.)
-  row += __umul24((uint32_t)(live ? r : 0), D) + (uint32_t)(c * VEC);
+  T* row = nullptr;
+  if constexpr (!COMPACT) {
+    row = in_q ? token_row0<T, LONG_INDEX>(q, (int64_t)t, p.q_stride)
+               : token_row0<T, LONG_INDEX>(k, (int64_t)t, p.k_stride);
+    // r * D < 2^22: a 24-bit multiply. (A full 32-bit multiply-add becomes
+    // v_mad_u64_u32 with an undefined high addend, which the register allocator
+    // may place in a register a pending load writes, forcing a wait on it.)
+    row += __umul24((uint32_t)(live ? r : 0), D) + (uint32_t)(c * VEC);
+  }
 
   // Vector-memory loads complete in issue order, so the order of issue below is
   // what lets the cos/sin evaluation overlap the row loads: this lane's inverse
@@ -423,8 +476,18 @@ __global__ __launch_bounds__(64) void rope_qk_group_kernel(T* __restrict__ q, T*
 #pragma unroll
   for (int i = 0; i < kMaxHalf / 64; ++i) f[i] = p.inv_freq[(uint32_t)lane + 64u * i];
   __builtin_amdgcn_sched_barrier(0);
-  int32_t seq;
-  const int32_t pos = resolve_position(ps, (int32_t)t, &seq);  // wave-uniform
+  int32_t pos;  // wave-uniform
+  if constexpr (COMPACT) {
+    int64_t tok = 0;
+    pos = compact_position(ps, (int32_t)t, p.T, &tok);
+    if (pos < 0) return;
+    row = in_q ? token_row0<T, LONG_INDEX>(q, tok, p.q_stride)
+               : token_row0<T, LONG_INDEX>(k, tok, p.k_stride);
+    row += __umul24((uint32_t)(live ? r : 0), D) + (uint32_t)(c * VEC);
+  } else {
+    int32_t seq;
+    pos = resolve_position(ps, (int32_t)t, &seq);
+  }
   if (pos < 0 || (TABLE && pos >= p.tab_rows)) return;
   C lo = load_chunk<T, VEC>(row);
   C hi = load_chunk<T, VEC>(row + half);
@@ -461,8 +524,10 @@ __global__ __launch_bounds__(64) void rope_qk_group_kernel(T* __restrict__ q, T*
       sn[e] = lds_sn[c * VEC + e];
     }
     rotate_chunk(lo, hi, cs, sn);
-    store_chunk<T, VEC>(row, lo);
-    store_chunk<T, VEC>(row + half, hi);
+    // the wave's last memory operations: written through to memory, not left
+    // dirty in L2
+    store_chunk_through<T, VEC>(row, lo);
+    store_chunk_through<T, VEC>(row + half, hi);
   }
 }
 
@@ -478,6 +543,42 @@ __global__ __launch_bounds__(kBlock) void rope_positions_kernel(const PosSource 
   if (ps.position_ids != nullptr || ps.num_seqs > 0) pos = resolve_position(ps, t, &seq);
   if (pos_out) pos_out[t] = pos;
   if (seq_out) seq_out[t] = seq;
+}
+
+// Running count of rotated tokens per sequence, the cu_valid of a compact launch:
+// out[0] = 0 and out[s+1] = out[s] + min(seqused[s], cu[s+1] - cu[s]) (the length
+// alone without seqused), each term clamped at 0, summed in 64 bits and saturated
+// at INT32_MAX. One workgroup; each step scans kBlock sequences in LDS
+// (Hillis-Steele) and carries the step's total into the next.
+__global__ __launch_bounds__(kBlock) void rope_valid_prefix_kernel(const int32_t* __restrict__ cu,
+                                                                   int32_t num_seqs,
+                                                                   const int32_t* __restrict__ seqused,
+                                                                   int32_t* __restrict__ out) {
+  __shared__ int64_t scan[kBlock];
+  const int i = threadIdx.x;
+  if (i == 0) out[0] = 0;
+  int64_t carry = 0;
+  for (int64_t base = 0; base < num_seqs; base += kBlock) {
+    const int64_t s = base + i;
+    int64_t used = 0;
+    if (s < num_seqs) {
+      const int64_t len = (int64_t)cu[s + 1] - (int64_t)cu[s];
+      used = seqused != nullptr && (int64_t)seqused[s] < len ? (int64_t)seqused[s] : len;
+      used = used < 0 ? 0 : used;
+    }
+    scan[i] = used;
+    __syncthreads();
+    for (int d = 1; d < kBlock; d <<= 1) {
+      const int64_t add = i >= d ? scan[i - d] : 0;
+      __syncthreads();
+      scan[i] += add;
+      __syncthreads();
+    }
+    const int64_t incl = carry + scan[i];
+    if (s < num_seqs) out[s + 1] = incl > (int64_t)INT32_MAX ? INT32_MAX : (int32_t)incl;
+    carry += scan[kBlock - 1];
+    __syncthreads();  // scan[] is rewritten by the next step
+  }
 }
 
 // Row i of the tables is position positions[i], or position i when positions is
@@ -569,12 +670,20 @@ int32_t launch_vec(void* q, void* k, const PosSource& ps, const RopeParams& p, b
   T* kt = static_cast<T*>(k);
   if (group_blocks > 0) {
     const uint32_t lds = group_dynamic_lds(group_blocks, p.gq, p.gk);
-    if (long_index)
-      hipLaunchKernelGGL((rope_qk_group_kernel<T, VEC, true, TABLE>), dim3(group_blocks), dim3(64),
-                         lds, stream, qt, kt, ps, p);
-    else
-      hipLaunchKernelGGL((rope_qk_group_kernel<T, VEC, false, TABLE>), dim3(group_blocks), dim3(64),
-                         lds, stream, qt, kt, ps, p);
+    if (!TABLE && ps.cu_valid != nullptr) {
+      if (long_index)
+        hipLaunchKernelGGL((rope_qk_group_kernel<T, VEC, true, false, true>), dim3(group_blocks),
+                           dim3(64), lds, stream, qt, kt, ps, p);
+      else
+        hipLaunchKernelGGL((rope_qk_group_kernel<T, VEC, false, false, true>), dim3(group_blocks),
+                           dim3(64), lds, stream, qt, kt, ps, p);
+    } else if (long_index) {
+      hipLaunchKernelGGL((rope_qk_group_kernel<T, VEC, true, TABLE, false>), dim3(group_blocks),
+                         dim3(64), lds, stream, qt, kt, ps, p);
+    } else {
+      hipLaunchKernelGGL((rope_qk_group_kernel<T, VEC, false, TABLE, false>), dim3(group_blocks),
+                         dim3(64), lds, stream, qt, kt, ps, p);
+    }
     return hipGetLastError() == hipSuccess ? ROPE_OK : ROPE_ELAUNCH;
   }
   if (long_index)
@@ -607,26 +716,35 @@ int32_t auto_tokens_per_wave(int64_t T) {
 // Grid of the row-group kernel (one 64-lane workgroup per token and row group), or
 // 0 when that kernel does not apply: the caller chose tokens per wave, nc does not
 // divide 64, the grid would exceed the dispatch size limit, or seqused marks a
-// padded layout. In the last case many rows are skipped; the row-group kernel
-// spends one workgroup per row group of each skipped token where the token kernel
-// spends one wave per token, and it measures slower there (Qwen3-8B batch padded
-// to 8 x 2048 rows: 34.2-34.4 vs 33.1-33.4 us), so padded layouts keep the token
-// kernel.
-int64_t group_grid(const RopeParams& p, bool geometry_chosen, bool padded) {
-  if (geometry_chosen || padded || 64 % p.nc != 0) return 0;
+// padded layout and the launch is not compact. In that case many rows are
+// skipped; the row-group kernel spends one workgroup per row group of each
+// skipped token where the token kernel spends one wave per token, and it measures
+// slower there (Qwen3-8B batch padded to 8 x 2048 rows: 34.2-34.4 vs 33.1-33.4
+// us), so such launches keep the token kernel. A compact launch (compact_rows >=
+// 0 rotated tokens, cu_valid given) covers only the rotated tokens and takes the
+// row-group kernel (28.3 against 32.0 us on that batch).
+int64_t group_grid(const RopeParams& p, bool geometry_chosen, bool padded, int64_t compact_rows) {
+  const bool compact = compact_rows >= 0;
+  if (geometry_chosen || (padded && !compact) || 64 % p.nc != 0) return 0;
   const int step_r = 64 / p.nc;
   const int64_t groups = (p.Hq + step_r - 1) / step_r + (p.Hkv + step_r - 1) / step_r;
-  const int64_t blocks = p.T * groups;
+  const int64_t blocks = (compact ? compact_rows : p.T) * groups;
   // < 2^26 workgroups: the dispatch limit, and the range of fastdiv::div
   return blocks <= (int64_t)0xffffffffu / 64 ? blocks : 0;
 }
 
+// compact_rows: rotated tokens of a compact launch (ps.cu_valid set), else -1. When
+// the row-group kernel does not apply, a compact launch falls back to the token
+// kernel over all rows with seqused, which rotates the same tokens.
 template <typename T>
-int32_t launch_typed(void* q, void* k, const PosSource& ps, RopeParams& p, int32_t bytes,
-                     bool long_index, bool geometry_chosen, hipStream_t stream) {
+int32_t launch_typed(void* q, void* k, PosSource ps, RopeParams& p, int32_t bytes,
+                     bool long_index, bool geometry_chosen, int64_t compact_rows,
+                     hipStream_t stream) {
   const int32_t vec = bytes / (int32_t)sizeof(T);
   p.nc = (p.D / 2) / vec;
-  const int64_t group_blocks = group_grid(p, geometry_chosen, ps.seqused != nullptr);
+  const int64_t group_blocks =
+      group_grid(p, geometry_chosen, ps.seqused != nullptr, ps.cu_valid ? compact_rows : -1);
+  if (group_blocks == 0) ps.cu_valid = nullptr;
   if (group_blocks > 0) {
     const int step_r = 64 / p.nc;
     p.gq = (uint32_t)((p.Hq + step_r - 1) / step_r);
@@ -659,9 +777,12 @@ extern "C" {
 // Shared by rope_qk_apply_ex (cos/sin evaluated from theta and pos_scale) and
 // rope_qk_apply_table (tab_cos != NULL: cos/sin read from the caller's tables;
 // theta and pos_scale unused).
+// cu_valid / valid_tokens: a compact launch over a padded layout (rope_qk_apply_padded);
+// valid_tokens = -1 for every other entry point.
 static int32_t apply_impl(void* q, void* k, int64_t T, int32_t Hq, int32_t Hkv, int32_t D,
                           int64_t q_token_stride, int64_t k_token_stride,
                           const int32_t* cu_seqlens, int32_t num_seqs, const int32_t* seqused,
+                          const int32_t* cu_valid, int64_t valid_tokens,
                           const int32_t* seq_offsets, const int32_t* position_ids, double theta,
                           double pos_scale, const float* tab_cos, const float* tab_sin,
                           int32_t tab_rows, int32_t dtype, int32_t direction, int32_t index_mode,
@@ -686,6 +807,12 @@ static int32_t apply_impl(void* q, void* k, int64_t T, int32_t Hq, int32_t Hkv, 
     if (cu_seqlens == nullptr) return ROPE_EINVAL;
   }
   if ((Hq > 0 && q == nullptr) || (Hkv > 0 && k == nullptr)) return ROPE_EINVAL;
+  const bool compact = valid_tokens >= 0;
+  if (compact) {
+    if (valid_tokens > T) return ROPE_EINVAL;
+    if (valid_tokens == 0) return ROPE_OK;  // nothing is rotated
+    if (cu_valid == nullptr) return ROPE_EINVAL;
+  }
 
   const int64_t qs = q_token_stride == 0 ? (int64_t)Hq * D : q_token_stride;
   const int64_t ks = k_token_stride == 0 ? (int64_t)Hkv * D : k_token_stride;
@@ -728,6 +855,7 @@ static int32_t apply_impl(void* q, void* k, int64_t T, int32_t Hq, int32_t Hkv, 
   ps.seqused = position_ids ? nullptr : seqused;
   ps.seq_offsets = position_ids ? nullptr : seq_offsets;
   ps.num_seqs = position_ids ? 0 : num_seqs;
+  ps.cu_valid = compact ? cu_valid : nullptr;
 
   void* qp = Hq > 0 ? q : nullptr;
   void* kp = Hkv > 0 ? k : nullptr;
@@ -735,9 +863,12 @@ static int32_t apply_impl(void* q, void* k, int64_t T, int32_t Hq, int32_t Hkv, 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool chosen = tokens_per_wave != 0;
   switch (dtype) {
-    case ROPE_F32: return launch_typed<float>(qp, kp, ps, p, bytes, long_index, chosen, s);
-    case ROPE_BF16: return launch_typed<__bf16>(qp, kp, ps, p, bytes, long_index, chosen, s);
-    default: return launch_typed<_Float16>(qp, kp, ps, p, bytes, long_index, chosen, s);
+    case ROPE_F32:
+      return launch_typed<float>(qp, kp, ps, p, bytes, long_index, chosen, valid_tokens, s);
+    case ROPE_BF16:
+      return launch_typed<__bf16>(qp, kp, ps, p, bytes, long_index, chosen, valid_tokens, s);
+    default:
+      return launch_typed<_Float16>(qp, kp, ps, p, bytes, long_index, chosen, valid_tokens, s);
   }
 }
 
@@ -748,8 +879,20 @@ int32_t rope_qk_apply_ex(void* q, void* k, int64_t T, int32_t Hq, int32_t Hkv, i
                          double pos_scale, int32_t dtype, int32_t direction, int32_t index_mode,
                          int32_t tokens_per_wave, void* stream) {
   return apply_impl(q, k, T, Hq, Hkv, D, q_token_stride, k_token_stride, cu_seqlens, num_seqs,
-                    seqused, seq_offsets, position_ids, theta, pos_scale, nullptr, nullptr, 0,
-                    dtype, direction, index_mode, tokens_per_wave, stream);
+                    seqused, nullptr, -1, seq_offsets, position_ids, theta, pos_scale, nullptr,
+                    nullptr, 0, dtype, direction, index_mode, tokens_per_wave, stream);
+}
+
+int32_t rope_qk_apply_padded(void* q, void* k, int64_t T, int32_t Hq, int32_t Hkv, int32_t D,
+                             int64_t q_token_stride, int64_t k_token_stride,
+                             const int32_t* cu_seqlens, int32_t num_seqs, const int32_t* seqused,
+                             const int32_t* cu_valid, int64_t valid_tokens,
+                             const int32_t* seq_offsets, double theta, double pos_scale,
+                             int32_t dtype, int32_t direction, int32_t index_mode, void* stream) {
+  if (valid_tokens < 0) return ROPE_EINVAL;
+  return apply_impl(q, k, T, Hq, Hkv, D, q_token_stride, k_token_stride, cu_seqlens, num_seqs,
+                    seqused, cu_valid, valid_tokens, seq_offsets, nullptr, theta, pos_scale,
+                    nullptr, nullptr, 0, dtype, direction, index_mode, 0, stream);
 }
 
 int32_t rope_qk_apply_table(void* q, void* k, int64_t T, int32_t Hq, int32_t Hkv, int32_t D,
@@ -762,8 +905,8 @@ int32_t rope_qk_apply_table(void* q, void* k, int64_t T, int32_t Hq, int32_t Hkv
   if (dtype != ROPE_F32 && dtype != ROPE_BF16 && dtype != ROPE_F16) return ROPE_EUNSUPPORTED;
   if (cos_tab == nullptr || sin_tab == nullptr || tab_rows < 1) return ROPE_EINVAL;
   return apply_impl(q, k, T, Hq, Hkv, D, q_token_stride, k_token_stride, cu_seqlens, num_seqs,
-                    seqused, seq_offsets, position_ids, 1.0, 1.0, cos_tab, sin_tab, tab_rows,
-                    dtype, direction, index_mode, tokens_per_wave, stream);
+                    seqused, nullptr, -1, seq_offsets, position_ids, 1.0, 1.0, cos_tab, sin_tab,
+                    tab_rows, dtype, direction, index_mode, tokens_per_wave, stream);
 }
 
 int32_t rope_qk_apply(void* q, void* k, int64_t T, int32_t Hq, int32_t Hkv, int32_t D,
@@ -813,6 +956,7 @@ int32_t rope_positions_ex(const int32_t* cu_seqlens, int32_t num_seqs, const int
   const int64_t blocks = (T + kBlock - 1) / kBlock;
   if (blocks > kMaxBlocksX) return ROPE_EINVAL;
   PosSource ps;
+  ps.cu_valid = nullptr;
   ps.position_ids = position_ids;
   ps.cu = position_ids ? nullptr : cu_seqlens;
   ps.seqused = position_ids ? nullptr : seqused;
@@ -820,6 +964,15 @@ int32_t rope_positions_ex(const int32_t* cu_seqlens, int32_t num_seqs, const int
   ps.num_seqs = position_ids ? 0 : num_seqs;
   hipLaunchKernelGGL(rope_positions_kernel, dim3((unsigned)blocks), dim3(kBlock), 0,
                      static_cast<hipStream_t>(stream), ps, T, pos_out, seq_out);
+  return hipGetLastError() == hipSuccess ? ROPE_OK : ROPE_ELAUNCH;
+}
+
+int32_t rope_valid_prefix(const int32_t* cu_seqlens, int32_t num_seqs, const int32_t* seqused,
+                          int32_t* cu_valid_out, void* stream) {
+  if (num_seqs < 0 || num_seqs == INT32_MAX || cu_valid_out == nullptr) return ROPE_EINVAL;
+  if (num_seqs > 0 && cu_seqlens == nullptr) return ROPE_EINVAL;
+  hipLaunchKernelGGL(rope_valid_prefix_kernel, dim3(1), dim3(kBlock), 0,
+                     static_cast<hipStream_t>(stream), cu_seqlens, num_seqs, seqused, cu_valid_out);
   return hipGetLastError() == hipSuccess ? ROPE_OK : ROPE_ELAUNCH;
 }
 

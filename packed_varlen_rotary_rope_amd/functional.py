@@ -6,6 +6,8 @@ module only wires them into torch.autograd (no arithmetic of its own).
 
     qkv = rope_qkv(qkv, Hq, Hkv, cu_seqlens, theta)  # fused QKV output, in place
     q, k = rope_qk(q, k, cu_seqlens, theta)        # returns q and k, rotated
+    q, k = rope_qk(q, k, cu, theta, seqused=su,    # padded layout, launched over its
+                   cu_valid=valid_prefix(cu, su), valid_tokens=n)  # n rotated tokens only
     q, k = rope_qk_table(q, k, cos_tab, sin_tab, cu_seqlens)  # cos/sin from tables
     h = glu("swiglu", e, g)                        # h = silu(e) * g
     h = glu_fused("geglu", gate_up)                # e, g = halves of gate_up
@@ -32,31 +34,49 @@ from __future__ import annotations
 
 import torch
 
-from . import glu_bwd, glu_fwd, qk_apply_ex_, qk_apply_table_
+from . import glu_bwd, glu_fwd, qk_apply_ex_, qk_apply_padded_, qk_apply_table_
+
+
+def _rotate(q, k, theta, direction, cu, su, pid, so, pos_scale, cv, valid):
+    """One launch: the compact padded launch when cu_valid is given, else the general one."""
+    if cv is not None:
+        qk_apply_padded_(q, k, theta, direction, cu, su, cv, valid, seq_offsets=so,
+                         pos_scale=pos_scale)
+    else:
+        qk_apply_ex_(q, k, theta, direction, cu_seqlens=cu, seqused=su, seq_offsets=so,
+                     position_ids=pid, pos_scale=pos_scale)
+
+
+def _padded_args(position_ids, cu_valid, valid_tokens):
+    if cu_valid is None:
+        return None
+    if position_ids is not None or valid_tokens is None:
+        raise ValueError("cu_valid goes with cu_seqlens and valid_tokens, not position_ids")
+    return int(valid_tokens)
 
 
 class _RopeQK(torch.autograd.Function):
     @staticmethod
     def forward(ctx, q, k, cu_seqlens, theta, seqused, position_ids, seq_offsets, pos_scale,
-                inplace_backward):
-        qk_apply_ex_(q, k, theta, 1, cu_seqlens=cu_seqlens, seqused=seqused,
-                     seq_offsets=seq_offsets, position_ids=position_ids, pos_scale=pos_scale)
+                inplace_backward, cu_valid, valid_tokens):
+        _rotate(q, k, theta, 1, cu_seqlens, seqused, position_ids, seq_offsets, pos_scale,
+                cu_valid, valid_tokens)
         ctx.mark_dirty(q, k)
-        ctx.save_for_backward(cu_seqlens, seqused, position_ids, seq_offsets)
+        ctx.save_for_backward(cu_seqlens, seqused, position_ids, seq_offsets, cu_valid)
         ctx.theta, ctx.pos_scale, ctx.inplace = theta, pos_scale, inplace_backward
+        ctx.valid = valid_tokens
         return q, k
 
     @staticmethod
     def backward(ctx, dq, dk):
         # gradients that did not flow arrive as zeros (materialized by autograd)
-        cu, su, pid, so = ctx.saved_tensors
+        cu, su, pid, so, cv = ctx.saved_tensors
         if not (ctx.inplace and dq.is_contiguous()):
             dq = dq.clone(memory_format=torch.contiguous_format)
         if not (ctx.inplace and dk.is_contiguous()):
             dk = dk.clone(memory_format=torch.contiguous_format)
-        qk_apply_ex_(dq, dk, ctx.theta, -1, cu_seqlens=cu, seqused=su, seq_offsets=so,
-                     position_ids=pid, pos_scale=ctx.pos_scale)
-        return dq, dk, None, None, None, None, None, None, None
+        _rotate(dq, dk, ctx.theta, -1, cu, su, pid, so, ctx.pos_scale, cv, ctx.valid)
+        return dq, dk, None, None, None, None, None, None, None, None, None
 
 
 def _own_storage(t: torch.Tensor) -> torch.Tensor:
@@ -69,14 +89,18 @@ def _own_storage(t: torch.Tensor) -> torch.Tensor:
 
 def rope_qk(q: torch.Tensor, k: torch.Tensor, cu_seqlens=None, theta: float = 10000.0,
             seqused=None, position_ids=None, seq_offsets=None, pos_scale: float = 1.0,
-            inplace_backward: bool = False):
+            inplace_backward: bool = False, cu_valid=None, valid_tokens=None):
     """Differentiable RoPE of q [T, Hq, D] and k [T, Hkv, D] (views with contiguous
     heads, e.g. slices of a fused QKV output, are accepted), in place unless q or k
     is a view that requires grad (then on a copy of it; see the module docstring and
     rope_qkv). Positions come from cu_seqlens (with optional seqused / seq_offsets)
-    or position_ids, as in ``qk_apply_ex_``. Returns (q, k), rotated."""
+    or position_ids, as in ``qk_apply_ex_``; with ``cu_valid`` (from ``valid_prefix``)
+    and ``valid_tokens``, a padded layout is launched over its rotated tokens only, as
+    in ``qk_apply_padded_`` (same results). Returns (q, k), rotated."""
+    valid = _padded_args(position_ids, cu_valid, valid_tokens)
     return _RopeQK.apply(_own_storage(q), _own_storage(k), cu_seqlens, float(theta), seqused,
-                         position_ids, seq_offsets, float(pos_scale), bool(inplace_backward))
+                         position_ids, seq_offsets, float(pos_scale), bool(inplace_backward),
+                         cu_valid, valid)
 
 
 def _qkv_split(qkv: torch.Tensor, Hq: int, Hkv: int):
@@ -106,38 +130,40 @@ def _qkv_split(qkv: torch.Tensor, Hq: int, Hkv: int):
 class _RopeQKV(torch.autograd.Function):
     @staticmethod
     def forward(ctx, qkv, Hq, Hkv, cu_seqlens, theta, seqused, position_ids, seq_offsets,
-                pos_scale, inplace_backward):
+                pos_scale, inplace_backward, cu_valid, valid_tokens):
         q, k = _qkv_split(qkv, Hq, Hkv)
-        qk_apply_ex_(q, k, theta, 1, cu_seqlens=cu_seqlens, seqused=seqused,
-                     seq_offsets=seq_offsets, position_ids=position_ids, pos_scale=pos_scale)
+        _rotate(q, k, theta, 1, cu_seqlens, seqused, position_ids, seq_offsets, pos_scale,
+                cu_valid, valid_tokens)
         ctx.mark_dirty(qkv)
-        ctx.save_for_backward(cu_seqlens, seqused, position_ids, seq_offsets)
+        ctx.save_for_backward(cu_seqlens, seqused, position_ids, seq_offsets, cu_valid)
         ctx.heads, ctx.theta, ctx.pos_scale = (Hq, Hkv), theta, pos_scale
-        ctx.inplace = inplace_backward
+        ctx.inplace, ctx.valid = inplace_backward, valid_tokens
         return qkv
 
     @staticmethod
     def backward(ctx, g):
-        cu, su, pid, so = ctx.saved_tensors
+        cu, su, pid, so, cv = ctx.saved_tensors
         if not (ctx.inplace and g.is_contiguous()):
             g = g.clone(memory_format=torch.contiguous_format)
         dq, dk = _qkv_split(g, *ctx.heads)
-        qk_apply_ex_(dq, dk, ctx.theta, -1, cu_seqlens=cu, seqused=su, seq_offsets=so,
-                     position_ids=pid, pos_scale=ctx.pos_scale)
-        return g, None, None, None, None, None, None, None, None, None
+        _rotate(dq, dk, ctx.theta, -1, cu, su, pid, so, ctx.pos_scale, cv, ctx.valid)
+        return g, None, None, None, None, None, None, None, None, None, None, None
 
 
 def rope_qkv(qkv: torch.Tensor, num_q_heads: int, num_kv_heads: int, cu_seqlens=None,
              theta: float = 10000.0, seqused=None, position_ids=None, seq_offsets=None,
-             pos_scale: float = 1.0, inplace_backward: bool = False) -> torch.Tensor:
+             pos_scale: float = 1.0, inplace_backward: bool = False, cu_valid=None,
+             valid_tokens=None) -> torch.Tensor:
     """Differentiable in-place RoPE of the Q and K heads inside a fused QKV projection
     output qkv [T, (Hq + 2 Hkv) * D] or [T, Hq + 2 Hkv, D] (Q heads, then K, then V;
     each token's columns contiguous, rows of any stride), one kernel launch per
     pass; the V heads and their gradient pass through unchanged. qkv may be a view
-    (e.g. ``(x @ W_qkv).view(T, -1, D)``). Positions as in ``rope_qk``. Returns qkv."""
+    (e.g. ``(x @ W_qkv).view(T, -1, D)``). Positions (and the compact padded launch)
+    as in ``rope_qk``. Returns qkv."""
+    valid = _padded_args(position_ids, cu_valid, valid_tokens)
     return _RopeQKV.apply(qkv, int(num_q_heads), int(num_kv_heads), cu_seqlens, float(theta),
                           seqused, position_ids, seq_offsets, float(pos_scale),
-                          bool(inplace_backward))
+                          bool(inplace_backward), cu_valid, valid)
 
 
 class _RopeQKTable(torch.autograd.Function):

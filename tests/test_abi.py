@@ -50,7 +50,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert rope.abi_version() == 4
+    assert rope.abi_version() == 5
     lib = rope._lib
     for st in (0, -1, -2, -3):
         assert lib.rope_status_str(st).decode().startswith("ROPE_")
@@ -168,6 +168,51 @@ def test_validation_table(kw, expect):
     """The table entry point validates like rope_qk_apply_ex, plus its tables; it has
     no theta or scale to check."""
     assert apply_table(**kw) == expect
+
+
+def apply_padded(**kw):
+    a = dict(q=FAKE, k=FAKE, T=16, Hq=4, Hkv=2, D=128, qs=0, ks=0, cu=FAKE, num_seqs=2,
+             seqused=FAKE, cv=FAKE, valid=10, offsets=None, theta=1e4, scale=1.0, dtype=1,
+             direction=1, index_mode=0, stream=None)
+    a.update(kw)
+    return rope._lib.rope_qk_apply_padded(a["q"], a["k"], a["T"], a["Hq"], a["Hkv"], a["D"],
+                                          a["qs"], a["ks"], a["cu"], a["num_seqs"],
+                                          a["seqused"], a["cv"], a["valid"], a["offsets"],
+                                          a["theta"], a["scale"], a["dtype"], a["direction"],
+                                          a["index_mode"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(valid=-1), EINVAL),
+    (dict(valid=17), EINVAL),                   # more rotated tokens than rows
+    (dict(cv=None), EINVAL),
+    (dict(dtype=4), EUNSUPPORTED),
+    (dict(theta=0.5), EINVAL),
+    (dict(scale=0.5), EINVAL),
+    (dict(D=127), EINVAL),
+    (dict(direction=0), EINVAL),
+    (dict(index_mode=3), EINVAL),
+    (dict(cu=None), EINVAL),
+    (dict(q=None), EINVAL),
+    (dict(qs=4 * 128 - 1), EINVAL),
+    (dict(T=524288, Hq=32, Hkv=8, D=128, index_mode=1, valid=100), EINVAL),
+    # Empty work: valid, and returns before touching the GPU.
+    (dict(valid=0, cv=None), OK),
+    (dict(num_seqs=0, cu=None, cv=None), OK),
+    (dict(T=0, q=None, k=None, cu=None, cv=None, valid=0), OK),
+])
+def test_validation_padded(kw, expect):
+    """The compact padded entry point validates like rope_qk_apply_ex, plus its
+    rotated-token count (0..T) and its cu_valid array."""
+    assert apply_padded(**kw) == expect
+
+
+def test_valid_prefix_validation():
+    lib = rope._lib
+    assert lib.rope_valid_prefix(FAKE, -1, None, FAKE, None) == EINVAL
+    assert lib.rope_valid_prefix(FAKE, 2**31 - 1, None, FAKE, None) == EINVAL
+    assert lib.rope_valid_prefix(FAKE, 2, None, None, None) == EINVAL
+    assert lib.rope_valid_prefix(None, 2, FAKE, FAKE, None) == EINVAL
 
 
 def test_fwd_bwd_positions_cos_sin_validation():

@@ -13,7 +13,7 @@ import bench
 import workloads
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-GROUP = "_ZN12_GLOBAL__N_120rope_qk_group_kernelIDF16bLi8ELb0ELb0EEEvPT_S2_"
+GROUP = "_ZN12_GLOBAL__N_120rope_qk_group_kernelIDF16bLi8ELb0ELb0ELb0EEEvPT_S2_"
 COPY = "__amd_rocclr_copyBuffer"
 
 
@@ -55,19 +55,31 @@ def test_algorithmic_bytes():
 def test_kernel_choice():
     assert bench.rope_kernel_name(workloads.get("qwen3_4b_packed"), 0) == "rope_qk_group_kernel"
     assert bench.rope_kernel_name(workloads.get("qwen3_4b_packed"), 1) == "rope_qk_kernel"
-    assert bench.rope_kernel_name(workloads.get("qwen3_8b_padded"), 0) == "rope_qk_kernel"
+    pad = workloads.get("qwen3_8b_padded")
+    assert bench.rope_kernel_name(pad, 0) == "rope_qk_group_kernel"          # compact launch
+    assert bench.rope_kernel_name(pad, 0, "seqused") == "rope_qk_kernel"
+    assert bench.compact_launch(pad) and not bench.compact_launch(workloads.get("qwen3_4b_packed"))
+    # grid of the compact launch: the rotated tokens' row groups only
+    assert bench.expected_grid_threads(pad) == pad.valid_tokens * 5 * 64
+    assert bench.expected_grid_threads(pad, "seqused") == pad.T * 64
 
 
 def test_kernel_instance_names():
     """The mangled-name fragments the summaries filter rocprofv3 records by."""
     w5, w2 = workloads.get("long_ctx_512k"), workloads.get("qwen3_4b_packed")
     assert bench.needs_long_index(w5) and not bench.needs_long_index(w2)
-    assert bench.rope_kernel_instance(w5, True) == "rope_qk_group_kernelIDF16bLi8ELb1ELb0E"
+    assert bench.rope_kernel_instance(w5, True) == "rope_qk_group_kernelIDF16bLi8ELb1ELb0ELb0E"
     assert bench.rope_kernel_instance(w2, False) in GROUP
     assert bench.rope_kernel_instance(workloads.get("tiny_packed"), False) == \
-        "rope_qk_group_kernelIfLi4ELb0ELb0E"
-    assert bench.rope_kernel_instance(workloads.get("qwen3_8b_padded"), False) == \
+        "rope_qk_group_kernelIfLi4ELb0ELb0ELb0E"
+    pad = workloads.get("qwen3_8b_padded")
+    assert bench.rope_kernel_instance(pad, False) == "rope_qk_group_kernelIDF16bLi8ELb0ELb0ELb1E"
+    assert bench.rope_kernel_instance(pad, False, "seqused") == \
         "rope_qk_kernelIDF16bLi8ELb0ELb0E"
+    assert bench.rope_instance_names(pad, False)[1] == \
+        "rope_qk_group_kernel<__bf16, 8, false, false, true>"
+    assert bench.rope_instance_names(w5, True)[1] == \
+        "rope_qk_group_kernel<__bf16, 8, true, false, false>"
 
 
 def test_linear_fit():
@@ -104,7 +116,7 @@ def test_traffic_summary_request_counts(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "traffic_path", lambda workload: str(out))
     w = workloads.get("long_ctx_512k")
     bpl = bench.algorithmic_bytes_per_launch(w)
-    long_k = "_ZN12_GLOBAL__N_120rope_qk_group_kernelIDF16bLi8ELb1ELb0EEEvPT_S2_"
+    long_k = "_ZN12_GLOBAL__N_120rope_qk_group_kernelIDF16bLi8ELb1ELb0ELb0EEEvPT_S2_"
     kib = 1024.0
     for name, ctr, val in (("cf", "FETCH_SIZE", 2 ** 30 / kib / 2), ("cw", "WRITE_SIZE", 2 ** 30 / kib)):
         _counter_csv(str(tmp_path / f"{name}.csv"), [(COPY, ctr, val)])

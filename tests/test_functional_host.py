@@ -89,3 +89,36 @@ def test_rope_qkv_rejects_bad_layouts():
         F._qkv_split(torch.zeros(T, Hq + 2 * Hkv + 1, D), Hq, Hkv)
     with pytest.raises(ValueError):
         F._qkv_split(torch.zeros(D, Hq + 2 * Hkv, T).transpose(0, 2), Hq, Hkv)
+
+
+def test_rope_qk_compact_padded_routing(monkeypatch):
+    """With cu_valid and valid_tokens, forward and backward both take the compact padded
+    entry point with the same metadata; position_ids or a missing count are refused."""
+    calls = []
+
+    def fake_padded(q, k, theta, direction, cu_seqlens, seqused, cu_valid, valid_tokens, **kw):
+        calls.append((direction, cu_valid.data_ptr(), valid_tokens))
+        with torch.no_grad():
+            q.mul_(2.0)
+            k.mul_(3.0)
+        return q, k
+
+    def no_ex(*a, **kw):
+        raise AssertionError("the general entry point was called")
+
+    monkeypatch.setattr(F, "qk_apply_padded_", fake_padded)
+    monkeypatch.setattr(F, "qk_apply_ex_", no_ex)
+    x = torch.randn(T, (Hq + Hkv) * D, requires_grad=True)
+    q = (x[:, :Hq * D] * 1.0).reshape(T, Hq, D).contiguous()
+    k = (x[:, Hq * D:] * 1.0).reshape(T, Hkv, D).contiguous()
+    su = torch.tensor([1, 3], dtype=torch.int32)
+    cv = torch.tensor([0, 1, 4], dtype=torch.int32)
+    qr, kr = F.rope_qk(q, k, cu(), 1e4, seqused=su, cu_valid=cv, valid_tokens=4)
+    (qr.sum() + kr.sum()).backward()
+    assert calls == [(1, cv.data_ptr(), 4), (-1, cv.data_ptr(), 4)]
+    assert torch.allclose(x.grad[:, :Hq * D], torch.full((T, Hq * D), 2.0))
+    with pytest.raises(ValueError):
+        F.rope_qk(q.detach(), k.detach(), cu(), 1e4, cu_valid=cv)  # no count
+    with pytest.raises(ValueError):
+        F.rope_qk(q.detach(), k.detach(), None, 1e4, position_ids=torch.zeros(T, dtype=torch.int32),
+                  cu_valid=cv, valid_tokens=4)

@@ -68,6 +68,34 @@ def test_rope_autograd_matches_direct_launches(lib, inplace_backward):
     assert int(np.abs(ordered(got) - ordered(want)).max()) <= 1
 
 
+def test_rope_autograd_compact_padded(lib):
+    """The padded Qwen3-8B batch through rope_qk with cu_valid / valid_tokens (the
+    compact launch, both passes): output and gradients bit for bit those of the
+    seqused launch, padded rows and their gradients passed through unchanged."""
+    rope, F = lib
+    w = workloads.get("qwen3_8b_padded")
+    print("[autograd] rope_qk compact padded", flush=True)
+    cu = torch.from_numpy(w.cu_seqlens).to(DEV)
+    su = torch.from_numpy(w.seqused).to(DEV)
+    cv = rope.valid_prefix(cu, su)
+    wq = workloads.make_tensor(w.shape("q"), 43, "bf16", device=DEV)
+    wk = workloads.make_tensor(w.shape("k"), 44, "bf16", device=DEV)
+    res = []
+    for compact in (True, False):
+        q0 = workloads.make_tensor(w.shape("q"), 41, "bf16", device=DEV).requires_grad_()
+        k0 = workloads.make_tensor(w.shape("k"), 42, "bf16", device=DEV).requires_grad_()
+        kw = dict(cu_valid=cv, valid_tokens=w.valid_tokens) if compact else {}
+        qr, kr = F.rope_qk(q0 * 1, k0 * 1, cu, w.theta, seqused=su, **kw)
+        ((qr.float() * wq.float()).sum() + (kr.float() * wk.float()).sum()).backward()
+        torch.cuda.synchronize()
+        res.append([bits16(t) for t in (qr, kr, q0.grad, k0.grad)])
+    for a, b in zip(*res):
+        assert np.array_equal(a, b)
+    pos, _ = oracle.positions(w.cu_seqlens, w.T, w.seqused)
+    pad = pos < 0
+    assert np.array_equal(res[0][2][pad], bits16(wq)[pad])  # gradient of a padded row: wq
+
+
 @pytest.mark.parametrize("inplace_backward", [False, True])
 def test_rope_table_autograd_matches_theta_path(lib, inplace_backward):
     """rope_qk_table with the library's own cos/sin tables gives the outputs and the

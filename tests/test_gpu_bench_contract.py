@@ -40,4 +40,7 @@ def test_bench_json_contract():
     assert set(d["per_config"]) == {"tiny_packed", "qwen3_4b_packed", "qwen3_8b_packed",
                                     "qwen3_8b_padded", "qwen3_32b_packed", "long_ctx_512k"}
     assert d["per_config"]["qwen3_8b_packed"].get("headline") is True
-    assert 1.0 < d["per_config"]["qwen3_8b_padded"]["t_over_packed"] < 2.0
+    pad = d["per_config"]["qwen3_8b_padded"]
+    assert pad["padded_launch"] == "compact" and pad["kernel"] == "rope_qk_group_kernel"
+    assert 0.8 < pad["t_over_packed"] < 1.5 and pad["valid_fraction"] < 0.6
+    assert pad["seqused_kernel"] == "rope_qk_kernel" and pad["seqused_launch_us"] > 0

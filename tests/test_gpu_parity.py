@@ -782,3 +782,189 @@ def test_concurrent_streams(rope):
     for (qr, kr), (qg, kg) in zip(ref, got):
         assert torch.equal(qg.view(torch.int16), qr.view(torch.int16))
         assert torch.equal(kg.view(torch.int16), kr.view(torch.int16))
+
+
+# ---------------------------------------------------------------- compact padded launches
+
+def _used(cu_np, su_np):
+    lens = np.diff(np.asarray(cu_np, dtype=np.int64))
+    used = lens if su_np is None else np.minimum(np.asarray(su_np, dtype=np.int64), lens)
+    return np.maximum(used, 0)
+
+
+def _cu_valid(cu_np, su_np):
+    return np.concatenate([[0], np.cumsum(_used(cu_np, su_np))]).astype(np.int32)
+
+
+def _compact_seqused(cu_np, su_np, cv_np, valid):
+    """Per sequence, the tokens a compact launch rotates for a non-decreasing cu_valid
+    (matching or not) and count `valid`: workgroup index v lands in sequence s for
+    cu_valid[s] <= v < cu_valid[s+1], at position v - cu_valid[s], so s rotates its
+    first min(cu_valid[s+1], valid) - cu_valid[s] positions, at most its used count."""
+    cv = np.asarray(cv_np, dtype=np.int64)
+    eff = np.minimum(cv[1:], valid) - cv[:-1]
+    return np.clip(eff, 0, _used(cu_np, su_np)).astype(np.int32)
+
+
+def run_compact(rope, name, host, cu_np, su_np, cv_np, valid, theta, dtype, seq_offsets=None,
+                pos_scale=1.0, index_mode=0, expect_seqused=None):
+    """Forward on (q, k) and backward on (dq, dk) through rope_qk_apply_padded, against
+    the oracle with `expect_seqused` (default: su_np) as the rotated prefix of each
+    sequence; untouched rows and guard regions bit for bit."""
+    print(f"[parity] compact {name} T={host['q'].shape[0]} {dtype} valid={valid}", flush=True)
+    cu = torch.from_numpy(np.asarray(cu_np, dtype=np.int32)).to(DEV)
+    su = None if su_np is None else torch.from_numpy(np.asarray(su_np, dtype=np.int32)).to(DEV)
+    cv = torch.from_numpy(np.asarray(cv_np, dtype=np.int32)).to(DEV)
+    so = None if seq_offsets is None else \
+        torch.from_numpy(np.asarray(seq_offsets, dtype=np.int32)).to(DEV)
+    dev, flats = {}, {}
+    for what, t in host.items():
+        dev[what], flats[what], g = guarded(t)
+    for a, b, direction in (("q", "k", 1), ("dq", "dk", -1)):
+        rope.qk_apply_padded_(dev[a], dev[b], theta, direction, cu, su, cv, valid,
+                              seq_offsets=so, pos_scale=pos_scale, index_mode=index_mode)
+    torch.cuda.synchronize()
+    want_su = su_np if expect_seqused is None else expect_seqused
+    T = host["q"].shape[0]
+    pos, _ = oracle.positions(cu_np, T, want_su, seq_offsets)
+    touched = pos >= 0
+    for what, direction in (("q", 1), ("k", 1), ("dq", -1), ("dk", -1)):
+        x = bits(host[what])
+        ref = oracle.rope(x, cu_np, theta, direction, dtype, want_su, NTHREADS,
+                          seq_offsets=seq_offsets, pos_scale=pos_scale)
+        assert_parity(dtype, bits(dev[what]), ref, x, touched, f"compact {name}:{what}")
+        assert guards_intact(flats[what], g), f"compact {name}:{what}: guard region written"
+    return {what: bits(t) for what, t in dev.items()}
+
+
+def test_padded_compact_workload(rope):
+    """The Qwen3-8B batch padded to 8 x 2048 rows through the compact launch, with
+    cu_valid from the library's prefix kernel: every element against the oracle,
+    padded rows untouched, and bit for bit the seqused launch's result."""
+    w = workloads.get("qwen3_8b_padded")
+    host = make_host(w)
+    cu = torch.from_numpy(w.cu_seqlens).to(DEV)
+    su = torch.from_numpy(w.seqused).to(DEV)
+    cv_dev = rope.valid_prefix(cu, su)
+    cv = _cu_valid(w.cu_seqlens, w.seqused)
+    assert np.array_equal(cv_dev.cpu().numpy(), cv)
+    got = run_compact(rope, w.name, host, w.cu_seqlens, w.seqused, cv, int(cv[-1]), w.theta,
+                      w.dtype)
+    ref = run_and_check(rope, w.name, host, w.cu_seqlens, w.seqused, w.theta, w.dtype)
+    for what in ("q", "k", "dq", "dk"):
+        assert np.array_equal(got[what], ref[what]), what
+
+
+def _ragged_padded(seed, B, S, Hq, Hkv, D, dtype, tail=0):
+    """B sequences padded to S rows each (plus `tail` rows after the last), with an
+    empty sequence, seqused beyond the length, a negative seqused and a zero one."""
+    rng = np.random.default_rng(seed)
+    cu = (np.arange(B + 1, dtype=np.int64) * S).astype(np.int32)
+    su = rng.integers(1, S + 1, size=B).astype(np.int32)
+    su[1], su[2], su[3] = S + 50, -3, 0
+    cu[B] = cu[B] - 7                    # the last sequence is 7 rows short
+    cu[5] = cu[4]                        # sequence 4 is empty
+    T = B * S + tail
+    host = {what: workloads.make_tensor((T, Hq if what in ("q", "dq") else Hkv, D), seed + i,
+                                        dtype) for i, what in enumerate(("q", "k", "dq", "dk"))}
+    return host, cu, su
+
+
+COMPACT_EDGE = [
+    # name, dtype, D, Hq, Hkv, extra
+    ("bf16_D128", "bf16", 128, 4, 2, {}),
+    ("f32_D64", "f32", 64, 3, 1, {}),
+    ("f16_D128_offsets", "f16", 128, 2, 2, {"offsets": True}),
+    ("bf16_pos_scale", "bf16", 128, 4, 2, {"pos_scale": 4.0}),
+    ("bf16_int64", "bf16", 128, 4, 2, {"index_mode": 2}),
+    ("bf16_no_seqused", "bf16", 128, 4, 2, {"no_seqused": True}),
+    ("bf16_D80_fallback", "bf16", 80, 4, 2, {}),     # nc = 5: the seqused launch runs
+    ("bf16_valid_short", "bf16", 128, 4, 2, {"valid_delta": -100}),
+    ("bf16_cv_wide", "bf16", 128, 4, 2, {"cv_gap": 9}),
+    ("bf16_cv_narrow", "bf16", 128, 4, 2, {"cv_gap": -9}),
+]
+
+
+@pytest.mark.parametrize("case", COMPACT_EDGE, ids=[c[0] for c in COMPACT_EDGE])
+def test_padded_compact_edges(rope, case):
+    """Ragged padded batches through the compact launch against the oracle: empty
+    sequences, seqused past the length, negative and zero seqused, a token tail,
+    per-sequence offsets (some shifting positions out of range), position scaling,
+    forced 64-bit offsets, no seqused, a head size that falls back to the seqused
+    launch, and cu_valid / counts that do not match the layout (fewer tokens rotated,
+    never wrong ones)."""
+    name, dtype, D, Hq, Hkv, extra = case
+    B, S = 12, 96
+    host, cu, su = _ragged_padded(7100 + len(name), B, S, Hq, Hkv, D, dtype, tail=5)
+    if extra.get("no_seqused"):
+        su = None
+    offsets = None
+    if extra.get("offsets"):
+        offsets = np.full(B, 1000, dtype=np.int32)
+        offsets[0], offsets[6] = -40, 2**31 - 60   # some positions leave [0, 2^31)
+    cv = _cu_valid(cu, su)
+    valid = int(cv[-1])
+    expect = None
+    if "valid_delta" in extra:
+        valid += extra["valid_delta"]
+        expect = _compact_seqused(cu, su, cv, valid)
+    if "cv_gap" in extra:
+        gaps = np.diff(cv.astype(np.int64)) + extra["cv_gap"]
+        cv = np.concatenate([[0], np.cumsum(np.maximum(gaps, 0))]).astype(np.int32)
+        valid = min(int(cv[-1]), host["q"].shape[0])
+        expect = _compact_seqused(cu, su, cv, valid)
+    run_compact(rope, name, host, cu, su, cv, valid, 1e4, dtype, seq_offsets=offsets,
+                pos_scale=extra.get("pos_scale", 1.0), index_mode=extra.get("index_mode", 0),
+                expect_seqused=expect)
+
+
+def test_padded_compact_qkv_views(rope):
+    """The compact launch on Q and K as views into fused QKV outputs of a padded batch:
+    bit for bit the seqused launch on the same views, V and padded rows untouched."""
+    w = workloads.get("qwen3_8b_padded")
+    Hq, Hkv, D = w.Hq, w.Hkv, w.D
+    print("[parity] compact on fused qkv views", flush=True)
+    qkv0 = workloads.make_tensor((w.T, (Hq + 2 * Hkv) * D), 9300, "bf16", device=DEV)
+    cu = torch.from_numpy(w.cu_seqlens).to(DEV)
+    su = torch.from_numpy(w.seqused).to(DEV)
+    cv = rope.valid_prefix(cu, su)
+    valid = int(_cu_valid(w.cu_seqlens, w.seqused)[-1])
+    a, b = qkv0.clone(), qkv0.clone()
+    for direction in (1, -1):
+        qa, ka, _ = _qkv_views(a, Hq, Hkv, D)
+        qb, kb, _ = _qkv_views(b, Hq, Hkv, D)
+        rope.qk_apply_padded_(qa, ka, w.theta, direction, cu, su, cv, valid)
+        rope.qk_apply_ex_(qb, kb, w.theta, direction, cu_seqlens=cu, seqused=su)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    pos, _ = oracle.positions(w.cu_seqlens, w.T, w.seqused)
+    pad = torch.from_numpy(pos < 0).to(DEV)
+    assert torch.equal(a[pad].view(torch.int16), qkv0[pad].view(torch.int16))
+    _, _, v = _qkv_views(a, Hq, Hkv, D)
+    _, _, v0 = _qkv_views(qkv0, Hq, Hkv, D)
+    assert torch.equal(v.view(torch.int16), v0.view(torch.int16))
+
+
+@pytest.mark.parametrize("B", [0, 1, 7, 255, 256, 257, 1000, 5000])
+def test_valid_prefix(rope, B):
+    """rope_valid_prefix against the running sum of min(seqused, length) clamped at 0,
+    with and without seqused, over several scan steps: bit-exact."""
+    print(f"[parity] valid_prefix B={B}", flush=True)
+    rng = np.random.default_rng(7300 + B)
+    lens = rng.integers(0, 3000, size=B)
+    lens[rng.random(B) < 0.1] = 0
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    su = rng.integers(-5, 3200, size=B).astype(np.int32)
+    for seqused in (su, None):
+        got = rope.valid_prefix(torch.from_numpy(cu).to(DEV),
+                                None if seqused is None else torch.from_numpy(seqused).to(DEV))
+        assert np.array_equal(got.cpu().numpy(), _cu_valid(cu, seqused))
+
+
+def test_valid_prefix_saturates(rope):
+    """Counts beyond INT32_MAX saturate; a decreasing cu_seqlens contributes 0."""
+    big = 2**31 - 1
+    cu = torch.tensor([-big, big, -big, big], dtype=torch.int32, device=DEV)
+    su = torch.full((3,), big, dtype=torch.int32, device=DEV)
+    got = rope.valid_prefix(cu, su).cpu().numpy()
+    assert got.tolist() == [0, big, big, big]
