@@ -648,18 +648,18 @@ int32_t chunk_bytes(int32_t D, int32_t esize, const void* q, const void* k, int6
 // Workgroups of the row-group kernel resident per CU. Unrestricted, its 64-lane
 // workgroups fill every wave slot of a CU (32); fewer in flight move data faster.
 // The cap is set by reserving LDS the kernel does not use: each workgroup asks
-// for lds_per_cu / cap bytes in all. Measured on MI355X (bf16, D = 128,
-// back-to-back launches on the same buffers, caps 16-32): 24 is within 0.5% of
-// the best cap on every batch below 2^19 workgroups (Qwen3-4B batch 51.8 us vs
-// 53.0 uncapped) and on launches of the 64 + 8 head shape of any length;
-// launches of 2^19 workgroups or more where K has at least a fifth of the row
-// groups (32 + 8 heads) do best at 20 (524288 tokens: 1652 us vs 1686 at 24 and
-// 1796 uncapped; 131072 and 262144 tokens: 0.5-1% better than 24).
+// for lds_per_cu / cap bytes in all. Measured on MI355X with the write-through
+// stores (bf16, D = 128, caps 16-32 and none, interleaved on the same buffers):
+// 20 is the best cap, or within 0.5% of it, for 32 + 8, 32 + 4, 16 + 8 and 40 + 8
+// heads from 2048 to 524288 tokens (8554 tokens 27.85 us vs 27.95 at 24 and 28.54
+// uncapped; 524288 tokens 1609 vs 1637 at 24 and 1750 uncapped); Q-heavy launches
+// (64 + 8 heads) of 2^18 workgroups or more do best at 28 (32768 tokens 179.8 vs
+// 182.2 us at 24; 65536 and 131072 tokens 2.5-3% better than 24).
 constexpr uint32_t kLdsPerCU = 160 * 1024;
 constexpr uint32_t kGroupStaticLds = 2 * kMaxHalf * sizeof(float);
 uint32_t group_dynamic_lds(unsigned group_blocks, uint32_t gq, uint32_t gk) {
-  const bool long_kv_heavy = group_blocks >= (1u << 19) && 5 * gk >= gq + gk;
-  const uint32_t cap = long_kv_heavy ? 20 : 24;
+  const bool long_q_heavy = group_blocks >= (1u << 18) && gq >= 8 * gk;
+  const uint32_t cap = long_q_heavy ? 28 : 20;
   return kLdsPerCU / cap - kGroupStaticLds;
 }
 
