@@ -64,8 +64,10 @@ TRAFFIC_FILE = traffic_path("qwen3_4b_packed")
 
 # The sources each kernel is compiled from: a traffic summary taken on other
 # sources does not describe the kernel being timed.
-ROPE_SOURCES = ["rope_qk.hip", "storage.h", "cr_sincos.h", "trig_constants.h", "fast_div.h"]
-GLU_SOURCES = ["glu.hip", "storage.h", "glu_constants.h"]
+# what a kernel's code depends on: its sources and the build script (its flags)
+ROPE_SOURCES = ["rope_qk.hip", "storage.h", "cr_sincos.h", "trig_constants.h", "fast_div.h",
+                "../build.py"]
+GLU_SOURCES = ["glu.hip", "storage.h", "glu_constants.h", "../build.py"]
 GLU_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "glu_swiglu_qwen3_4b_traffic.txt")
 # bf16, 16-byte chunks, SwiGLU, dense, 32-bit offsets: forward and backward instances
 GLU_KERNEL_KEYS = {"fwd": "glu_kernelIDF16bLi8ELi0ELb0ELb1Ej", "bwd": "glu_kernelIDF16bLi8ELi0ELb1ELb1Ej"}

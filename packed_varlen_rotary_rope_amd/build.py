@@ -20,7 +20,6 @@ HIPCC_FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     # every product and sum is rounded as written: the Kahan rotation and the
     # double-double sin/cos rely on it
     "-ffp-contract=off",
@@ -30,15 +29,33 @@ HIPCC_FLAGS = [
     "-I", os.path.join(ROOT, "include"),
 ]
 
+# Per-source flags. The RoPE kernels take the kernel arguments a wave needs before
+# its first loads as 12 leading dwords; the compiler preloads those into SGPRs at
+# wave launch (gfx950 kernel-argument preload; on firmware without it the compiled
+# prologue loads them instead), which shortens every launch's start.
+SRC_FLAGS = {
+    "rope_qk.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=12"],
+}
+
 
 def hipcc() -> str:
     return os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
 
 
 def build(extra_flags=(), out: str = LIB_PATH) -> str:
+    """Compile each source to an object with its own flags, then link the library."""
+    import tempfile
     tmp = out + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, *extra_flags, "-o", tmp, *SRCS]
-    subprocess.run(cmd, check=True)
+    with tempfile.TemporaryDirectory() as d:
+        objs = []
+        for src in SRCS:
+            obj = os.path.join(d, os.path.basename(src) + ".o")
+            cmd = [hipcc(), *HIPCC_FLAGS, *SRC_FLAGS.get(os.path.basename(src), []),
+                   *extra_flags, "-c", "-o", obj, src]
+            subprocess.run(cmd, check=True)
+            objs.append(obj)
+        subprocess.run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs],
+                       check=True)
     os.replace(tmp, out)
     return out
 

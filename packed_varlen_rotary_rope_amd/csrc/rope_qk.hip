@@ -161,10 +161,12 @@ __device__ inline int32_t resolve_position(const PosSource& ps, I t, int32_t* se
 // when v lies past the rotated tokens, or when the metadata puts the row outside
 // sequence s's rotated prefix or outside [0, T): nothing is touched then, so any
 // metadata stays memory-safe, and no row is rotated twice (p is one-to-one in v).
-__device__ inline int32_t compact_position(const PosSource& ps, int32_t v, int64_t T,
-                                           int64_t* row) {
+// cu_valid is passed on its own (it is a preloaded kernel argument; ps.cu_valid
+// holds the same pointer).
+__device__ inline int32_t compact_position(const PosSource& ps, const int32_t* __restrict__ cu_valid,
+                                           int32_t num_seqs, int32_t v, int64_t T, int64_t* row) {
   int32_t s;
-  const int32_t p = token_position(ps.cu_valid, ps.num_seqs, (const int32_t*)nullptr, v, &s);
+  const int32_t p = token_position(cu_valid, num_seqs, (const int32_t*)nullptr, v, &s);
   if (p < 0) return -1;
   const int64_t start = ps.cu[s];
   const int64_t r = start + p;
@@ -431,21 +433,42 @@ __device__ inline void store_chunk_through(T* p, const Chunk<T, VEC>& c) {
 // the token instead of once per token. Requires nc to divide 64.
 // TABLE as in rope_qk_kernel. COMPACT: the grid covers only the rotated tokens of
 // a padded layout (compact_position), so no workgroup is spent on padded rows.
+//
+// Everything a wave needs before its first loads leads the argument list as 12
+// plain dwords, which the library's build preloads into SGPRs at wave launch
+// (the compiler's kernel-argument preload), so the wave does not first wait for
+// a load of its arguments: q, k, cu_seqlens (cu_valid for COMPACT: the array the
+// position search runs over); q_stride, k_stride (elements between
+// tokens, < 2^32); groups_mul, the multiplier of the division of the workgroup
+// index by the row groups per token (fast_div.h); geo = gq | gk << 13 | nc_shift
+// << 26 | position-source flags << 29 (kFlag*); heads = Hq | Hkv << 13 |
+// (division shift - 26) << 26; num_seqs. The rest (frequencies, sign, scale,
+// tables, the other position sources) comes from ps and p, read after the row
+// loads are issued or only on the paths that need them. D follows from nc_shift:
+// a half row is 2^nc_shift chunks of VEC elements.
+constexpr uint32_t kFlagIds = 1, kFlagOffsets = 2, kFlagSeqused = 4;
 template <typename T, int VEC, bool LONG_INDEX, bool TABLE, bool COMPACT>
-__global__ __launch_bounds__(64) void rope_qk_group_kernel(T* __restrict__ q, T* __restrict__ k,
-                                                           const PosSource ps, const RopeParams p) {
+__global__ __launch_bounds__(64) void rope_qk_group_kernel(
+    T* __restrict__ q, T* __restrict__ k, const int32_t* __restrict__ cu, uint32_t q_stride,
+    uint32_t k_stride, uint32_t groups_mul, uint32_t geo, uint32_t heads, int32_t num_seqs,
+    const PosSource ps, const RopeParams p) {
   __shared__ float lds_cs[kMaxHalf];
   __shared__ float lds_sn[kMaxHalf];
   using C = Chunk<T, VEC>;
   const int lane = threadIdx.x;
+  const uint32_t gq = geo & 0x1fffu;
+  const uint32_t gk = (geo >> 13) & 0x1fffu;
+  const uint32_t ns = (geo >> 26) & 7u;
+  const uint32_t flags = geo >> 29;
+  const int Hq = (int)(heads & 0x1fffu);
+  const int Hkv = (int)((heads >> 13) & 0x1fffu);
   // Workgroup -> (token, row group) with host-made constants: a multiply and a
   // shift instead of integer divisions, so the wave reaches its loads sooner.
-  const uint32_t ns = p.nc_shift;
-  const uint32_t gq = p.gq;
-  const uint32_t t = fastdiv::div(blockIdx.x, p.groups);  // < 2^26; COMPACT: rotated-token index
-  const uint32_t g = blockIdx.x - t * (gq + p.gk);
-  const uint32_t D = (uint32_t)p.D;
-  const uint32_t half = D >> 1;
+  const fastdiv::FastDiv groups{groups_mul, fastdiv::kMaxDividendBits + (heads >> 26)};
+  const uint32_t t = fastdiv::div(blockIdx.x, groups);  // < 2^26; COMPACT: rotated-token index
+  const uint32_t g = blockIdx.x - t * (gq + gk);
+  const uint32_t half = (uint32_t)VEC << ns;
+  const uint32_t D = half << 1;
 
   // a4/a5 addresses: this lane's row of the group, and its chunk of the row
   // halves. Lanes past the last row of a partial group address row 0 of the
@@ -453,11 +476,11 @@ __global__ __launch_bounds__(64) void rope_qk_group_kernel(T* __restrict__ q, T*
   const int c = lane & ((1 << ns) - 1);
   const bool in_q = g < gq;
   const int r = (int)(((in_q ? g : g - gq) << (6 - ns)) + ((uint32_t)lane >> ns));
-  const bool live = r < (in_q ? p.Hq : p.Hkv);
+  const bool live = r < (in_q ? Hq : Hkv);
   T* row = nullptr;
   if constexpr (!COMPACT) {
-    row = in_q ? token_row0<T, LONG_INDEX>(q, (int64_t)t, p.q_stride)
-               : token_row0<T, LONG_INDEX>(k, (int64_t)t, p.k_stride);
+    row = in_q ? token_row0<T, LONG_INDEX>(q, (int64_t)t, (int64_t)q_stride)
+               : token_row0<T, LONG_INDEX>(k, (int64_t)t, (int64_t)k_stride);
     // r * D < 2^22: a 24-bit multiply. (A full 32-bit multiply-add becomes
     // v_mad_u64_u32 with an undefined high addend, which the register allocator
     // may place in a register a pending load writes, forcing a wait on it.)
@@ -479,14 +502,17 @@ __global__ __launch_bounds__(64) void rope_qk_group_kernel(T* __restrict__ q, T*
   int32_t pos;  // wave-uniform
   if constexpr (COMPACT) {
     int64_t tok = 0;
-    pos = compact_position(ps, (int32_t)t, p.T, &tok);
+    pos = compact_position(ps, cu, num_seqs, (int32_t)t, p.T, &tok);  // cu: cu_valid
     if (pos < 0) return;
-    row = in_q ? token_row0<T, LONG_INDEX>(q, tok, p.q_stride)
-               : token_row0<T, LONG_INDEX>(k, tok, p.k_stride);
+    row = in_q ? token_row0<T, LONG_INDEX>(q, tok, (int64_t)q_stride)
+               : token_row0<T, LONG_INDEX>(k, tok, (int64_t)k_stride);
     row += __umul24((uint32_t)(live ? r : 0), D) + (uint32_t)(c * VEC);
   } else {
     int32_t seq;
-    pos = resolve_position(ps, (int32_t)t, &seq);
+    // cu_seqlens alone (the packed default) from the preloaded arguments; the
+    // other position sources through ps
+    pos = flags == 0 ? token_position(cu, num_seqs, (const int32_t*)nullptr, (int32_t)t, &seq)
+                     : resolve_position(ps, (int32_t)t, &seq);
   }
   if (pos < 0 || (TABLE && pos >= p.tab_rows)) return;
   C lo = load_chunk<T, VEC>(row);
@@ -663,6 +689,25 @@ uint32_t group_dynamic_lds(unsigned group_blocks, uint32_t gq, uint32_t gk) {
   return kLdsPerCU / cap - kGroupStaticLds;
 }
 
+// The leading scalar arguments of rope_qk_group_kernel (see there).
+struct GroupScalars {
+  const int32_t* search;  // cu_seqlens, or cu_valid for a compact launch
+  uint32_t q_stride, k_stride, groups_mul, geo, heads;
+};
+GroupScalars group_scalars(const RopeParams& p, const PosSource& ps) {
+  const uint32_t flags = (ps.position_ids ? kFlagIds : 0u) | (ps.seq_offsets ? kFlagOffsets : 0u) |
+                         (ps.seqused ? kFlagSeqused : 0u);
+  GroupScalars g;
+  g.search = ps.cu_valid != nullptr ? ps.cu_valid : ps.cu;
+  g.q_stride = (uint32_t)p.q_stride;
+  g.k_stride = (uint32_t)p.k_stride;
+  g.groups_mul = p.groups.mul;
+  g.geo = p.gq | p.gk << 13 | p.nc_shift << 26 | flags << 29;
+  g.heads = (uint32_t)p.Hq | (uint32_t)p.Hkv << 13 |
+            (p.groups.shift - fastdiv::kMaxDividendBits) << 26;
+  return g;
+}
+
 template <typename T, int VEC, bool TABLE>
 int32_t launch_vec(void* q, void* k, const PosSource& ps, const RopeParams& p, bool long_index,
                    unsigned blocks, unsigned group_blocks, hipStream_t stream) {
@@ -670,20 +715,21 @@ int32_t launch_vec(void* q, void* k, const PosSource& ps, const RopeParams& p, b
   T* kt = static_cast<T*>(k);
   if (group_blocks > 0) {
     const uint32_t lds = group_dynamic_lds(group_blocks, p.gq, p.gk);
+    const GroupScalars s = group_scalars(p, ps);
+#define ROPE_GROUP_ARGS                                                                     \
+  dim3(group_blocks), dim3(64), lds, stream, qt, kt, s.search, s.q_stride, s.k_stride,    \
+      s.groups_mul, s.geo, s.heads, ps.num_seqs, ps, p
     if (!TABLE && ps.cu_valid != nullptr) {
       if (long_index)
-        hipLaunchKernelGGL((rope_qk_group_kernel<T, VEC, true, false, true>), dim3(group_blocks),
-                           dim3(64), lds, stream, qt, kt, ps, p);
+        hipLaunchKernelGGL((rope_qk_group_kernel<T, VEC, true, false, true>), ROPE_GROUP_ARGS);
       else
-        hipLaunchKernelGGL((rope_qk_group_kernel<T, VEC, false, false, true>), dim3(group_blocks),
-                           dim3(64), lds, stream, qt, kt, ps, p);
+        hipLaunchKernelGGL((rope_qk_group_kernel<T, VEC, false, false, true>), ROPE_GROUP_ARGS);
     } else if (long_index) {
-      hipLaunchKernelGGL((rope_qk_group_kernel<T, VEC, true, TABLE, false>), dim3(group_blocks),
-                         dim3(64), lds, stream, qt, kt, ps, p);
+      hipLaunchKernelGGL((rope_qk_group_kernel<T, VEC, true, TABLE, false>), ROPE_GROUP_ARGS);
     } else {
-      hipLaunchKernelGGL((rope_qk_group_kernel<T, VEC, false, TABLE, false>), dim3(group_blocks),
-                         dim3(64), lds, stream, qt, kt, ps, p);
+      hipLaunchKernelGGL((rope_qk_group_kernel<T, VEC, false, TABLE, false>), ROPE_GROUP_ARGS);
     }
+#undef ROPE_GROUP_ARGS
     return hipGetLastError() == hipSuccess ? ROPE_OK : ROPE_ELAUNCH;
   }
   if (long_index)
@@ -715,8 +761,9 @@ int32_t auto_tokens_per_wave(int64_t T) {
 
 // Grid of the row-group kernel (one 64-lane workgroup per token and row group), or
 // 0 when that kernel does not apply: the caller chose tokens per wave, nc does not
-// divide 64, the grid would exceed the dispatch size limit, or seqused marks a
-// padded layout and the launch is not compact. In that case many rows are
+// divide 64, a token stride is 2^32 elements or more, the grid would exceed the
+// dispatch size limit, or seqused marks a padded layout and the launch is not
+// compact. In that case many rows are
 // skipped; the row-group kernel spends one workgroup per row group of each
 // skipped token where the token kernel spends one wave per token, and it measures
 // slower there (Qwen3-8B batch padded to 8 x 2048 rows: 34.2-34.4 vs 33.1-33.4
@@ -726,6 +773,8 @@ int32_t auto_tokens_per_wave(int64_t T) {
 int64_t group_grid(const RopeParams& p, bool geometry_chosen, bool padded, int64_t compact_rows) {
   const bool compact = compact_rows >= 0;
   if (geometry_chosen || (padded && !compact) || 64 % p.nc != 0) return 0;
+  // token strides travel as 32-bit kernel arguments
+  if (p.q_stride > (int64_t)UINT32_MAX || p.k_stride > (int64_t)UINT32_MAX) return 0;
   const int step_r = 64 / p.nc;
   const int64_t groups = (p.Hq + step_r - 1) / step_r + (p.Hkv + step_r - 1) / step_r;
   const int64_t blocks = (compact ? compact_rows : p.T) * groups;
