@@ -612,6 +612,34 @@ def test_stride_forces_64bit_offsets(rope):
     torch.cuda.empty_cache()
 
 
+def test_stride_beyond_32_bits(rope):
+    """A Q token stride of 2^32 + 256 elements (two tokens 8 GiB apart in bf16): the
+    row-group kernel takes 32-bit strides, so the library runs the token kernel; the
+    result matches the oracle (positions shifted by an offset so neither is the
+    identity) and the memory between the rows stays untouched."""
+    D, stride = 128, (1 << 32) + 256
+    print("[parity] token stride beyond 32 bits", flush=True)
+    buf = torch.zeros(stride + D, dtype=torch.bfloat16, device=DEV)
+    vals = workloads.make_tensor((2, 2, D), 9400, "bf16", device=DEV)
+    q = buf.as_strided((2, 1, D), (stride, D, 1))
+    q.copy_(vals[:, :1])
+    k = vals[:, 1:].clone()
+    cu_h = np.array([0, 2], dtype=np.int32)
+    off_h = np.array([1000], dtype=np.int32)
+    rope.qk_apply_ex_(q, k, 1e6, 1, cu_seqlens=torch.from_numpy(cu_h).to(DEV),
+                      seq_offsets=torch.from_numpy(off_h).to(DEV))
+    torch.cuda.synchronize()
+    touched = np.ones(2, dtype=bool)
+    for what, x0, got in (("q", vals[:, :1], q), ("k", vals[:, 1:], k)):
+        x = bits(x0)
+        ref = oracle.rope(x, cu_h, 1e6, 1, "bf16", seq_offsets=off_h)
+        assert_parity("bf16", bits(got), ref, x, touched, f"stride32:{what}")
+    assert torch.count_nonzero(buf[D:1 << 20]).item() == 0
+    assert torch.count_nonzero(buf[stride - (1 << 20):stride]).item() == 0
+    del buf
+    torch.cuda.empty_cache()
+
+
 # ---------------------------------------------------------------- cos/sin tables
 
 @pytest.mark.parametrize("name", ["qwen3_4b_packed", "qwen3_8b_padded"])
