@@ -80,11 +80,31 @@ def glu_instance(code: int, bwd: int) -> str:
     return f"glu_kernelIDF16bLi8ELi{code}ELb{bwd}ELb1E{index}"
 
 
+def _code_text(name: str, raw: bytes) -> bytes:
+    """The code of a source file without its comments, blank lines and (Python)
+    docstrings, so that editing documentation does not invalidate a profile taken on
+    the same code, while any change to code or build flags does."""
+    text = raw.decode()
+    if name.endswith(".py"):
+        import ast
+        tree = ast.parse(text)
+        for node in ast.walk(tree):
+            body = getattr(node, "body", None)
+            if (isinstance(node, (ast.Module, ast.FunctionDef, ast.ClassDef)) and body and
+                    isinstance(body[0], ast.Expr) and isinstance(body[0].value, ast.Constant) and
+                    isinstance(body[0].value.value, str)):
+                node.body = body[1:] or [ast.Pass()]
+        return ast.dump(tree).encode()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    lines = (re.sub(r"//.*", "", ln).rstrip() for ln in text.splitlines())
+    return "\n".join(ln for ln in lines if ln.strip()).encode()
+
+
 def kernel_source_hash(sources=ROPE_SOURCES) -> str:
     h = hashlib.sha256()
     for name in sources:
         with open(os.path.join(KERNEL_SRC, name), "rb") as fh:
-            h.update(name.encode() + b"\0" + fh.read())
+            h.update(name.encode() + b"\0" + _code_text(name, fh.read()))
     return h.hexdigest()[:16]
 
 

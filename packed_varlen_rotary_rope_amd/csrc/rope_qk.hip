@@ -438,11 +438,11 @@ __device__ inline void store_chunk_through(T* p, const Chunk<T, VEC>& c) {
 // plain dwords, which the library's build preloads into SGPRs at wave launch
 // (the compiler's kernel-argument preload), so the wave does not first wait for
 // a load of its arguments: q, k, cu_seqlens (cu_valid for COMPACT: the array the
-// position search runs over); q_stride, k_stride (elements between
-// tokens, < 2^32); groups_mul, the multiplier of the division of the workgroup
-// index by the row groups per token (fast_div.h); geo = gq | gk << 13 | nc_shift
-// << 26 | position-source flags << 29 (kFlag*); heads = Hq | Hkv << 13 |
-// (division shift - 26) << 26; num_seqs. The rest (frequencies, sign, scale,
+// position search runs over); q_stride, k_stride (elements between tokens,
+// < 2^32); groups_mul, the multiplier of the division of the workgroup index by
+// the row groups per token (fast_div.h); geo = gq | gk << 13 | nc_shift << 26 |
+// position-source flags << 29 (kFlag*); heads = Hq | Hkv << 13 | (division
+// shift - 26) << 26; num_seqs. The rest (frequencies, sign, scale,
 // tables, the other position sources) comes from ps and p, read after the row
 // loads are issued or only on the paths that need them. D follows from nc_shift:
 // a half row is 2^nc_shift chunks of VEC elements.
@@ -763,11 +763,11 @@ int32_t auto_tokens_per_wave(int64_t T) {
 // 0 when that kernel does not apply: the caller chose tokens per wave, nc does not
 // divide 64, a token stride is 2^32 elements or more, the grid would exceed the
 // dispatch size limit, or seqused marks a padded layout and the launch is not
-// compact. In that case many rows are
-// skipped; the row-group kernel spends one workgroup per row group of each
-// skipped token where the token kernel spends one wave per token, and it measures
-// slower there (Qwen3-8B batch padded to 8 x 2048 rows: 34.2-34.4 vs 33.1-33.4
-// us), so such launches keep the token kernel. A compact launch (compact_rows >=
+// compact. In that last case many rows are skipped; the row-group kernel spends
+// one workgroup per row group of each skipped token where the token kernel spends
+// one wave per token, and it measures slower there (Qwen3-8B batch padded to
+// 8 x 2048 rows: 34.2-34.4 vs 33.1-33.4 us), so such launches keep the token
+// kernel. A compact launch (compact_rows >=
 // 0 rotated tokens, cu_valid given) covers only the rotated tokens and takes the
 // row-group kernel (28.3 against 32.0 us on that batch).
 int64_t group_grid(const RopeParams& p, bool geometry_chosen, bool padded, int64_t compact_rows) {
