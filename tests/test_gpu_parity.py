@@ -946,6 +946,47 @@ def test_padded_compact_edges(rope, case):
                 expect_seqused=expect)
 
 
+def test_padded_compact_long_context(rope):
+    """A padded layout that needs 64-bit offsets by itself: 4 sequences padded to
+    131072 rows each (524288 rows, 32 + 8 heads, bf16), 54-97% of each row block
+    used, through the compact launch forward and backward: sampled rows (sequence
+    ends, both sides of every used / padded boundary, random rows) against the
+    oracle, padded rows untouched."""
+    S, B, Hq, Hkv, D = 131072, 4, 32, 8, 128
+    T = S * B
+    assert T * (Hq + Hkv) * D >= 1 << 31
+    print("[parity] compact padded, 64-bit offsets", flush=True)
+    cu_h = (np.arange(B + 1, dtype=np.int64) * S).astype(np.int32)
+    su_h = np.array([127000, 71003, 131072, 100001], dtype=np.int32)
+    cu, su = torch.from_numpy(cu_h).to(DEV), torch.from_numpy(su_h).to(DEV)
+    cv = rope.valid_prefix(cu, su)
+    valid = int(su_h.sum())
+    dev = {what: workloads.make_tensor((T, Hq if what in ("q", "dq") else Hkv, D), 9500 + i,
+                                       "bf16", device=DEV, chunk_rows=65536)
+           for i, what in enumerate(("q", "k", "dq", "dk"))}
+    rng = np.random.default_rng(9550)
+    marks = [np.arange(c - 3, c + 3) for c in cu_h[1:-1]]
+    marks += [np.arange(a + u - 3, a + u + 3) for a, u in zip(cu_h[:-1], su_h)]
+    tokens = np.unique(np.concatenate([np.arange(0, 32), np.arange(T - 32, T), *marks,
+                                       rng.integers(0, T, 4096)]))
+    tokens = tokens[(tokens >= 0) & (tokens < T)]
+    tok_dev = torch.from_numpy(tokens).to(DEV)
+    before = {what: bits(t.index_select(0, tok_dev)) for what, t in dev.items()}
+    rope.qk_apply_padded_(dev["q"], dev["k"], 1e6, 1, cu, su, cv, valid)
+    rope.qk_apply_padded_(dev["dq"], dev["dk"], 1e6, -1, cu, su, cv, valid)
+    torch.cuda.synchronize()
+    pos, _ = oracle.positions(cu_h, T, su_h)
+    touched = pos[tokens] >= 0
+    assert touched.any() and (~touched).any()
+    for what, direction in (("q", 1), ("k", 1), ("dq", -1), ("dk", -1)):
+        got = bits(dev[what].index_select(0, tok_dev))
+        ref = oracle.rope_rows(before[what], tokens, cu_h, 1e6, direction, "bf16", su_h,
+                               NTHREADS)
+        assert_parity("bf16", got, ref, before[what], touched, f"compact-long:{what}")
+    del dev
+    torch.cuda.empty_cache()
+
+
 def test_padded_compact_qkv_views(rope):
     """The compact launch on Q and K as views into fused QKV outputs of a padded batch:
     bit for bit the seqused launch on the same views, V and padded rows untouched."""
