@@ -696,6 +696,11 @@ struct GroupScalars {
   const int32_t* search;  // cu_seqlens, or cu_valid for a compact launch
   uint32_t q_stride, k_stride, groups_mul, geo, heads;
 };
+// Field widths of the packed words: head and row-group counts below 2^13 (at most
+// kMaxHeads), nc_shift below 8 (nc <= 64), the division shift minus 26 below 16
+// (l = ceil(log2(gq + gk)) <= 13), three flag bits.
+static_assert(kMaxHeads < (1 << 13), "head counts must fit 13 bits");
+static_assert(kMaxHalf <= 256, "nc_shift must fit 3 bits");
 GroupScalars group_scalars(const RopeParams& p, const PosSource& ps) {
   const uint32_t flags = (ps.position_ids ? kFlagIds : 0u) | (ps.seq_offsets ? kFlagOffsets : 0u) |
                          (ps.seqused ? kFlagSeqused : 0u);
