@@ -66,8 +66,9 @@ TRAFFIC_FILE = traffic_path("qwen3_4b_packed")
 # sources does not describe the kernel being timed.
 # what a kernel's code depends on: its sources and the build script (its flags)
 ROPE_SOURCES = ["rope_qk.hip", "storage.h", "cr_sincos.h", "trig_constants.h", "fast_div.h",
-                "../build.py"]
-GLU_SOURCES = ["glu.hip", "storage.h", "glu_constants.h", "../build.py"]
+                "../../include/rope_qk.h", "../build.py"]
+GLU_SOURCES = ["glu.hip", "storage.h", "glu_constants.h", "../../include/glu.h",
+               "../../include/rope_qk.h", "../build.py"]
 GLU_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "glu_swiglu_qwen3_4b_traffic.txt")
 # bf16, 16-byte chunks, SwiGLU, dense, 32-bit offsets: forward and backward instances
 GLU_KERNEL_KEYS = {"fwd": "glu_kernelIDF16bLi8ELi0ELb0ELb1Ej", "bwd": "glu_kernelIDF16bLi8ELi0ELb1ELb1Ej"}

@@ -197,8 +197,9 @@ int32_t rope_qk_apply_table(void* q, void* k, int64_t T, int32_t Hq, int32_t Hkv
  * When they do not match, memory stays safe and no token is rotated twice or
  * with a wrong position, but tokens outside the ranges they describe may be
  * left untouched. Where the row-group geometry does not apply (nc does not
- * divide 64, or a grid beyond the dispatch limit) the call runs the seqused
- * launch of rope_qk_apply_ex instead, with the same results.
+ * divide 64, a token stride of 2^32 elements or more, or a grid beyond the
+ * dispatch limit) the call runs the seqused launch of rope_qk_apply_ex instead,
+ * which rotates every token seqused describes.
  * Errors: ROPE_EINVAL for valid_tokens < 0 or > T, or a NULL cu_valid with
  * valid_tokens > 0 (valid_tokens == 0 enqueues nothing); otherwise as in
  * rope_qk_apply_ex. Other arguments as in rope_qk_apply_ex. */

@@ -204,16 +204,20 @@ def qk_apply_padded_(q, k, theta: float, direction: int, cu_seqlens, seqused, cu
     return q, k
 
 
-def valid_prefix(cu_seqlens, seqused=None):
+def valid_prefix(cu_seqlens, seqused=None, out=None):
     """int32[B+1] on cu_seqlens' GPU: the running count of the tokens each sequence
-    rotates (min(seqused[s], its length)), the cu_valid of qk_apply_padded_."""
+    rotates (min(seqused[s], its length)), the cu_valid of qk_apply_padded_; written
+    to `out` (int32[B+1]) when given."""
     dev = cu_seqlens.device
     cu = _index_tensor(cu_seqlens, "cu_seqlens", dev)
     su = _index_tensor(seqused, "seqused", dev)
     num_seqs = cu.numel() - 1
     if num_seqs < 0 or (su is not None and su.numel() != num_seqs):
         raise ValueError("cu_seqlens needs >= 1 entry and seqused one entry per sequence")
-    out = torch.empty(num_seqs + 1, dtype=torch.int32, device=dev)
+    if out is None:
+        out = torch.empty(num_seqs + 1, dtype=torch.int32, device=dev)
+    elif _index_tensor(out, "out", dev).numel() != num_seqs + 1:
+        raise ValueError("out must have num_seqs + 1 entries")
     _check(_lib.rope_valid_prefix(_ptr(cu), num_seqs, _ptr(su), _ptr(out), _stream(dev)),
            "rope_valid_prefix")
     return out

@@ -228,19 +228,19 @@ def test_source_hash_ignores_documentation(tmp_path, monkeypatch):
     docstrings: a comment edit keeps it, a code or flag edit changes it."""
     import shutil
     for name in bench.ROPE_SOURCES:
-        dst = tmp_path / "csrc" / name
+        dst = tmp_path / "pkg" / "csrc" / name
         dst.parent.mkdir(parents=True, exist_ok=True)
         shutil.copy(os.path.join(bench.KERNEL_SRC, name), dst)
-    monkeypatch.setattr(bench, "KERNEL_SRC", str(tmp_path / "csrc"))
+    monkeypatch.setattr(bench, "KERNEL_SRC", str(tmp_path / "pkg" / "csrc"))
     base = bench.kernel_source_hash()
-    hip = tmp_path / "csrc" / "rope_qk.hip"
+    hip = tmp_path / "pkg" / "csrc" / "rope_qk.hip"
     text = hip.read_text()
     hip.write_text(text.replace("// ", "//  ", 5) + "\n/* a note */\n// another\n")
     assert bench.kernel_source_hash() == base
     hip.write_text(text.replace("constexpr int kBlock = 256;", "constexpr int kBlock = 128;"))
     assert bench.kernel_source_hash() != base
     hip.write_text(text)
-    build = tmp_path / "build.py"
+    build = tmp_path / "pkg" / "build.py"
     code = build.read_text()
     build.write_text(code.replace('"""', '"""Edited docstring. ', 1) + "\n# a comment\n")
     assert bench.kernel_source_hash() == base

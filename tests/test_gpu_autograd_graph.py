@@ -257,13 +257,19 @@ def test_glu_autograd(lib, kind):
 
 
 def test_graph_capture_replay(lib):
-    """RoPE forward + backward and SwiGLU forward + backward captured in one HIP
-    graph on static buffers; four replays, each after fresh inputs are copied in
-    and with eager launches and synchronizations between replays, each equal bit
-    for bit to eager launches on the same inputs."""
+    """RoPE forward + backward, a compact padded forward (with its cu_valid made by
+    the prefix kernel inside the graph) and SwiGLU forward + backward captured in
+    one HIP graph on static buffers; four replays, each after fresh inputs are
+    copied in and with eager launches and synchronizations between replays, each
+    equal bit for bit to eager launches on the same inputs."""
     rope, F = lib
     w = workloads.get("qwen3_4b_packed")
     cu = torch.from_numpy(w.cu_seqlens).to(DEV)
+    wp = workloads.get("qwen3_8b_padded")
+    cu_p, su_p = torch.from_numpy(wp.cu_seqlens).to(DEV), torch.from_numpy(wp.seqused).to(DEV)
+    cv = torch.full((cu_p.numel(),), -1, dtype=torch.int32, device=DEV)
+    pq = torch.empty(wp.shape("q"), dtype=torch.bfloat16, device=DEV)
+    pk = torch.empty(wp.shape("k"), dtype=torch.bfloat16, device=DEV)
     rows, cols = 2048, 4096
     static = {n: torch.empty(w.shape(n), dtype=torch.bfloat16, device=DEV)
               for n in ("q", "k", "dq", "dk")}
@@ -276,6 +282,8 @@ def test_graph_capture_replay(lib):
         rope.qk_bwd_(static["dq"], static["dk"], cu, w.theta)
         rope.glu_fwd("swiglu", ge, gg, out=gh)
         rope.glu_bwd("swiglu", gdh, ge, gg, de=gde, dg=gdg)
+        rope.valid_prefix(cu_p, su_p, out=cv)
+        rope.qk_apply_padded_(pq, pk, wp.theta, 1, cu_p, su_p, cv, wp.valid_tokens)
 
     # warm up on a side stream, as torch requires before capture
     s = torch.cuda.Stream()
@@ -298,6 +306,11 @@ def test_graph_capture_replay(lib):
             static[n].copy_(inputs[n])
         for dst, src in zip((ge, gg, gdh), ins):
             dst.copy_(src)
+        pin = [workloads.make_tensor(wp.shape(n), 700 + 10 * rep + i, "bf16", device=DEV)
+               for i, n in enumerate(("q", "k"))]
+        pq.copy_(pin[0])
+        pk.copy_(pin[1])
+        cv.fill_(-1)
         torch.cuda.synchronize()
         graph.replay()
         # eager reference on separate copies, with its own synchronizations
@@ -306,7 +319,10 @@ def test_graph_capture_replay(lib):
         rope.qk_bwd_(eager["dq"], eager["dk"], cu, w.theta)
         h = rope.glu_fwd("swiglu", ins[0], ins[1])
         de, dg = rope.glu_bwd("swiglu", ins[2], ins[0], ins[1])
+        rope.qk_apply_ex_(pin[0], pin[1], wp.theta, 1, cu_seqlens=cu_p, seqused=su_p)
         torch.cuda.synchronize()
+        assert np.array_equal(bits16(pq), bits16(pin[0])) and np.array_equal(bits16(pk), bits16(pin[1]))
+        assert cv.cpu().tolist() == rope.valid_prefix(cu_p, su_p).cpu().tolist()
         for n in static:
             assert np.array_equal(bits16(static[n]), bits16(eager[n])), (rep, n)
         for a, b in ((gh, h), (gde, de), (gdg, dg)):
