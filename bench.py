@@ -126,9 +126,45 @@ def rope_kernel_name(w: workloads.Workload, tokens_per_wave: int, padded: str = 
     return "rope_qk_kernel"
 
 
-def algorithmic_bytes_per_launch(w: workloads.Workload) -> int:
+# The library's kPieceBlocks: a long pass of the row-group kernel on a Q-heavy shape
+# is issued as consecutive launches of about this many workgroups.
+PIECE_BLOCKS = 327680
+
+
+def group_pieces(rows: int, w: workloads.Workload) -> list:
+    """Tokens of each launch the row-group kernel is issued as over `rows` tokens of
+    w's head shape: one launch, except that a pass of 2 x PIECE_BLOCKS workgroups or
+    more, when Q holds at least 4x K's row groups, is issued as launches of about
+    PIECE_BLOCKS workgroups over consecutive token ranges that start at multiples of
+    8 tokens (the library's group_piece_tokens)."""
+    nc = max(1, (w.D // 2) // (16 // w.elem_bytes))
+    rows_per_group = 64 // nc
+    gq, gk = -(-w.Hq // rows_per_group), -(-w.Hkv // rows_per_group)
+    blocks = rows * (gq + gk)
+    if gq < 4 * gk or blocks < 2 * PIECE_BLOCKS:
+        return [rows]
+    n = -(-blocks // PIECE_BLOCKS)
+    piece = (-(-rows // n) + 7) // 8 * 8
+    return [min(piece, rows - t0) for t0 in range(0, rows, piece)]
+
+
+def launch_pieces(w: workloads.Workload, padded: str = "compact", tokens_per_wave: int = 0) -> list:
+    """Tokens (rotated tokens, for a compact launch) of each launch of one default
+    pass, in order."""
+    if rope_kernel_name(w, tokens_per_wave, padded) != "rope_qk_group_kernel":
+        return [w.T]
+    return group_pieces(w.valid_tokens if compact_launch(w, padded) else w.T, w)
+
+
+def algorithmic_bytes_per_pass(w: workloads.Workload) -> int:
     """One read and one write of every rotated element of Q and K (or dQ and dK)."""
     return 2 * w.valid_tokens * (w.Hq + w.Hkv) * w.D * w.elem_bytes
+
+
+def algorithmic_bytes_per_launch(w: workloads.Workload, padded: str = "compact") -> float:
+    """The pass's bytes over its launches (an average where the last launch of a
+    multi-launch pass is shorter)."""
+    return algorithmic_bytes_per_pass(w) / len(launch_pieces(w, padded))
 
 
 def read_traffic(path: str = TRAFFIC_FILE, sources=ROPE_SOURCES, field="hbm_bytes_per_launch"):
@@ -307,7 +343,9 @@ def write_traffic_summary(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, 
     header = [
         f"# HBM traffic of the RoPE kernel instance {key}",
         f"# on the {w.name} workload (T={w.T}, {w.valid_tokens} valid tokens, {seq}; Hq={w.Hq},",
-        f"# Hkv={w.Hkv}, D={w.D}, {w.dtype}), one launch = forward or backward over Q and K.",
+        f"# Hkv={w.Hkv}, D={w.D}, {w.dtype}), one launch = forward or backward over Q and K"
+        + ("." if len(launch_pieces(w)) == 1 else
+           f" of one of the {len(launch_pieces(w))} token ranges a pass is issued as."),
         "# Two rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE) over the same bench",
         "# command, each counter scaled by its reading for a plain 1 GiB device copy.",
         f"# commands: {command}",
@@ -526,17 +564,17 @@ def trace_summary_path(workload: str) -> str:
     return os.path.join(ROOT, "profiles", f"rope_qk_{workload}_kernel_trace.txt")
 
 
-def expected_grid_threads(w: workloads.Workload, padded: str = "compact") -> int:
-    """Work-items of the default launch for this workload: one 64-lane workgroup per
-    (token, row group) for the row-group kernel (per rotated token only, for a compact
-    padded launch), one 64-lane wave per token for the token kernel."""
+def expected_grid_threads(w: workloads.Workload, padded: str = "compact") -> list:
+    """Work-items of each launch of the default pass for this workload: one 64-lane
+    workgroup per (token, row group) for the row-group kernel (per rotated token only,
+    for a compact padded launch), one 64-lane wave per token for the token kernel."""
     vec = 16 // w.elem_bytes
     nc = max(1, (w.D // 2) // vec)
     if rope_kernel_name(w, 0, padded) == "rope_qk_group_kernel":
         rows = 64 // nc
-        tokens = w.valid_tokens if compact_launch(w, padded) else w.T
-        return tokens * (-(-w.Hq // rows) + -(-w.Hkv // rows)) * 64
-    return w.T * 64
+        groups = -(-w.Hq // rows) + -(-w.Hkv // rows)
+        return [t * groups * 64 for t in launch_pieces(w, padded)]
+    return [w.T * 64]
 
 
 def write_trace_summary(trace_csv: str, workload: str, command: str) -> None:
@@ -549,18 +587,20 @@ def write_trace_summary(trace_csv: str, workload: str, command: str) -> None:
     w = workloads.get(workload)
     keys = rope_instance_names(w, needs_long_index(w))
     key = keys[0]
-    grid = expected_grid_threads(w)
-    durs, names, shape = [], set(), None
+    grids = expected_grid_threads(w)
+    pieces = len(grids)
+    durs, names, shapes = [], set(), {}
     with open(trace_csv) as fh:
         for row in csv.DictReader(fh):
-            if not any(k in row["Kernel_Name"] for k in keys) or int(row["Grid_Size_X"]) != grid:
+            if not any(k in row["Kernel_Name"] for k in keys) or \
+                    int(row["Grid_Size_X"]) not in grids:
                 continue
             durs.append((int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3)
             names.add(row["Kernel_Name"])
-            shape = (row["Grid_Size_X"], row["Workgroup_Size_X"], row["VGPR_Count"],
-                     row["LDS_Block_Size"])
+            shapes[row["Grid_Size_X"]] = (row["Grid_Size_X"], row["Workgroup_Size_X"],
+                                          row["VGPR_Count"], row["LDS_Block_Size"])
     if not durs:
-        raise SystemExit(f"no dispatch of {key} with {grid} work-items in {trace_csv}")
+        raise SystemExit(f"no dispatch of {key} with {grids} work-items in {trace_csv}")
     d = np.array(durs)
     bpl = algorithmic_bytes_per_launch(w)
 
@@ -573,26 +613,33 @@ def write_trace_summary(trace_csv: str, workload: str, command: str) -> None:
         f"# rocprofv3 kernel trace: RoPE kernel on the {w.name} workload",
         f"# (T={w.T} rows, {w.valid_tokens} valid tokens in {len(w.cu_seqlens) - 1} sequences, "
         f"{seq}; Hq={w.Hq}, Hkv={w.Hkv}, D={w.D}, {w.dtype}, theta={w.theta:g})",
-        "# every timed step = forward(Q, K) + backward(dQ, dK), one launch each;",
+        "# every timed step = forward(Q, K) + backward(dQ, dK), one launch each"
+        + ("" if pieces == 1 else f" (here {pieces} launches each, over consecutive token ranges)")
+        + ";",
         "# buffer sets rotate so that no launch is served from the Infinity Cache",
         f"# command (R = repository root, on one MI355X): {command}",
         "",
     ]
-    lines = [
-        "kernel: " + ", ".join(sorted(names)),
-        f"grid_threads, workgroup, vgprs, static_lds_bytes: {', '.join(shape)}",
-    ]
+    lines = ["kernel: " + ", ".join(sorted(names))]
+    lines += [f"grid_threads, workgroup, vgprs, static_lds_bytes: {', '.join(sh)}"
+              for sh in shapes.values()]
     if any("group_kernel" in n for n in names):
         lines += ["(rocprofv3's LDS column is the kernel's static LDS only: the dynamic LDS the",
                   " row-group launch reserves to cap residency per CU is allocated but not shown)"]
+    if pieces > 1:
+        lines.append(f"launches_per_pass: {pieces} (tokens per launch: "
+                     f"{', '.join(str(t) for t in sorted(set(launch_pieces(w))))})")
     lines += [
         f"dispatches: {len(d)} (warmup included)",
-        f"algorithmic_bytes_per_launch: {bpl} (one read + one write of every rotated element)",
+        f"algorithmic_bytes_per_launch: {bpl:.0f} (one read + one write of every rotated element"
+        + ("" if pieces == 1 else f"; the pass's {algorithmic_bytes_per_pass(w)} over {pieces} launches")
+        + ")",
         f"average: {rate(float(d.mean()))}",
         f"median:  {rate(float(np.median(d)))}",
         f"minimum: {rate(float(d.min()))}",
         f"maximum: {float(d.max()):.2f} us",
-        f"valid_tokens_per_s_at_average: {w.valid_tokens / (float(d.mean()) * 1e-6):.4g} per launch",
+        f"valid_tokens_per_s_at_average: {w.valid_tokens / (pieces * float(d.mean()) * 1e-6):.4g} "
+        "per pass (forward or backward)",
     ]
     _write_summary(trace_summary_path(workload), header, lines)
 
@@ -751,7 +798,7 @@ def cpu_baseline(w, budget_s: float, nthreads: int):
 
     reps, total = _timed_reps(one(nthreads), budget_s, 10000)
     reps1, total1 = _timed_reps(one(1), budget_s / 4, 10000)
-    step_bytes = 2 * algorithmic_bytes_per_launch(w)  # the GPU's byte count for fwd + bwd
+    step_bytes = 2 * algorithmic_bytes_per_pass(w)  # the GPU's byte count for fwd + bwd
     return {
         "value": w.valid_tokens * reps / total,
         "unit": "tokens/s",
@@ -953,17 +1000,19 @@ def time_workload(rope, w: workloads.Workload, dev, n_steps: int, warmup: int,
         n = max(n_steps, math.ceil(min_timed_s * 1e6 / step_us))
         return region_us(stream, step, n) / 2, n
 
-    launch_us, n_steps = timed(step_compact if compact else step_plain)
-    bpl = algorithmic_bytes_per_launch(w)
-    gbps = bpl / (launch_us * 1e-6) / 1e9
+    pass_us, n_steps = timed(step_compact if compact else step_plain)
+    pieces = len(launch_pieces(w, padded))
+    bpp = algorithmic_bytes_per_pass(w)
+    gbps = bpp / (pass_us * 1e-6) / 1e9
     out = {
         "T": w.T, "valid_tokens": w.valid_tokens, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D,
         "dtype": w.dtype, "kernel": rope_kernel_name(w, 0, padded),
         "index": "64-bit" if needs_long_index(w) else "32-bit",
-        "bytes_per_launch": bpl, "avg_launch_us": launch_us, "GBps": gbps,
+        "launches_per_pass": pieces, "bytes_per_launch": bpp / pieces,
+        "avg_launch_us": pass_us / pieces, "avg_pass_us": pass_us, "GBps": gbps,
         "frac": gbps / HBM_PEAK_GBPS,
-        "fwd_bwd_tokens_per_s": w.valid_tokens / (2 * launch_us * 1e-6),
-        "launches_timed": 2 * n_steps,
+        "fwd_bwd_tokens_per_s": w.valid_tokens / (2 * pass_us * 1e-6),
+        "passes_timed": 2 * n_steps,
     }
     if w.seqused is not None:
         out["padded_launch"] = padded
@@ -971,12 +1020,12 @@ def time_workload(rope, w: workloads.Workload, dev, n_steps: int, warmup: int,
             plain_us, _ = timed(step_plain)
             out["seqused_launch_us"] = plain_us
             out["seqused_kernel"] = rope_kernel_name(w, 0, "seqused")
-            out["seqused_frac"] = bpl / (plain_us * 1e-6) / 1e9 / HBM_PEAK_GBPS
+            out["seqused_frac"] = bpp / (plain_us * 1e-6) / 1e9 / HBM_PEAK_GBPS
     if w.seqused is None:
         ref_us = inplace_reference_us(sets, nsets, stream, 2 * n_steps)
         out["torch_inplace_us"] = ref_us
-        out["torch_inplace_GBps"] = bpl / (ref_us * 1e-6) / 1e9
-        out["frac_of_ceiling"] = ref_us / launch_us
+        out["torch_inplace_GBps"] = bpp / (ref_us * 1e-6) / 1e9
+        out["frac_of_ceiling"] = ref_us / pass_us
     del sets
     torch.cuda.empty_cache()
     return out
@@ -1045,13 +1094,14 @@ def size_sweep(rope, dev, n_steps: int) -> dict:
     for T in SWEEP_TOKENS:
         print(f"[sweep] T={T}", file=sys.stderr, flush=True)
         r = time_workload(rope, sweep_workload(T), dev, n_steps, 20)
-        rows.append({"T": T, "avg_launch_us": r["avg_launch_us"],
+        rows.append({"T": T, "avg_pass_us": r["avg_pass_us"],
+                     "launches_per_pass": r["launches_per_pass"],
                      "torch_inplace_us": r["torch_inplace_us"], "GBps": r["GBps"],
                      "index": r["index"]})
     per_token = 2 * (SWEEP_HEADS[0] + SWEEP_HEADS[1]) * SWEEP_HEADS[2] * 2
     out = {"sweep": "RoPE launch time vs tokens (one sequence, 32+8 heads, D=128, bf16)",
            "bytes_per_token": per_token, "rows": rows}
-    for key in ("avg_launch_us", "torch_inplace_us"):
+    for key in ("avg_pass_us", "torch_inplace_us"):
         t0, b = linear_fit([r["T"] for r in rows], [r[key] for r in rows])
         out[f"fit_{key}"] = {"t0_us": t0, "us_per_token": b,
                              "asymptotic_GBps": per_token / (b * 1e-6) / 1e9}
@@ -1061,35 +1111,44 @@ def size_sweep(rope, dev, n_steps: int) -> dict:
 def write_sweep_summary(run_dir: str, command: str) -> None:
     """profiles/rope_qk_size_sweep.txt from a rocprofv3 --kernel-trace of bench.py
     --sweep (run_dir/**/*kernel_trace.csv) and that run's JSON line
-    (run_dir/sweep.json): per size, the RoPE kernel's average dispatch duration
-    (trace) and region timing, torch's in-place reference (region timing), and
-    t = t0 + b T fitted to each."""
+    (run_dir/sweep.json): per size, the RoPE pass's average duration from the trace
+    (the sum of its launches' durations where a pass is several launches) and from
+    region timing, torch's in-place reference (region timing), and t = t0 + b T
+    fitted to each. The sizes run one after another, each one contiguous run of RoPE
+    dispatches between torch's own kernels, which is how the trace is split."""
     import glob
     with open(os.path.join(run_dir, "sweep.json")) as fh:
         js = json.loads([ln for ln in fh if ln.startswith("{")][-1])
-    Hq, Hkv, D = SWEEP_HEADS
-    groups = -(-Hq // 8) + -(-Hkv // 8)
-    durs = {}
+    events = []
     for path in glob.glob(os.path.join(run_dir, "**", "*kernel_trace.csv"), recursive=True):
         with open(path) as fh:
             for row in csv.DictReader(fh):
-                if "rope_qk_group_kernel" not in row["Kernel_Name"]:
-                    continue
-                T = int(row["Grid_Size_X"]) // (64 * groups)
-                durs.setdefault(T, []).append(
-                    (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3)
+                events.append((int(row["Start_Timestamp"]), int(row["End_Timestamp"]),
+                               "rope_qk_group_kernel" in row["Kernel_Name"]))
+    runs, cur = [], []
+    for start, end, is_rope in sorted(events):
+        if is_rope:
+            cur.append((end - start) / 1e3)
+        elif cur:
+            runs.append(cur)
+            cur = []
+    if cur:
+        runs.append(cur)
+    if len(runs) != len(js["rows"]):
+        raise SystemExit(f"{len(runs)} runs of RoPE dispatches for {len(js['rows'])} sizes")
     per_token = js["bytes_per_token"]
-    lines = [f"{'tokens':>8s} {'trace avg us':>13s} {'GB/s':>6s} {'% peak':>7s} "
+    lines = [f"{'tokens':>8s} {'launches':>8s} {'trace avg us':>13s} {'GB/s':>6s} {'% peak':>7s} "
              f"{'region us':>10s} {'torch neg_ us':>14s} {'torch GB/s':>10s} {'ratio':>6s} index"]
     xs, ys = [], []
-    for r in js["rows"]:
-        T = r["T"]
-        d = np.array(durs.get(T, [np.nan]))
-        avg = float(np.mean(d))
+    for r, run in zip(js["rows"], runs):
+        T, n = r["T"], r["launches_per_pass"]
+        if len(run) % n:
+            raise SystemExit(f"T={T}: {len(run)} dispatches, not whole passes of {n}")
+        avg = float(np.mean(np.array(run).reshape(-1, n).sum(1)))
         gb = per_token * T / (avg * 1e-6) / 1e9
         tgb = per_token * T / (r["torch_inplace_us"] * 1e-6) / 1e9
-        lines.append(f"{T:8d} {avg:13.2f} {gb:6.0f} {100 * gb / HBM_PEAK_GBPS:6.1f}% "
-                     f"{r['avg_launch_us']:10.2f} {r['torch_inplace_us']:14.2f} {tgb:10.0f} "
+        lines.append(f"{T:8d} {n:8d} {avg:13.2f} {gb:6.0f} {100 * gb / HBM_PEAK_GBPS:6.1f}% "
+                     f"{r['avg_pass_us']:10.2f} {r['torch_inplace_us']:14.2f} {tgb:10.0f} "
                      f"{r['torch_inplace_us'] / avg:6.3f} {r['index']}")
         if np.isfinite(avg):
             xs.append(T)
@@ -1117,7 +1176,8 @@ def write_sweep_summary(run_dir: str, command: str) -> None:
                      f" of 8 TB/s")
     header = [
         "# RoPE launch time against token count: one sequence of T tokens, Hq=32, Hkv=8, D=128,",
-        "# bf16, theta=1e6, default launch (row-group kernel; 64-bit offsets at T=524288), each",
+        "# bf16, theta=1e6, default launch (row-group kernel; 64-bit offsets at T=524288; a pass",
+        "# of 2 x 327680 workgroups or more issued as launches over consecutive token ranges), each",
         "# size on its own rotating buffer sets (>= 2 GiB between touches of one buffer); beside",
         "# it torch's in-place neg_ over the same bytes (Q then K), the achievable-pattern reference.",
         f"# algorithmic bytes per token and launch: {per_token}",
@@ -1476,6 +1536,14 @@ def main():
         and tables is None
     if compact:
         cv, valid = padded_metadata(rope, w, cu, su)
+    # launches per pass: one per call, or the row-group kernel's pieces of a long pass
+    nc = max(1, (w.D // 2) // (16 // w.elem_bytes))
+    if tpw != 0 or 64 % nc != 0 or (su is not None and not compact and pid is None):
+        pieces = len(shards) if shards is not None else 1
+    elif shards is not None:
+        pieces = sum(len(group_pieces(b - a, w)) for a, b, _, _ in shards)
+    else:
+        pieces = len(group_pieces(w.valid_tokens if compact else w.T, w))
 
     def launch(qt, kt, direction):
         if compact:
@@ -1547,14 +1615,17 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     region_s = region[0].elapsed_ms(region[1]) / 1e3
-    # Average duration of one pass (forward or backward: one launch, or one per
-    # shard with --positions shards4), gaps between launches included.
-    avg_launch_s = region_s / (2 * args.steps)
-    bpl = algorithmic_bytes_per_launch(w)
+    # Average duration of one pass (forward or backward: one launch, or one per shard
+    # with --positions shards4, or the row-group kernel's pieces of a long pass) and
+    # of one launch, gaps between launches included.
+    avg_pass_s = region_s / (2 * args.steps)
+    avg_launch_s = avg_pass_s / pieces
+    bpp = algorithmic_bytes_per_pass(w)
+    bpl = bpp / pieces
     achieved = bpl / avg_launch_s / 1e9
 
-    # Sampled per-launch durations, after the timed region: HIP events around both
-    # launches of each of up to 250 further steps (context: minimum and median).
+    # Sampled per-pass durations, after the timed region: HIP events around both
+    # passes of each of up to 250 further steps (context: minimum and median).
     events = [[HipEvent() for _ in range(4)] for _ in range(min(250, args.steps))]
     for i, ev in enumerate(events):
         step(sets[i % nsets], ev)
@@ -1611,21 +1682,23 @@ def main():
             "frac": achieved / HBM_PEAK_GBPS,
             "traffic": traffic,
             "kernel": rope_kernel_name(w, tpw, args.padded if compact else "seqused"),
+            "launches_per_pass": pieces,
             "bytes_per_launch": bpl,
             "avg_launch_us": avg_launch_s * 1e6,
-            "timing": "HIP events around the timed region / (2 x steps)",
-            "sampled_launches": len(launch_ms),
-            "sampled_avg_launch_us": float(np.mean(launch_ms)) * 1e3,
-            "sampled_median_launch_us": float(np.median(launch_ms)) * 1e3,
-            "sampled_min_launch_us": float(np.min(launch_ms)) * 1e3,
+            "avg_pass_us": avg_pass_s * 1e6,
+            "timing": "HIP events around the timed region / (2 x steps x launches per pass)",
+            "sampled_passes": len(launch_ms),
+            "sampled_avg_pass_us": float(np.mean(launch_ms)) * 1e3,
+            "sampled_median_pass_us": float(np.median(launch_ms)) * 1e3,
+            "sampled_min_pass_us": float(np.min(launch_ms)) * 1e3,
         },
     }
     if ref_us is not None:
-        out["roofline"]["frac_of_ceiling"] = ref_us / (avg_launch_s * 1e6)
+        out["roofline"]["frac_of_ceiling"] = ref_us / (avg_pass_s * 1e6)
         out["roofline"]["ceiling_reference"] = {
-            "op": "torch in-place neg_ on Q, then on K (same bytes as one launch)",
-            "avg_pass_us": ref_us, "GBps": bpl / (ref_us * 1e-6) / 1e9,
-            "frac_of_ceiling": "reference time / RoPE launch time"}
+            "op": "torch in-place neg_ on Q, then on K (same bytes as one pass)",
+            "avg_pass_us": ref_us, "GBps": bpp / (ref_us * 1e-6) / 1e9,
+            "frac_of_ceiling": "reference time / RoPE pass time"}
     if args.cpu_seconds > 0:
         nthreads = max(1, min(16, len(os.sched_getaffinity(0))))
         if w.T * (w.Hq + w.Hkv) * w.D > 2 ** 28:  # too large to process whole on the host
@@ -1643,20 +1716,21 @@ def main():
                     "D": w.D, "dtype": w.dtype,
                     "kernel": rope_kernel_name(w, 0, args.padded if compact else "seqused"),
                     "index": "64-bit" if needs_long_index(w) else "32-bit",
-                    "bytes_per_launch": bpl, "avg_launch_us": avg_launch_s * 1e6,
+                    "launches_per_pass": pieces, "bytes_per_launch": bpl,
+                    "avg_launch_us": avg_launch_s * 1e6, "avg_pass_us": avg_pass_s * 1e6,
                     "GBps": achieved, "frac": achieved / HBM_PEAK_GBPS,
-                    "fwd_bwd_tokens_per_s": w.valid_tokens / (2 * avg_launch_s),
-                    "launches_timed": 2 * args.steps, "headline": True}
+                    "fwd_bwd_tokens_per_s": w.valid_tokens / (2 * avg_pass_s),
+                    "passes_timed": 2 * args.steps, "headline": True}
                 if ref_us is not None:
                     per[name]["torch_inplace_us"] = ref_us
-                    per[name]["frac_of_ceiling"] = ref_us / (avg_launch_s * 1e6)
+                    per[name]["frac_of_ceiling"] = ref_us / (avg_pass_s * 1e6)
                 continue
             sw = workloads.get(name)
             print(f"[bench] timing {name}", file=sys.stderr, flush=True)
             per[name] = time_workload(rope, sw, dev, 200, 20, padded=args.padded)
         if "qwen3_8b_padded" in per and "qwen3_8b_packed" in per:
             pad, pk = per["qwen3_8b_padded"], per["qwen3_8b_packed"]
-            pad["t_over_packed"] = pad["avg_launch_us"] / pk["avg_launch_us"]
+            pad["t_over_packed"] = pad["avg_pass_us"] / pk["avg_pass_us"]
             pad["valid_fraction"] = pad["valid_tokens"] / pad["T"]
         out["per_config"] = per
     print(json.dumps(out))

@@ -39,15 +39,21 @@
  * nothing, keeps no state between calls, never synchronizes and never reads
  * device memory from the host. Calls only enqueue work on `stream` (a
  * hipStream_t; NULL means the null stream) and return. Calls on different
- * streams are independent; the library is reentrant.
+ * streams are independent; the library is reentrant. A pass is one kernel launch,
+ * except that the default geometry issues a long pass (Q holding at least four
+ * times K's head-row groups, 655360 workgroups or more, e.g. 131072 tokens of 32 + 8
+ * heads at D = 128) as several launches of the same kernel, one after another on
+ * the same stream, over consecutive token ranges: results are identical, and the
+ * shorter launches keep the GPU's eight dies streaming neighbouring addresses.
  *
  * Errors. Arguments are validated on the host before any HIP call; a rejected
  * call enqueues nothing. A launch failure reported by hipGetLastError maps to
- * ROPE_ELAUNCH. Faults during execution surface at the caller's next
- * synchronization. Not validated (undefined behaviour): the contents of
- * cu_seqlens (must be non-decreasing and within [0, T] for meaningful results;
- * any contents stay memory-safe, because a work item only touches its own
- * token's rows), and aliasing between Q and K.
+ * ROPE_ELAUNCH (when a later launch of a multi-launch pass is rejected, the
+ * earlier token ranges have been enqueued). Faults during execution surface at
+ * the caller's next synchronization. Not validated (undefined behaviour): the
+ * contents of cu_seqlens (must be non-decreasing and within [0, T] for meaningful
+ * results; any contents stay memory-safe, because a work item only touches its
+ * own token's rows), and aliasing between Q and K.
  */
 #ifndef ROPE_QK_H
 #define ROPE_QK_H
@@ -74,7 +80,8 @@ typedef enum rope_status {
  * T * (Hq + Hkv) * D >= 2^31 (the int64 specialization), 32-bit otherwise. */
 typedef enum rope_index_mode { ROPE_INDEX_AUTO = 0, ROPE_INDEX_32 = 1, ROPE_INDEX_64 = 2 } rope_index_mode;
 
-/* Forward RoPE on Q and K in place, in one kernel launch.
+/* Forward RoPE on Q and K in place, in one kernel launch (a long pass: several, see
+ * above).
  *  q, k        device pointers to Q[T, Hq, D] and K[T, Hkv, D]; may be NULL only if
  *              that tensor has no elements (T == 0 or its head count is 0)
  *  T           rows (tokens) of Q and K, >= 0

@@ -30,11 +30,11 @@ HIPCC_FLAGS = [
 ]
 
 # Per-source flags. The RoPE kernels take the kernel arguments a wave needs before
-# its first loads as 12 leading dwords; the compiler preloads those into SGPRs at
+# its first loads as 13 leading dwords; the compiler preloads those into SGPRs at
 # wave launch (gfx950 kernel-argument preload; on firmware without it the compiled
 # prologue loads them instead), which shortens every launch's start.
 SRC_FLAGS = {
-    "rope_qk.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=12"],
+    "rope_qk.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=13"],
 }
 
 

@@ -20,7 +20,8 @@
 // rotates it and stores it back, so the in-place update needs no synchronization
 // between lanes. Loads and stores are non-temporal: the data is streamed once; the
 // row-group kernel's stores also write through L2 at device scope.
-// Two kernels, one launch per pass either way:
+// Two kernels, one launch per pass either way (long passes of the row-group kernel
+// as several launches over consecutive token ranges, see group_piece_tokens):
 //  * rope_qk_group_kernel (the default): one 64-lane workgroup per (token, group
 //    of 64/nc head rows), Q's groups then K's; for D = 128 in bf16 a group is 8
 //    rows = 2 KB, one chunk pair per lane. The wave maps its token to (sequence,
@@ -442,7 +443,8 @@ __device__ inline void store_chunk_through(T* p, const Chunk<T, VEC>& c) {
 // < 2^32); groups_mul, the multiplier of the division of the workgroup index by
 // the row groups per token (fast_div.h); geo = gq | gk << 13 | nc_shift << 26 |
 // position-source flags << 29 (kFlag*); heads = Hq | Hkv << 13 | (division
-// shift - 26) << 26; num_seqs. The rest (frequencies, sign, scale,
+// shift - 26) << 26; num_seqs; t_base, the token (COMPACT: rotated token) of
+// workgroup 0, nonzero when a long pass is issued as several launches. The rest (frequencies, sign, scale,
 // tables, the other position sources) comes from ps and p, read after the row
 // loads are issued or only on the paths that need them. D follows from nc_shift:
 // a half row is 2^nc_shift chunks of VEC elements.
@@ -451,7 +453,7 @@ template <typename T, int VEC, bool LONG_INDEX, bool TABLE, bool COMPACT>
 __global__ __launch_bounds__(64) void rope_qk_group_kernel(
     T* __restrict__ q, T* __restrict__ k, const int32_t* __restrict__ cu, uint32_t q_stride,
     uint32_t k_stride, uint32_t groups_mul, uint32_t geo, uint32_t heads, int32_t num_seqs,
-    const PosSource ps, const RopeParams p) {
+    uint32_t t_base, const PosSource ps, const RopeParams p) {
   __shared__ float lds_cs[kMaxHalf];
   __shared__ float lds_sn[kMaxHalf];
   using C = Chunk<T, VEC>;
@@ -465,8 +467,9 @@ __global__ __launch_bounds__(64) void rope_qk_group_kernel(
   // Workgroup -> (token, row group) with host-made constants: a multiply and a
   // shift instead of integer divisions, so the wave reaches its loads sooner.
   const fastdiv::FastDiv groups{groups_mul, fastdiv::kMaxDividendBits + (heads >> 26)};
-  const uint32_t t = fastdiv::div(blockIdx.x, groups);  // < 2^26; COMPACT: rotated-token index
-  const uint32_t g = blockIdx.x - t * (gq + gk);
+  const uint32_t tl = fastdiv::div(blockIdx.x, groups);
+  const uint32_t g = blockIdx.x - tl * (gq + gk);
+  const uint32_t t = t_base + tl;  // < 2^26; COMPACT: rotated-token index
   const uint32_t half = (uint32_t)VEC << ns;
   const uint32_t D = half << 1;
 
@@ -691,6 +694,30 @@ uint32_t group_dynamic_lds(unsigned group_blocks, uint32_t gq, uint32_t gk) {
   return kLdsPerCU / cap - kGroupStaticLds;
 }
 
+// Long passes as several launches. Workgroup i of a launch runs on XCC i mod 8
+// for the whole launch, and the eight XCCs drift apart as it runs (a probe that
+// recorded each workgroup's XCC and start time: on 524288 tokens of 32 + 8 heads
+// the spread between the most and the least advanced XCC grows from ~250 to
+// ~8600 tokens; within 65536 tokens it stays under ~900). The XCCs then stream
+// from separate address ranges instead of neighbouring ones, which HBM serves
+// more slowly; a launch boundary brings them back together. Passes of Q-heavy
+// shapes (Q holding at least 4x K's row groups) of 2 * kPieceBlocks workgroups or
+// more are therefore issued as consecutive launches of about kPieceBlocks each
+// over consecutive token ranges, every range starting at a multiple of 8 tokens
+// so that each (token, row group) keeps the XCC it has in a single launch (ranges
+// one token off that alignment lose most of the gain). Measured, bf16, D = 128,
+// one sequence, interleaved, bit-identical: 32 + 8 heads, 524288 tokens 1604.7 ->
+// 1576.2 us per pass (8 launches), 262144 tokens -1.1%, 131072 tokens -0.4%;
+// 64 + 8 heads, 262144 tokens 1514.6 -> 1427.9 us (8 launches). Not applied to
+// 16 + 8 heads, which measured 0.6-1.5% slower split at every piece count.
+constexpr uint32_t kPieceBlocks = 327680;
+uint32_t group_piece_tokens(uint32_t rows, uint32_t gq, uint32_t gk) {
+  const uint64_t blocks = (uint64_t)rows * (gq + gk);
+  if (gq < 4 * gk || blocks < 2ull * kPieceBlocks) return rows;
+  const uint64_t n = (blocks + kPieceBlocks - 1) / kPieceBlocks;
+  return (uint32_t)(((rows + n - 1) / n + 7) / 8 * 8);
+}
+
 // The leading scalar arguments of rope_qk_group_kernel (see there).
 struct GroupScalars {
   const int32_t* search;  // cu_seqlens, or cu_valid for a compact launch
@@ -723,21 +750,28 @@ int32_t launch_vec(void* q, void* k, const PosSource& ps, const RopeParams& p, b
   if (group_blocks > 0) {
     const uint32_t lds = group_dynamic_lds(group_blocks, p.gq, p.gk);
     const GroupScalars s = group_scalars(p, ps);
+    const uint32_t groups = p.gq + p.gk;
+    const uint32_t rows = group_blocks / groups;
+    const uint32_t piece = group_piece_tokens(rows, p.gq, p.gk);
+    for (uint32_t t0 = 0; t0 < rows; t0 += piece) {
+      const uint32_t n = rows - t0 < piece ? rows - t0 : piece;
 #define ROPE_GROUP_ARGS                                                                     \
-  dim3(group_blocks), dim3(64), lds, stream, qt, kt, s.search, s.q_stride, s.k_stride,    \
-      s.groups_mul, s.geo, s.heads, ps.num_seqs, ps, p
-    if (!TABLE && ps.cu_valid != nullptr) {
-      if (long_index)
-        hipLaunchKernelGGL((rope_qk_group_kernel<T, VEC, true, false, true>), ROPE_GROUP_ARGS);
-      else
-        hipLaunchKernelGGL((rope_qk_group_kernel<T, VEC, false, false, true>), ROPE_GROUP_ARGS);
-    } else if (long_index) {
-      hipLaunchKernelGGL((rope_qk_group_kernel<T, VEC, true, TABLE, false>), ROPE_GROUP_ARGS);
-    } else {
-      hipLaunchKernelGGL((rope_qk_group_kernel<T, VEC, false, TABLE, false>), ROPE_GROUP_ARGS);
-    }
+  dim3(n * groups), dim3(64), lds, stream, qt, kt, s.search, s.q_stride, s.k_stride,      \
+      s.groups_mul, s.geo, s.heads, ps.num_seqs, t0, ps, p
+      if (!TABLE && ps.cu_valid != nullptr) {
+        if (long_index)
+          hipLaunchKernelGGL((rope_qk_group_kernel<T, VEC, true, false, true>), ROPE_GROUP_ARGS);
+        else
+          hipLaunchKernelGGL((rope_qk_group_kernel<T, VEC, false, false, true>), ROPE_GROUP_ARGS);
+      } else if (long_index) {
+        hipLaunchKernelGGL((rope_qk_group_kernel<T, VEC, true, TABLE, false>), ROPE_GROUP_ARGS);
+      } else {
+        hipLaunchKernelGGL((rope_qk_group_kernel<T, VEC, false, TABLE, false>), ROPE_GROUP_ARGS);
+      }
 #undef ROPE_GROUP_ARGS
-    return hipGetLastError() == hipSuccess ? ROPE_OK : ROPE_ELAUNCH;
+      if (hipGetLastError() != hipSuccess) return ROPE_ELAUNCH;
+    }
+    return ROPE_OK;
   }
   if (long_index)
     hipLaunchKernelGGL((rope_qk_kernel<T, VEC, true, TABLE>), dim3(blocks), dim3(kTokenBlock), 0, stream,

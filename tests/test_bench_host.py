@@ -26,7 +26,7 @@ def _counter_csv(path, rows):
             wr.writerow({"Kernel_Name": kernel, "Counter_Name": counter, "Counter_Value": value})
 
 
-def _trace_csv(path, durations_ns, kernel=GROUP):
+def _trace_csv(path, durations_ns, kernel=GROUP, grid=5242880):
     os.makedirs(os.path.dirname(path), exist_ok=True)
     fields = ["Kernel_Name", "Start_Timestamp", "End_Timestamp", "Grid_Size_X",
               "Workgroup_Size_X", "VGPR_Count", "LDS_Block_Size"]
@@ -36,7 +36,7 @@ def _trace_csv(path, durations_ns, kernel=GROUP):
         t = 1000
         for d in durations_ns:
             wr.writerow({"Kernel_Name": kernel, "Start_Timestamp": t, "End_Timestamp": t + d,
-                         "Grid_Size_X": 5242880, "Workgroup_Size_X": 64, "VGPR_Count": 24,
+                         "Grid_Size_X": grid, "Workgroup_Size_X": 64, "VGPR_Count": 24,
                          "LDS_Block_Size": 2048})
             wr.writerow({"Kernel_Name": COPY, "Start_Timestamp": t, "End_Timestamp": t + 7,
                          "Grid_Size_X": 64, "Workgroup_Size_X": 64, "VGPR_Count": 8,
@@ -50,6 +50,38 @@ def test_algorithmic_bytes():
     p = workloads.get("qwen3_8b_padded")  # only the valid tokens count
     assert bench.algorithmic_bytes_per_launch(p) == 2 * p.valid_tokens * 40 * 128 * 2
     assert p.valid_tokens < p.T
+    # the 524288-token pass is 8 launches: per-launch bytes are an eighth of the pass's
+    w5 = workloads.get("long_ctx_512k")
+    assert bench.algorithmic_bytes_per_pass(w5) == 2 * 524288 * 40 * 128 * 2
+    assert bench.algorithmic_bytes_per_launch(w5) == bench.algorithmic_bytes_per_pass(w5) / 8
+
+
+def _shape(T, Hq, Hkv, D=128, dtype="bf16"):
+    return workloads.Workload(f"s{T}", 91, T, Hq, Hkv, D, dtype, 1e6, np.array([0, T], dtype=np.int32))
+
+
+def test_launch_pieces():
+    """The library's rule for issuing a long row-group pass as several launches:
+    Q-heavy shapes (gq >= 4 gk) of 2 x 327680 workgroups or more, in launches of
+    about 327680 workgroups over token ranges starting at multiples of 8."""
+    assert bench.launch_pieces(workloads.get("long_ctx_512k")) == [65536] * 8   # 5 groups/token
+    assert bench.launch_pieces(workloads.get("qwen3_4b_packed")) == [16384]
+    assert bench.launch_pieces(workloads.get("qwen3_32b_packed")) == [32768]  # 294912 workgroups
+    assert bench.launch_pieces(_shape(131072, 32, 8)) == [65536, 65536]        # exactly 2 x 327680
+    assert bench.launch_pieces(_shape(131071, 32, 8)) == [131071]              # one workgroup short
+    assert bench.launch_pieces(_shape(262144, 64, 8)) == [32768] * 8           # 9 groups/token
+    assert bench.launch_pieces(_shape(524288, 16, 8)) == [524288]              # gq = 2 gk: never split
+    assert bench.launch_pieces(_shape(524288, 32, 8), tokens_per_wave=1) == [524288]  # token kernel
+    # ragged: 200003 tokens x 5 groups -> 4 launches of ceil(200003 / 4) rounded up to 8
+    pieces = bench.launch_pieces(_shape(200003, 32, 8))
+    assert pieces == [50008, 50008, 50008, 49979] and sum(pieces) == 200003
+    assert all(p % 8 == 0 for p in pieces[:-1])
+    # D = 64 in bf16: 16 rows per group, so 32 + 8 heads are 2 + 1 groups (gq < 4 gk)
+    assert bench.launch_pieces(_shape(524288, 32, 8, D=64)) == [524288]
+    # a compact padded launch counts rotated tokens
+    pad = workloads.get("qwen3_8b_padded")
+    assert bench.launch_pieces(pad) == [pad.valid_tokens]
+    assert bench.launch_pieces(pad, "seqused") == [pad.T]
 
 
 def test_kernel_choice():
@@ -60,8 +92,9 @@ def test_kernel_choice():
     assert bench.rope_kernel_name(pad, 0, "seqused") == "rope_qk_kernel"
     assert bench.compact_launch(pad) and not bench.compact_launch(workloads.get("qwen3_4b_packed"))
     # grid of the compact launch: the rotated tokens' row groups only
-    assert bench.expected_grid_threads(pad) == pad.valid_tokens * 5 * 64
-    assert bench.expected_grid_threads(pad, "seqused") == pad.T * 64
+    assert bench.expected_grid_threads(pad) == [pad.valid_tokens * 5 * 64]
+    assert bench.expected_grid_threads(pad, "seqused") == [pad.T * 64]
+    assert bench.expected_grid_threads(workloads.get("long_ctx_512k")) == [65536 * 5 * 64] * 8
 
 
 def test_kernel_instance_names():
@@ -150,14 +183,15 @@ def test_sweep_summary(tmp_path, monkeypatch):
     out = tmp_path / "sweep.txt"
     monkeypatch.setattr(bench, "SWEEP_FILE", str(out))
     sizes = [2048, 16384, 65536]
+    pieces = {2048: 1, 16384: 1, 65536: 2}  # the largest size as two launches per pass
     rows, trace = [], []
     for T in sizes:
         us = 1.5 + 0.003 * T
-        rows.append({"T": T, "avg_launch_us": us + 0.1, "torch_inplace_us": 2 + 0.0035 * T,
-                     "GBps": 0.0, "index": "32-bit"})
+        rows.append({"T": T, "avg_pass_us": us + 0.1, "launches_per_pass": pieces[T],
+                     "torch_inplace_us": 2 + 0.0035 * T, "GBps": 0.0, "index": "32-bit"})
         trace.append((T, int(us * 1e3)))
     js = {"bytes_per_token": 20480, "rows": rows}
-    for key in ("avg_launch_us", "torch_inplace_us"):
+    for key in ("avg_pass_us", "torch_inplace_us"):
         t0, b = bench.linear_fit(sizes, [r[key] for r in rows])
         js[f"fit_{key}"] = {"t0_us": t0, "us_per_token": b,
                             "asymptotic_GBps": 20480 / (b * 1e-6) / 1e9}
@@ -167,10 +201,17 @@ def test_sweep_summary(tmp_path, monkeypatch):
     with open(tmp_path / "tr" / "x_kernel_trace.csv", "w", newline="") as fh:
         wr = csv.DictWriter(fh, fieldnames=fields)
         wr.writeheader()
+        clock = 0
+        # each size: one run of RoPE dispatches (3 passes) between torch's own kernels
         for T, ns in trace:
-            for _ in range(3):
-                wr.writerow({"Kernel_Name": GROUP, "Start_Timestamp": 0, "End_Timestamp": ns,
-                             "Grid_Size_X": T * 5 * 64})
+            n = pieces[T]
+            for _ in range(3 * n):
+                wr.writerow({"Kernel_Name": GROUP, "Start_Timestamp": clock,
+                             "End_Timestamp": clock + ns // n, "Grid_Size_X": T // n * 5 * 64})
+                clock += ns
+            wr.writerow({"Kernel_Name": COPY, "Start_Timestamp": clock, "End_Timestamp": clock + 5,
+                         "Grid_Size_X": 64})
+            clock += 10
     bench.write_sweep_summary(str(tmp_path), "cmd")
     text = out.read_text()
     assert "fit, RoPE kernel, trace averages, all sizes: t = 1.50 us + T x 3.0000 ns" in text, text
@@ -190,6 +231,28 @@ def test_trace_summary(tmp_path, monkeypatch):
     assert f"average: {mean:.2f} us -> {gbps:.0f} GB/s" in text
     assert "minimum: 50.00 us" in text and "maximum: 60.00 us" in text
     assert "static LDS only" in text
+    assert "launches_per_pass" not in text
+
+
+def test_trace_summary_multi_launch_pass(tmp_path, monkeypatch):
+    """The 524288-token pass is 8 launches of 65536 tokens: per-launch bytes are an
+    eighth of the pass's, and tokens/s count whole passes."""
+    out = tmp_path / "trace.txt"
+    monkeypatch.setattr(bench, "trace_summary_path", lambda workload: str(out))
+    long_k = "_ZN12_GLOBAL__N_120rope_qk_group_kernelIDF16bLi8ELb1ELb0ELb0EEEvPT_S2_"
+    durations = [200000] * 16
+    _trace_csv(str(tmp_path / "t.csv"), durations, kernel=long_k, grid=65536 * 5 * 64)
+    bench.write_trace_summary(str(tmp_path / "t.csv"), "long_ctx_512k", "cmd")
+    text = out.read_text()
+    assert "launches_per_pass: 8 (tokens per launch: 65536)" in text
+    assert "algorithmic_bytes_per_launch: 1342177280" in text
+    gbps = 1342177280 / 200e-6 / 1e9
+    assert f"average: 200.00 us -> {gbps:.0f} GB/s" in text
+    assert f"valid_tokens_per_s_at_average: {524288 / (8 * 200e-6):.4g} per pass" in text
+    # dispatches with another grid (another workload's launches) are not counted
+    _trace_csv(str(tmp_path / "u.csv"), durations, kernel=long_k, grid=524288 * 5 * 64)
+    with pytest.raises(SystemExit):
+        bench.write_trace_summary(str(tmp_path / "u.csv"), "long_ctx_512k", "cmd")
 
 
 def test_counters_summary(tmp_path, monkeypatch):
@@ -244,5 +307,5 @@ def test_source_hash_ignores_documentation(tmp_path, monkeypatch):
     code = build.read_text()
     build.write_text(code.replace('"""', '"""Edited docstring. ', 1) + "\n# a comment\n")
     assert bench.kernel_source_hash() == base
-    build.write_text(code.replace("-amdgpu-kernarg-preload-count=12", "-amdgpu-kernarg-preload-count=8"))
+    build.write_text(code.replace("-amdgpu-kernarg-preload-count=13", "-amdgpu-kernarg-preload-count=8"))
     assert bench.kernel_source_hash() != base

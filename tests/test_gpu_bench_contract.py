@@ -35,11 +35,16 @@ def test_bench_json_contract():
     assert abs(r["frac"] - r["achieved"] / r["peak"]) < 1e-9
     assert abs(r["achieved"] - r["bytes_per_launch"] / (r["avg_launch_us"] * 1e-6) / 1e9) < 1e-6
     assert 0.3 < r["frac"] < 1.0 and r["frac_of_ceiling"] > 0
+    assert r["launches_per_pass"] == 1
+    assert abs(r["avg_pass_us"] - r["avg_launch_us"] * r["launches_per_pass"]) < 1e-6
     c = d["cpu_baseline"]
     assert c["kind"] == "oracle" and c["cores"] >= 1 and c["value"] > 0 and c["sample"]
     assert set(d["per_config"]) == {"tiny_packed", "qwen3_4b_packed", "qwen3_8b_packed",
                                     "qwen3_8b_padded", "qwen3_32b_packed", "long_ctx_512k"}
     assert d["per_config"]["qwen3_8b_packed"].get("headline") is True
+    long = d["per_config"]["long_ctx_512k"]  # 2621440 workgroups: 8 launches per pass
+    assert long["launches_per_pass"] == 8 and long["index"] == "64-bit"
+    assert abs(long["avg_pass_us"] - 8 * long["avg_launch_us"]) < 1e-6
     pad = d["per_config"]["qwen3_8b_padded"]
     assert pad["padded_launch"] == "compact" and pad["kernel"] == "rope_qk_group_kernel"
     assert 0.8 < pad["t_over_packed"] < 1.5 and pad["valid_fraction"] < 0.6

@@ -206,6 +206,151 @@ def test_long_context_full(rope):
     torch.cuda.empty_cache()
 
 
+# ------------------------------------------------- passes issued as several launches
+# A long pass of the row-group kernel on a Q-heavy head shape goes out as several
+# launches over consecutive token ranges (bench.group_pieces mirrors the rule); these
+# cases cross the range boundaries with sequences, offsets and untouched tokens.
+
+def _guarded_dev(t: torch.Tensor, guard: int = 4096):
+    """A copy of device tensor t inside a larger buffer whose guard regions hold canaries."""
+    n = t.numel()
+    flat = torch.empty(n + 2 * guard, dtype=t.dtype, device=DEV)
+    flat.view(_word(t.dtype)).fill_(_canary(t.dtype))
+    view = flat[guard:guard + n].view(t.shape)
+    view.copy_(t)
+    return view, flat, guard
+
+
+def _piece_marks(pieces, T, width=8):
+    """Tokens on both sides of every boundary between the launches of a pass."""
+    edges = np.cumsum(pieces)[:-1]
+    marks = np.concatenate([np.arange(e - width, e + width) for e in edges] +
+                           [np.arange(0, 16), np.arange(T - 16, T)])
+    return marks[(marks >= 0) & (marks < T)]
+
+
+def test_split_pass_ragged_full(rope):
+    """32 + 8 heads, bf16, 200003 rows: 4 launches over 50008, 50008, 50008 and 49979
+    tokens. Sequences start on, next to and across the range boundaries, and the last
+    13 rows lie past cu_seqlens' end (untouched). Every element of Q, K, dQ and dK
+    against the oracle; guard regions intact."""
+    import bench
+    T, Hq, Hkv, D = 200003, 32, 8, 128
+    w = workloads.Workload("split", 92, T, Hq, Hkv, D, "bf16", 1e6,
+                           np.array([0, T], dtype=np.int32))
+    pieces = bench.group_pieces(T, w)
+    assert pieces == [50008, 50008, 50008, 49979]
+    rng = np.random.default_rng(9600)
+    cuts = set(rng.integers(1, T - 13, 12).tolist()) | {50008, 100017, 150023, 150024}
+    cu_h = np.array([0, *sorted(cuts), T - 13], dtype=np.int32)
+    print(f"[parity] split pass, {len(cu_h) - 1} sequences, pieces {pieces}", flush=True)
+    cu = torch.from_numpy(cu_h).to(DEV)
+    dev, flats = {}, {}
+    for i, what in enumerate(("q", "k", "dq", "dk")):
+        shape = (T, Hq if what in ("q", "dq") else Hkv, D)
+        t = workloads.make_tensor(shape, 9610 + i, "bf16", device=DEV, chunk_rows=32768)
+        dev[what], flats[what], g = _guarded_dev(t)
+        del t
+    before = {what: bits(t) for what, t in dev.items()}
+    rope.qk_fwd_(dev["q"], dev["k"], cu, 1e6)
+    rope.qk_bwd_(dev["dq"], dev["dk"], cu, 1e6)
+    torch.cuda.synchronize()
+    pos, _ = oracle.positions(cu_h, T)
+    chunk = 32768
+    for what, direction in (("q", 1), ("k", 1), ("dq", -1), ("dk", -1)):
+        assert guards_intact(flats[what], g), f"split:{what}: guard region written"
+        for a in range(0, T, chunk):
+            b = min(T, a + chunk)
+            tokens = np.arange(a, b, dtype=np.int64)
+            x = np.ascontiguousarray(before[what][a:b])
+            ref = oracle.rope_rows(x, tokens, cu_h, 1e6, direction, "bf16", None, NTHREADS)
+            assert_parity("bf16", bits(dev[what][a:b]), ref, x, pos[a:b] >= 0,
+                          f"split:{what}[{a}:{b}]")
+    del dev, flats, before
+    torch.cuda.empty_cache()
+
+
+SPLIT_CASES = [  # name, T, Hq, Hkv, dtype, expected pieces
+    ("cu", 73000, 64, 8, "bf16", [24336, 24336, 24328]),
+    ("offsets", 73000, 64, 8, "bf16", [24336, 24336, 24328]),
+    ("ids", 73000, 64, 8, "bf16", [24336, 24336, 24328]),
+    ("scale", 73000, 64, 8, "bf16", [24336, 24336, 24328]),
+    ("table", 73000, 64, 8, "bf16", [24336, 24336, 24328]),
+    ("f32", 70000, 32, 8, "f32", [23336, 23336, 23328]),
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=[c[0] for c in SPLIT_CASES])
+def test_split_pass_position_sources(rope, case):
+    """Passes issued as several launches with every position source (cu_seqlens alone,
+    per-sequence offsets, explicit ids with untouched tokens, linear scaling, cos/sin
+    tables) and fp32 storage: the whole tensors bit for bit against the token kernel
+    (tokens_per_wave=1, never split) and sampled rows (both sides of every launch
+    boundary, random rows) against the oracle."""
+    import bench
+    name, T, Hq, Hkv, dtype, expect = case
+    D, theta = 128, 1e6
+    w = workloads.Workload("split", 93, T, Hq, Hkv, D, dtype, theta,
+                           np.array([0, T], dtype=np.int32))
+    pieces = bench.group_pieces(T, w)
+    assert pieces == expect
+    print(f"[parity] split pass {name}: T={T} {Hq}+{Hkv} {dtype} pieces {pieces}", flush=True)
+    rng = np.random.default_rng(9700)
+    cu_h = np.array([0, *sorted(set(rng.integers(1, T, 9).tolist()) | {pieces[0] + 3}), T],
+                    dtype=np.int32)
+    B = len(cu_h) - 1
+    offs_h = rng.integers(0, 400000, B).astype(np.int32) if name == "offsets" else None
+    ids_h = None
+    if name == "ids":
+        ids_h = rng.integers(0, 500000, T).astype(np.int32)
+        ids_h[rng.choice(T, 2000, replace=False)] = -1
+        ids_h[pieces[0] - 2:pieces[0] + 2] = [-1, 7, -1, 524287]
+    scale = 4.0 if name == "scale" else 1.0
+    cu = torch.from_numpy(cu_h).to(DEV)
+    offs = None if offs_h is None else torch.from_numpy(offs_h).to(DEV)
+    ids = None if ids_h is None else torch.from_numpy(ids_h).to(DEV)
+    src = {what: workloads.make_tensor((T, Hq if what in ("q", "dq") else Hkv, D), 9710 + i,
+                                       dtype, device=DEV, chunk_rows=32768)
+           for i, what in enumerate(("q", "k", "dq", "dk"))}
+    marks = _piece_marks(pieces, T)
+    tokens = np.unique(np.concatenate([marks, rng.integers(0, T, 2048)]))
+    tok_dev = torch.from_numpy(tokens).to(DEV)
+    tables = None
+    if name == "table":
+        tables = rope.cos_sin_table(int(np.diff(cu_h).max()), D, theta, DEV)
+
+    def apply(q, k, direction, **kw):
+        if tables is not None and not kw:
+            rope.qk_apply_table_(q, k, tables[0], tables[1], direction, cu_seqlens=cu)
+            return
+        rope.qk_apply_ex_(q, k, theta, direction, cu_seqlens=None if ids is not None else cu,
+                          seq_offsets=offs, position_ids=ids, pos_scale=scale, **kw)
+
+    for fwd, grad, direction in (("q", "k", 1), ("dq", "dk", -1)):
+        a_q, a_k = src[fwd].clone(), src[grad].clone()
+        b_q, b_k = src[fwd].clone(), src[grad].clone()
+        apply(a_q, a_k, direction)
+        apply(b_q, b_k, direction, tokens_per_wave=1)
+        torch.cuda.synchronize()
+        assert torch.equal(a_q.view(_word(a_q.dtype)), b_q.view(_word(b_q.dtype))), (name, fwd)
+        assert torch.equal(a_k.view(_word(a_k.dtype)), b_k.view(_word(b_k.dtype))), (name, grad)
+        for what, got_t in ((fwd, a_q), (grad, a_k)):
+            x = bits(src[what].index_select(0, tok_dev))
+            got = bits(got_t.index_select(0, tok_dev))
+            if ids_h is not None:
+                ref = oracle.rope_rows(x, tokens, None, theta, direction, dtype, None, NTHREADS,
+                                       position_ids=ids_h)
+                touched = ids_h[tokens] >= 0
+            else:
+                ref = oracle.rope_rows(x, tokens, cu_h, theta, direction, dtype, None, NTHREADS,
+                                       seq_offsets=offs_h, pos_scale=scale)
+                touched = np.ones(len(tokens), dtype=bool)
+            assert_parity(dtype, got, ref, x, touched, f"split-{name}:{what}")
+        del a_q, a_k, b_q, b_k
+    del src
+    torch.cuda.empty_cache()
+
+
 # ---------------------------------------------------------------- exports
 
 @pytest.mark.parametrize("name", workloads.names())
@@ -949,9 +1094,11 @@ def test_padded_compact_edges(rope, case):
 def test_padded_compact_long_context(rope):
     """A padded layout that needs 64-bit offsets by itself: 4 sequences padded to
     131072 rows each (524288 rows, 32 + 8 heads, bf16), 54-97% of each row block
-    used, through the compact launch forward and backward: sampled rows (sequence
-    ends, both sides of every used / padded boundary, random rows) against the
-    oracle, padded rows untouched."""
+    used, through the compact launch forward and backward (its 429076 rotated tokens
+    issued as 7 launches): sampled rows (sequence ends, both sides of every used /
+    padded boundary and of every launch boundary, random rows) against the oracle,
+    padded rows untouched."""
+    import bench
     S, B, Hq, Hkv, D = 131072, 4, 32, 8, 128
     T = S * B
     assert T * (Hq + Hkv) * D >= 1 << 31
@@ -967,6 +1114,14 @@ def test_padded_compact_long_context(rope):
     rng = np.random.default_rng(9550)
     marks = [np.arange(c - 3, c + 3) for c in cu_h[1:-1]]
     marks += [np.arange(a + u - 3, a + u + 3) for a, u in zip(cu_h[:-1], su_h)]
+    # launch boundaries, from rotated-token index to row
+    wv = workloads.Workload("c", 0, valid, Hq, Hkv, D, "bf16", 1e6,
+                            np.array([0, valid], dtype=np.int32))
+    vb = np.cumsum(bench.group_pieces(valid, wv))[:-1]
+    assert len(vb) == 6
+    cv_h = np.concatenate([[0], np.cumsum(su_h.astype(np.int64))])
+    s_of = np.searchsorted(cv_h, vb, side="right") - 1
+    marks += [np.arange(r - 4, r + 4) for r in cu_h[s_of] + (vb - cv_h[s_of])]
     tokens = np.unique(np.concatenate([np.arange(0, 32), np.arange(T - 32, T), *marks,
                                        rng.integers(0, T, 4096)]))
     tokens = tokens[(tokens >= 0) & (tokens < T)]
