@@ -1228,6 +1228,26 @@ def compare_glu_unfused(rope, w, kind, sets, nsets, args) -> None:
                       "dtype": w.dtype, **res}))
 
 
+# The library's kGluPieceBlocks: a GLU call of 2x this many workgroups or more goes
+# out as launches of about this many.
+GLU_PIECE_BLOCKS = 32768
+
+
+def glu_pieces(w) -> list:
+    """Workgroups of each launch of one dense GLU call on workload w (1024 chunks of
+    16 bytes, or of the row's widest dividing access, per workgroup; the library's
+    glu_piece_blocks)."""
+    vec = 16 // w.elem_bytes
+    while (w.cols * w.elem_bytes) % (vec * w.elem_bytes):
+        vec //= 2
+    want = -(-(w.rows * (w.cols // vec)) // 1024)
+    if want < 2 * GLU_PIECE_BLOCKS:
+        return [want]
+    n = -(-want // GLU_PIECE_BLOCKS)
+    piece = (-(-want // n) + 7) // 8 * 8
+    return [min(piece, want - b) for b in range(0, want, piece)]
+
+
 def bench_glu(args) -> None:
     """One step = glu_fwd (e, g -> h) + glu_bwd (dh, e, g -> de, dg), out of place,
     on [tokens, intermediate] tensors resident in HBM; buffer sets rotate so no
@@ -1300,6 +1320,7 @@ def bench_glu(args) -> None:
     bwd_all = [ev[2].elapsed_ms(ev[3]) * 1e3 for ev in events]
     fwd_bytes, bwd_bytes = 3 * n * w.elem_bytes, 5 * n * w.elem_bytes
     achieved = bwd_bytes / (bwd_us * 1e-6) / 1e9
+    pieces = len(glu_pieces(w))  # launches per call
     out = {
         "metric": GLU_METRIC,
         "value": w.rows * args.steps / elapsed,
@@ -1322,13 +1343,17 @@ def bench_glu(args) -> None:
             "traffic": (read_traffic(GLU_TRAFFIC_FILE, GLU_SOURCES, "bwd_hbm_bytes_per_launch")
                         if kind == "swiglu" and w.name == "glu_qwen3_4b" else None),
             "kernel": "glu_kernel (backward)",
-            "bytes_per_launch": bwd_bytes, "avg_launch_us": bwd_us,
-            "timing": f"HIP events around {reps} back-to-back backward launches / {reps}",
-            "min_launch_us": float(np.min(bwd_all)), "median_launch_us": float(np.median(bwd_all)),
+            "launches_per_call": pieces,
+            "bytes_per_launch": bwd_bytes / pieces, "avg_launch_us": bwd_us / pieces,
+            "avg_call_us": bwd_us,
+            "timing": f"HIP events around {reps} back-to-back backward calls / ({reps} x "
+                      "launches per call)",
+            "min_call_us": float(np.min(bwd_all)), "median_call_us": float(np.median(bwd_all)),
         },
-        "forward": {"bytes_per_launch": fwd_bytes, "avg_launch_us": fwd_us,
-                    "min_launch_us": float(np.min(fwd_all)),
-                    "median_launch_us": float(np.median(fwd_all)),
+        "forward": {"launches_per_call": pieces, "bytes_per_launch": fwd_bytes / pieces,
+                    "avg_launch_us": fwd_us / pieces, "avg_call_us": fwd_us,
+                    "min_call_us": float(np.min(fwd_all)),
+                    "median_call_us": float(np.median(fwd_all)),
                     "achieved_GBps": fwd_bytes / (fwd_us * 1e-6) / 1e9},
     }
     if args.cpu_seconds > 0:

@@ -22,7 +22,12 @@
  * two halves of one fused gate/up projection output [rows, 2*cols]
  * (in_stride = 2*cols). h and dh use out_stride. Arithmetic is fp32 with one
  * rounding to the storage dtype per output; the library allocates nothing, keeps
- * no state and never synchronizes. Calls on one stream run in order.
+ * no state and never synchronizes. Calls on one stream run in order. A call is one
+ * kernel launch, except that a call of 65536 workgroups or more (each covers 1024
+ * chunks of 16 bytes or less, e.g. 2^26 bf16 elements per 8192 workgroups) goes
+ * out as several launches of about 32768 workgroups, one after another on the same
+ * stream, over consecutive ranges of the elements: results are identical, and the
+ * shorter launches keep the GPU's eight dies streaming neighbouring addresses.
  *
  * Aliasing: an output may be the same memory as one of its own-shape inputs at
  * the same address and stride (h over e or g in the forward; de over e and dg
@@ -33,7 +38,8 @@
  * kind, rows or cols < 0, a stride below cols, a NULL pointer with rows*cols > 0,
  * a span rows*stride above 2^48 elements, or index_mode ROPE_INDEX_32 when 64-bit
  * offsets are needed; ROPE_EUNSUPPORTED for an unknown dtype; ROPE_ELAUNCH if
- * the launch fails. rows*cols == 0 returns ROPE_OK without launching.
+ * a launch fails (the earlier ranges of a multi-launch call stay enqueued).
+ * rows*cols == 0 returns ROPE_OK without launching.
  *
  * index_mode (rope_index_mode): ROPE_INDEX_AUTO picks 64-bit offsets when some
  * element offset of the call reaches 2^31, and otherwise 32-bit offsets, except

@@ -289,7 +289,8 @@ def qk_bwd_pos_(dq, dk, position_ids, theta: float):
 
 
 def qk_fwd_(q, k, cu_seqlens, theta: float, seqused=None):
-    """Forward RoPE on q and k in place (one launch). Returns (q, k)."""
+    """Forward RoPE on q and k in place (one launch; a long pass several, over
+    consecutive token ranges). Returns (q, k)."""
     T, Hq, Hkv, D, cu, num_seqs, su = _qk_args(q, k, cu_seqlens, seqused)
     st = _lib.rope_qk_fwd(_ptr(q), _ptr(k), T, Hq, Hkv, D, _ptr(cu), num_seqs, _ptr(su),
                           float(theta), _DTYPE_CODE[q.dtype], _stream(q.device))
@@ -387,7 +388,8 @@ def _glu_group(tensors, names):
 
 def glu_fwd(kind: str, e, g, out=None, index_mode: int = INDEX_AUTO):
     """h = act(e) * g for act = silu ("swiglu"), exact gelu ("geglu") or tanh gelu
-    ("geglu_tanh"), one launch on the current stream. e and g: [rows, cols] with
+    ("geglu_tanh"), on the current stream (one launch; a long call several, one after
+    another over consecutive element ranges). e and g: [rows, cols] with
     contiguous columns and one row stride (two dense tensors, or the two halves of
     a fused gate/up output). out: a [rows, cols] tensor (new and dense if None; it
     may be e or g itself). Returns out."""
@@ -404,7 +406,7 @@ def glu_fwd(kind: str, e, g, out=None, index_mode: int = INDEX_AUTO):
 
 
 def glu_bwd(kind: str, dh, e, g, de=None, dg=None, index_mode: int = INDEX_AUTO):
-    """de = dh * g * act'(e), dg = dh * act(e), one launch. de and dg take the
+    """de = dh * g * act'(e), dg = dh * act(e), launched like glu_fwd. de and dg take the
     layout of e and g (new tensors with e's strides if None; pass de=e, dg=g to
     update the inputs in place). Returns (de, dg)."""
     rows, cols, in_stride = _glu_group([e, g], ["e", "g"])

@@ -1,8 +1,9 @@
 """Autograd entry points over the C ABI: the packed-varlen QK rotary embedding
 and the SwiGLU / GeGLU activations as differentiable torch functions.
 
-Every pass is one launch of the library's kernels on the current stream; this
-module only wires them into torch.autograd (no arithmetic of its own).
+Every pass is one launch of the library's kernels on the current stream (a long
+pass: several, over consecutive ranges); this module only wires them into
+torch.autograd (no arithmetic of its own).
 
     qkv = rope_qkv(qkv, Hq, Hkv, cu_seqlens, theta)  # fused QKV output, in place
     q, k = rope_qk(q, k, cu_seqlens, theta)        # returns q and k, rotated

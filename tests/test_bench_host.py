@@ -97,6 +97,15 @@ def test_kernel_choice():
     assert bench.expected_grid_threads(workloads.get("long_ctx_512k")) == [65536 * 5 * 64] * 8
 
 
+def test_glu_pieces():
+    """The library's rule for issuing a long GLU call as several launches: 65536
+    workgroups (of 1024 16-byte chunks) or more, in launches of about 32768."""
+    assert bench.glu_pieces(workloads.glu_get("glu_qwen3_4b")) == [19456]
+    assert bench.glu_pieces(workloads.glu_get("glu_qwen3_8b")) == [12831]
+    assert bench.glu_pieces(workloads.glu_get("glu_tiny")) == [1]
+    assert bench.glu_pieces(workloads.glu_get("glu_long_512k")) == [32768] * 19
+
+
 def test_kernel_instance_names():
     """The mangled-name fragments the summaries filter rocprofv3 records by."""
     w5, w2 = workloads.get("long_ctx_512k"), workloads.get("qwen3_4b_packed")

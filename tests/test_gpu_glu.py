@@ -256,6 +256,45 @@ def test_fused_gate_up_layout(rope, kind):
     assert_glu_parity("bf16", words(h), ref_h, values(we, "bf16"), f"fused:{kind}:h")
 
 
+@pytest.mark.parametrize("kind", KINDS)
+def test_split_call_fused_layout(rope, kind):
+    """A call long enough to go out as several launches on the 32-bit path: 70001 rows
+    x 7680 bf16 as the halves of a fused gate/up output (65626 workgroups of 1024
+    16-byte chunks: 3 launches of 21880, 21880 and 21866 workgroups, whose boundaries
+    fall inside rows 23338 and 46677). Bit-identical to dense copies of e and g;
+    rows around the launch boundaries and every 37th row against the oracle,
+    forward and backward."""
+    rows, cols = 70001, 7680
+    print(f"[glu parity] split call, fused gate/up {kind}", flush=True)
+    gu = make((rows, 2 * cols), 9450, "bf16")
+    dh = make((rows, cols), 9451, "bf16")
+    e, g = gu[:, :cols], gu[:, cols:]
+    h = rope.glu_fwd(kind, e, g)
+    de, dg = rope.glu_bwd(kind, dh, e, g)
+    ec, gc = e.contiguous(), g.contiguous()
+    h2 = rope.glu_fwd(kind, ec, gc)
+    de2, dg2 = rope.glu_bwd(kind, dh, ec, gc)
+    torch.cuda.synchronize()
+    for a, b in ((h, h2), (de, de2), (dg, dg2)):
+        assert torch.equal(a.contiguous().view(torch.int16), b.contiguous().view(torch.int16))
+    chunks_per_row = cols // 8
+    edges = [21880 * 1024 * m // chunks_per_row for m in (1, 2)]
+    assert edges == [23338, 46677]
+    sel = np.unique(np.concatenate([np.arange(0, 3), np.arange(rows - 3, rows),
+                                    *[np.arange(r - 2, r + 3) for r in edges],
+                                    np.arange(0, rows, 37)]))
+    idx = torch.from_numpy(sel).to(DEV)
+    we, wg, wd = (words(t.index_select(0, idx)) for t in (e, g, dh))
+    ev = values(we, "bf16")
+    ref_h = glu_oracle.fwd(kind, we, wg, "bf16", NTHREADS)
+    ref_de, ref_dg = glu_oracle.bwd(kind, wd, we, wg, "bf16", NTHREADS)
+    assert_glu_parity("bf16", words(h.index_select(0, idx)), ref_h, ev, f"split:{kind}:h")
+    assert_glu_parity("bf16", words(de.index_select(0, idx)), ref_de, ev, f"split:{kind}:de")
+    assert_glu_parity("bf16", words(dg.index_select(0, idx)), ref_dg, ev, f"split:{kind}:dg")
+    del gu, dh, e, g, h, de, dg, ec, gc, h2, de2, dg2
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("dtype,cols,lead,in_pad,out_pad", [
     ("bf16", 1000, 0, 0, 0),     # 16-byte chunks, dense
     ("bf16", 1000, 4, 0, 0),     # base 8 bytes off: 8-byte chunks
@@ -338,9 +377,11 @@ def test_empty(rope):
 @pytest.mark.parametrize("kind", KINDS)
 def test_long_context_int64(rope, kind):
     """524288 tokens x 9728 (5.1e9 elements, 2.4 x 2^31): the 64-bit path, for each
-    kind. Forward and in-place backward; rows at the start, around the 2^31-element
-    boundary, at the end, and every 97th row (a prime stride, so the sampled rows'
-    offsets take every residue of the power-of-two tile sizes) against the oracle."""
+    kind, as 19 launches of 32768 workgroups (8192 elements each). Forward and
+    in-place backward; rows at the start, around the 2^31-element boundary, around
+    every launch boundary, at the end, and every 97th row (a prime stride, so the
+    sampled rows' offsets take every residue of the power-of-two tile sizes) against
+    the oracle."""
     w = workloads.glu_get("glu_long_512k")
     print(f"[glu parity] glu_long_512k int64 path {kind}", flush=True)
     assert w.elements >= 2 ** 31
@@ -350,7 +391,9 @@ def test_long_context_int64(rope, kind):
     with pytest.raises(rope.RopeError):
         rope.glu_fwd(kind, e, g, out=h, index_mode=rope.INDEX_32)
     boundary_row = (2 ** 31) // w.cols
+    launch_rows = [m * 32768 * 8192 // w.cols for m in range(1, 19)]
     rows = np.unique(np.concatenate([np.arange(0, 4), np.arange(boundary_row - 2, boundary_row + 3),
+                                     *[np.arange(r - 1, r + 2) for r in launch_rows],
                                      np.arange(w.rows - 4, w.rows), np.arange(0, w.rows, 97)]))
     idx = torch.from_numpy(rows).to(DEV)
     e_s, g_s = words(e.index_select(0, idx)), words(g.index_select(0, idx))
