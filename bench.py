@@ -164,7 +164,8 @@ def algorithmic_bytes_per_pass(w: workloads.Workload) -> int:
 def algorithmic_bytes_per_launch(w: workloads.Workload, padded: str = "compact") -> float:
     """The pass's bytes over its launches (an average where the last launch of a
     multi-launch pass is shorter)."""
-    return algorithmic_bytes_per_pass(w) / len(launch_pieces(w, padded))
+    total, n = algorithmic_bytes_per_pass(w), len(launch_pieces(w, padded))
+    return total // n if total % n == 0 else total / n
 
 
 def read_traffic(path: str = TRAFFIC_FILE, sources=ROPE_SOURCES, field="hbm_bytes_per_launch"):
@@ -345,7 +346,7 @@ def write_traffic_summary(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, 
         f"# on the {w.name} workload (T={w.T}, {w.valid_tokens} valid tokens, {seq}; Hq={w.Hq},",
         f"# Hkv={w.Hkv}, D={w.D}, {w.dtype}), one launch = forward or backward over Q and K"
         + ("." if len(launch_pieces(w)) == 1 else
-           f" of one of the {len(launch_pieces(w))} token ranges a pass is issued as."),
+           f"\n# of one of the {len(launch_pieces(w))} token ranges a pass is issued as."),
         "# Two rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE) over the same bench",
         "# command, each counter scaled by its reading for a plain 1 GiB device copy.",
         f"# commands: {command}",
