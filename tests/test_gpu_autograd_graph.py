@@ -258,10 +258,12 @@ def test_glu_autograd(lib, kind):
 
 def test_graph_capture_replay(lib):
     """RoPE forward + backward, a compact padded forward (with its cu_valid made by
-    the prefix kernel inside the graph) and SwiGLU forward + backward captured in
-    one HIP graph on static buffers; four replays, each after fresh inputs are
-    copied in and with eager launches and synchronizations between replays, each
-    equal bit for bit to eager launches on the same inputs."""
+    the prefix kernel inside the graph), SwiGLU forward + backward, and two calls
+    long enough to go out as several launches (a RoPE forward over 73000 tokens of
+    64 + 8 heads: 3 launches; a SwiGLU forward over 65536 x 8192: 2 launches)
+    captured in one HIP graph on static buffers; four replays, each after fresh
+    inputs are copied in and with eager launches and synchronizations between
+    replays, each equal bit for bit to eager launches on the same inputs."""
     rope, F = lib
     w = workloads.get("qwen3_4b_packed")
     cu = torch.from_numpy(w.cu_seqlens).to(DEV)
@@ -276,6 +278,13 @@ def test_graph_capture_replay(lib):
     ge, gg, gdh = (torch.empty((rows, cols), dtype=torch.bfloat16, device=DEV) for _ in range(3))
     gh = torch.empty_like(ge)
     gde, gdg = torch.empty_like(ge), torch.empty_like(ge)
+    LT, LHq, LHkv = 73000, 64, 8  # 657000 workgroups: 3 launches
+    lcu = torch.tensor([0, 20000, 24336, 50001, LT], dtype=torch.int32, device=DEV)
+    lq = torch.empty((LT, LHq, 128), dtype=torch.bfloat16, device=DEV)
+    lk = torch.empty((LT, LHkv, 128), dtype=torch.bfloat16, device=DEV)
+    Lr, Lc = 65536, 8192  # 65536 workgroups: 2 launches
+    le, lg = (torch.empty((Lr, Lc), dtype=torch.bfloat16, device=DEV) for _ in range(2))
+    lh = torch.empty_like(le)
 
     def body():
         rope.qk_fwd_(static["q"], static["k"], cu, w.theta)
@@ -284,6 +293,8 @@ def test_graph_capture_replay(lib):
         rope.glu_bwd("swiglu", gdh, ge, gg, de=gde, dg=gdg)
         rope.valid_prefix(cu_p, su_p, out=cv)
         rope.qk_apply_padded_(pq, pk, wp.theta, 1, cu_p, su_p, cv, wp.valid_tokens)
+        rope.qk_fwd_(lq, lk, lcu, 1e6)
+        rope.glu_fwd("swiglu", le, lg, out=lh)
 
     # warm up on a side stream, as torch requires before capture
     s = torch.cuda.Stream()
@@ -311,6 +322,10 @@ def test_graph_capture_replay(lib):
         pq.copy_(pin[0])
         pk.copy_(pin[1])
         cv.fill_(-1)
+        lin = [workloads.make_tensor(shape, 800 + 10 * rep + i, "bf16", device=DEV, chunk_rows=8192)
+               for i, shape in enumerate(((LT, LHq, 128), (LT, LHkv, 128), (Lr, Lc), (Lr, Lc)))]
+        for dst, src in zip((lq, lk, le, lg), lin):
+            dst.copy_(src)
         torch.cuda.synchronize()
         graph.replay()
         # eager reference on separate copies, with its own synchronizations
@@ -320,7 +335,12 @@ def test_graph_capture_replay(lib):
         h = rope.glu_fwd("swiglu", ins[0], ins[1])
         de, dg = rope.glu_bwd("swiglu", ins[2], ins[0], ins[1])
         rope.qk_apply_ex_(pin[0], pin[1], wp.theta, 1, cu_seqlens=cu_p, seqused=su_p)
+        rope.qk_fwd_(lin[0], lin[1], lcu, 1e6)
+        lh_eager = rope.glu_fwd("swiglu", lin[2], lin[3])
         torch.cuda.synchronize()
+        assert torch.equal(lq.view(torch.int16), lin[0].view(torch.int16)), rep
+        assert torch.equal(lk.view(torch.int16), lin[1].view(torch.int16)), rep
+        assert torch.equal(lh.view(torch.int16), lh_eager.view(torch.int16)), rep
         assert np.array_equal(bits16(pq), bits16(pin[0])) and np.array_equal(bits16(pk), bits16(pin[1]))
         assert cv.cpu().tolist() == rope.valid_prefix(cu_p, su_p).cpu().tolist()
         for n in static:
