@@ -708,8 +708,9 @@ uint32_t group_dynamic_lds(unsigned group_blocks, uint32_t gq, uint32_t gk) {
 // one token off that alignment lose most of the gain). Measured, bf16, D = 128,
 // one sequence, interleaved, bit-identical: 32 + 8 heads, 524288 tokens 1604.7 ->
 // 1576.2 us per pass (8 launches), 262144 tokens -1.1%, 131072 tokens -0.4%;
-// 64 + 8 heads, 262144 tokens 1514.6 -> 1427.9 us (8 launches). Not applied to
-// 16 + 8 heads, which measured 0.6-1.5% slower split at every piece count.
+// 64 + 8 heads, 262144 tokens 1514.6 -> 1427.9 us (8 launches); 40 + 8, 48 + 8 and
+// 32 + 4 heads 1.3-4.4% faster. Below the 4x ratio splitting measured neutral or
+// slower at every piece count (24 + 8, 16 + 8, 16 + 4, 8 + 8 heads: -0.7 to +6.9%).
 constexpr uint32_t kPieceBlocks = 327680;
 uint32_t group_piece_tokens(uint32_t rows, uint32_t gq, uint32_t gk) {
   const uint64_t blocks = (uint64_t)rows * (gq + gk);
