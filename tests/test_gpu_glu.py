@@ -295,6 +295,41 @@ def test_split_call_fused_layout(rope, kind):
     torch.cuda.empty_cache()
 
 
+def test_split_call_f32(rope):
+    """fp32 storage, a call of 65544 workgroups on the 32-bit path (8193 rows x 32768,
+    4-element chunks: 3 launches of 21848 workgroups): rows around
+    the launch boundaries and every 41st row against the oracle, forward and
+    backward, within the fp32 bound."""
+    rows, cols = 8193, 32768
+    print("[glu parity] split call f32", flush=True)
+    e = make((rows, cols), 9460, "f32")
+    g = make((rows, cols), 9461, "f32")
+    dh = make((rows, cols), 9462, "f32")
+    h = rope.glu_fwd("swiglu", e, g)
+    de, dg = rope.glu_bwd("swiglu", dh, e, g)
+    torch.cuda.synchronize()
+    chunks_per_row = cols // 4
+    edges = [21848 * 1024 * m // chunks_per_row for m in (1, 2)]
+    sel = np.unique(np.concatenate([np.arange(0, 2), np.arange(rows - 2, rows),
+                                    *[np.arange(r - 1, r + 2) for r in edges],
+                                    np.arange(0, rows, 41)]))
+    idx = torch.from_numpy(sel).to(DEV)
+    we, wg, wd = (words(t.index_select(0, idx)) for t in (e, g, dh))
+    ev = values(we, "f32")
+    ref_h = glu_oracle.fwd("swiglu", we, wg, "f32", NTHREADS)
+    ref_de, ref_dg = glu_oracle.bwd("swiglu", wd, we, wg, "f32", NTHREADS)
+    gv, dv = np.abs(values(wg, "f32")), np.abs(values(wd, "f32"))
+    grow = 1.0 + np.abs(ev)
+    assert_glu_parity("f32", words(h.index_select(0, idx)), ref_h, ev, "split-f32:h", "swiglu",
+                      gv * grow)
+    assert_glu_parity("f32", words(de.index_select(0, idx)), ref_de, ev, "split-f32:de", "swiglu",
+                      dv * gv * grow)
+    assert_glu_parity("f32", words(dg.index_select(0, idx)), ref_dg, ev, "split-f32:dg", "swiglu",
+                      dv * grow)
+    del e, g, dh, h, de, dg
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("dtype,cols,lead,in_pad,out_pad", [
     ("bf16", 1000, 0, 0, 0),     # 16-byte chunks, dense
     ("bf16", 1000, 4, 0, 0),     # base 8 bytes off: 8-byte chunks

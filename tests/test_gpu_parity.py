@@ -277,6 +277,8 @@ SPLIT_CASES = [  # name, T, Hq, Hkv, dtype, expected pieces
     ("scale", 73000, 64, 8, "bf16", [24336, 24336, 24328]),
     ("table", 73000, 64, 8, "bf16", [24336, 24336, 24328]),
     ("f32", 70000, 32, 8, "f32", [23336, 23336, 23328]),
+    ("f16", 73000, 64, 8, "f16", [24336, 24336, 24328]),
+    ("int64", 73000, 64, 8, "bf16", [24336, 24336, 24328]),
 ]
 
 
@@ -284,9 +286,9 @@ SPLIT_CASES = [  # name, T, Hq, Hkv, dtype, expected pieces
 def test_split_pass_position_sources(rope, case):
     """Passes issued as several launches with every position source (cu_seqlens alone,
     per-sequence offsets, explicit ids with untouched tokens, linear scaling, cos/sin
-    tables) and fp32 storage: the whole tensors bit for bit against the token kernel
-    (tokens_per_wave=1, never split) and sampled rows (both sides of every launch
-    boundary, random rows) against the oracle."""
+    tables), fp32 and fp16 storage, and 64-bit offsets forced: the whole tensors bit
+    for bit against the token kernel (tokens_per_wave=1, never split) and sampled
+    rows (both sides of every launch boundary, random rows) against the oracle."""
     import bench
     name, T, Hq, Hkv, dtype, expect = case
     D, theta = 128, 1e6
@@ -319,12 +321,15 @@ def test_split_pass_position_sources(rope, case):
     if name == "table":
         tables = rope.cos_sin_table(int(np.diff(cu_h).max()), D, theta, DEV)
 
+    index_mode = rope.INDEX_64 if name == "int64" else rope.INDEX_AUTO
+
     def apply(q, k, direction, **kw):
         if tables is not None and not kw:
             rope.qk_apply_table_(q, k, tables[0], tables[1], direction, cu_seqlens=cu)
             return
         rope.qk_apply_ex_(q, k, theta, direction, cu_seqlens=None if ids is not None else cu,
-                          seq_offsets=offs, position_ids=ids, pos_scale=scale, **kw)
+                          seq_offsets=offs, position_ids=ids, pos_scale=scale,
+                          index_mode=index_mode, **kw)
 
     for fwd, grad, direction in (("q", "k", 1), ("dq", "dk", -1)):
         a_q, a_k = src[fwd].clone(), src[grad].clone()
@@ -348,6 +353,31 @@ def test_split_pass_position_sources(rope, case):
             assert_parity(dtype, got, ref, x, touched, f"split-{name}:{what}")
         del a_q, a_k, b_q, b_k
     del src
+    torch.cuda.empty_cache()
+
+
+def test_split_pass_fused_qkv_views(rope):
+    """A pass issued as several launches on Q and K as strided views into fused QKV
+    outputs (73000 tokens, 64 + 8 heads: 3 launches): bit for bit the token kernel on
+    the same views, forward and backward, V untouched."""
+    T, Hq, Hkv, D = 73000, 64, 8, 128
+    print("[parity] split pass on fused qkv views", flush=True)
+    qkv0 = workloads.make_tensor((T, (Hq + 2 * Hkv) * D), 9800, "bf16", device=DEV, chunk_rows=8192)
+    cu = torch.tensor([0, 30000, 48670, T], dtype=torch.int32, device=DEV)
+    a, b = qkv0.clone(), qkv0.clone()
+    for direction in (1, -1):
+        qa, ka, _ = _qkv_views(a, Hq, Hkv, D)
+        qb, kb, _ = _qkv_views(b, Hq, Hkv, D)
+        rope.qk_apply_ex_(qa, ka, 1e6, direction, cu_seqlens=cu)
+        rope.qk_apply_ex_(qb, kb, 1e6, direction, cu_seqlens=cu, tokens_per_wave=1)
+        torch.cuda.synchronize()
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), direction
+        if direction == 1:  # the forward rotated the last token range too
+            assert not torch.equal(a[-100:].view(torch.int16), qkv0[-100:].view(torch.int16))
+    _, _, v = _qkv_views(a, Hq, Hkv, D)
+    _, _, v0 = _qkv_views(qkv0, Hq, Hkv, D)
+    assert torch.equal(v.view(torch.int16), v0.view(torch.int16))
+    del qkv0, a, b
     torch.cuda.empty_cache()
 
 
