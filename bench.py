@@ -1699,7 +1699,7 @@ def main():
                if w.seqused is not None else {}),
             "launch": "hip graph per step" if args.graph else "eager",
         },
-        "step_hbm_GBps": 2 * bpl * args.steps / elapsed / 1e9,
+        "step_hbm_GBps": 2 * bpp * args.steps / elapsed / 1e9,
         "roofline": {
             "bound": "hbm",
             "achieved": achieved,

@@ -37,6 +37,8 @@ def test_bench_json_contract():
     assert 0.3 < r["frac"] < 1.0 and r["frac_of_ceiling"] > 0
     assert r["launches_per_pass"] == 1
     assert abs(r["avg_pass_us"] - r["avg_launch_us"] * r["launches_per_pass"]) < 1e-6
+    step_gbps = 2 * r["bytes_per_launch"] * r["launches_per_pass"] / (d["ms_per_step"] * 1e-3) / 1e9
+    assert abs(d["step_hbm_GBps"] - step_gbps) < 1e-6 * step_gbps
     c = d["cpu_baseline"]
     assert c["kind"] == "oracle" and c["cores"] >= 1 and c["value"] > 0 and c["sample"]
     assert set(d["per_config"]) == {"tiny_packed", "qwen3_4b_packed", "qwen3_8b_packed",
@@ -49,3 +51,21 @@ def test_bench_json_contract():
     assert pad["padded_launch"] == "compact" and pad["kernel"] == "rope_qk_group_kernel"
     assert 0.8 < pad["t_over_packed"] < 1.5 and pad["valid_fraction"] < 0.6
     assert pad["seqused_kernel"] == "rope_qk_kernel" and pad["seqused_launch_us"] > 0
+
+
+def test_bench_json_multi_launch_pass():
+    """The 524288-token workload, whose passes are 8 launches: per-launch and per-pass
+    figures consistent with each other and with the step time, the traffic (when the
+    committed counter summary matches the sources) per launch."""
+    d = run_bench("--workload", "long_ctx_512k", "--configs", "none", "--steps", "3",
+                  "--warmup", "1", "--cpu-seconds", "0.5")
+    r = d["roofline"]
+    assert d["config"]["workload"] == "long_ctx_512k" and r["launches_per_pass"] == 8
+    assert r["bytes_per_launch"] == 524288 * 20480 // 8
+    assert abs(r["avg_pass_us"] - 8 * r["avg_launch_us"]) < 1e-6 * r["avg_pass_us"]
+    assert abs(r["achieved"] - r["bytes_per_launch"] / (r["avg_launch_us"] * 1e-6) / 1e9) < 1e-6
+    step_gbps = 2 * r["bytes_per_launch"] * 8 / (d["ms_per_step"] * 1e-3) / 1e9
+    assert abs(d["step_hbm_GBps"] - step_gbps) < 1e-6 * step_gbps
+    assert 0.5 < r["frac"] < 1.0
+    assert r["traffic"] is None or abs(r["traffic"] / r["bytes_per_launch"] - 1) < 0.01
+    assert d["cpu_baseline"]["kind"] == "oracle" and d["cpu_baseline"]["value"] > 0
