@@ -119,11 +119,38 @@ def rope_kernel_name(w: workloads.Workload, tokens_per_wave: int, padded: str = 
     """The kernel the library picks for this call: row groups by default and for
     compact padded launches, one wave per token when the caller sets tokens per wave
     or passes seqused to the plain entry points."""
-    nc = max(1, (w.D // 2) // (16 // w.elem_bytes))
-    if tokens_per_wave == 0 and 64 % nc == 0 and (w.seqused is None or
-                                                   compact_launch(w, padded)):
+    if tokens_per_wave == 0 and group_geometry(w) and (w.seqused is None or
+                                                       compact_launch(w, padded)):
         return "rope_qk_group_kernel"
     return "rope_qk_kernel"
+
+
+def chunk_bytes(w: workloads.Workload) -> int:
+    """The widest access (<= 16 bytes) that divides a half row, for contiguous
+    aligned tensors (the library also checks strides and addresses)."""
+    half_bytes = (w.D // 2) * w.elem_bytes
+    b = 16
+    while b > w.elem_bytes and half_bytes % b:
+        b //= 2
+    return b
+
+
+def chunks_per_half_row(w: workloads.Workload) -> int:
+    """nc: chunks per half row."""
+    return (w.D // 2) * w.elem_bytes // chunk_bytes(w)
+
+
+def group_geometry(w: workloads.Workload) -> bool:
+    """Whether the row-group kernel takes this head size: nc divides 64, or the
+    staged instance applies."""
+    return 64 % chunks_per_half_row(w) == 0 or staged_geometry(w)
+
+
+def staged_geometry(w: workloads.Workload) -> bool:
+    """The row-group kernel's STAGED instance: 16-byte chunks, at most 10 per half row
+    and not 8 (the library's staged_geometry)."""
+    nc = chunks_per_half_row(w)
+    return chunk_bytes(w) == 16 and nc <= 10 and nc != 8
 
 
 # The library's kPieceBlocks: a long pass of the row-group kernel on a Q-heavy shape
@@ -137,8 +164,7 @@ def group_pieces(rows: int, w: workloads.Workload) -> list:
     more, when Q holds at least 4x K's row groups, is issued as launches of about
     PIECE_BLOCKS workgroups over consecutive token ranges that start at multiples of
     8 tokens (the library's group_piece_tokens)."""
-    nc = max(1, (w.D // 2) // (16 // w.elem_bytes))
-    rows_per_group = 64 // nc
+    rows_per_group = 64 // chunks_per_half_row(w)
     gq, gk = -(-w.Hq // rows_per_group), -(-w.Hkv // rows_per_group)
     blocks = rows * (gq + gk)
     if gq < 4 * gk or blocks < 2 * PIECE_BLOCKS:
@@ -569,10 +595,8 @@ def expected_grid_threads(w: workloads.Workload, padded: str = "compact") -> lis
     """Work-items of each launch of the default pass for this workload: one 64-lane
     workgroup per (token, row group) for the row-group kernel (per rotated token only,
     for a compact padded launch), one 64-lane wave per token for the token kernel."""
-    vec = 16 // w.elem_bytes
-    nc = max(1, (w.D // 2) // vec)
     if rope_kernel_name(w, 0, padded) == "rope_qk_group_kernel":
-        rows = 64 // nc
+        rows = 64 // chunks_per_half_row(w)
         groups = -(-w.Hq // rows) + -(-w.Hkv // rows)
         return [t * groups * 64 for t in launch_pieces(w, padded)]
     return [w.T * 64]
@@ -907,13 +931,13 @@ def compare_unfused(rope, w, cu, su, sets, nsets, args, stream):
 def rope_kernel_instance(w: workloads.Workload, long_index: bool, padded: str = "compact") -> str:
     """Mangled-name fragment of the default path's kernel instance for this workload
     (kernel, dtype, chunk width, index width, no tables, and for the row-group kernel
-    whether the launch is compact), as rocprofv3 lists it."""
+    whether the launch is compact and whether it is staged), as rocprofv3 lists it."""
     base = rope_kernel_name(w, 0, padded)
     dt = {"bf16": "DF16b", "f16": "DF16_", "f32": "f"}[w.dtype]
-    vec = 16 // w.elem_bytes
+    vec = chunk_bytes(w) // w.elem_bytes
     name = f"{base}I{dt}Li{vec}ELb{int(long_index)}ELb0E"
     if base == "rope_qk_group_kernel":
-        name += f"Lb{int(compact_launch(w, padded))}E"
+        name += f"Lb{int(compact_launch(w, padded))}ELb{int(staged_geometry(w))}E"
     return name
 
 
@@ -921,10 +945,11 @@ def rope_instance_names(w: workloads.Workload, long_index: bool, padded: str = "
     """The instance's name as rocprofv3 may list it: mangled, or demangled."""
     base = rope_kernel_name(w, 0, padded)
     dt = {"bf16": "__bf16", "f16": "_Float16", "f32": "float"}[w.dtype]
-    vec = 16 // w.elem_bytes
+    vec = chunk_bytes(w) // w.elem_bytes
     flags = [str(long_index).lower(), "false"]
     if base == "rope_qk_group_kernel":
         flags.append(str(compact_launch(w, padded)).lower())
+        flags.append(str(staged_geometry(w)).lower())
     demangled = f"{base}<{dt}, {vec}, {', '.join(flags)}>"
     return rope_kernel_instance(w, long_index, padded), demangled
 
@@ -1563,8 +1588,7 @@ def main():
     if compact:
         cv, valid = padded_metadata(rope, w, cu, su)
     # launches per pass: one per call, or the row-group kernel's pieces of a long pass
-    nc = max(1, (w.D // 2) // (16 // w.elem_bytes))
-    if tpw != 0 or 64 % nc != 0 or (su is not None and not compact and pid is None):
+    if tpw != 0 or not group_geometry(w) or (su is not None and not compact and pid is None):
         pieces = len(shards) if shards is not None else 1
     elif shards is not None:
         pieces = sum(len(group_pieces(b - a, w)) for a, b, _, _ in shards)

@@ -23,8 +23,8 @@
 // Two kernels, one launch per pass either way (long passes of the row-group kernel
 // as several launches over consecutive token ranges, see group_piece_tokens):
 //  * rope_qk_group_kernel (the default): one 64-lane workgroup per (token, group
-//    of 64/nc head rows), Q's groups then K's; for D = 128 in bf16 a group is 8
-//    rows = 2 KB, one chunk pair per lane. The wave maps its token to (sequence,
+//    of 64/nc head rows, rounded down), Q's groups then K's; for D = 128 in bf16
+//    a group is 8 rows = 2 KB, one chunk pair per lane. The wave maps its token to (sequence,
 //    position) with a wave-uniform binary search over cu_seqlens [U-Pack],
 //    issues its row loads, evaluates the token's correctly rounded fp32 cos/sin
 //    (one frequency per lane) into a wave-local LDS table while the loads are in
@@ -32,7 +32,8 @@
 //  * rope_qk_kernel: a 64-lane wave walks whole tokens (tokens_per_wave of them),
 //    evaluating each token's cos/sin once and rotating its Q rows then its K rows
 //    [U-Group]; used for padded layouts (seqused), head sizes whose chunk count
-//    does not divide 64, and when the caller chooses tokens per wave.
+//    neither divides 64 nor comes in 16-byte chunks, and when the caller chooses
+//    tokens per wave.
 // Both take cos/sin from caller-supplied tables instead (TABLE instances) for
 // rope_qk_apply_table.
 #include <hip/hip_runtime.h>
@@ -431,11 +432,15 @@ __device__ inline void store_chunk_through(T* p, const Chunk<T, VEC>& c) {
 // token: more short-lived waves overlap the cos/sin evaluation of some with the
 // memory traffic of others, and each wave's reads and writes stay within 2 KB.
 // The cost is evaluating each (token, frequency) cos/sin once per row group of
-// the token instead of once per token. Requires nc to divide 64.
+// the token instead of once per token.
 // TABLE as in rope_qk_kernel. COMPACT: the grid covers only the rotated tokens of
 // a padded layout (compact_position), so no workgroup is spent on padded rows.
+// STAGED (see the address computation below): row halves that are not whole
+// 128-byte lines, e.g. D = 64, 80, 96 or 112 in 16-bit storage, move through LDS
+// in whole lines. Otherwise nc is a power of two, the groups are 64 / nc rows and
+// the lane split is a shift.
 //
-// Everything a wave needs before its first loads leads the argument list as 12
+// Everything a wave needs before its first loads leads the argument list as 13
 // plain dwords, which the library's build preloads into SGPRs at wave launch
 // (the compiler's kernel-argument preload), so the wave does not first wait for
 // a load of its arguments: q, k, cu_seqlens (cu_valid for COMPACT: the array the
@@ -444,18 +449,20 @@ __device__ inline void store_chunk_through(T* p, const Chunk<T, VEC>& c) {
 // the row groups per token (fast_div.h); geo = gq | gk << 13 | nc_shift << 26 |
 // position-source flags << 29 (kFlag*); heads = Hq | Hkv << 13 | (division
 // shift - 26) << 26; num_seqs; t_base, the token (COMPACT: rotated token) of
-// workgroup 0, nonzero when a long pass is issued as several launches. The rest (frequencies, sign, scale,
-// tables, the other position sources) comes from ps and p, read after the row
-// loads are issued or only on the paths that need them. D follows from nc_shift:
-// a half row is 2^nc_shift chunks of VEC elements.
+// workgroup 0, nonzero when a long pass is issued as several launches. The rest
+// (frequencies, sign, scale, tables, the other position sources) comes from ps
+// and p, read after the row loads are issued or only on the paths that need them.
+// Unless STAGED, D follows from nc_shift: a half row is 2^nc_shift chunks of VEC
+// elements.
 constexpr uint32_t kFlagIds = 1, kFlagOffsets = 2, kFlagSeqused = 4;
-template <typename T, int VEC, bool LONG_INDEX, bool TABLE, bool COMPACT>
+template <typename T, int VEC, bool LONG_INDEX, bool TABLE, bool COMPACT, bool STAGED>
 __global__ __launch_bounds__(64) void rope_qk_group_kernel(
     T* __restrict__ q, T* __restrict__ k, const int32_t* __restrict__ cu, uint32_t q_stride,
     uint32_t k_stride, uint32_t groups_mul, uint32_t geo, uint32_t heads, int32_t num_seqs,
     uint32_t t_base, const PosSource ps, const RopeParams p) {
   __shared__ float lds_cs[kMaxHalf];
   __shared__ float lds_sn[kMaxHalf];
+  extern __shared__ __align__(16) unsigned char lds_dyn[];  // the residency cap's reserve
   using C = Chunk<T, VEC>;
   const int lane = threadIdx.x;
   const uint32_t gq = geo & 0x1fffu;
@@ -470,16 +477,42 @@ __global__ __launch_bounds__(64) void rope_qk_group_kernel(
   const uint32_t tl = fastdiv::div(blockIdx.x, groups);
   const uint32_t g = blockIdx.x - tl * (gq + gk);
   const uint32_t t = t_base + tl;  // < 2^26; COMPACT: rotated-token index
-  const uint32_t half = (uint32_t)VEC << ns;
-  const uint32_t D = half << 1;
 
   // a4/a5 addresses: this lane's row of the group, and its chunk of the row
-  // halves. Lanes past the last row of a partial group address row 0 of the
-  // same token and tensor (valid memory) and store nothing.
-  const int c = lane & ((1 << ns) - 1);
+  // halves. Lanes past the last row of a partial group address row 0 of the same
+  // token and tensor (valid memory) and store nothing.
+  // STAGED: nc (16-byte chunks per half row) is at most 10 and not 8, so the row
+  // halves are not whole 128-byte lines (e.g. D = 64, 80, 96 or 112 in 16-bit
+  // storage; staged_geometry). A group is then 64 / nc rows (rounded down)
+  // and is moved as one contiguous range: two coalesced 16-byte loads and stores
+  // per lane cover its up to 128 chunks, and the (lo, hi) pairs meet in LDS, in the
+  // dynamic LDS the residency cap reserves anyway. Each lane's row and chunk in
+  // the group come from a division by nc (read from p).
   const bool in_q = g < gq;
-  const int r = (int)(((in_q ? g : g - gq) << (6 - ns)) + ((uint32_t)lane >> ns));
-  const bool live = r < (in_q ? Hq : Hkv);
+  uint32_t half;
+  int c, r;
+  bool live;
+  uint32_t rl = 0, g0 = 0, nchunks = 0;  // STAGED: lane's row in the group, first row, chunks
+  if constexpr (STAGED) {
+    const uint32_t nc = (uint32_t)p.nc;
+    const uint32_t rows = 64u / nc;
+    rl = (uint32_t)lane / nc;
+    c = lane - (int)(rl * nc);
+    half = (uint32_t)VEC * nc;
+    g0 = (in_q ? g : g - gq) * rows;
+    const uint32_t H = (uint32_t)(in_q ? Hq : Hkv);
+    const uint32_t grows = H - g0 < rows ? H - g0 : rows;  // >= 1
+    nchunks = grows * 2u * nc;                              // <= 128
+    r = (int)(g0 + rl);
+    live = rl < grows;
+  } else {
+    c = lane & ((1 << ns) - 1);
+    half = (uint32_t)VEC << ns;
+    r = (int)(((in_q ? g : g - gq) << (6 - ns)) + ((uint32_t)lane >> ns));
+    live = r < (in_q ? Hq : Hkv);
+  }
+  const uint32_t D = half << 1;
+  // !STAGED: this lane's chunk of its row; STAGED: the group's first element
   T* row = nullptr;
   if constexpr (!COMPACT) {
     row = in_q ? token_row0<T, LONG_INDEX>(q, (int64_t)t, (int64_t)q_stride)
@@ -487,7 +520,10 @@ __global__ __launch_bounds__(64) void rope_qk_group_kernel(
     // r * D < 2^22: a 24-bit multiply. (A full 32-bit multiply-add becomes
     // v_mad_u64_u32 with an undefined high addend, which the register allocator
     // may place in a register a pending load writes, forcing a wait on it.)
-    row += __umul24((uint32_t)(live ? r : 0), D) + (uint32_t)(c * VEC);
+    if constexpr (STAGED)
+      row += __umul24(g0, D);
+    else
+      row += __umul24((uint32_t)(live ? r : 0), D) + (uint32_t)(c * VEC);
   }
 
   // Vector-memory loads complete in issue order, so the order of issue below is
@@ -511,7 +547,10 @@ __global__ __launch_bounds__(64) void rope_qk_group_kernel(
     if (pos < 0) return;
     row = in_q ? token_row0<T, LONG_INDEX>(q, tok, (int64_t)q_stride)
                : token_row0<T, LONG_INDEX>(k, tok, (int64_t)k_stride);
-    row += __umul24((uint32_t)(live ? r : 0), D) + (uint32_t)(c * VEC);
+    if constexpr (STAGED)
+      row += __umul24(g0, D);
+    else
+      row += __umul24((uint32_t)(live ? r : 0), D) + (uint32_t)(c * VEC);
   } else {
     int32_t seq;
     // cu_seqlens alone (the packed default) from the preloaded arguments; the
@@ -520,8 +559,17 @@ __global__ __launch_bounds__(64) void rope_qk_group_kernel(
                      : resolve_position(ps, (int32_t)t, &seq);
   }
   if (pos < 0 || (TABLE && pos >= p.tab_rows)) return;
-  C lo = load_chunk<T, VEC>(row);
-  C hi = load_chunk<T, VEC>(row + half);
+  C lo, hi;
+  if constexpr (STAGED) {
+    // chunks lane and lane + 64 of the group; lanes past its end load its last chunk
+    const uint32_t i0 = (uint32_t)lane < nchunks ? (uint32_t)lane : nchunks - 1;
+    const uint32_t i1 = (uint32_t)lane + 64u < nchunks ? (uint32_t)lane + 64u : nchunks - 1;
+    lo = load_chunk<T, VEC>(row + i0 * VEC);
+    hi = load_chunk<T, VEC>(row + i1 * VEC);
+  } else {
+    lo = load_chunk<T, VEC>(row);
+    hi = load_chunk<T, VEC>(row + half);
+  }
   __builtin_amdgcn_sched_barrier(0);
 
   // a3: the token's fp32 cos/sin table
@@ -545,9 +593,35 @@ __global__ __launch_bounds__(64) void rope_qk_group_kernel(
       }
     }
   }
+  if constexpr (STAGED) {
+    C* stage = reinterpret_cast<C*>(lds_dyn);
+    if ((uint32_t)lane < nchunks) stage[lane] = lo;
+    if ((uint32_t)lane + 64u < nchunks) stage[lane + 64] = hi;
+  }
   wave_lds_sync();
 
-  if (live) {
+  if constexpr (STAGED) {
+    C* stage = reinterpret_cast<C*>(lds_dyn);
+    if (live) {
+      const uint32_t i = rl * 2u * (half / VEC) + (uint32_t)c;  // this lane's lo chunk
+      C a = stage[i];
+      C b = stage[i + half / VEC];
+      float cs[VEC], sn[VEC];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        cs[e] = lds_cs[c * VEC + e];
+        sn[e] = lds_sn[c * VEC + e];
+      }
+      rotate_chunk(a, b, cs, sn);
+      stage[i] = a;
+      stage[i + half / VEC] = b;
+    }
+    wave_lds_sync();
+    // written through to memory, whole lines of the group at a time
+    if ((uint32_t)lane < nchunks) store_chunk_through<T, VEC>(row + lane * VEC, stage[lane]);
+    if ((uint32_t)lane + 64u < nchunks)
+      store_chunk_through<T, VEC>(row + ((uint32_t)lane + 64u) * VEC, stage[lane + 64]);
+  } else if (live) {
     float cs[VEC], sn[VEC];
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
@@ -688,10 +762,26 @@ int32_t chunk_bytes(int32_t D, int32_t esize, const void* q, const void* k, int6
 // 182.2 us at 24; 65536 and 131072 tokens 2.5-3% better than 24).
 constexpr uint32_t kLdsPerCU = 160 * 1024;
 constexpr uint32_t kGroupStaticLds = 2 * kMaxHalf * sizeof(float);
+constexpr uint32_t kCap = 20, kCapLongQHeavy = 28;
 uint32_t group_dynamic_lds(unsigned group_blocks, uint32_t gq, uint32_t gk) {
   const bool long_q_heavy = group_blocks >= (1u << 18) && gq >= 8 * gk;
-  const uint32_t cap = long_q_heavy ? 28 : 20;
+  const uint32_t cap = long_q_heavy ? kCapLongQHeavy : kCap;
   return kLdsPerCU / cap - kGroupStaticLds;
+}
+// The STAGED instances keep a group's up to 128 16-byte chunks in that reserve.
+static_assert(kLdsPerCU / kCapLongQHeavy - kGroupStaticLds >= 128 * 16,
+              "the residency reserve must hold a staged group");
+
+// The row-group kernel's STAGED instance: 16-byte chunks and row halves that are
+// not whole 128-byte lines (nc other than 8), at most 10 chunks per half row so
+// that a group holds at least 6 rows. Measured against the token kernel
+// (interleaved, bit-identical, bf16, 16384 tokens): D = 32, 64, 80, 96, 112 and 160
+// 7-44% faster (D = 96: 96.8 -> 74.4 us per pass for 32 + 32 heads; D = 64: 48.1
+// -> 43.2), but D = 192 (12 chunks, 5 rows per group, 16 + 16 heads) 14% slower:
+// groups that short spend as much per workgroup on the search and cos/sin as a
+// full group for fewer bytes, so from 11 chunks on the token kernel runs.
+bool staged_geometry(int32_t nc, int32_t chunk_bytes) {
+  return chunk_bytes == 16 && nc <= 10 && nc != 8;
 }
 
 // Long passes as several launches. Workgroup i of a launch runs on XCC i mod 8
@@ -743,6 +833,28 @@ GroupScalars group_scalars(const RopeParams& p, const PosSource& ps) {
   return g;
 }
 
+// One launch of the row-group kernel over tokens [t0, t0 + n) (rotated-token
+// indices for a compact launch).
+template <typename T, int VEC, bool TABLE, bool STAGED>
+void launch_group(T* qt, T* kt, const PosSource& ps, const RopeParams& p, const GroupScalars& s,
+                  bool long_index, uint32_t lds, uint32_t t0, uint32_t n, hipStream_t stream) {
+  const dim3 grid(n * (p.gq + p.gk));
+#define ROPE_GROUP_ARGS                                                                     \
+  grid, dim3(64), lds, stream, qt, kt, s.search, s.q_stride, s.k_stride, s.groups_mul,    \
+      s.geo, s.heads, ps.num_seqs, t0, ps, p
+  if (!TABLE && ps.cu_valid != nullptr) {
+    if (long_index)
+      hipLaunchKernelGGL((rope_qk_group_kernel<T, VEC, true, false, true, STAGED>), ROPE_GROUP_ARGS);
+    else
+      hipLaunchKernelGGL((rope_qk_group_kernel<T, VEC, false, false, true, STAGED>), ROPE_GROUP_ARGS);
+  } else if (long_index) {
+    hipLaunchKernelGGL((rope_qk_group_kernel<T, VEC, true, TABLE, false, STAGED>), ROPE_GROUP_ARGS);
+  } else {
+    hipLaunchKernelGGL((rope_qk_group_kernel<T, VEC, false, TABLE, false, STAGED>), ROPE_GROUP_ARGS);
+  }
+#undef ROPE_GROUP_ARGS
+}
+
 template <typename T, int VEC, bool TABLE>
 int32_t launch_vec(void* q, void* k, const PosSource& ps, const RopeParams& p, bool long_index,
                    unsigned blocks, unsigned group_blocks, hipStream_t stream) {
@@ -751,25 +863,19 @@ int32_t launch_vec(void* q, void* k, const PosSource& ps, const RopeParams& p, b
   if (group_blocks > 0) {
     const uint32_t lds = group_dynamic_lds(group_blocks, p.gq, p.gk);
     const GroupScalars s = group_scalars(p, ps);
-    const uint32_t groups = p.gq + p.gk;
-    const uint32_t rows = group_blocks / groups;
+    const uint32_t rows = group_blocks / (p.gq + p.gk);
     const uint32_t piece = group_piece_tokens(rows, p.gq, p.gk);
+    const bool staged = staged_geometry(p.nc, VEC * (int)sizeof(T));
     for (uint32_t t0 = 0; t0 < rows; t0 += piece) {
       const uint32_t n = rows - t0 < piece ? rows - t0 : piece;
-#define ROPE_GROUP_ARGS                                                                     \
-  dim3(n * groups), dim3(64), lds, stream, qt, kt, s.search, s.q_stride, s.k_stride,      \
-      s.groups_mul, s.geo, s.heads, ps.num_seqs, t0, ps, p
-      if (!TABLE && ps.cu_valid != nullptr) {
-        if (long_index)
-          hipLaunchKernelGGL((rope_qk_group_kernel<T, VEC, true, false, true>), ROPE_GROUP_ARGS);
+      if constexpr (VEC * sizeof(T) == 16) {
+        if (staged)
+          launch_group<T, VEC, TABLE, true>(qt, kt, ps, p, s, long_index, lds, t0, n, stream);
         else
-          hipLaunchKernelGGL((rope_qk_group_kernel<T, VEC, false, false, true>), ROPE_GROUP_ARGS);
-      } else if (long_index) {
-        hipLaunchKernelGGL((rope_qk_group_kernel<T, VEC, true, TABLE, false>), ROPE_GROUP_ARGS);
+          launch_group<T, VEC, TABLE, false>(qt, kt, ps, p, s, long_index, lds, t0, n, stream);
       } else {
-        hipLaunchKernelGGL((rope_qk_group_kernel<T, VEC, false, TABLE, false>), ROPE_GROUP_ARGS);
+        launch_group<T, VEC, TABLE, false>(qt, kt, ps, p, s, long_index, lds, t0, n, stream);
       }
-#undef ROPE_GROUP_ARGS
       if (hipGetLastError() != hipSuccess) return ROPE_ELAUNCH;
     }
     return ROPE_OK;
@@ -802,8 +908,9 @@ int32_t auto_tokens_per_wave(int64_t T) {
 }
 
 // Grid of the row-group kernel (one 64-lane workgroup per token and row group), or
-// 0 when that kernel does not apply: the caller chose tokens per wave, nc does not
-// divide 64, a token stride is 2^32 elements or more, the grid would exceed the
+// 0 when that kernel does not apply: the caller chose tokens per wave, nc neither
+// divides 64 nor takes the staged instance (staged_geometry; wide: 16-byte
+// chunks), a token stride is 2^32 elements or more, the grid would exceed the
 // dispatch size limit, or seqused marks a padded layout and the launch is not
 // compact. In that last case many rows are skipped; the row-group kernel spends
 // one workgroup per row group of each skipped token where the token kernel spends
@@ -812,9 +919,11 @@ int32_t auto_tokens_per_wave(int64_t T) {
 // kernel. A compact launch (compact_rows >=
 // 0 rotated tokens, cu_valid given) covers only the rotated tokens and takes the
 // row-group kernel (28.3 against 32.0 us on that batch).
-int64_t group_grid(const RopeParams& p, bool geometry_chosen, bool padded, int64_t compact_rows) {
+int64_t group_grid(const RopeParams& p, bool geometry_chosen, bool padded, int64_t compact_rows,
+                   bool wide) {
   const bool compact = compact_rows >= 0;
-  if (geometry_chosen || (padded && !compact) || 64 % p.nc != 0) return 0;
+  if (geometry_chosen || (padded && !compact)) return 0;
+  if (64 % p.nc != 0 && !staged_geometry(p.nc, wide ? 16 : 0)) return 0;
   // token strides travel as 32-bit kernel arguments
   if (p.q_stride > (int64_t)UINT32_MAX || p.k_stride > (int64_t)UINT32_MAX) return 0;
   const int step_r = 64 / p.nc;
@@ -833,8 +942,8 @@ int32_t launch_typed(void* q, void* k, PosSource ps, RopeParams& p, int32_t byte
                      hipStream_t stream) {
   const int32_t vec = bytes / (int32_t)sizeof(T);
   p.nc = (p.D / 2) / vec;
-  const int64_t group_blocks =
-      group_grid(p, geometry_chosen, ps.seqused != nullptr, ps.cu_valid ? compact_rows : -1);
+  const int64_t group_blocks = group_grid(p, geometry_chosen, ps.seqused != nullptr,
+                                          ps.cu_valid ? compact_rows : -1, bytes == 16);
   if (group_blocks == 0) ps.cu_valid = nullptr;
   if (group_blocks > 0) {
     const int step_r = 64 / p.nc;

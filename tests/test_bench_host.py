@@ -13,7 +13,7 @@ import bench
 import workloads
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-GROUP = "_ZN12_GLOBAL__N_120rope_qk_group_kernelIDF16bLi8ELb0ELb0ELb0EEEvPT_S2_"
+GROUP = "_ZN12_GLOBAL__N_120rope_qk_group_kernelIDF16bLi8ELb0ELb0ELb0ELb0EEEvPT_S2_"
 COPY = "__amd_rocclr_copyBuffer"
 
 
@@ -106,22 +106,48 @@ def test_glu_pieces():
     assert bench.glu_pieces(workloads.glu_get("glu_long_512k")) == [32768] * 19
 
 
+def test_staged_head_sizes():
+    """Head sizes whose row halves are not whole 128-byte lines, or whose chunk count
+    is not a power of two, take the row-group kernel's staged instance when the
+    chunks are 16 bytes wide."""
+    for D, dtype, nc, staged in ((128, "bf16", 8, False), (256, "bf16", 16, False),
+                                 (512, "bf16", 32, False), (96, "bf16", 6, True),
+                                 (80, "bf16", 5, True), (112, "f16", 7, True),
+                                 (160, "bf16", 10, True), (64, "bf16", 4, True),
+                                 (48, "bf16", 3, True), (64, "f32", 8, False)):
+        w = _shape(1024, 32, 8, D=D, dtype=dtype)
+        assert bench.chunks_per_half_row(w) == nc and bench.chunk_bytes(w) == 16
+        assert bench.rope_kernel_name(w, 0) == "rope_qk_group_kernel"
+        assert bench.staged_geometry(w) is staged, D
+        assert bench.rope_kernel_instance(w, False).endswith(f"ELb{int(staged)}E")
+    # 11 chunks or more that do not divide 64 (too few rows per group): the token kernel
+    for D, dtype in ((192, "bf16"), (96, "f32"), (384, "bf16"), (176, "bf16")):
+        w = _shape(1024, 32, 8, D=D, dtype=dtype)
+        assert bench.rope_kernel_name(w, 0) == "rope_qk_kernel", D
+    # D = 100 in bf16: 100-byte half rows, 4-byte chunks, nc = 25: the token kernel
+    w = _shape(1024, 32, 8, D=100)
+    assert bench.chunk_bytes(w) == 4 and bench.rope_kernel_name(w, 0) == "rope_qk_kernel"
+    # D = 96 bf16, 32 + 8 heads: 10 rows per group, 4 + 1 groups per token
+    w = _shape(131072, 32, 8, D=96)
+    assert bench.expected_grid_threads(w) == [65536 * 5 * 64] * 2
+
+
 def test_kernel_instance_names():
     """The mangled-name fragments the summaries filter rocprofv3 records by."""
     w5, w2 = workloads.get("long_ctx_512k"), workloads.get("qwen3_4b_packed")
     assert bench.needs_long_index(w5) and not bench.needs_long_index(w2)
-    assert bench.rope_kernel_instance(w5, True) == "rope_qk_group_kernelIDF16bLi8ELb1ELb0ELb0E"
+    assert bench.rope_kernel_instance(w5, True) == "rope_qk_group_kernelIDF16bLi8ELb1ELb0ELb0ELb0E"
     assert bench.rope_kernel_instance(w2, False) in GROUP
     assert bench.rope_kernel_instance(workloads.get("tiny_packed"), False) == \
-        "rope_qk_group_kernelIfLi4ELb0ELb0ELb0E"
+        "rope_qk_group_kernelIfLi4ELb0ELb0ELb0ELb1E"  # D = 16 in fp32: staged
     pad = workloads.get("qwen3_8b_padded")
-    assert bench.rope_kernel_instance(pad, False) == "rope_qk_group_kernelIDF16bLi8ELb0ELb0ELb1E"
+    assert bench.rope_kernel_instance(pad, False) == "rope_qk_group_kernelIDF16bLi8ELb0ELb0ELb1ELb0E"
     assert bench.rope_kernel_instance(pad, False, "seqused") == \
         "rope_qk_kernelIDF16bLi8ELb0ELb0E"
     assert bench.rope_instance_names(pad, False)[1] == \
-        "rope_qk_group_kernel<__bf16, 8, false, false, true>"
+        "rope_qk_group_kernel<__bf16, 8, false, false, true, false>"
     assert bench.rope_instance_names(w5, True)[1] == \
-        "rope_qk_group_kernel<__bf16, 8, true, false, false>"
+        "rope_qk_group_kernel<__bf16, 8, true, false, false, false>"
 
 
 def test_linear_fit():
@@ -158,7 +184,7 @@ def test_traffic_summary_request_counts(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "traffic_path", lambda workload: str(out))
     w = workloads.get("long_ctx_512k")
     bpl = bench.algorithmic_bytes_per_launch(w)
-    long_k = "_ZN12_GLOBAL__N_120rope_qk_group_kernelIDF16bLi8ELb1ELb0ELb0EEEvPT_S2_"
+    long_k = "_ZN12_GLOBAL__N_120rope_qk_group_kernelIDF16bLi8ELb1ELb0ELb0ELb0EEEvPT_S2_"
     kib = 1024.0
     for name, ctr, val in (("cf", "FETCH_SIZE", 2 ** 30 / kib / 2), ("cw", "WRITE_SIZE", 2 ** 30 / kib)):
         _counter_csv(str(tmp_path / f"{name}.csv"), [(COPY, ctr, val)])
@@ -248,7 +274,7 @@ def test_trace_summary_multi_launch_pass(tmp_path, monkeypatch):
     eighth of the pass's, and tokens/s count whole passes."""
     out = tmp_path / "trace.txt"
     monkeypatch.setattr(bench, "trace_summary_path", lambda workload: str(out))
-    long_k = "_ZN12_GLOBAL__N_120rope_qk_group_kernelIDF16bLi8ELb1ELb0ELb0EEEvPT_S2_"
+    long_k = "_ZN12_GLOBAL__N_120rope_qk_group_kernelIDF16bLi8ELb1ELb0ELb0ELb0EEEvPT_S2_"
     durations = [200000] * 16
     _trace_csv(str(tmp_path / "t.csv"), durations, kernel=long_k, grid=65536 * 5 * 64)
     bench.write_trace_summary(str(tmp_path / "t.csv"), "long_ctx_512k", "cmd")

@@ -493,6 +493,14 @@ EDGE = [
     ("bf16_D12_vec2", [30, 3], 33, 2, 2, 12, "bf16", 1e4, None, None),
     ("bf16_D40_vec4", [30, 3], 33, 2, 2, 40, "bf16", 1e4, None, None),
     ("bf16_D80_nc5", [50, 70], 120, 3, 2, 80, "bf16", 1e6, None, None),
+    ("bf16_D96_nc6", [50, 70, 3], 123, 32, 8, 96, "bf16", 1e6, None, None),
+    ("f16_D112_nc7", [50, 1, 70], 121, 9, 7, 112, "f16", 1e6, None, None),
+    ("bf16_D160_nc10", [64, 57], 121, 13, 5, 160, "bf16", 1e6, None, None),
+    ("bf16_D192_nc12", [64, 57], 121, 6, 1, 192, "bf16", 1e6, None, None),
+    ("f32_D96_nc12", [30, 40], 70, 5, 3, 96, "f32", 1e4, None, None),
+    ("bf16_D48_nc3", [30, 40], 70, 22, 21, 48, "bf16", 1e4, None, None),
+    ("bf16_D320_nc20", [30, 40], 70, 7, 2, 320, "bf16", 1e6, None, None),
+    ("bf16_D100_vec2", [30, 40], 70, 3, 2, 100, "bf16", 1e4, None, None),
     ("bf16_D256", [50, 70], 120, 3, 2, 256, "bf16", 1e6, None, None),
     ("bf16_D512_max", [50, 70], 120, 2, 1, 512, "bf16", 1e6, None, None),
     ("f32_D64", [10, 100, 17], 127, 4, 4, 64, "f32", 1e4, None, None),
@@ -520,6 +528,116 @@ def test_edge_cases(rope, case):
             "dq": workloads.make_tensor((T, Hq, D), g + 2, dtype),
             "dk": workloads.make_tensor((T, Hkv, D), g + 3, dtype)}
     run_and_check(rope, label, host, cu, su, theta, dtype)
+
+
+STAGED_CASES = [  # (D, dtype, Hq, Hkv): row halves that are not whole 128-byte lines
+    (80, "bf16", 32, 32), (96, "bf16", 32, 8), (112, "f16", 28, 4), (160, "bf16", 16, 16),
+    (48, "bf16", 40, 8), (64, "bf16", 32, 8), (32, "bf16", 16, 4), (16, "f32", 8, 8),
+    (64, "f16", 12, 2),
+]
+
+
+@pytest.mark.parametrize("case", STAGED_CASES, ids=[f"{c[1]}_D{c[0]}" for c in STAGED_CASES])
+def test_staged_chunk_count(rope, case):
+    """The row-group kernel's staged instance (a group of 64 / nc rows, rounded down,
+    moved through LDS in whole lines): bit for bit the token kernel with cu_seqlens, per-sequence offsets,
+    explicit ids and cos/sin tables, forward and backward, on 3000 tokens in ragged
+    sequences; sampled rows against the oracle."""
+    D, dtype, Hq, Hkv = case
+    T = 3000
+    print(f"[parity] staged D={D} {dtype} {Hq}+{Hkv}", flush=True)
+    rng = np.random.default_rng(9900 + D)
+    cu_h = np.array([0, 1, 700, 701, 2100, 2999, T], dtype=np.int32)
+    cu = torch.from_numpy(cu_h).to(DEV)
+    offs_h = rng.integers(0, 100000, len(cu_h) - 1).astype(np.int32)
+    offs = torch.from_numpy(offs_h).to(DEV)
+    ids_h = rng.integers(0, 70000, T).astype(np.int32)
+    ids_h[rng.choice(T, 100, replace=False)] = -1
+    ids = torch.from_numpy(ids_h).to(DEV)
+    tables = rope.cos_sin_table(int(np.diff(cu_h).max()), D, 1e6, DEV)
+    src = {what: workloads.make_tensor((T, Hq if what in ("q", "dq") else Hkv, D), 9910 + i,
+                                       dtype, device=DEV)
+           for i, what in enumerate(("q", "k", "dq", "dk"))}
+    modes = {
+        "cu": dict(cu_seqlens=cu),
+        "offsets": dict(cu_seqlens=cu, seq_offsets=offs),
+        "ids": dict(position_ids=ids),
+    }
+    word = _word(src["q"].dtype)
+    tokens = np.unique(np.concatenate([np.arange(0, 8), np.arange(T - 8, T),
+                                       rng.integers(0, T, 200)]))
+    tok_dev = torch.from_numpy(tokens).to(DEV)
+    for fwd, grad, direction in (("q", "k", 1), ("dq", "dk", -1)):
+        for mode, kw in modes.items():
+            a_q, a_k = src[fwd].clone(), src[grad].clone()
+            b_q, b_k = src[fwd].clone(), src[grad].clone()
+            rope.qk_apply_ex_(a_q, a_k, 1e6, direction, **kw)
+            rope.qk_apply_ex_(b_q, b_k, 1e6, direction, tokens_per_wave=1, **kw)
+            torch.cuda.synchronize()
+            assert torch.equal(a_q.view(word), b_q.view(word)), (mode, fwd)
+            assert torch.equal(a_k.view(word), b_k.view(word)), (mode, grad)
+            for what, got_t in ((fwd, a_q), (grad, a_k)):
+                x = bits(src[what].index_select(0, tok_dev))
+                got = bits(got_t.index_select(0, tok_dev))
+                if mode == "ids":
+                    ref = oracle.rope_rows(x, tokens, None, 1e6, direction, dtype, None,
+                                           NTHREADS, position_ids=ids_h)
+                    touched = ids_h[tokens] >= 0
+                else:
+                    ref = oracle.rope_rows(x, tokens, cu_h, 1e6, direction, dtype, None,
+                                           NTHREADS, seq_offsets=offs_h if mode == "offsets"
+                                           else None)
+                    touched = np.ones(len(tokens), dtype=bool)
+                assert_parity(dtype, got, ref, x, touched, f"staged-{mode}:{what}")
+        t_q, t_k = src[fwd].clone(), src[grad].clone()
+        c_q, c_k = src[fwd].clone(), src[grad].clone()
+        rope.qk_apply_table_(t_q, t_k, tables[0], tables[1], direction, cu_seqlens=cu)
+        rope.qk_apply_ex_(c_q, c_k, 1e6, direction, cu_seqlens=cu)
+        torch.cuda.synchronize()
+        assert torch.equal(t_q.view(word), c_q.view(word)) and torch.equal(t_k.view(word),
+                                                                            c_k.view(word))
+
+
+def test_staged_chunk_count_split_and_compact(rope):
+    """The staged instance (D = 96, bf16, 32 + 8 heads: 10 rows per group, 4 + 1
+    groups per token) in a pass issued as 2 launches (131072 tokens) and in a compact
+    padded launch: bit for bit the token kernel, sampled rows against the oracle."""
+    import bench
+    T, Hq, Hkv, D = 131072, 32, 8, 96
+    w = workloads.Workload("g", 94, T, Hq, Hkv, D, "bf16", 1e6, np.array([0, T], dtype=np.int32))
+    assert bench.group_pieces(T, w) == [65536, 65536]
+    print("[parity] staged, split pass and compact launch", flush=True)
+    cu_h = np.array([0, 65530, 65541, T], dtype=np.int32)
+    cu = torch.from_numpy(cu_h).to(DEV)
+    q0 = workloads.make_tensor((T, Hq, D), 9950, "bf16", device=DEV, chunk_rows=32768)
+    k0 = workloads.make_tensor((T, Hkv, D), 9951, "bf16", device=DEV, chunk_rows=32768)
+    a_q, a_k, b_q, b_k = q0.clone(), k0.clone(), q0.clone(), k0.clone()
+    rope.qk_fwd_(a_q, a_k, cu, 1e6)
+    rope.qk_apply_ex_(b_q, b_k, 1e6, 1, cu_seqlens=cu, tokens_per_wave=1)
+    torch.cuda.synchronize()
+    assert torch.equal(a_q.view(torch.int16), b_q.view(torch.int16))
+    assert torch.equal(a_k.view(torch.int16), b_k.view(torch.int16))
+    tokens = np.unique(np.concatenate([np.arange(65520, 65560), np.arange(T - 8, T),
+                                       np.arange(0, T, 997)]))
+    tok_dev = torch.from_numpy(tokens).to(DEV)
+    x = bits(q0.index_select(0, tok_dev))
+    ref = oracle.rope_rows(x, tokens, cu_h, 1e6, 1, "bf16", None, NTHREADS)
+    assert_parity("bf16", bits(a_q.index_select(0, tok_dev)), ref, x,
+                  np.ones(len(tokens), bool), "staged-split:q")
+    # compact: 8 sequences padded to 16384 rows, 40-100% used
+    S, B = 16384, 8
+    cu_p = torch.from_numpy((np.arange(B + 1) * S).astype(np.int32)).to(DEV)
+    su_h = np.array([16384, 9000, 6554, 16000, 12345, 7000, 8191, 16383], dtype=np.int32)
+    su = torch.from_numpy(su_h).to(DEV)
+    cv = rope.valid_prefix(cu_p, su)
+    c_q, c_k, d_q, d_k = q0.clone(), k0.clone(), q0.clone(), k0.clone()
+    rope.qk_apply_padded_(c_q, c_k, 1e6, -1, cu_p, su, cv, int(su_h.sum()))
+    rope.qk_apply_ex_(d_q, d_k, 1e6, -1, cu_seqlens=cu_p, seqused=su)
+    torch.cuda.synchronize()
+    assert torch.equal(c_q.view(torch.int16), d_q.view(torch.int16))
+    assert torch.equal(c_k.view(torch.int16), d_k.view(torch.int16))
+    del q0, k0, a_q, a_k, b_q, b_k, c_q, c_k, d_q, d_k
+    torch.cuda.empty_cache()
 
 
 def test_misaligned_views(rope):
@@ -846,7 +964,7 @@ TABLE_CASES = [
     ("bf16", 128, 8, 2, 0, "cu"),
     ("bf16", 128, 8, 2, 3, "cu"),
     ("f16", 64, 3, 5, 1, "offsets"),
-    ("bf16", 80, 2, 1, 0, "ids"),       # 5 chunks per half row: the general lane layout
+    ("bf16", 80, 2, 1, 0, "ids"),       # 5 chunks per half row: the staged instance
     ("f32", 128, 5, 0, 0, "ids"),       # Q only
 ]
 
@@ -1081,7 +1199,8 @@ COMPACT_EDGE = [
     ("bf16_pos_scale", "bf16", 128, 4, 2, {"pos_scale": 4.0}),
     ("bf16_int64", "bf16", 128, 4, 2, {"index_mode": 2}),
     ("bf16_no_seqused", "bf16", 128, 4, 2, {"no_seqused": True}),
-    ("bf16_D80_fallback", "bf16", 80, 4, 2, {}),     # nc = 5: the seqused launch runs
+    ("bf16_D80_staged", "bf16", 80, 4, 2, {}),       # nc = 5: the staged row-group instance
+    ("bf16_D100_fallback", "bf16", 100, 4, 2, {}),   # 4-byte chunks, nc = 25: the seqused launch
     ("bf16_valid_short", "bf16", 128, 4, 2, {"valid_delta": -100}),
     ("bf16_cv_wide", "bf16", 128, 4, 2, {"cv_gap": 9}),
     ("bf16_cv_narrow", "bf16", 128, 4, 2, {"cv_gap": -9}),
@@ -1093,8 +1212,7 @@ def test_padded_compact_edges(rope, case):
     """Ragged padded batches through the compact launch against the oracle: empty
     sequences, seqused past the length, negative and zero seqused, a token tail,
     per-sequence offsets (some shifting positions out of range), position scaling,
-    forced 64-bit offsets, no seqused, a head size that falls back to the seqused
-    launch, and cu_valid / counts that do not match the layout (fewer tokens rotated,
+    forced 64-bit offsets, no seqused, a staged head size, one that falls back to the seqused launch, and cu_valid / counts that do not match the layout (fewer tokens rotated,
     never wrong ones)."""
     name, dtype, D, Hq, Hkv, extra = case
     B, S = 12, 96
