@@ -762,14 +762,19 @@ int32_t chunk_bytes(int32_t D, int32_t esize, const void* q, const void* k, int6
 // 182.2 us at 24; 65536 and 131072 tokens 2.5-3% better than 24).
 constexpr uint32_t kLdsPerCU = 160 * 1024;
 constexpr uint32_t kGroupStaticLds = 2 * kMaxHalf * sizeof(float);
-constexpr uint32_t kCap = 20, kCapLongQHeavy = 28;
-uint32_t group_dynamic_lds(unsigned group_blocks, uint32_t gq, uint32_t gk) {
+// The STAGED instances (staged_geometry) wait longer per workgroup (the pairs meet
+// in LDS) and do best with as many workgroups in flight as the waves allow: 32 per
+// CU, 12% faster than 20 for D = 96 and D = 160 (32 + 32 and 16 + 16 heads, 16384
+// tokens, 73.6 -> 64.7 and 63.8 -> 56.0 us), 9% for D = 80, 1% for D = 64 (24:
+// 2%).
+constexpr uint32_t kCap = 20, kCapLongQHeavy = 28, kCapStaged = 32;
+uint32_t group_dynamic_lds(unsigned group_blocks, uint32_t gq, uint32_t gk, bool staged) {
   const bool long_q_heavy = group_blocks >= (1u << 18) && gq >= 8 * gk;
-  const uint32_t cap = long_q_heavy ? kCapLongQHeavy : kCap;
+  const uint32_t cap = staged ? kCapStaged : long_q_heavy ? kCapLongQHeavy : kCap;
   return kLdsPerCU / cap - kGroupStaticLds;
 }
 // The STAGED instances keep a group's up to 128 16-byte chunks in that reserve.
-static_assert(kLdsPerCU / kCapLongQHeavy - kGroupStaticLds >= 128 * 16,
+static_assert(kLdsPerCU / kCapStaged - kGroupStaticLds >= 128 * 16,
               "the residency reserve must hold a staged group");
 
 // The row-group kernel's STAGED instance: 16-byte chunks and row halves that are
@@ -861,11 +866,11 @@ int32_t launch_vec(void* q, void* k, const PosSource& ps, const RopeParams& p, b
   T* qt = static_cast<T*>(q);
   T* kt = static_cast<T*>(k);
   if (group_blocks > 0) {
-    const uint32_t lds = group_dynamic_lds(group_blocks, p.gq, p.gk);
+    const bool staged = staged_geometry(p.nc, VEC * (int)sizeof(T));
+    const uint32_t lds = group_dynamic_lds(group_blocks, p.gq, p.gk, staged);
     const GroupScalars s = group_scalars(p, ps);
     const uint32_t rows = group_blocks / (p.gq + p.gk);
     const uint32_t piece = group_piece_tokens(rows, p.gq, p.gk);
-    const bool staged = staged_geometry(p.nc, VEC * (int)sizeof(T));
     for (uint32_t t0 = 0; t0 < rows; t0 += piece) {
       const uint32_t n = rows - t0 < piece ? rows - t0 : piece;
       if constexpr (VEC * sizeof(T) == 16) {
