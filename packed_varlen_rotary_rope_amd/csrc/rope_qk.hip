@@ -762,15 +762,21 @@ int32_t chunk_bytes(int32_t D, int32_t esize, const void* q, const void* k, int6
 // 182.2 us at 24; 65536 and 131072 tokens 2.5-3% better than 24).
 constexpr uint32_t kLdsPerCU = 160 * 1024;
 constexpr uint32_t kGroupStaticLds = 2 * kMaxHalf * sizeof(float);
-// The STAGED instances (staged_geometry) wait longer per workgroup (the pairs meet
-// in LDS) and do best with as many workgroups in flight as the waves allow: 32 per
-// CU, 12% faster than 20 for D = 96 and D = 160 (32 + 32 and 16 + 16 heads, 16384
-// tokens, 73.6 -> 64.7 and 63.8 -> 56.0 us), 9% for D = 80, 1% for D = 64 (24:
-// 2%).
+// Workgroups that take longer each want more of them in flight. The STAGED
+// instances (staged_geometry: the pairs meet in LDS) do best with as many as the
+// waves allow, 32 per CU: 12% faster than 20 for D = 96 and D = 160 (32 + 32 and
+// 16 + 16 heads, 16384 tokens, 73.6 -> 64.7 and 63.8 -> 56.0 us), 9% for D = 80,
+// 1% for D = 64. So do half rows of more than 64 frequencies, whose cos/sin take
+// each lane two or four evaluations: D = 256 at 28 (83.1 -> 80.5 us for 16 + 16
+// heads, 250.9 -> 240.6 for 16 + 8 heads over 65536 tokens), D = 512 at 32
+// (109.7 -> 99.7 us for 8 + 8 heads).
 constexpr uint32_t kCap = 20, kCapLongQHeavy = 28, kCapStaged = 32;
-uint32_t group_dynamic_lds(unsigned group_blocks, uint32_t gq, uint32_t gk, bool staged) {
+uint32_t group_dynamic_lds(unsigned group_blocks, uint32_t gq, uint32_t gk, bool staged,
+                           uint32_t half) {
   const bool long_q_heavy = group_blocks >= (1u << 18) && gq >= 8 * gk;
-  const uint32_t cap = staged ? kCapStaged : long_q_heavy ? kCapLongQHeavy : kCap;
+  const uint32_t cap = staged || half > 128 ? kCapStaged
+                       : half > 64 || long_q_heavy ? kCapLongQHeavy
+                                                   : kCap;
   return kLdsPerCU / cap - kGroupStaticLds;
 }
 // The STAGED instances keep a group's up to 128 16-byte chunks in that reserve.
@@ -867,7 +873,7 @@ int32_t launch_vec(void* q, void* k, const PosSource& ps, const RopeParams& p, b
   T* kt = static_cast<T*>(k);
   if (group_blocks > 0) {
     const bool staged = staged_geometry(p.nc, VEC * (int)sizeof(T));
-    const uint32_t lds = group_dynamic_lds(group_blocks, p.gq, p.gk, staged);
+    const uint32_t lds = group_dynamic_lds(group_blocks, p.gq, p.gk, staged, (uint32_t)p.D / 2);
     const GroupScalars s = group_scalars(p, ps);
     const uint32_t rows = group_blocks / (p.gq + p.gk);
     const uint32_t piece = group_piece_tokens(rows, p.gq, p.gk);
