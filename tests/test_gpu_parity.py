@@ -541,8 +541,8 @@ STAGED_CASES = [  # (D, dtype, Hq, Hkv): row halves that are not whole 128-byte 
 def test_staged_chunk_count(rope, case):
     """The row-group kernel's staged instance (a group of 64 / nc rows, rounded down,
     moved through LDS in whole lines): bit for bit the token kernel with cu_seqlens, per-sequence offsets,
-    explicit ids and cos/sin tables, forward and backward, on 3000 tokens in ragged
-    sequences; sampled rows against the oracle."""
+    explicit ids, 64-bit offsets forced and cos/sin tables, forward and backward, on
+    3000 tokens in ragged sequences; sampled rows against the oracle."""
     D, dtype, Hq, Hkv = case
     T = 3000
     print(f"[parity] staged D={D} {dtype} {Hq}+{Hkv}", flush=True)
@@ -562,6 +562,7 @@ def test_staged_chunk_count(rope, case):
         "cu": dict(cu_seqlens=cu),
         "offsets": dict(cu_seqlens=cu, seq_offsets=offs),
         "ids": dict(position_ids=ids),
+        "int64": dict(cu_seqlens=cu, index_mode=rope.INDEX_64),
     }
     word = _word(src["q"].dtype)
     tokens = np.unique(np.concatenate([np.arange(0, 8), np.arange(T - 8, T),
@@ -596,6 +597,29 @@ def test_staged_chunk_count(rope, case):
         torch.cuda.synchronize()
         assert torch.equal(t_q.view(word), c_q.view(word)) and torch.equal(t_k.view(word),
                                                                             c_k.view(word))
+
+
+def test_staged_on_fused_qkv_views(rope):
+    """The staged instance on Q and K as strided views into fused QKV outputs (D = 96,
+    bf16, 32 + 8 heads, 4000 tokens): bit for bit the token kernel on the same views,
+    forward and backward, V untouched."""
+    T, Hq, Hkv, D = 4000, 32, 8, 96
+    print("[parity] staged on fused qkv views", flush=True)
+    qkv0 = workloads.make_tensor((T, (Hq + 2 * Hkv) * D), 9960, "bf16", device=DEV)
+    cu = torch.tensor([0, 1500, 1501, T], dtype=torch.int32, device=DEV)
+    a, b = qkv0.clone(), qkv0.clone()
+    for direction in (1, -1):
+        qa, ka, _ = _qkv_views(a, Hq, Hkv, D)
+        qb, kb, _ = _qkv_views(b, Hq, Hkv, D)
+        rope.qk_apply_ex_(qa, ka, 1e6, direction, cu_seqlens=cu)
+        rope.qk_apply_ex_(qb, kb, 1e6, direction, cu_seqlens=cu, tokens_per_wave=1)
+        torch.cuda.synchronize()
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), direction
+        if direction == 1:
+            assert not torch.equal(a.view(torch.int16), qkv0.view(torch.int16))
+    _, _, v = _qkv_views(a, Hq, Hkv, D)
+    _, _, v0 = _qkv_views(qkv0, Hq, Hkv, D)
+    assert torch.equal(v.view(torch.int16), v0.view(torch.int16))
 
 
 def test_staged_chunk_count_split_and_compact(rope):
