@@ -153,6 +153,15 @@ def staged_geometry(w: workloads.Workload) -> bool:
     return chunk_bytes(w) == 16 and nc <= 10 and nc != 8
 
 
+def group_rows(nc: int) -> int:
+    """Head rows per row group (the library's group_rows): 64 // nc, rounded down to
+    whole 128-byte lines of 16-byte chunks (rows * nc a multiple of 4) when that keeps
+    at least 48 of the 64 lanes busy."""
+    r = 64 // nc
+    a = r & ~3 if nc & 1 else r & ~1 if (nc & 3) == 2 else r
+    return a if a * nc >= 48 else r
+
+
 # The library's kPieceBlocks: a long pass of the row-group kernel on a Q-heavy shape
 # is issued as consecutive launches of about this many workgroups.
 PIECE_BLOCKS = 327680
@@ -164,7 +173,7 @@ def group_pieces(rows: int, w: workloads.Workload) -> list:
     more, when Q holds at least 4x K's row groups, is issued as launches of about
     PIECE_BLOCKS workgroups over consecutive token ranges that start at multiples of
     8 tokens (the library's group_piece_tokens)."""
-    rows_per_group = 64 // chunks_per_half_row(w)
+    rows_per_group = group_rows(chunks_per_half_row(w))
     gq, gk = -(-w.Hq // rows_per_group), -(-w.Hkv // rows_per_group)
     blocks = rows * (gq + gk)
     if gq < 4 * gk or blocks < 2 * PIECE_BLOCKS:
@@ -596,7 +605,7 @@ def expected_grid_threads(w: workloads.Workload, padded: str = "compact") -> lis
     workgroup per (token, row group) for the row-group kernel (per rotated token only,
     for a compact padded launch), one 64-lane wave per token for the token kernel."""
     if rope_kernel_name(w, 0, padded) == "rope_qk_group_kernel":
-        rows = 64 // chunks_per_half_row(w)
+        rows = group_rows(chunks_per_half_row(w))
         groups = -(-w.Hq // rows) + -(-w.Hkv // rows)
         return [t * groups * 64 for t in launch_pieces(w, padded)]
     return [w.T * 64]

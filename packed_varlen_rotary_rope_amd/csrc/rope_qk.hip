@@ -421,8 +421,25 @@ __device__ inline void store_chunk_through(T* p, const Chunk<T, VEC>& c) {
   }
 }
 
+// Rows per group for nc chunks per half row: the 64 / nc rows whose chunk pairs
+// the 64 lanes hold, rounded down to a group of whole 128-byte lines when at least
+// 48 lanes stay busy (16-byte chunks, the one size whose groups can end inside a
+// line: rows * nc a multiple of 4). A group that
+// ends inside a line shares it with the next group, which runs on another XCC, and
+// the two partial writes of that line cost more than the idle lanes: D = 112 in
+// bf16 (nc = 7) as 8 rows of 224 bytes (14 lines) instead of 9 ran 10-21% faster
+// (interleaved, bit-identical; 32 + 32 heads, 16384 tokens: 92.2 -> 72.7 us per
+// pass), D = 48 (nc = 3, 20 rows instead of 21) 4-11%. For nc = 9 (D = 144) the
+// aligned group is 4 rows, 36 busy lanes, which measured 18-20% slower than 7.
+// Other nc give whole lines already.
+__host__ __device__ inline uint32_t group_rows(uint32_t nc) {
+  const uint32_t r = 64u / nc;
+  const uint32_t a = (nc & 1u) != 0 ? r & ~3u : (nc & 3u) == 2u ? r & ~1u : r;
+  return a * nc >= 48u ? a : r;
+}
+
 // ---- the default geometry: one wave per (token, row group) --------------------------
-// A 64-lane workgroup owns one group of step_r = 64 / nc consecutive head rows of
+// A 64-lane workgroup owns one group of group_rows(nc) consecutive head rows of
 // one token (Q rows first, then K rows; the last group of each may be partial).
 // For D = 128 in bf16 that is 8 rows = 2 KB, one 16-byte lo and one 16-byte hi
 // chunk per lane. The wave issues its loads first, then evaluates the token's
@@ -483,7 +500,7 @@ __global__ __launch_bounds__(64) void rope_qk_group_kernel(
   // token and tensor (valid memory) and store nothing.
   // STAGED: nc (16-byte chunks per half row) is at most 10 and not 8, so the row
   // halves are not whole 128-byte lines (e.g. D = 64, 80, 96 or 112 in 16-bit
-  // storage; staged_geometry). A group is then 64 / nc rows (rounded down)
+  // storage; staged_geometry). A group is then group_rows(nc) rows
   // and is moved as one contiguous range: two coalesced 16-byte loads and stores
   // per lane cover its up to 128 chunks, and the (lo, hi) pairs meet in LDS, in the
   // dynamic LDS the residency cap reserves anyway. Each lane's row and chunk in
@@ -495,7 +512,7 @@ __global__ __launch_bounds__(64) void rope_qk_group_kernel(
   uint32_t rl = 0, g0 = 0, nchunks = 0;  // STAGED: lane's row in the group, first row, chunks
   if constexpr (STAGED) {
     const uint32_t nc = (uint32_t)p.nc;
-    const uint32_t rows = 64u / nc;
+    const uint32_t rows = group_rows(nc);
     rl = (uint32_t)lane / nc;
     c = lane - (int)(rl * nc);
     half = (uint32_t)VEC * nc;
@@ -937,7 +954,7 @@ int64_t group_grid(const RopeParams& p, bool geometry_chosen, bool padded, int64
   if (64 % p.nc != 0 && !staged_geometry(p.nc, wide ? 16 : 0)) return 0;
   // token strides travel as 32-bit kernel arguments
   if (p.q_stride > (int64_t)UINT32_MAX || p.k_stride > (int64_t)UINT32_MAX) return 0;
-  const int step_r = 64 / p.nc;
+  const int step_r = (int)group_rows((uint32_t)p.nc);
   const int64_t groups = (p.Hq + step_r - 1) / step_r + (p.Hkv + step_r - 1) / step_r;
   const int64_t blocks = (compact ? compact_rows : p.T) * groups;
   // < 2^26 workgroups: the dispatch limit, and the range of fastdiv::div
@@ -957,7 +974,7 @@ int32_t launch_typed(void* q, void* k, PosSource ps, RopeParams& p, int32_t byte
                                           ps.cu_valid ? compact_rows : -1, bytes == 16);
   if (group_blocks == 0) ps.cu_valid = nullptr;
   if (group_blocks > 0) {
-    const int step_r = 64 / p.nc;
+    const int step_r = (int)group_rows((uint32_t)p.nc);
     p.gq = (uint32_t)((p.Hq + step_r - 1) / step_r);
     p.gk = (uint32_t)((p.Hkv + step_r - 1) / step_r);
     p.nc_shift = 0;

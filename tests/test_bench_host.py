@@ -132,6 +132,38 @@ def test_staged_head_sizes():
     assert bench.expected_grid_threads(w) == [65536 * 5 * 64] * 2
 
 
+def test_group_rows_whole_lines(tmp_path):
+    """Rows per row group: 64 // nc rounded down so that a group of 16-byte chunks
+    spans whole 128-byte lines, when at least 48 lanes stay busy. The library's
+    group_rows (compiled from its source with g++), bench.py's mirror and a brute
+    force over the definition agree for every nc; D = 112 and 48 take aligned groups,
+    D = 144 keeps 7 rows."""
+    def brute(nc):
+        whole = [r for r in range(64 // nc, 0, -1) if (r * nc * 32) % 128 == 0]
+        return whole[0] if whole and whole[0] * nc >= 48 else 64 // nc
+    src_text = open(os.path.join(ROOT, "packed_varlen_rotary_rope_amd", "csrc", "rope_qk.hip")).read()
+    i = src_text.index("__host__ __device__ inline uint32_t group_rows(uint32_t nc) {")
+    j = src_text.index("\n}\n", i) + 3
+    src = tmp_path / "group_rows.cpp"
+    src.write_text("#include <cstdint>\n#include <cstdio>\n#define __host__\n#define __device__\n"
+                   + src_text[i:j]
+                   + "int main() { for (uint32_t nc = 1; nc <= 64; ++nc) printf(\"%u\\n\", group_rows(nc)); }\n")
+    exe = tmp_path / "group_rows"
+    subprocess.run(["g++", "-O2", "-std=c++17", "-o", str(exe), str(src)], check=True)
+    lib = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True,
+                                          check=True).stdout.split()]
+    for nc in range(1, 65):
+        assert lib[nc - 1] == bench.group_rows(nc) == brute(nc), nc
+    assert [bench.group_rows(nc) for nc in (3, 5, 6, 7, 9, 10)] == [20, 12, 10, 8, 7, 6]
+    for nc in (1, 2, 4, 8, 16, 32, 64):
+        assert bench.group_rows(nc) == 64 // nc
+    # D = 112 bf16, 32 + 8 heads: 8 rows per group, 4 + 1 groups per token
+    assert bench.expected_grid_threads(_shape(1000, 32, 8, D=112)) == [1000 * 5 * 64]
+    # D = 48, 40 + 8 heads: 20 rows, 2 + 1 groups; D = 144, 14 + 2 heads: 7 rows, 2 + 1
+    assert bench.expected_grid_threads(_shape(1000, 40, 8, D=48)) == [1000 * 3 * 64]
+    assert bench.expected_grid_threads(_shape(1000, 14, 2, D=144)) == [1000 * 3 * 64]
+
+
 def test_kernel_instance_names():
     """The mangled-name fragments the summaries filter rocprofv3 records by."""
     w5, w2 = workloads.get("long_ctx_512k"), workloads.get("qwen3_4b_packed")

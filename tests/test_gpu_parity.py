@@ -533,16 +533,17 @@ def test_edge_cases(rope, case):
 STAGED_CASES = [  # (D, dtype, Hq, Hkv): row halves that are not whole 128-byte lines
     (80, "bf16", 32, 32), (96, "bf16", 32, 8), (112, "f16", 28, 4), (160, "bf16", 16, 16),
     (48, "bf16", 40, 8), (64, "bf16", 32, 8), (32, "bf16", 16, 4), (16, "f32", 8, 8),
-    (64, "f16", 12, 2),
+    (64, "f16", 12, 2), (112, "bf16", 20, 4), (48, "f16", 27, 3), (144, "bf16", 14, 2),
 ]
 
 
 @pytest.mark.parametrize("case", STAGED_CASES, ids=[f"{c[1]}_D{c[0]}" for c in STAGED_CASES])
 def test_staged_chunk_count(rope, case):
-    """The row-group kernel's staged instance (a group of 64 / nc rows, rounded down,
-    moved through LDS in whole lines): bit for bit the token kernel with cu_seqlens, per-sequence offsets,
-    explicit ids, 64-bit offsets forced and cos/sin tables, forward and backward, on
-    3000 tokens in ragged sequences; sampled rows against the oracle."""
+    """The row-group kernel's staged instance (a group of group_rows(nc) rows, e.g. 8
+    for D = 112, 20 for D = 48, 7 for D = 144, moved through LDS in whole lines): bit
+    for bit the token kernel with cu_seqlens, per-sequence offsets, explicit ids,
+    64-bit offsets forced and cos/sin tables, forward and backward, on 3000 tokens in
+    ragged sequences; sampled rows against the oracle."""
     D, dtype, Hq, Hkv = case
     T = 3000
     print(f"[parity] staged D={D} {dtype} {Hq}+{Hkv}", flush=True)
