@@ -23,8 +23,9 @@
 // Two kernels, one launch per pass either way (long passes of the row-group kernel
 // as several launches over consecutive token ranges, see group_piece_tokens):
 //  * rope_qk_group_kernel (the default): one 64-lane workgroup per (token, group
-//    of 64/nc head rows, rounded down), Q's groups then K's; for D = 128 in bf16
-//    a group is 8 rows = 2 KB, one chunk pair per lane. The wave maps its token to (sequence,
+//    of group_rows(nc) head rows: 64 / nc, rounded down, to whole 128-byte lines
+//    where that keeps 48 lanes busy), Q's groups then K's; for D = 128 in bf16 a
+//    group is 8 rows = 2 KB, one chunk pair per lane. The wave maps its token to (sequence,
 //    position) with a wave-uniform binary search over cu_seqlens [U-Pack],
 //    issues its row loads, evaluates the token's correctly rounded fp32 cos/sin
 //    (one frequency per lane) into a wave-local LDS table while the loads are in
@@ -32,8 +33,8 @@
 //  * rope_qk_kernel: a 64-lane wave walks whole tokens (tokens_per_wave of them),
 //    evaluating each token's cos/sin once and rotating its Q rows then its K rows
 //    [U-Group]; used for padded layouts (seqused), head sizes whose chunk count
-//    neither divides 64 nor comes in 16-byte chunks, and when the caller chooses
-//    tokens per wave.
+//    neither divides 64 nor fits the staged instance (16-byte chunks, at most 10
+//    per half row), and when the caller chooses tokens per wave.
 // Both take cos/sin from caller-supplied tables instead (TABLE instances) for
 // rope_qk_apply_table.
 #include <hip/hip_runtime.h>
