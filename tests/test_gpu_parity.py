@@ -623,15 +623,17 @@ def test_staged_on_fused_qkv_views(rope):
     assert torch.equal(v.view(torch.int16), v0.view(torch.int16))
 
 
-def test_staged_chunk_count_split_and_compact(rope):
-    """The staged instance (D = 96, bf16, 32 + 8 heads: 10 rows per group, 4 + 1
-    groups per token) in a pass issued as 2 launches (131072 tokens) and in a compact
-    padded launch: bit for bit the token kernel, sampled rows against the oracle."""
+@pytest.mark.parametrize("D", [96, 112])
+def test_staged_chunk_count_split_and_compact(rope, D):
+    """The staged instance (bf16, 32 + 8 heads; D = 96: 10 rows per group, D = 112:
+    8 rows, whole lines; 4 + 1 groups per token either way) in a pass issued as 2
+    launches (131072 tokens) and in a compact padded launch: bit for bit the token
+    kernel, sampled rows against the oracle."""
     import bench
-    T, Hq, Hkv, D = 131072, 32, 8, 96
+    T, Hq, Hkv = 131072, 32, 8
     w = workloads.Workload("g", 94, T, Hq, Hkv, D, "bf16", 1e6, np.array([0, T], dtype=np.int32))
     assert bench.group_pieces(T, w) == [65536, 65536]
-    print("[parity] staged, split pass and compact launch", flush=True)
+    print(f"[parity] staged D={D}, split pass and compact launch", flush=True)
     cu_h = np.array([0, 65530, 65541, T], dtype=np.int32)
     cu = torch.from_numpy(cu_h).to(DEV)
     q0 = workloads.make_tensor((T, Hq, D), 9950, "bf16", device=DEV, chunk_rows=32768)
