@@ -162,6 +162,17 @@ def group_rows(nc: int) -> int:
     return a if a * nc >= 48 else r
 
 
+def group_steps(w: workloads.Workload) -> int:
+    """Row steps per row-group workgroup (the library's group_steps): 2 for half rows
+    of more than 128 elements in 16-byte chunks (D = 512), else 1."""
+    return 2 if chunk_bytes(w) == 16 and w.D // 2 > 128 else 1
+
+
+def rows_per_workgroup(w: workloads.Workload) -> int:
+    """Head rows one row-group workgroup rotates: group_rows x group_steps."""
+    return group_rows(chunks_per_half_row(w)) * group_steps(w)
+
+
 # The library's kPieceBlocks: a long pass of the row-group kernel on a Q-heavy shape
 # is issued as consecutive launches of about this many workgroups.
 PIECE_BLOCKS = 327680
@@ -173,7 +184,7 @@ def group_pieces(rows: int, w: workloads.Workload) -> list:
     more, when Q holds at least 4x K's row groups, is issued as launches of about
     PIECE_BLOCKS workgroups over consecutive token ranges that start at multiples of
     8 tokens (the library's group_piece_tokens)."""
-    rows_per_group = group_rows(chunks_per_half_row(w))
+    rows_per_group = rows_per_workgroup(w)
     gq, gk = -(-w.Hq // rows_per_group), -(-w.Hkv // rows_per_group)
     blocks = rows * (gq + gk)
     if gq < 4 * gk or blocks < 2 * PIECE_BLOCKS:
@@ -605,7 +616,7 @@ def expected_grid_threads(w: workloads.Workload, padded: str = "compact") -> lis
     workgroup per (token, row group) for the row-group kernel (per rotated token only,
     for a compact padded launch), one 64-lane wave per token for the token kernel."""
     if rope_kernel_name(w, 0, padded) == "rope_qk_group_kernel":
-        rows = group_rows(chunks_per_half_row(w))
+        rows = rows_per_workgroup(w)
         groups = -(-w.Hq // rows) + -(-w.Hkv // rows)
         return [t * groups * 64 for t in launch_pieces(w, padded)]
     return [w.T * 64]
@@ -940,13 +951,15 @@ def compare_unfused(rope, w, cu, su, sets, nsets, args, stream):
 def rope_kernel_instance(w: workloads.Workload, long_index: bool, padded: str = "compact") -> str:
     """Mangled-name fragment of the default path's kernel instance for this workload
     (kernel, dtype, chunk width, index width, no tables, and for the row-group kernel
-    whether the launch is compact and whether it is staged), as rocprofv3 lists it."""
+    whether the launch is compact, whether it is staged and its row steps), as
+    rocprofv3 lists it."""
     base = rope_kernel_name(w, 0, padded)
     dt = {"bf16": "DF16b", "f16": "DF16_", "f32": "f"}[w.dtype]
     vec = chunk_bytes(w) // w.elem_bytes
     name = f"{base}I{dt}Li{vec}ELb{int(long_index)}ELb0E"
     if base == "rope_qk_group_kernel":
-        name += f"Lb{int(compact_launch(w, padded))}ELb{int(staged_geometry(w))}E"
+        name += (f"Lb{int(compact_launch(w, padded))}ELb{int(staged_geometry(w))}E"
+                 f"Li{group_steps(w)}E")
     return name
 
 
@@ -959,6 +972,7 @@ def rope_instance_names(w: workloads.Workload, long_index: bool, padded: str = "
     if base == "rope_qk_group_kernel":
         flags.append(str(compact_launch(w, padded)).lower())
         flags.append(str(staged_geometry(w)).lower())
+        flags.append(str(group_steps(w)))
     demangled = f"{base}<{dt}, {vec}, {', '.join(flags)}>"
     return rope_kernel_instance(w, long_index, padded), demangled
 
@@ -1141,6 +1155,88 @@ def size_sweep(rope, dev, n_steps: int) -> dict:
         out[f"fit_{key}"] = {"t0_us": t0, "us_per_token": b,
                              "asymptotic_GBps": per_token / (b * 1e-6) / 1e9}
     return out
+
+
+# Head shapes beside the Qwen3 batches: (Hq, Hkv, D, dtype), one sequence of
+# HEAD_SHAPE_TOKENS tokens each. D = 128 with the Qwen3-1.7B (16 + 8), 4B/8B (32 + 8),
+# 14B (40 + 8) and 32B (64 + 8) head counts; the staged head sizes (half rows that
+# are not whole 128-byte lines), D = 192 on the token kernel, the long half rows
+# D = 256 and 512, and the other storage types.
+HEAD_SHAPES = [
+    (16, 8, 128, "bf16"), (32, 8, 128, "bf16"), (40, 8, 128, "bf16"), (64, 8, 128, "bf16"),
+    (32, 32, 32, "bf16"), (32, 32, 48, "bf16"), (32, 32, 64, "bf16"), (64, 8, 64, "bf16"),
+    (32, 32, 80, "bf16"), (32, 32, 96, "bf16"), (32, 8, 96, "bf16"), (32, 32, 112, "bf16"),
+    (32, 8, 112, "bf16"), (16, 16, 144, "bf16"), (16, 16, 160, "bf16"), (16, 16, 192, "bf16"),
+    (16, 16, 256, "bf16"), (16, 8, 256, "bf16"), (8, 8, 512, "bf16"),
+    (32, 8, 128, "f16"), (32, 8, 128, "f32"), (32, 8, 64, "f32"),
+]
+HEAD_SHAPE_TOKENS = 16384
+HEAD_SHAPES_FILE = os.path.join(ROOT, "profiles", "rope_qk_head_shapes.txt")
+
+
+def head_shape_workload(Hq: int, Hkv: int, D: int, dtype: str,
+                        T: int = HEAD_SHAPE_TOKENS) -> workloads.Workload:
+    """One sequence of T tokens of the given head shape, theta = 1e6."""
+    return workloads.Workload(f"h{Hq}x{Hkv}_d{D}_{dtype}", 92, T, Hq, Hkv, D, dtype, 1e6,
+                              np.array([0, T], dtype=np.int32),
+                              description=f"one sequence, T={T}, {Hq}+{Hkv} heads, D={D}")
+
+
+def head_geometry(w: workloads.Workload) -> str:
+    """The default launch's geometry for w: the row-group kernel (staged or not) with
+    its rows per group, or the token kernel."""
+    if rope_kernel_name(w, 0) != "rope_qk_group_kernel":
+        return "token kernel"
+    kind = "staged" if staged_geometry(w) else "row-group"
+    steps = group_steps(w)
+    rows = group_rows(chunks_per_half_row(w))
+    return f"{kind}, {rows} rows" + (f" x {steps}" if steps > 1 else "")
+
+
+def head_shape_survey(rope, dev, n_steps: int) -> dict:
+    """Region-timed default launches (forward + backward per step, rotating buffer
+    sets) and the torch in-place reference for every shape of HEAD_SHAPES."""
+    rows = []
+    for Hq, Hkv, D, dtype in HEAD_SHAPES:
+        w = head_shape_workload(Hq, Hkv, D, dtype)
+        print(f"[head shapes] {w.name}", file=sys.stderr, flush=True)
+        r = time_workload(rope, w, dev, n_steps, 20)
+        rows.append({"Hq": Hq, "Hkv": Hkv, "D": D, "dtype": dtype, "T": w.T,
+                     "geometry": head_geometry(w), "launches_per_pass": r["launches_per_pass"],
+                     "avg_pass_us": r["avg_pass_us"], "GBps": r["GBps"], "frac": r["frac"],
+                     "torch_inplace_us": r["torch_inplace_us"],
+                     "frac_of_ceiling": r["frac_of_ceiling"]})
+    return {"head_shapes": f"RoPE pass per head shape (one sequence of {HEAD_SHAPE_TOKENS} "
+                           "tokens, theta=1e6)", "rows": rows}
+
+
+def write_head_shapes_summary(json_path: str, command: str) -> None:
+    """profiles/rope_qk_head_shapes.txt from the JSON line of bench.py --head-shapes."""
+    with open(json_path) as fh:
+        js = json.loads([ln for ln in fh if ln.startswith("{")][-1])
+    lines = [f"{'heads':>7s} {'D':>4s} {'dtype':>5s} {'geometry':>18s} {'launches':>8s} "
+             f"{'pass us':>9s} {'GB/s':>6s} {'% peak':>7s} {'torch neg_ us':>14s} {'ratio':>6s}"]
+    for r in js["rows"]:
+        lines.append(f"{str(r['Hq']) + '+' + str(r['Hkv']):>7s} {r['D']:4d} {r['dtype']:>5s} "
+                     f"{r['geometry']:>18s} {r['launches_per_pass']:8d} {r['avg_pass_us']:9.2f} "
+                     f"{r['GBps']:6.0f} {100 * r['frac']:6.1f}% {r['torch_inplace_us']:14.2f} "
+                     f"{r['frac_of_ceiling']:6.3f}")
+    text = "\n".join([
+        "# RoPE pass (one forward or backward launch set) per head shape on one MI355X:",
+        f"# {js['head_shapes']}; bench.py region timing (HIP events over back-to-back",
+        "# forward + backward steps on rotating buffer sets that exceed the Infinity Cache),",
+        "# GB/s = one read + one write of every Q and K element / pass time. 'torch neg_ us':",
+        "# torch's in-place negation of the same Q and K tensors (two launches), the same",
+        "# bytes through a bare elementwise kernel; ratio = its time / the RoPE pass time.",
+        "# geometry: the default launch's kernel (staged: half rows that are not whole",
+        "# 128-byte lines, moved through LDS) and its head rows per workgroup.",
+        f"# command (R = repository root, on one MI355X): {command}",
+        f"# kernel_source_sha256_16: {kernel_source_hash()}",
+        "",
+        *lines, ""])
+    with open(HEAD_SHAPES_FILE, "w") as fh:
+        fh.write(text)
+    print(text)
 
 
 def write_sweep_summary(run_dir: str, command: str) -> None:
@@ -1428,6 +1524,12 @@ def main():
     ap.add_argument("--sweep-summary", default=None, metavar="RUN_DIR",
                     help="write profiles/rope_qk_size_sweep.txt from RUN_DIR (rocprofv3 kernel "
                          "trace of --sweep and its JSON line in RUN_DIR/sweep.json), then exit")
+    ap.add_argument("--head-shapes", action="store_true",
+                    help="time the default launch on every head shape of HEAD_SHAPES (one "
+                         "sequence each) beside torch's in-place reference; one JSON line")
+    ap.add_argument("--head-shapes-summary", default=None, metavar="JSON",
+                    help="write profiles/rope_qk_head_shapes.txt from the JSON line of "
+                         "--head-shapes in this file, then exit")
     ap.add_argument("--configs", default="all", choices=["all", "none"],
                     help="all: also time every other RoPE workload's default launches and put "
                          "them in the JSON line (per_config); none: the chosen workload only")
@@ -1493,6 +1595,9 @@ def main():
     if args.sweep_summary:
         write_sweep_summary(args.sweep_summary, args.trace_command)
         return
+    if args.head_shapes_summary:
+        write_head_shapes_summary(args.head_shapes_summary, args.trace_command)
+        return
     if args.glu_valu_summary:
         write_glu_valu_summary(args.glu_valu_summary, args.trace_command)
         return
@@ -1545,6 +1650,9 @@ def main():
     dev = torch.device("cuda:0")
     if args.sweep:
         print(json.dumps(size_sweep(rope, dev, max(50, min(args.steps, 500)))))
+        return
+    if args.head_shapes:
+        print(json.dumps(head_shape_survey(rope, dev, max(50, min(args.steps, 500)))))
         return
     w = workloads.get(args.workload)
     set_bytes = 2 * w.T * (w.Hq + w.Hkv) * w.D * w.elem_bytes  # Q, K, dQ, dK

@@ -456,7 +456,9 @@ __host__ __device__ inline uint32_t group_rows(uint32_t nc) {
 // STAGED (see the address computation below): row halves that are not whole
 // 128-byte lines, e.g. D = 64, 80, 96 or 112 in 16-bit storage, move through LDS
 // in whole lines. Otherwise nc is a power of two, the groups are 64 / nc rows and
-// the lane split is a shift.
+// the lane split is a shift. STEPS (group_steps; 1 or 2, never with STAGED): a
+// group is STEPS times 64 / nc rows, each lane rotating its chunk pair in STEPS
+// rows 64 / nc apart with the one cos/sin table of the token.
 //
 // Everything a wave needs before its first loads leads the argument list as 13
 // plain dwords, which the library's build preloads into SGPRs at wave launch
@@ -473,7 +475,7 @@ __host__ __device__ inline uint32_t group_rows(uint32_t nc) {
 // Unless STAGED, D follows from nc_shift: a half row is 2^nc_shift chunks of VEC
 // elements.
 constexpr uint32_t kFlagIds = 1, kFlagOffsets = 2, kFlagSeqused = 4;
-template <typename T, int VEC, bool LONG_INDEX, bool TABLE, bool COMPACT, bool STAGED>
+template <typename T, int VEC, bool LONG_INDEX, bool TABLE, bool COMPACT, bool STAGED, int STEPS>
 __global__ __launch_bounds__(64) void rope_qk_group_kernel(
     T* __restrict__ q, T* __restrict__ k, const int32_t* __restrict__ cu, uint32_t q_stride,
     uint32_t k_stride, uint32_t groups_mul, uint32_t geo, uint32_t heads, int32_t num_seqs,
@@ -526,15 +528,18 @@ __global__ __launch_bounds__(64) void rope_qk_group_kernel(
   } else {
     c = lane & ((1 << ns) - 1);
     half = (uint32_t)VEC << ns;
-    r = (int)(((in_q ? g : g - gq) << (6 - ns)) + ((uint32_t)lane >> ns));
+    r = (int)((((in_q ? g : g - gq) * (uint32_t)STEPS) << (6 - ns)) + ((uint32_t)lane >> ns));
     live = r < (in_q ? Hq : Hkv);
   }
+  [[maybe_unused]] const int H = in_q ? Hq : Hkv;
   const uint32_t D = half << 1;
   // !STAGED: this lane's chunk of its row; STAGED: the group's first element
   T* row = nullptr;
+  T* trow = nullptr;  // STEPS > 1: the token's first row in the tensor
   if constexpr (!COMPACT) {
     row = in_q ? token_row0<T, LONG_INDEX>(q, (int64_t)t, (int64_t)q_stride)
                : token_row0<T, LONG_INDEX>(k, (int64_t)t, (int64_t)k_stride);
+    trow = row;
     // r * D < 2^22: a 24-bit multiply. (A full 32-bit multiply-add becomes
     // v_mad_u64_u32 with an undefined high addend, which the register allocator
     // may place in a register a pending load writes, forcing a wait on it.)
@@ -565,6 +570,7 @@ __global__ __launch_bounds__(64) void rope_qk_group_kernel(
     if (pos < 0) return;
     row = in_q ? token_row0<T, LONG_INDEX>(q, tok, (int64_t)q_stride)
                : token_row0<T, LONG_INDEX>(k, tok, (int64_t)k_stride);
+    trow = row;
     if constexpr (STAGED)
       row += __umul24(g0, D);
     else
@@ -587,6 +593,18 @@ __global__ __launch_bounds__(64) void rope_qk_group_kernel(
   } else {
     lo = load_chunk<T, VEC>(row);
     hi = load_chunk<T, VEC>(row + half);
+  }
+  // STEPS > 1: the lane's chunk pair in rows r + j * (64 / nc), j = 1 .. STEPS - 1
+  // (row 0 of the token for rows past the tensor's last, which store nothing)
+  C lo_s[STEPS > 1 ? STEPS - 1 : 1], hi_s[STEPS > 1 ? STEPS - 1 : 1];
+  if constexpr (STEPS > 1) {
+#pragma unroll
+    for (int j = 1; j < STEPS; ++j) {
+      const uint32_t rj = (uint32_t)r + ((uint32_t)j << (6 - ns));
+      T* pj = trow + __umul24(rj < (uint32_t)H ? rj : 0u, D) + (uint32_t)(c * VEC);
+      lo_s[j - 1] = load_chunk<T, VEC>(pj);
+      hi_s[j - 1] = load_chunk<T, VEC>(pj + half);
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
 
@@ -651,6 +669,18 @@ __global__ __launch_bounds__(64) void rope_qk_group_kernel(
     // dirty in L2
     store_chunk_through<T, VEC>(row, lo);
     store_chunk_through<T, VEC>(row + half, hi);
+    if constexpr (STEPS > 1) {
+#pragma unroll
+      for (int j = 1; j < STEPS; ++j) {
+        const uint32_t rj = (uint32_t)r + ((uint32_t)j << (6 - ns));
+        if (rj < (uint32_t)H) {
+          T* pj = trow + __umul24(rj, D) + (uint32_t)(c * VEC);
+          rotate_chunk(lo_s[j - 1], hi_s[j - 1], cs, sn);
+          store_chunk_through<T, VEC>(pj, lo_s[j - 1]);
+          store_chunk_through<T, VEC>(pj + half, hi_s[j - 1]);
+        }
+      }
+    }
   }
 }
 
@@ -786,13 +816,16 @@ constexpr uint32_t kGroupStaticLds = 2 * kMaxHalf * sizeof(float);
 // 16 + 16 heads, 16384 tokens, 73.6 -> 64.7 and 63.8 -> 56.0 us), 9% for D = 80,
 // 1% for D = 64. So do half rows of more than 64 frequencies, whose cos/sin take
 // each lane two or four evaluations: D = 256 at 28 (83.1 -> 80.5 us for 16 + 16
-// heads, 250.9 -> 240.6 for 16 + 8 heads over 65536 tokens), D = 512 at 32
-// (109.7 -> 99.7 us for 8 + 8 heads).
+// heads, 250.9 -> 240.6 for 16 + 8 heads over 65536 tokens), D = 512 at 32 with
+// one row step (109.7 -> 99.7 us for 8 + 8 heads). A workgroup of two row steps
+// (group_steps) carries twice the bytes and does best at 20 again: 14-15% faster
+// than one step at 32 for D = 512 in bf16, 3% of it from the cap (32 -> 20).
 constexpr uint32_t kCap = 20, kCapLongQHeavy = 28, kCapStaged = 32;
 uint32_t group_dynamic_lds(unsigned group_blocks, uint32_t gq, uint32_t gk, bool staged,
-                           uint32_t half) {
+                           uint32_t half, int32_t steps) {
   const bool long_q_heavy = group_blocks >= (1u << 18) && gq >= 8 * gk;
-  const uint32_t cap = staged || half > 128 ? kCapStaged
+  const uint32_t cap = steps > 1                   ? kCap
+                       : staged || half > 128       ? kCapStaged
                        : half > 64 || long_q_heavy ? kCapLongQHeavy
                                                    : kCap;
   return kLdsPerCU / cap - kGroupStaticLds;
@@ -811,6 +844,23 @@ static_assert(kLdsPerCU / kCapStaged - kGroupStaticLds >= 128 * 16,
 // full group for fewer bytes, so from 11 chunks on the token kernel runs.
 bool staged_geometry(int32_t nc, int32_t chunk_bytes) {
   return chunk_bytes == 16 && nc <= 10 && nc != 8;
+}
+
+// Row steps per row-group workgroup: 2 for half rows of more than 128 elements in
+// 16-byte chunks (D = 512), 1 otherwise. Such a row takes each lane four cos/sin
+// evaluations for one chunk pair; a second row step (the lane's chunk pair in the
+// row 64 / nc further on, loaded with the first) shares them, so a workgroup moves
+// 4 rows instead of 2 for the same VALU work. Measured against one step
+// (interleaved, bit-identical, 16384 tokens, two boxes; with the cap of 20 that
+// group_dynamic_lds gives stepped launches): D = 512 in bf16 11-15% faster (8 + 8
+// heads 98.4 -> 83.7 and 95.9 -> 85.3 us per pass, 68-70% -> 79-80% of 8 TB/s),
+// 16 + 8 heads 12-15%, 32 + 8 heads over 65536 tokens 12-14%; in fp32 (8 + 8
+// heads) 5-8%. Four steps
+// gained less (D = 512 in bf16 -15 to -17% at the old cap of 32, against -17 to
+// -19% for two), and two steps cost 7-8% for D = 256 in fp32 and 1.5-4% in bf16,
+// whose lanes evaluate two cos/sin values.
+int32_t group_steps(int32_t half, int32_t chunk_bytes) {
+  return chunk_bytes == 16 && half > 128 ? 2 : 1;
 }
 
 // Long passes as several launches. Workgroup i of a launch runs on XCC i mod 8
@@ -864,7 +914,7 @@ GroupScalars group_scalars(const RopeParams& p, const PosSource& ps) {
 
 // One launch of the row-group kernel over tokens [t0, t0 + n) (rotated-token
 // indices for a compact launch).
-template <typename T, int VEC, bool TABLE, bool STAGED>
+template <typename T, int VEC, bool TABLE, bool STAGED, int STEPS>
 void launch_group(T* qt, T* kt, const PosSource& ps, const RopeParams& p, const GroupScalars& s,
                   bool long_index, uint32_t lds, uint32_t t0, uint32_t n, hipStream_t stream) {
   const dim3 grid(n * (p.gq + p.gk));
@@ -873,13 +923,13 @@ void launch_group(T* qt, T* kt, const PosSource& ps, const RopeParams& p, const 
       s.geo, s.heads, ps.num_seqs, t0, ps, p
   if (!TABLE && ps.cu_valid != nullptr) {
     if (long_index)
-      hipLaunchKernelGGL((rope_qk_group_kernel<T, VEC, true, false, true, STAGED>), ROPE_GROUP_ARGS);
+      hipLaunchKernelGGL((rope_qk_group_kernel<T, VEC, true, false, true, STAGED, STEPS>), ROPE_GROUP_ARGS);
     else
-      hipLaunchKernelGGL((rope_qk_group_kernel<T, VEC, false, false, true, STAGED>), ROPE_GROUP_ARGS);
+      hipLaunchKernelGGL((rope_qk_group_kernel<T, VEC, false, false, true, STAGED, STEPS>), ROPE_GROUP_ARGS);
   } else if (long_index) {
-    hipLaunchKernelGGL((rope_qk_group_kernel<T, VEC, true, TABLE, false, STAGED>), ROPE_GROUP_ARGS);
+    hipLaunchKernelGGL((rope_qk_group_kernel<T, VEC, true, TABLE, false, STAGED, STEPS>), ROPE_GROUP_ARGS);
   } else {
-    hipLaunchKernelGGL((rope_qk_group_kernel<T, VEC, false, TABLE, false, STAGED>), ROPE_GROUP_ARGS);
+    hipLaunchKernelGGL((rope_qk_group_kernel<T, VEC, false, TABLE, false, STAGED, STEPS>), ROPE_GROUP_ARGS);
   }
 #undef ROPE_GROUP_ARGS
 }
@@ -891,7 +941,9 @@ int32_t launch_vec(void* q, void* k, const PosSource& ps, const RopeParams& p, b
   T* kt = static_cast<T*>(k);
   if (group_blocks > 0) {
     const bool staged = staged_geometry(p.nc, VEC * (int)sizeof(T));
-    const uint32_t lds = group_dynamic_lds(group_blocks, p.gq, p.gk, staged, (uint32_t)p.D / 2);
+    const int32_t steps = group_steps(p.D / 2, VEC * (int)sizeof(T));
+    const uint32_t lds =
+        group_dynamic_lds(group_blocks, p.gq, p.gk, staged, (uint32_t)p.D / 2, steps);
     const GroupScalars s = group_scalars(p, ps);
     const uint32_t rows = group_blocks / (p.gq + p.gk);
     const uint32_t piece = group_piece_tokens(rows, p.gq, p.gk);
@@ -899,11 +951,13 @@ int32_t launch_vec(void* q, void* k, const PosSource& ps, const RopeParams& p, b
       const uint32_t n = rows - t0 < piece ? rows - t0 : piece;
       if constexpr (VEC * sizeof(T) == 16) {
         if (staged)
-          launch_group<T, VEC, TABLE, true>(qt, kt, ps, p, s, long_index, lds, t0, n, stream);
+          launch_group<T, VEC, TABLE, true, 1>(qt, kt, ps, p, s, long_index, lds, t0, n, stream);
+        else if (steps == 2)
+          launch_group<T, VEC, TABLE, false, 2>(qt, kt, ps, p, s, long_index, lds, t0, n, stream);
         else
-          launch_group<T, VEC, TABLE, false>(qt, kt, ps, p, s, long_index, lds, t0, n, stream);
+          launch_group<T, VEC, TABLE, false, 1>(qt, kt, ps, p, s, long_index, lds, t0, n, stream);
       } else {
-        launch_group<T, VEC, TABLE, false>(qt, kt, ps, p, s, long_index, lds, t0, n, stream);
+        launch_group<T, VEC, TABLE, false, 1>(qt, kt, ps, p, s, long_index, lds, t0, n, stream);
       }
       if (hipGetLastError() != hipSuccess) return ROPE_ELAUNCH;
     }
@@ -955,7 +1009,7 @@ int64_t group_grid(const RopeParams& p, bool geometry_chosen, bool padded, int64
   if (64 % p.nc != 0 && !staged_geometry(p.nc, wide ? 16 : 0)) return 0;
   // token strides travel as 32-bit kernel arguments
   if (p.q_stride > (int64_t)UINT32_MAX || p.k_stride > (int64_t)UINT32_MAX) return 0;
-  const int step_r = (int)group_rows((uint32_t)p.nc);
+  const int step_r = (int)group_rows((uint32_t)p.nc) * group_steps(p.D / 2, wide ? 16 : 0);
   const int64_t groups = (p.Hq + step_r - 1) / step_r + (p.Hkv + step_r - 1) / step_r;
   const int64_t blocks = (compact ? compact_rows : p.T) * groups;
   // < 2^26 workgroups: the dispatch limit, and the range of fastdiv::div
@@ -975,7 +1029,7 @@ int32_t launch_typed(void* q, void* k, PosSource ps, RopeParams& p, int32_t byte
                                           ps.cu_valid ? compact_rows : -1, bytes == 16);
   if (group_blocks == 0) ps.cu_valid = nullptr;
   if (group_blocks > 0) {
-    const int step_r = (int)group_rows((uint32_t)p.nc);
+    const int step_r = (int)group_rows((uint32_t)p.nc) * group_steps(p.D / 2, bytes);
     p.gq = (uint32_t)((p.Hq + step_r - 1) / step_r);
     p.gk = (uint32_t)((p.Hkv + step_r - 1) / step_r);
     p.nc_shift = 0;

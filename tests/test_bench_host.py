@@ -13,7 +13,7 @@ import bench
 import workloads
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-GROUP = "_ZN12_GLOBAL__N_120rope_qk_group_kernelIDF16bLi8ELb0ELb0ELb0ELb0EEEvPT_S2_"
+GROUP = "_ZN12_GLOBAL__N_120rope_qk_group_kernelIDF16bLi8ELb0ELb0ELb0ELb0ELi1EEEvPT_S2_"
 COPY = "__amd_rocclr_copyBuffer"
 
 
@@ -119,7 +119,9 @@ def test_staged_head_sizes():
         assert bench.chunks_per_half_row(w) == nc and bench.chunk_bytes(w) == 16
         assert bench.rope_kernel_name(w, 0) == "rope_qk_group_kernel"
         assert bench.staged_geometry(w) is staged, D
-        assert bench.rope_kernel_instance(w, False).endswith(f"ELb{int(staged)}E")
+        steps = 2 if D == 512 else 1  # half rows of more than 128 elements: two row steps
+        assert bench.group_steps(w) == steps
+        assert bench.rope_kernel_instance(w, False).endswith(f"ELb{int(staged)}ELi{steps}E")
     # 11 chunks or more that do not divide 64 (too few rows per group): the token kernel
     for D, dtype in ((192, "bf16"), (96, "f32"), (384, "bf16"), (176, "bf16")):
         w = _shape(1024, 32, 8, D=D, dtype=dtype)
@@ -164,22 +166,51 @@ def test_group_rows_whole_lines(tmp_path):
     assert bench.expected_grid_threads(_shape(1000, 14, 2, D=144)) == [1000 * 3 * 64]
 
 
+def test_row_steps(tmp_path):
+    """Two row steps per row-group workgroup for half rows of more than 128 elements
+    in 16-byte chunks (D = 512), one otherwise: the library's group_steps (compiled
+    from its source with g++) and bench.py's mirror agree; the grid follows."""
+    src_text = open(os.path.join(ROOT, "packed_varlen_rotary_rope_amd", "csrc", "rope_qk.hip")).read()
+    i = src_text.index("int32_t group_steps(int32_t half, int32_t chunk_bytes) {")
+    j = src_text.index("\n}\n", i) + 3
+    src = tmp_path / "group_steps.cpp"
+    src.write_text("#include <cstdint>\n#include <cstdio>\n" + src_text[i:j]
+                   + "int main() { for (int h = 8; h <= 256; h *= 2) for (int b = 2; b <= 16; b *= 2)"
+                   " printf(\"%d %d %d\\n\", h, b, group_steps(h, b)); }\n")
+    exe = tmp_path / "group_steps"
+    subprocess.run(["g++", "-O2", "-std=c++17", "-o", str(exe), str(src)], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout
+    for line in out.split("\n"):
+        if not line:
+            continue
+        half, cb, steps = (int(x) for x in line.split())
+        assert steps == (2 if cb == 16 and half > 128 else 1), line
+    for D, dtype, steps, rows in ((512, "bf16", 2, 4), (512, "f16", 2, 4), (512, "f32", 2, 2),
+                                  (256, "bf16", 1, 4), (256, "f32", 1, 2), (128, "bf16", 1, 8)):
+        w = _shape(1000, 7, 3, D=D, dtype=dtype)
+        assert bench.group_steps(w) == steps and bench.rows_per_workgroup(w) == rows, D
+        groups = -(-7 // rows) + -(-3 // rows)
+        assert bench.expected_grid_threads(w) == [1000 * groups * 64], (D, dtype)
+    w = _shape(1000, 8, 8, D=512)
+    assert bench.head_geometry(w) == "row-group, 2 rows x 2"
+
+
 def test_kernel_instance_names():
     """The mangled-name fragments the summaries filter rocprofv3 records by."""
     w5, w2 = workloads.get("long_ctx_512k"), workloads.get("qwen3_4b_packed")
     assert bench.needs_long_index(w5) and not bench.needs_long_index(w2)
-    assert bench.rope_kernel_instance(w5, True) == "rope_qk_group_kernelIDF16bLi8ELb1ELb0ELb0ELb0E"
+    assert bench.rope_kernel_instance(w5, True) == "rope_qk_group_kernelIDF16bLi8ELb1ELb0ELb0ELb0ELi1E"
     assert bench.rope_kernel_instance(w2, False) in GROUP
     assert bench.rope_kernel_instance(workloads.get("tiny_packed"), False) == \
-        "rope_qk_group_kernelIfLi4ELb0ELb0ELb0ELb1E"  # D = 16 in fp32: staged
+        "rope_qk_group_kernelIfLi4ELb0ELb0ELb0ELb1ELi1E"  # D = 16 in fp32: staged
     pad = workloads.get("qwen3_8b_padded")
-    assert bench.rope_kernel_instance(pad, False) == "rope_qk_group_kernelIDF16bLi8ELb0ELb0ELb1ELb0E"
+    assert bench.rope_kernel_instance(pad, False) == "rope_qk_group_kernelIDF16bLi8ELb0ELb0ELb1ELb0ELi1E"
     assert bench.rope_kernel_instance(pad, False, "seqused") == \
         "rope_qk_kernelIDF16bLi8ELb0ELb0E"
     assert bench.rope_instance_names(pad, False)[1] == \
-        "rope_qk_group_kernel<__bf16, 8, false, false, true, false>"
+        "rope_qk_group_kernel<__bf16, 8, false, false, true, false, 1>"
     assert bench.rope_instance_names(w5, True)[1] == \
-        "rope_qk_group_kernel<__bf16, 8, true, false, false, false>"
+        "rope_qk_group_kernel<__bf16, 8, true, false, false, false, 1>"
 
 
 def test_linear_fit():
@@ -216,7 +247,7 @@ def test_traffic_summary_request_counts(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "traffic_path", lambda workload: str(out))
     w = workloads.get("long_ctx_512k")
     bpl = bench.algorithmic_bytes_per_launch(w)
-    long_k = "_ZN12_GLOBAL__N_120rope_qk_group_kernelIDF16bLi8ELb1ELb0ELb0ELb0EEEvPT_S2_"
+    long_k = "_ZN12_GLOBAL__N_120rope_qk_group_kernelIDF16bLi8ELb1ELb0ELb0ELb0ELi1EEEvPT_S2_"
     kib = 1024.0
     for name, ctr, val in (("cf", "FETCH_SIZE", 2 ** 30 / kib / 2), ("cw", "WRITE_SIZE", 2 ** 30 / kib)):
         _counter_csv(str(tmp_path / f"{name}.csv"), [(COPY, ctr, val)])
@@ -285,6 +316,34 @@ def test_sweep_summary(tmp_path, monkeypatch):
     assert "fit, RoPE kernel, trace averages, T <= 65536: t = 1.50 us + T x 3.0000 ns" in text
 
 
+def test_head_shapes_summary(tmp_path, monkeypatch):
+    """The head-shape survey's summary: one row per shape with its geometry (the
+    library's kernel choice and rows per group, as bench.py mirrors it), pass time,
+    GB/s and the torch reference, from a synthetic JSON line."""
+    import json
+    out = tmp_path / "shapes.txt"
+    monkeypatch.setattr(bench, "HEAD_SHAPES_FILE", str(out))
+    rows = []
+    for Hq, Hkv, D, dtype in bench.HEAD_SHAPES:
+        w = bench.head_shape_workload(Hq, Hkv, D, dtype)
+        us = bench.algorithmic_bytes_per_pass(w) / 6.4e9 * 1e3  # 6.4 TB/s
+        rows.append({"Hq": Hq, "Hkv": Hkv, "D": D, "dtype": dtype, "T": w.T,
+                     "geometry": bench.head_geometry(w), "launches_per_pass": 1,
+                     "avg_pass_us": us, "GBps": 6400.0, "frac": 0.8,
+                     "torch_inplace_us": 1.2 * us, "frac_of_ceiling": 1.2})
+    js = tmp_path / "shapes.json"
+    js.write_text("noise\n" + json.dumps({"head_shapes": "synthetic", "rows": rows}) + "\n")
+    bench.write_head_shapes_summary(str(js), "python R/bench.py --head-shapes")
+    text = out.read_text()
+    body = [ln for ln in text.splitlines() if ln and not ln.startswith("#")]
+    assert len(body) == 1 + len(bench.HEAD_SHAPES)
+    assert "python R/bench.py --head-shapes" in text
+    assert f"kernel_source_sha256_16: {bench.kernel_source_hash()}" in text
+    assert any("staged, 8 rows" in ln and " 112 " in ln for ln in body)      # D = 112
+    assert any("token kernel" in ln and " 192 " in ln for ln in body)        # D = 192
+    assert all("80.0%" in ln for ln in body[1:])
+
+
 def test_trace_summary(tmp_path, monkeypatch):
     out = tmp_path / "trace.txt"
     monkeypatch.setattr(bench, "trace_summary_path", lambda workload: str(out))
@@ -306,7 +365,7 @@ def test_trace_summary_multi_launch_pass(tmp_path, monkeypatch):
     eighth of the pass's, and tokens/s count whole passes."""
     out = tmp_path / "trace.txt"
     monkeypatch.setattr(bench, "trace_summary_path", lambda workload: str(out))
-    long_k = "_ZN12_GLOBAL__N_120rope_qk_group_kernelIDF16bLi8ELb1ELb0ELb0ELb0EEEvPT_S2_"
+    long_k = "_ZN12_GLOBAL__N_120rope_qk_group_kernelIDF16bLi8ELb1ELb0ELb0ELb0ELi1EEEvPT_S2_"
     durations = [200000] * 16
     _trace_csv(str(tmp_path / "t.csv"), durations, kernel=long_k, grid=65536 * 5 * 64)
     bench.write_trace_summary(str(tmp_path / "t.csv"), "long_ctx_512k", "cmd")

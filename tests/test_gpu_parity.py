@@ -544,9 +544,27 @@ def test_staged_chunk_count(rope, case):
     for bit the token kernel with cu_seqlens, per-sequence offsets, explicit ids,
     64-bit offsets forced and cos/sin tables, forward and backward, on 3000 tokens in
     ragged sequences; sampled rows against the oracle."""
+    _check_group_instance(rope, case, "staged")
+
+
+ROW_STEP_CASES = [  # (D, dtype, Hq, Hkv): half rows of more than 128 elements, 2 row steps
+    (512, "bf16", 7, 3), (512, "f16", 8, 8), (512, "f32", 5, 3), (512, "bf16", 1, 1),
+]
+
+
+@pytest.mark.parametrize("case", ROW_STEP_CASES, ids=[f"{c[1]}_D{c[0]}_{c[2]}x{c[3]}"
+                                                      for c in ROW_STEP_CASES])
+def test_row_steps(rope, case):
+    """The row-group kernel with two row steps per workgroup (D = 512: 4 rows per
+    workgroup in 16-bit storage, 2 in fp32; head counts that end inside a step and
+    inside a group): the same checks as the staged instance."""
+    _check_group_instance(rope, case, "row steps")
+
+
+def _check_group_instance(rope, case, label):
     D, dtype, Hq, Hkv = case
     T = 3000
-    print(f"[parity] staged D={D} {dtype} {Hq}+{Hkv}", flush=True)
+    print(f"[parity] {label} D={D} {dtype} {Hq}+{Hkv}", flush=True)
     rng = np.random.default_rng(9900 + D)
     cu_h = np.array([0, 1, 700, 701, 2100, 2999, T], dtype=np.int32)
     cu = torch.from_numpy(cu_h).to(DEV)
@@ -590,7 +608,7 @@ def test_staged_chunk_count(rope, case):
                                            NTHREADS, seq_offsets=offs_h if mode == "offsets"
                                            else None)
                     touched = np.ones(len(tokens), dtype=bool)
-                assert_parity(dtype, got, ref, x, touched, f"staged-{mode}:{what}")
+                assert_parity(dtype, got, ref, x, touched, f"{label}-{mode}:{what}")
         t_q, t_k = src[fwd].clone(), src[grad].clone()
         c_q, c_k = src[fwd].clone(), src[grad].clone()
         rope.qk_apply_table_(t_q, t_k, tables[0], tables[1], direction, cu_seqlens=cu)
@@ -1227,6 +1245,7 @@ COMPACT_EDGE = [
     ("bf16_int64", "bf16", 128, 4, 2, {"index_mode": 2}),
     ("bf16_no_seqused", "bf16", 128, 4, 2, {"no_seqused": True}),
     ("bf16_D80_staged", "bf16", 80, 4, 2, {}),       # nc = 5: the staged row-group instance
+    ("bf16_D512_steps", "bf16", 512, 5, 3, {}),      # two row steps per workgroup
     ("bf16_D100_fallback", "bf16", 100, 4, 2, {}),   # 4-byte chunks, nc = 25: the seqused launch
     ("bf16_valid_short", "bf16", 128, 4, 2, {"valid_delta": -100}),
     ("bf16_cv_wide", "bf16", 128, 4, 2, {"cv_gap": 9}),
@@ -1239,8 +1258,9 @@ def test_padded_compact_edges(rope, case):
     """Ragged padded batches through the compact launch against the oracle: empty
     sequences, seqused past the length, negative and zero seqused, a token tail,
     per-sequence offsets (some shifting positions out of range), position scaling,
-    forced 64-bit offsets, no seqused, a staged head size, one that falls back to the seqused launch, and cu_valid / counts that do not match the layout (fewer tokens rotated,
-    never wrong ones)."""
+    forced 64-bit offsets, no seqused, a staged head size, one with two row steps per
+    workgroup, one that falls back to the seqused launch, and cu_valid / counts that do
+    not match the layout (fewer tokens rotated, never wrong ones)."""
     name, dtype, D, Hq, Hkv, extra = case
     B, S = 12, 96
     host, cu, su = _ragged_padded(7100 + len(name), B, S, Hq, Hkv, D, dtype, tail=5)
