@@ -850,7 +850,7 @@ bool staged_geometry(int32_t nc, int32_t chunk_bytes) {
 // 16-byte chunks (D = 512), 1 otherwise. Such a row takes each lane four cos/sin
 // evaluations for one chunk pair; a second row step (the lane's chunk pair in the
 // row 64 / nc further on, loaded with the first) shares them, so a workgroup moves
-// 4 rows instead of 2 for the same VALU work. Measured against one step
+// twice the rows (4 instead of 2 in 16-bit storage) for the same VALU work. Measured against one step
 // (interleaved, bit-identical, 16384 tokens, two boxes; with the cap of 20 that
 // group_dynamic_lds gives stepped launches): D = 512 in bf16 11-15% faster (8 + 8
 // heads 98.4 -> 83.7 and 95.9 -> 85.3 us per pass, 68-70% -> 79-80% of 8 TB/s),
