@@ -148,29 +148,32 @@ def group_geometry(w: workloads.Workload) -> bool:
 
 def staged_geometry(w: workloads.Workload) -> bool:
     """The row-group kernel's STAGED instance: 16-byte chunks, at most 10 per half row
-    and not 8 (the library's staged_geometry)."""
+    and not 8, or 11 to 15 with two steps (the library's staged_geometry)."""
     nc = chunks_per_half_row(w)
-    return chunk_bytes(w) == 16 and nc <= 10 and nc != 8
+    return chunk_bytes(w) == 16 and ((nc <= 10 and nc != 8) or 11 <= nc <= 15)
 
 
-def group_rows(nc: int) -> int:
-    """Head rows per row group (the library's group_rows): 64 // nc, rounded down to
-    whole 128-byte lines of 16-byte chunks (rows * nc a multiple of 4) when that keeps
-    at least 48 of the 64 lanes busy."""
-    r = 64 // nc
+def group_rows(nc: int, steps: int = 1) -> int:
+    """Head rows per row group (the library's group_rows): 64 * steps // nc, rounded
+    down to whole 128-byte lines of 16-byte chunks (rows * nc a multiple of 4) when
+    that keeps at least 48 lanes per step busy."""
+    r = 64 * steps // nc
     a = r & ~3 if nc & 1 else r & ~1 if (nc & 3) == 2 else r
-    return a if a * nc >= 48 else r
+    return a if a * nc >= 48 * steps else r
 
 
 def group_steps(w: workloads.Workload) -> int:
     """Row steps per row-group workgroup (the library's group_steps): 2 for half rows
-    of more than 128 elements in 16-byte chunks (D = 512), else 1."""
-    return 2 if chunk_bytes(w) == 16 and w.D // 2 > 128 else 1
+    of more than 128 elements in 16-byte chunks (D = 512) and for staged groups of
+    11 to 15 chunks per half row, else 1."""
+    nc = chunks_per_half_row(w)
+    two = chunk_bytes(w) == 16 and (w.D // 2 > 128 or 11 <= nc <= 15)
+    return 2 if two else 1
 
 
 def rows_per_workgroup(w: workloads.Workload) -> int:
-    """Head rows one row-group workgroup rotates: group_rows x group_steps."""
-    return group_rows(chunks_per_half_row(w)) * group_steps(w)
+    """Head rows one row-group workgroup rotates: group_rows(nc, group_steps)."""
+    return group_rows(chunks_per_half_row(w), group_steps(w))
 
 
 # The library's kPieceBlocks: a long pass of the row-group kernel on a Q-heavy shape
@@ -1189,6 +1192,8 @@ def head_geometry(w: workloads.Workload) -> str:
         return "token kernel"
     kind = "staged" if staged_geometry(w) else "row-group"
     steps = group_steps(w)
+    if steps > 1 and staged_geometry(w):
+        return f"{kind}, {rows_per_workgroup(w)} rows, 2 steps"
     rows = group_rows(chunks_per_half_row(w))
     return f"{kind}, {rows} rows" + (f" x {steps}" if steps > 1 else "")
 

@@ -433,10 +433,10 @@ __device__ inline void store_chunk_through(T* p, const Chunk<T, VEC>& c) {
 // pass), D = 48 (nc = 3, 20 rows instead of 21) 4-11%. For nc = 9 (D = 144) the
 // aligned group is 4 rows, 36 busy lanes, which measured 18-20% slower than 7.
 // Other nc give whole lines already.
-__host__ __device__ inline uint32_t group_rows(uint32_t nc) {
-  const uint32_t r = 64u / nc;
+__host__ __device__ inline uint32_t group_rows(uint32_t nc, uint32_t steps = 1) {
+  const uint32_t r = 64u * steps / nc;
   const uint32_t a = (nc & 1u) != 0 ? r & ~3u : (nc & 3u) == 2u ? r & ~1u : r;
-  return a * nc >= 48u ? a : r;
+  return a * nc >= 48u * steps ? a : r;
 }
 
 // ---- the default geometry: one wave per (token, row group) --------------------------
@@ -456,9 +456,11 @@ __host__ __device__ inline uint32_t group_rows(uint32_t nc) {
 // STAGED (see the address computation below): row halves that are not whole
 // 128-byte lines, e.g. D = 64, 80, 96 or 112 in 16-bit storage, move through LDS
 // in whole lines. Otherwise nc is a power of two, the groups are 64 / nc rows and
-// the lane split is a shift. STEPS (group_steps; 1 or 2, never with STAGED): a
-// group is STEPS times 64 / nc rows, each lane rotating its chunk pair in STEPS
-// rows 64 / nc apart with the one cos/sin table of the token.
+// the lane split is a shift. STEPS (group_steps, 1 or 2): without STAGED a group
+// is STEPS times 64 / nc rows, each lane rotating its chunk pair in STEPS rows
+// 64 / nc apart with the one cos/sin table of the token; with STAGED a group is
+// group_rows(nc, STEPS) rows, up to 128 * STEPS chunks moved through LDS, each lane
+// rotating (row, chunk) pairs lane and lane + 64 of the group.
 //
 // Everything a wave needs before its first loads leads the argument list as 13
 // plain dwords, which the library's build preloads into SGPRs at wave launch
@@ -515,14 +517,14 @@ __global__ __launch_bounds__(64) void rope_qk_group_kernel(
   uint32_t rl = 0, g0 = 0, nchunks = 0;  // STAGED: lane's row in the group, first row, chunks
   if constexpr (STAGED) {
     const uint32_t nc = (uint32_t)p.nc;
-    const uint32_t rows = group_rows(nc);
+    const uint32_t rows = group_rows(nc, STEPS);
     rl = (uint32_t)lane / nc;
     c = lane - (int)(rl * nc);
     half = (uint32_t)VEC * nc;
     g0 = (in_q ? g : g - gq) * rows;
     const uint32_t H = (uint32_t)(in_q ? Hq : Hkv);
     const uint32_t grows = H - g0 < rows ? H - g0 : rows;  // >= 1
-    nchunks = grows * 2u * nc;                              // <= 128
+    nchunks = grows * 2u * nc;                              // <= 128 * STEPS
     r = (int)(g0 + rl);
     live = rl < grows;
   } else {
@@ -596,8 +598,15 @@ __global__ __launch_bounds__(64) void rope_qk_group_kernel(
   }
   // STEPS > 1: the lane's chunk pair in rows r + j * (64 / nc), j = 1 .. STEPS - 1
   // (row 0 of the token for rows past the tensor's last, which store nothing)
+  // STAGED with STEPS = 2: chunks lane + 128 and lane + 192 of the group
   C lo_s[STEPS > 1 ? STEPS - 1 : 1], hi_s[STEPS > 1 ? STEPS - 1 : 1];
-  if constexpr (STEPS > 1) {
+  if constexpr (STAGED && STEPS > 1) {
+    static_assert(STEPS == 2, "staged groups hold at most 256 chunks");
+    const uint32_t i2 = (uint32_t)lane + 128u < nchunks ? (uint32_t)lane + 128u : nchunks - 1;
+    const uint32_t i3 = (uint32_t)lane + 192u < nchunks ? (uint32_t)lane + 192u : nchunks - 1;
+    lo_s[0] = load_chunk<T, VEC>(row + i2 * VEC);
+    hi_s[0] = load_chunk<T, VEC>(row + i3 * VEC);
+  } else if constexpr (STEPS > 1) {
 #pragma unroll
     for (int j = 1; j < STEPS; ++j) {
       const uint32_t rj = (uint32_t)r + ((uint32_t)j << (6 - ns));
@@ -633,6 +642,10 @@ __global__ __launch_bounds__(64) void rope_qk_group_kernel(
     C* stage = reinterpret_cast<C*>(lds_dyn);
     if ((uint32_t)lane < nchunks) stage[lane] = lo;
     if ((uint32_t)lane + 64u < nchunks) stage[lane + 64] = hi;
+    if constexpr (STEPS > 1) {
+      if ((uint32_t)lane + 128u < nchunks) stage[lane + 128] = lo_s[0];
+      if ((uint32_t)lane + 192u < nchunks) stage[lane + 192] = hi_s[0];
+    }
   }
   wave_lds_sync();
 
@@ -652,11 +665,38 @@ __global__ __launch_bounds__(64) void rope_qk_group_kernel(
       stage[i] = a;
       stage[i + half / VEC] = b;
     }
+    if constexpr (STEPS > 1) {
+      // the group's (row, chunk) pair lane + 64
+      const uint32_t ncv = half / VEC;
+      const uint32_t pi = (uint32_t)lane + 64u;
+      const uint32_t prow = pi / ncv;
+      const uint32_t pc = pi - prow * ncv;
+      if (prow * 2u * ncv < nchunks) {
+        const uint32_t i = prow * 2u * ncv + pc;
+        C a = stage[i];
+        C b = stage[i + ncv];
+        float cs[VEC], sn[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          cs[e] = lds_cs[pc * VEC + e];
+          sn[e] = lds_sn[pc * VEC + e];
+        }
+        rotate_chunk(a, b, cs, sn);
+        stage[i] = a;
+        stage[i + ncv] = b;
+      }
+    }
     wave_lds_sync();
     // written through to memory, whole lines of the group at a time
     if ((uint32_t)lane < nchunks) store_chunk_through<T, VEC>(row + lane * VEC, stage[lane]);
     if ((uint32_t)lane + 64u < nchunks)
       store_chunk_through<T, VEC>(row + ((uint32_t)lane + 64u) * VEC, stage[lane + 64]);
+    if constexpr (STEPS > 1) {
+      if ((uint32_t)lane + 128u < nchunks)
+        store_chunk_through<T, VEC>(row + ((uint32_t)lane + 128u) * VEC, stage[lane + 128]);
+      if ((uint32_t)lane + 192u < nchunks)
+        store_chunk_through<T, VEC>(row + ((uint32_t)lane + 192u) * VEC, stage[lane + 192]);
+    }
   } else if (live) {
     float cs[VEC], sn[VEC];
 #pragma unroll
@@ -836,31 +876,47 @@ static_assert(kLdsPerCU / kCapStaged - kGroupStaticLds >= 128 * 16,
 
 // The row-group kernel's STAGED instance: 16-byte chunks and row halves that are
 // not whole 128-byte lines (nc other than 8), at most 10 chunks per half row so
-// that a group holds at least 6 rows. Measured against the token kernel
+// that a one-step group holds at least 6 rows (11 to 15 with two steps, below).
+// Measured against the token kernel
 // (interleaved, bit-identical, bf16, 16384 tokens): D = 32, 64, 80, 96, 112 and 160
 // 7-44% faster (D = 96: 96.8 -> 74.4 us per pass for 32 + 32 heads; D = 64: 48.1
 // -> 43.2), but D = 192 (12 chunks, 5 rows per group, 16 + 16 heads) 14% slower:
 // groups that short spend as much per workgroup on the search and cos/sin as a
-// full group for fewer bytes, so from 11 chunks on the token kernel runs.
+// full group for fewer bytes, so from 11 chunks on a staged group takes two steps.
+// The staged instance with two steps (a group of group_rows(nc, 2) rows, up to 256
+// chunks, four coalesced loads and stores per lane, two (lo, hi) pairs per lane)
+// for 11 to 15 chunks per half row, which one step would leave at 4 or 5 rows per
+// group. Against the token kernel these head sizes took before (interleaved,
+// bit-identical, 16384 tokens, two boxes, per pass): in bf16, 16 + 16 heads, D = 176
+// 79.4-79.6 -> 66.2-66.7 us (58% -> 69% of 8 TB/s), D = 192 74.0-74.1 -> 68.8-69.2
+// (68% -> 73%), D = 208 105.2 -> 68.1 (52% -> 80%), D = 224 101.3 -> 74.3, D = 240
+// 111.2 -> 79.9; D = 192 with 32 + 8 heads 95.7-95.9 -> 77.4-78.8 (66% -> 80-81%);
+// fp32 D = 96, 32 + 8 heads, 95.2 -> 78.5 (66% -> 80%). For 10 chunks or fewer two
+// steps measured slower than one (D = 80 +14%, D = 96 +3 to +6%, D = 112 +1 to +3%;
+// D = 144 +5% for 16 + 16 heads, -5% for 32 + 8).
+bool staged_two_steps(int32_t nc, int32_t chunk_bytes) {
+  return chunk_bytes == 16 && nc >= 11 && nc <= 15;
+}
 bool staged_geometry(int32_t nc, int32_t chunk_bytes) {
-  return chunk_bytes == 16 && nc <= 10 && nc != 8;
+  return (chunk_bytes == 16 && nc <= 10 && nc != 8) || staged_two_steps(nc, chunk_bytes);
 }
 
 // Row steps per row-group workgroup: 2 for half rows of more than 128 elements in
-// 16-byte chunks (D = 512), 1 otherwise. Such a row takes each lane four cos/sin
+// 16-byte chunks (D = 512) and for the staged instance at 11 to 15 chunks per half
+// row (staged_two_steps), 1 otherwise. A D = 512 row takes each lane four cos/sin
 // evaluations for one chunk pair; a second row step (the lane's chunk pair in the
 // row 64 / nc further on, loaded with the first) shares them, so a workgroup moves
-// twice the rows (4 instead of 2 in 16-bit storage) for the same VALU work. Measured against one step
-// (interleaved, bit-identical, 16384 tokens, two boxes; with the cap of 20 that
-// group_dynamic_lds gives stepped launches): D = 512 in bf16 11-15% faster (8 + 8
-// heads 98.4 -> 83.7 and 95.9 -> 85.3 us per pass, 68-70% -> 79-80% of 8 TB/s),
-// 16 + 8 heads 12-15%, 32 + 8 heads over 65536 tokens 12-14%; in fp32 (8 + 8
-// heads) 5-8%. Four steps
-// gained less (D = 512 in bf16 -15 to -17% at the old cap of 32, against -17 to
-// -19% for two), and two steps cost 7-8% for D = 256 in fp32 and 1.5-4% in bf16,
-// whose lanes evaluate two cos/sin values.
-int32_t group_steps(int32_t half, int32_t chunk_bytes) {
-  return chunk_bytes == 16 && half > 128 ? 2 : 1;
+// twice the rows (4 instead of 2 in 16-bit storage) for the same VALU work.
+// Measured against one step (interleaved, bit-identical, 16384 tokens, two boxes;
+// with the cap of 20 that group_dynamic_lds gives stepped launches): D = 512 in
+// bf16 11-15% faster (8 + 8 heads 98.4 -> 83.7 and 95.9 -> 85.3 us per pass,
+// 68-70% -> 79-80% of 8 TB/s), 16 + 8 heads 12-15%, 32 + 8 heads over 65536
+// tokens 12-14%; in fp32 (8 + 8 heads) 5-8%. Four steps gained less (D = 512 in
+// bf16 -15 to -17% at the old cap of 32, against -17 to -19% for two), and two
+// steps cost 7-8% for D = 256 in fp32 and 1.5-4% in bf16, whose lanes evaluate two
+// cos/sin values.
+int32_t group_steps(int32_t nc, int32_t half, int32_t chunk_bytes) {
+  return (chunk_bytes == 16 && half > 128) || staged_two_steps(nc, chunk_bytes) ? 2 : 1;
 }
 
 // Long passes as several launches. Workgroup i of a launch runs on XCC i mod 8
@@ -941,7 +997,7 @@ int32_t launch_vec(void* q, void* k, const PosSource& ps, const RopeParams& p, b
   T* kt = static_cast<T*>(k);
   if (group_blocks > 0) {
     const bool staged = staged_geometry(p.nc, VEC * (int)sizeof(T));
-    const int32_t steps = group_steps(p.D / 2, VEC * (int)sizeof(T));
+    const int32_t steps = group_steps(p.nc, p.D / 2, VEC * (int)sizeof(T));
     const uint32_t lds =
         group_dynamic_lds(group_blocks, p.gq, p.gk, staged, (uint32_t)p.D / 2, steps);
     const GroupScalars s = group_scalars(p, ps);
@@ -950,7 +1006,9 @@ int32_t launch_vec(void* q, void* k, const PosSource& ps, const RopeParams& p, b
     for (uint32_t t0 = 0; t0 < rows; t0 += piece) {
       const uint32_t n = rows - t0 < piece ? rows - t0 : piece;
       if constexpr (VEC * sizeof(T) == 16) {
-        if (staged)
+        if (staged && steps == 2)
+          launch_group<T, VEC, TABLE, true, 2>(qt, kt, ps, p, s, long_index, lds, t0, n, stream);
+        else if (staged)
           launch_group<T, VEC, TABLE, true, 1>(qt, kt, ps, p, s, long_index, lds, t0, n, stream);
         else if (steps == 2)
           launch_group<T, VEC, TABLE, false, 2>(qt, kt, ps, p, s, long_index, lds, t0, n, stream);
@@ -1009,7 +1067,7 @@ int64_t group_grid(const RopeParams& p, bool geometry_chosen, bool padded, int64
   if (64 % p.nc != 0 && !staged_geometry(p.nc, wide ? 16 : 0)) return 0;
   // token strides travel as 32-bit kernel arguments
   if (p.q_stride > (int64_t)UINT32_MAX || p.k_stride > (int64_t)UINT32_MAX) return 0;
-  const int step_r = (int)group_rows((uint32_t)p.nc) * group_steps(p.D / 2, wide ? 16 : 0);
+  const int step_r = (int)group_rows((uint32_t)p.nc, group_steps(p.nc, p.D / 2, wide ? 16 : 0));
   const int64_t groups = (p.Hq + step_r - 1) / step_r + (p.Hkv + step_r - 1) / step_r;
   const int64_t blocks = (compact ? compact_rows : p.T) * groups;
   // < 2^26 workgroups: the dispatch limit, and the range of fastdiv::div
@@ -1029,7 +1087,7 @@ int32_t launch_typed(void* q, void* k, PosSource ps, RopeParams& p, int32_t byte
                                           ps.cu_valid ? compact_rows : -1, bytes == 16);
   if (group_blocks == 0) ps.cu_valid = nullptr;
   if (group_blocks > 0) {
-    const int step_r = (int)group_rows((uint32_t)p.nc) * group_steps(p.D / 2, bytes);
+    const int step_r = (int)group_rows((uint32_t)p.nc, group_steps(p.nc, p.D / 2, bytes));
     p.gq = (uint32_t)((p.Hq + step_r - 1) / step_r);
     p.gk = (uint32_t)((p.Hkv + step_r - 1) / step_r);
     p.nc_shift = 0;

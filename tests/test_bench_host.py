@@ -122,8 +122,16 @@ def test_staged_head_sizes():
         steps = 2 if D == 512 else 1  # half rows of more than 128 elements: two row steps
         assert bench.group_steps(w) == steps
         assert bench.rope_kernel_instance(w, False).endswith(f"ELb{int(staged)}ELi{steps}E")
-    # 11 chunks or more that do not divide 64 (too few rows per group): the token kernel
-    for D, dtype in ((192, "bf16"), (96, "f32"), (384, "bf16"), (176, "bf16")):
+    # 11 to 15 chunks per half row: the staged instance with two steps
+    for D, dtype, nc, rows in ((176, "bf16", 11, 11), (192, "bf16", 12, 10), (96, "f32", 12, 10),
+                               (208, "f16", 13, 8), (224, "bf16", 14, 8), (240, "bf16", 15, 8)):
+        w = _shape(1024, 32, 8, D=D, dtype=dtype)
+        assert bench.chunks_per_half_row(w) == nc and bench.rope_kernel_name(w, 0) == "rope_qk_group_kernel"
+        assert bench.staged_geometry(w) and bench.group_steps(w) == 2, D
+        assert bench.rows_per_workgroup(w) == rows, D
+        assert bench.rope_kernel_instance(w, False).endswith("ELb1ELi2E")
+    # more chunks that do not divide 64 (too few rows even with two steps): the token kernel
+    for D, dtype in ((272, "bf16"), (384, "bf16"), (176, "f32"), (320, "bf16")):
         w = _shape(1024, 32, 8, D=D, dtype=dtype)
         assert bench.rope_kernel_name(w, 0) == "rope_qk_kernel", D
     # D = 100 in bf16: 100-byte half rows, 4-byte chunks, nc = 25: the token kernel
@@ -140,22 +148,27 @@ def test_group_rows_whole_lines(tmp_path):
     group_rows (compiled from its source with g++), bench.py's mirror and a brute
     force over the definition agree for every nc; D = 112 and 48 take aligned groups,
     D = 144 keeps 7 rows."""
-    def brute(nc):
-        whole = [r for r in range(64 // nc, 0, -1) if (r * nc * 32) % 128 == 0]
-        return whole[0] if whole and whole[0] * nc >= 48 else 64 // nc
+    def brute(nc, steps=1):
+        top = 64 * steps // nc
+        whole = [r for r in range(top, 0, -1) if (r * nc * 32) % 128 == 0]
+        return whole[0] if whole and whole[0] * nc >= 48 * steps else top
     src_text = open(os.path.join(ROOT, "packed_varlen_rotary_rope_amd", "csrc", "rope_qk.hip")).read()
-    i = src_text.index("__host__ __device__ inline uint32_t group_rows(uint32_t nc) {")
+    i = src_text.index("__host__ __device__ inline uint32_t group_rows(uint32_t nc, uint32_t steps = 1) {")
     j = src_text.index("\n}\n", i) + 3
     src = tmp_path / "group_rows.cpp"
     src.write_text("#include <cstdint>\n#include <cstdio>\n#define __host__\n#define __device__\n"
                    + src_text[i:j]
-                   + "int main() { for (uint32_t nc = 1; nc <= 64; ++nc) printf(\"%u\\n\", group_rows(nc)); }\n")
+                   + "int main() { for (uint32_t nc = 1; nc <= 64; ++nc) printf(\"%u %u\\n\", "
+                     "group_rows(nc), group_rows(nc, 2)); }\n")
     exe = tmp_path / "group_rows"
     subprocess.run(["g++", "-O2", "-std=c++17", "-o", str(exe), str(src)], check=True)
     lib = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True,
                                           check=True).stdout.split()]
     for nc in range(1, 65):
-        assert lib[nc - 1] == bench.group_rows(nc) == brute(nc), nc
+        assert lib[2 * (nc - 1)] == bench.group_rows(nc) == brute(nc), nc
+        assert lib[2 * nc - 1] == bench.group_rows(nc, 2) == brute(nc, 2), nc
+    # two steps: D = 192 (nc = 12) 10 rows, D = 144 (nc = 9) 12, D = 512 (nc = 32) 4
+    assert [bench.group_rows(nc, 2) for nc in (9, 11, 12, 13, 15, 32)] == [12, 11, 10, 8, 8, 4]
     assert [bench.group_rows(nc) for nc in (3, 5, 6, 7, 9, 10)] == [20, 12, 10, 8, 7, 6]
     for nc in (1, 2, 4, 8, 16, 32, 64):
         assert bench.group_rows(nc) == 64 // nc
@@ -168,31 +181,37 @@ def test_group_rows_whole_lines(tmp_path):
 
 def test_row_steps(tmp_path):
     """Two row steps per row-group workgroup for half rows of more than 128 elements
-    in 16-byte chunks (D = 512), one otherwise: the library's group_steps (compiled
-    from its source with g++) and bench.py's mirror agree; the grid follows."""
+    in 16-byte chunks (D = 512) and for staged groups of 11 to 15 chunks per half row,
+    one otherwise: the library's group_steps and staged_two_steps (compiled from its
+    source with g++) and bench.py's mirror agree; the grid follows."""
     src_text = open(os.path.join(ROOT, "packed_varlen_rotary_rope_amd", "csrc", "rope_qk.hip")).read()
-    i = src_text.index("int32_t group_steps(int32_t half, int32_t chunk_bytes) {")
-    j = src_text.index("\n}\n", i) + 3
+    parts = []
+    for head in ("bool staged_two_steps(int32_t nc, int32_t chunk_bytes) {",
+                 "int32_t group_steps(int32_t nc, int32_t half, int32_t chunk_bytes) {"):
+        i = src_text.index(head)
+        parts.append(src_text[i:src_text.index("\n}\n", i) + 3])
     src = tmp_path / "group_steps.cpp"
-    src.write_text("#include <cstdint>\n#include <cstdio>\n" + src_text[i:j]
-                   + "int main() { for (int h = 8; h <= 256; h *= 2) for (int b = 2; b <= 16; b *= 2)"
-                   " printf(\"%d %d %d\\n\", h, b, group_steps(h, b)); }\n")
+    src.write_text("#include <cstdint>\n#include <cstdio>\n" + "".join(parts)
+                   + "int main() { for (int nc = 1; nc <= 64; ++nc) for (int h = 8; h <= 256; h *= 2)"
+                   " for (int b = 2; b <= 16; b *= 2)"
+                   " printf(\"%d %d %d %d\\n\", nc, h, b, group_steps(nc, h, b)); }\n")
     exe = tmp_path / "group_steps"
     subprocess.run(["g++", "-O2", "-std=c++17", "-o", str(exe), str(src)], check=True)
     out = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout
     for line in out.split("\n"):
         if not line:
             continue
-        half, cb, steps = (int(x) for x in line.split())
-        assert steps == (2 if cb == 16 and half > 128 else 1), line
+        nc, half, cb, steps = (int(x) for x in line.split())
+        assert steps == (2 if cb == 16 and (half > 128 or 11 <= nc <= 15) else 1), line
     for D, dtype, steps, rows in ((512, "bf16", 2, 4), (512, "f16", 2, 4), (512, "f32", 2, 2),
-                                  (256, "bf16", 1, 4), (256, "f32", 1, 2), (128, "bf16", 1, 8)):
+                                  (256, "bf16", 1, 4), (256, "f32", 1, 2), (128, "bf16", 1, 8),
+                                  (192, "bf16", 2, 10), (176, "f16", 2, 11), (96, "f32", 2, 10)):
         w = _shape(1000, 7, 3, D=D, dtype=dtype)
         assert bench.group_steps(w) == steps and bench.rows_per_workgroup(w) == rows, D
         groups = -(-7 // rows) + -(-3 // rows)
         assert bench.expected_grid_threads(w) == [1000 * groups * 64], (D, dtype)
-    w = _shape(1000, 8, 8, D=512)
-    assert bench.head_geometry(w) == "row-group, 2 rows x 2"
+    assert bench.head_geometry(_shape(1000, 8, 8, D=512)) == "row-group, 2 rows x 2"
+    assert bench.head_geometry(_shape(1000, 16, 16, D=192)) == "staged, 10 rows, 2 steps"
 
 
 def test_kernel_instance_names():
@@ -340,7 +359,7 @@ def test_head_shapes_summary(tmp_path, monkeypatch):
     assert "python R/bench.py --head-shapes" in text
     assert f"kernel_source_sha256_16: {bench.kernel_source_hash()}" in text
     assert any("staged, 8 rows" in ln and " 112 " in ln for ln in body)      # D = 112
-    assert any("token kernel" in ln and " 192 " in ln for ln in body)        # D = 192
+    assert any("staged, 10 rows, 2 steps" in ln and " 192 " in ln for ln in body)  # D = 192
     assert all("80.0%" in ln for ln in body[1:])
 
 

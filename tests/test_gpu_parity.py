@@ -547,8 +547,11 @@ def test_staged_chunk_count(rope, case):
     _check_group_instance(rope, case, "staged")
 
 
-ROW_STEP_CASES = [  # (D, dtype, Hq, Hkv): half rows of more than 128 elements, 2 row steps
+ROW_STEP_CASES = [  # (D, dtype, Hq, Hkv): two row steps per workgroup
     (512, "bf16", 7, 3), (512, "f16", 8, 8), (512, "f32", 5, 3), (512, "bf16", 1, 1),
+    # staged, 11 to 15 chunks per half row
+    (192, "bf16", 13, 3), (176, "f16", 16, 16), (96, "f32", 11, 3), (240, "bf16", 9, 1),
+    (208, "bf16", 8, 8),
 ]
 
 
@@ -556,8 +559,10 @@ ROW_STEP_CASES = [  # (D, dtype, Hq, Hkv): half rows of more than 128 elements, 
                                                       for c in ROW_STEP_CASES])
 def test_row_steps(rope, case):
     """The row-group kernel with two row steps per workgroup (D = 512: 4 rows per
-    workgroup in 16-bit storage, 2 in fp32; head counts that end inside a step and
-    inside a group): the same checks as the staged instance."""
+    workgroup in 16-bit storage, 2 in fp32; the staged instance at 11 to 15 chunks
+    per half row: 11 rows for D = 176, 10 for D = 192 and fp32 D = 96, 8 for D = 208
+    and 240; head counts that end inside a step and inside a group): the same checks
+    as the staged instance."""
     _check_group_instance(rope, case, "row steps")
 
 
@@ -1246,6 +1251,7 @@ COMPACT_EDGE = [
     ("bf16_no_seqused", "bf16", 128, 4, 2, {"no_seqused": True}),
     ("bf16_D80_staged", "bf16", 80, 4, 2, {}),       # nc = 5: the staged row-group instance
     ("bf16_D512_steps", "bf16", 512, 5, 3, {}),      # two row steps per workgroup
+    ("bf16_D192_staged_steps", "bf16", 192, 5, 3, {}),  # staged, two steps
     ("bf16_D100_fallback", "bf16", 100, 4, 2, {}),   # 4-byte chunks, nc = 25: the seqused launch
     ("bf16_valid_short", "bf16", 128, 4, 2, {"valid_delta": -100}),
     ("bf16_cv_wide", "bf16", 128, 4, 2, {"cv_gap": 9}),
