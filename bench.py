@@ -1163,13 +1163,14 @@ def size_sweep(rope, dev, n_steps: int) -> dict:
 # Head shapes beside the Qwen3 batches: (Hq, Hkv, D, dtype), one sequence of
 # HEAD_SHAPE_TOKENS tokens each. D = 128 with the Qwen3-1.7B (16 + 8), 4B/8B (32 + 8),
 # 14B (40 + 8) and 32B (64 + 8) head counts; the staged head sizes (half rows that
-# are not whole 128-byte lines), D = 192 on the token kernel, the long half rows
+# are not whole 128-byte lines, with one or two row steps), the long half rows
 # D = 256 and 512, and the other storage types.
 HEAD_SHAPES = [
     (16, 8, 128, "bf16"), (32, 8, 128, "bf16"), (40, 8, 128, "bf16"), (64, 8, 128, "bf16"),
     (32, 32, 32, "bf16"), (32, 32, 48, "bf16"), (32, 32, 64, "bf16"), (64, 8, 64, "bf16"),
     (32, 32, 80, "bf16"), (32, 32, 96, "bf16"), (32, 8, 96, "bf16"), (32, 32, 112, "bf16"),
     (32, 8, 112, "bf16"), (16, 16, 144, "bf16"), (16, 16, 160, "bf16"), (16, 16, 192, "bf16"),
+    (32, 8, 192, "bf16"), (16, 16, 224, "bf16"),
     (16, 16, 256, "bf16"), (16, 8, 256, "bf16"), (8, 8, 512, "bf16"),
     (32, 8, 128, "f16"), (32, 8, 128, "f32"), (32, 8, 64, "f32"),
 ]

@@ -118,10 +118,10 @@ int32_t rope_qk_bwd(void* dq, void* dk, int64_t T, int32_t Hq, int32_t Hkv, int3
  *                   (padded layouts skip many rows, which that geometry passes over
  *                   more cheaply; rope_qk_apply_padded spends nothing on them) or
  *                   when the row layout or the grid size rules the row groups out
- *                   (e.g. D = 192 in 16-bit storage: 12 chunks of 16 bytes per half
+ *                   (e.g. D = 384 in 16-bit storage: 24 chunks of 16 bytes per half
  *                   row, too few rows per group; half rows that are not whole
- *                   128-byte lines with at most 10 such chunks, e.g. D = 64, 80, 96,
- *                   move through LDS in whole lines instead).
+ *                   128-byte lines with at most 15 such chunks, e.g. D = 64, 80, 96,
+ *                   192, move through LDS in whole lines instead).
  *                   1..1024: each 64-lane wave rotates this many consecutive
  *                   tokens, one at a time, all Q and K heads of each, evaluating
  *                   each token's cos/sin once. Results do not depend on it.
