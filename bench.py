@@ -1220,11 +1220,11 @@ def write_head_shapes_summary(json_path: str, command: str) -> None:
     """profiles/rope_qk_head_shapes.txt from the JSON line of bench.py --head-shapes."""
     with open(json_path) as fh:
         js = json.loads([ln for ln in fh if ln.startswith("{")][-1])
-    lines = [f"{'heads':>7s} {'D':>4s} {'dtype':>5s} {'geometry':>22s} {'launches':>8s} "
+    lines = [f"{'heads':>7s} {'D':>4s} {'dtype':>5s} {'geometry':>24s} {'launches':>8s} "
              f"{'pass us':>9s} {'GB/s':>6s} {'% peak':>7s} {'torch neg_ us':>14s} {'ratio':>6s}"]
     for r in js["rows"]:
         lines.append(f"{str(r['Hq']) + '+' + str(r['Hkv']):>7s} {r['D']:4d} {r['dtype']:>5s} "
-                     f"{r['geometry']:>22s} {r['launches_per_pass']:8d} {r['avg_pass_us']:9.2f} "
+                     f"{r['geometry']:>24s} {r['launches_per_pass']:8d} {r['avg_pass_us']:9.2f} "
                      f"{r['GBps']:6.0f} {100 * r['frac']:6.1f}% {r['torch_inplace_us']:14.2f} "
                      f"{r['frac_of_ceiling']:6.3f}")
     text = "\n".join([
