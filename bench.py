@@ -156,10 +156,10 @@ def staged_geometry(w: workloads.Workload) -> bool:
 def group_rows(nc: int, steps: int = 1) -> int:
     """Head rows per row group (the library's group_rows): 64 * steps // nc, rounded
     down to whole 128-byte lines of 16-byte chunks (rows * nc a multiple of 4) when
-    that keeps at least 48 lanes per step busy."""
+    that keeps at least 5/8 of the 64 * steps lane slots busy."""
     r = 64 * steps // nc
     a = r & ~3 if nc & 1 else r & ~1 if (nc & 3) == 2 else r
-    return a if a * nc >= 48 * steps else r
+    return a if 8 * a * nc >= 5 * 64 * steps else r
 
 
 def group_steps(w: workloads.Workload) -> int:

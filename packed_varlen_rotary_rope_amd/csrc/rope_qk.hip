@@ -422,21 +422,22 @@ __device__ inline void store_chunk_through(T* p, const Chunk<T, VEC>& c) {
   }
 }
 
-// Rows per group for nc chunks per half row: the 64 / nc rows whose chunk pairs
-// the 64 lanes hold, rounded down to a group of whole 128-byte lines when at least
-// 48 lanes stay busy (16-byte chunks, the one size whose groups can end inside a
-// line: rows * nc a multiple of 4). A group that
-// ends inside a line shares it with the next group, which runs on another XCC, and
-// the two partial writes of that line cost more than the idle lanes: D = 112 in
-// bf16 (nc = 7) as 8 rows of 224 bytes (14 lines) instead of 9 ran 10-21% faster
-// (interleaved, bit-identical; 32 + 32 heads, 16384 tokens: 92.2 -> 72.7 us per
-// pass), D = 48 (nc = 3, 20 rows instead of 21) 4-11%. For nc = 9 (D = 144) the
-// aligned group is 4 rows, 36 busy lanes, which measured 18-20% slower than 7.
-// Other nc give whole lines already.
+// Rows per group for nc chunks per half row and `steps` row steps: the 64 * steps
+// / nc rows whose chunk pairs the lanes hold, rounded down to a group of whole
+// 128-byte lines when at least 5/8 of the 64 * steps lane slots stay busy (16-byte
+// chunks, the one size whose groups can end inside a line: rows * nc a multiple of
+// 4). A group that ends inside a line shares it with the next group, which runs on
+// another XCC, and the two partial writes of that line cost more than the idle
+// lanes: D = 112 in bf16 (nc = 7) as 8 rows of 224 bytes (14 lines) instead of 9 ran
+// 10-21% faster (interleaved, bit-identical; 32 + 32 heads, 16384 tokens: 92.2 ->
+// 72.7 us per pass), D = 48 (nc = 3, 20 rows instead of 21) 4-11%, and with two
+// steps D = 176 (nc = 11, 8 rows instead of 11, 88 of 128 slots) 8-18%. For nc = 9
+// (D = 144) the aligned one-step group is 4 rows, 36 busy lanes, which measured
+// 18-20% slower than 7. Other nc give whole lines already.
 __host__ __device__ inline uint32_t group_rows(uint32_t nc, uint32_t steps = 1) {
   const uint32_t r = 64u * steps / nc;
   const uint32_t a = (nc & 1u) != 0 ? r & ~3u : (nc & 3u) == 2u ? r & ~1u : r;
-  return a * nc >= 48u * steps ? a : r;
+  return 8u * a * nc >= 5u * 64u * steps ? a : r;
 }
 
 // ---- the default geometry: one wave per (token, row group) --------------------------
@@ -888,7 +889,7 @@ static_assert(kLdsPerCU / kCapStaged - kGroupStaticLds >= 128 * 16,
 // for 11 to 15 chunks per half row, which one step would leave at 4 or 5 rows per
 // group. Against the token kernel these head sizes took before (interleaved,
 // bit-identical, 16384 tokens, two boxes, per pass): in bf16, 16 + 16 heads, D = 176
-// 79.4-79.6 -> 66.2-66.7 us (58% -> 69% of 8 TB/s), D = 192 74.0-74.1 -> 68.8-69.2
+// 79.4-79.6 -> 66.2-66.7 us (58% -> 69% of 8 TB/s; 60.0 us, 77%, with 8 rows, above), D = 192 74.0-74.1 -> 68.8-69.2
 // (68% -> 73%), D = 208 105.2 -> 68.1 (52% -> 80%), D = 224 101.3 -> 74.3, D = 240
 // 111.2 -> 79.9; D = 192 with 32 + 8 heads 95.7-95.9 -> 77.4-78.8 (66% -> 80-81%);
 // fp32 D = 96, 32 + 8 heads, 95.2 -> 78.5 (66% -> 80%). For 10 chunks or fewer two

@@ -560,8 +560,7 @@ ROW_STEP_CASES = [  # (D, dtype, Hq, Hkv): two row steps per workgroup
 def test_row_steps(rope, case):
     """The row-group kernel with two row steps per workgroup (D = 512: 4 rows per
     workgroup in 16-bit storage, 2 in fp32; the staged instance at 11 to 15 chunks
-    per half row: 11 rows for D = 176, 10 for D = 192 and fp32 D = 96, 8 for D = 208
-    and 240; head counts that end inside a step and inside a group): the same checks
+    per half row: 10 rows for D = 192 and fp32 D = 96, 8 for D = 176, 208 and 240; head counts that end inside a step and inside a group): the same checks
     as the staged instance."""
     _check_group_instance(rope, case, "row steps")
 
