@@ -1170,7 +1170,7 @@ HEAD_SHAPES = [
     (32, 32, 32, "bf16"), (32, 32, 48, "bf16"), (32, 32, 64, "bf16"), (64, 8, 64, "bf16"),
     (32, 32, 80, "bf16"), (32, 32, 96, "bf16"), (32, 8, 96, "bf16"), (32, 32, 112, "bf16"),
     (32, 8, 112, "bf16"), (16, 16, 144, "bf16"), (16, 16, 160, "bf16"), (16, 16, 192, "bf16"),
-    (32, 8, 192, "bf16"), (16, 16, 224, "bf16"),
+    (16, 16, 176, "bf16"), (32, 8, 192, "bf16"), (16, 16, 224, "bf16"),
     (16, 16, 256, "bf16"), (16, 8, 256, "bf16"), (8, 8, 512, "bf16"),
     (32, 8, 128, "f16"), (32, 8, 128, "f32"), (32, 8, 64, "f32"),
 ]
